@@ -1,0 +1,130 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module only draws random numbers and rounds them to fp16/bf16 bit
+patterns. It holds none of the GEMM or epilogue arithmetic, and it is the only
+code that both the HIP path's callers and the oracle's callers use.
+
+Recipe (one numpy PCG64 generator per workload, seeded from the workload):
+  1. draw A, then B, then bias, in that order, as float32;
+     N(0, v) means variance v (so std sqrt(v)); U(-1, 1) is uniform on [-1, 1);
+  2. scale in float32;
+  3. round to the storage type with round-to-nearest-even (numpy's float16
+     cast for fp16; the top-16-bit RNE rule for bf16).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest, ties to even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f16":
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    raise ValueError(dtype)
+
+
+def _draw(rng: np.random.Generator, shape, dist: str, scale: float) -> np.ndarray:
+    if dist == "normal":
+        x = rng.standard_normal(shape, dtype=np.float32)
+    elif dist == "uniform":
+        x = rng.random(shape, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
+    else:
+        raise ValueError(dist)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    return x
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    dtype: str              # "f16" | "bf16"
+    act: str                # "none" | "relu" | "sigmoid" | "gelu"
+    bias: bool
+    seed: int
+    a_dist: str = "normal"
+    a_std: float = 1.0
+    b_dist: str = "normal"
+    b_std: float = 1.0
+    bias_dist: str = "normal"
+    bias_std: float = 1.0
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    def with_act(self, act: str) -> "Workload":
+        return dataclasses.replace(self, act=act)
+
+
+# The five workloads: shapes, dtypes, distributions and epilogues as stated for
+# this library's validation and benchmark set.
+WORKLOADS = {
+    # 256^3 fp16, A,B ~ N(0,1); plain GEMM, then bias ~ N(0,1) + erf-GELU.
+    "c1_plain": Workload("c1_plain", 256, 256, 256, "f16", "none", False, 1),
+    "c1_gelu": Workload("c1_gelu", 256, 256, 256, "f16", "gelu", True, 1),
+    # 1024^3 fp16 ~ N(0,1), no epilogue (the pages' demo GEMM shape).
+    "c2_plain": Workload("c2_plain", 1024, 1024, 1024, "f16", "none", False, 2),
+    # 4096^3 fp16 ~ N(0,1)/sqrt(2), bias ~ N(0,1), erf-GELU: the headline workload.
+    "c3_gelu": Workload("c3_gelu", 4096, 4096, 4096, "f16", "gelu", True, 3,
+                        a_std=1 / math.sqrt(2), b_std=1 / math.sqrt(2)),
+    # Ragged 3000x5120x1000 fp16 ~ U(-1,1), bias ~ U(-1,1), ReLU and sigmoid.
+    "c4_relu": Workload("c4_relu", 3000, 5120, 1000, "f16", "relu", True, 4,
+                        a_dist="uniform", b_dist="uniform", bias_dist="uniform"),
+    "c4_sigmoid": Workload("c4_sigmoid", 3000, 5120, 1000, "f16", "sigmoid", True, 4,
+                           a_dist="uniform", b_dist="uniform", bias_dist="uniform"),
+    # LLM-MLP shape, bf16: A ~ N(0,1), B ~ N(0,1/K), bias ~ N(0,0.02), erf-GELU.
+    "c5_gelu": Workload("c5_gelu", 16384, 14336, 4096, "bf16", "gelu", True, 5,
+                        b_std=1 / math.sqrt(4096), bias_std=math.sqrt(0.02)),
+}
+
+
+def make_inputs(w: Workload, M: Optional[int] = None, N: Optional[int] = None,
+                K: Optional[int] = None):
+    """Return (A, B, bias) as uint16 bit arrays; bias is None when w.bias is False.
+
+    M/N/K override the workload's sizes (same distributions, same seed) for
+    reduced-size parity cases.
+    """
+    M = w.M if M is None else M
+    N = w.N if N is None else N
+    K = w.K if K is None else K
+    rng = np.random.default_rng(w.seed)
+    A = to_bits(_draw(rng, (M, K), w.a_dist, w.a_std), w.dtype)
+    B = to_bits(_draw(rng, (K, N), w.b_dist, w.b_std), w.dtype)
+    bias = to_bits(_draw(rng, (N,), w.bias_dist, w.bias_std), w.dtype) if w.bias else None
+    return A, B, bias
+
+
+def random_bits(shape, dtype: str, seed: int, dist: str = "normal", scale: float = 1.0):
+    rng = np.random.default_rng(seed)
+    return to_bits(_draw(rng, shape, dist, scale), dtype)
+
+
+def sample_rows(M: int, n: int = 64, seed: int = 0) -> np.ndarray:
+    """n distinct rows in [0, M), always holding 0 and M-1, sorted."""
+    if M <= n:
+        return np.arange(M, dtype=np.int64)
+    rng = np.random.default_rng(10_000 + seed)
+    picked = set([0, M - 1])
+    cand = rng.permutation(np.arange(1, M - 1))
+    for c in cand:
+        if len(picked) >= n:
+            break
+        picked.add(int(c))
+    return np.array(sorted(picked), dtype=np.int64)

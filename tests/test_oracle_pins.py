@@ -1,0 +1,461 @@
+"""Pins for the CPU oracle: facts that do not come from the oracle itself.
+
+Each test checks one part of oracle/gemm_oracle.c against something fixed
+independently of it: exact rational arithmetic on tiny inputs, closed forms
+(identity, permutation, zero, rank-1, exact integers), numpy's float16 cast and
+float64 matmul, mpmath's arbitrary-precision erf/exp, and tabulated values in
+tests/golden/. They are chosen so that a dropped term, a wrong index, a
+transposed operand, a wrong sign or a misplaced bias fails at least one of
+them (test_oracle_mutants.py plants such mistakes and checks exactly that).
+"""
+from fractions import Fraction
+import math
+import os
+
+import mpmath
+import numpy as np
+import pytest
+
+import oracle
+from oracle import compare
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+mpmath.mp.dps = 40
+
+
+def f16(vals):
+    return np.asarray(vals, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+# ---------------------------------------------------------------- decoders --
+
+F16_KNOWN = {
+    0x0000: 0.0, 0x3C00: 1.0, 0xBC00: -1.0, 0x4000: 2.0, 0xC000: -2.0,
+    0x3800: 0.5, 0x3555: 0.333251953125, 0x7BFF: 65504.0, 0x0400: 2.0 ** -14,
+    0x0001: 2.0 ** -24, 0x03FF: 1023 * 2.0 ** -24, 0x7C00: math.inf,
+    0xFC00: -math.inf, 0x4248: 3.140625,
+}
+BF16_KNOWN = {
+    0x0000: 0.0, 0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0x4049: 3.140625,
+    0x3EAB: 0.333984375, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127, 0x0080: 2.0 ** -126,
+    0x0001: 2.0 ** -133, 0x7F80: math.inf, 0xFF80: -math.inf,
+}
+
+
+def test_decode_f16_known_bit_patterns(orc):
+    bits = np.array(list(F16_KNOWN), dtype=np.uint16)
+    got = orc.decode(bits, "f16")
+    assert list(got) == list(F16_KNOWN.values())
+    assert math.copysign(1.0, orc.decode(np.array([0x8000], np.uint16), "f16")[0]) == -1.0
+
+
+def test_decode_bf16_known_bit_patterns(orc):
+    bits = np.array(list(BF16_KNOWN), dtype=np.uint16)
+    assert list(orc.decode(bits, "bf16")) == list(BF16_KNOWN.values())
+
+
+def test_decode_f16_all_patterns_match_numpy(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.decode(bits, "f16")
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_decode_bf16_all_patterns_are_top_half_of_float32(orc):
+    # bfloat16 is by definition the upper 16 bits of an IEEE binary32.
+    bits = np.arange(65536, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        ref = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    got = orc.decode(bits.astype(np.uint16), "bf16")
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+# ---------------------------------------------------------------- encoders --
+
+def test_encode_f16_matches_numpy_rne(orc):
+    rng = np.random.default_rng(7)
+    x = np.concatenate([
+        rng.standard_normal(200_000) * np.exp2(rng.integers(-30, 17, 200_000)),
+        [0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e9, -1e9, 2.0 ** -25, 2.0 ** -25 * 1.0001,
+         3 * 2.0 ** -26, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 2.0 ** -14 - 2.0 ** -25],
+    ])
+    got = orc.encode(x, "f16")
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)   # numpy: float64 -> half, RNE
+    assert np.array_equal(got, ref)
+
+
+def test_encode_f16_ties_go_to_even(orc):
+    # 1 + 2^-11 is exactly half-way between 1 and 1 + 2^-10: even is 1.0.
+    # 1 + 3*2^-11 is half-way between 1+2^-10 (odd) and 1+2^-9 (even).
+    got = orc.encode([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 2.0 ** -25, 3 * 2.0 ** -25], "f16")
+    assert list(got) == [0x3C00, 0x3C02, 0x0000, 0x0002]
+
+
+def _nearest_bf16_exact(x: float) -> int:
+    """Brute force: the bf16 pattern nearest to x, ties to even, in exact rationals."""
+    fx = Fraction(x)
+    cand = []
+    base = int((np.array([x], np.float32).view(np.uint32)[0] >> 16))
+    for b in range(max(base - 2, 0), min(base + 3, 0x7F80)):
+        v = Fraction((np.array([b << 16], np.uint32).view(np.float32)[0]).item())
+        cand.append((abs(v - fx), b & 1, b))
+    cand.sort()
+    return cand[0][2]
+
+
+def test_encode_bf16_against_exact_rational_nearest(orc):
+    rng = np.random.default_rng(11)
+    x = np.abs(rng.standard_normal(3000) * np.exp2(rng.integers(-40, 40, 3000)))
+    # exact ties: midpoints between adjacent bf16 values
+    lo = rng.integers(0x3000, 0x5000, 200).astype(np.uint32)
+    mids = ((lo << 16).view(np.float32).astype(np.float64)
+            + ((lo + 1) << 16).view(np.float32).astype(np.float64)) / 2
+    x = np.concatenate([x, mids])
+    got = orc.encode(x, "bf16")
+    want = np.array([_nearest_bf16_exact(float(v)) for v in x], dtype=np.uint16)
+    assert np.array_equal(got, want)
+    assert np.array_equal(orc.encode(-x, "bf16"), want | 0x8000)
+
+
+def test_encode_decode_round_trip_every_finite_pattern(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for dt, expmask in (("f16", 0x7C00), ("bf16", 0x7F80)):
+        finite = bits[(bits & expmask) != expmask]
+        back = orc.encode(orc.decode(finite, dt), dt)
+        assert np.array_equal(back, finite), dt
+
+
+def test_encode_overflow_to_inf(orc):
+    assert list(orc.encode([65520.0, -70000.0], "f16")) == [0x7C00, 0xFC00]
+    big = (2 - 2.0 ** -8) * 2.0 ** 127      # half-way above bf16's max: rounds to inf
+    assert list(orc.encode([big, -big], "bf16")) == [0x7F80, 0xFF80]
+
+
+# ------------------------------------------------------------- epilogues --
+
+def _golden_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "erf_phi_table.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].split()
+            if line:
+                rows.append((line[0], float(line[1]), float(line[2])))
+    return rows
+
+
+def test_golden_table_is_consistent_with_mpmath():
+    for kind, x, v in _golden_table():
+        ref = mpmath.erf(x) if kind == "erf" else mpmath.ncdf(x)
+        assert abs(float(ref) - v) < 2e-16 * max(1, abs(v)) * 4, (kind, x, v)
+
+
+def test_gelu_matches_tabulated_phi(orc):
+    for kind, x, v in _golden_table():
+        if kind == "phi":
+            got = orc.act([x, -x], "gelu")
+            assert got[0] == pytest.approx(x * v, rel=1e-14, abs=0)
+            assert got[1] == pytest.approx(-x * (1 - v), rel=1e-12, abs=0)
+        else:
+            # erf(x) = 2 Phi(x sqrt2) - 1 = 2 GELU(x sqrt2) / (x sqrt2) - 1
+            z = x * math.sqrt(2)
+            assert 2 * orc.act([z], "gelu")[0] / z - 1 == pytest.approx(v, rel=1e-14)
+
+
+def test_gelu_closed_forms(orc):
+    assert orc.act([0.0], "gelu")[0] == 0.0
+    assert orc.act([1.0], "gelu")[0] == pytest.approx(0.8413447460685429, rel=1e-15)
+    x = np.linspace(-12, 12, 2401)
+    g = orc.act(x, "gelu")
+    gm = orc.act(-x, "gelu")
+    # Phi(-z) = 1 - Phi(z)  =>  GELU(-x) = GELU(x) - x
+    assert np.all(np.abs(gm - (g - x)) <= 4e-15 * np.maximum(1, np.abs(x)))
+    big = x >= 10
+    np.testing.assert_array_equal(g[big], x[big])   # Phi(10) = 1 - 7.6e-24
+
+
+def test_gelu_dense_grid_against_mpmath(orc):
+    x = np.concatenate([np.linspace(-40, 40, 4001), np.geomspace(1e-300, 1e3, 500)])
+    x = np.concatenate([x, -x])
+    got = orc.act(x, "gelu")
+    ref = np.array([float(mpmath.mpf(v) * mpmath.ncdf(v)) for v in x])
+    # Deep in the left tail Phi(z) ~ exp(-z^2/2): the rounding of z/sqrt(2) alone
+    # is amplified by ~z^2, so the relative bound grows as (1 + z^2) * 1e-15.
+    rel = np.abs(got - ref) / np.maximum(np.abs(ref), 1e-300)
+    assert np.all(rel <= np.maximum(1e-13, (1 + x * x) * 1e-15))
+
+
+def test_sigmoid_closed_forms_and_mpmath(orc):
+    assert orc.act([0.0], "sigmoid")[0] == 0.5
+    assert orc.act([math.log(3.0)], "sigmoid")[0] == pytest.approx(0.75, rel=1e-15)
+    x = np.linspace(-700, 700, 7001)
+    s = orc.act(x, "sigmoid")
+    np.testing.assert_allclose(s + orc.act(-x, "sigmoid"), 1.0, rtol=0, atol=2.3e-16)
+    ref = np.array([float(1 / (1 + mpmath.exp(-mpmath.mpf(v)))) for v in x])
+    np.testing.assert_allclose(s, ref, rtol=1e-14, atol=0)
+
+
+def test_relu_and_identity(orc):
+    x = np.linspace(-5, 5, 1001)
+    r = orc.act(x, "relu")
+    np.testing.assert_array_equal(r - orc.act(-x, "relu"), x)
+    np.testing.assert_array_equal(r, np.where(x > 0, x, 0.0))
+    np.testing.assert_array_equal(orc.act(x, "none"), x)
+
+
+# ------------------------------------------------------------ GEMM core ----
+
+def _hand_gemm():
+    d = {}
+    with open(os.path.join(GOLDEN, "hand_gemm.txt")) as f:
+        for line in f:
+            t = line.split("#", 1)[0].split()
+            if t:
+                d[t[0]] = [float(v) for v in t[1:]]
+    A = np.array(d["A"][2:]).reshape(int(d["A"][0]), int(d["A"][1]))
+    B = np.array(d["B"][2:]).reshape(int(d["B"][0]), int(d["B"][1]))
+    return A, B, np.array(d["bias"]), d
+
+
+def test_hand_worked_example(orc):
+    A, B, bias, d = _hand_gemm()
+    a, b, bb = f16(A), f16(B), f16(bias)
+    np.testing.assert_array_equal(orc.gemm_bias_act(a, b, None, "none").ravel(), d["none"])
+    np.testing.assert_array_equal(orc.gemm_bias_act(a, b, bb, "none").ravel(), d["zb"])
+    np.testing.assert_array_equal(orc.gemm_bias_act(a, b, bb, "relu").ravel(), d["relu"])
+    for act in ("sigmoid", "gelu"):
+        np.testing.assert_allclose(orc.gemm_bias_act(a, b, bb, act).ravel(), d[act],
+                                   rtol=1e-14, atol=1e-30)
+
+
+def _fraction_gemm(Av, Bv, biasv):
+    M, K = Av.shape
+    N = Bv.shape[1]
+    out = np.empty((M, N), dtype=object)
+    for i in range(M):
+        for j in range(N):
+            s = sum((Fraction(Av[i, k]) * Fraction(Bv[k, j]) for k in range(K)), Fraction(0))
+            if biasv is not None:
+                s += Fraction(biasv[j])
+            out[i, j] = s
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 5, 7), (7, 4, 9), (5, 6, 1), (4, 3, 33)])
+def test_gemm_equals_exact_rational_sum(orc, dtype, shape):
+    M, N, K = shape
+    A = synth.random_bits((M, K), dtype, 100 + M)
+    B = synth.random_bits((K, N), dtype, 200 + N)
+    bias = synth.random_bits((N,), dtype, 300 + K)
+    Av, Bv, bv = orc.decode(A, dtype), orc.decode(B, dtype), orc.decode(bias, dtype)
+    exact = _fraction_gemm(Av, Bv, bv)
+    got, S = orc.gemm_bias_act(A, B, bias, "none", dtype, with_abs=True)
+    for i in range(M):
+        for j in range(N):
+            # fp64 summation error <= (K+1) * 2^-53 * sum|terms| (textbook bound)
+            bound = (K + 1) * 2.0 ** -53 * S[i, j]
+            assert abs(Fraction(got[i, j]) - exact[i, j]) <= Fraction(bound), (i, j)
+            sabs = sum(abs(Fraction(Av[i, k]) * Fraction(Bv[k, j])) for k in range(K))
+            assert S[i, j] == pytest.approx(float(sabs + abs(Fraction(bv[j]))), rel=1e-14)
+
+
+def test_identity_and_permutation(orc):
+    K, N = 48, 40
+    B = synth.random_bits((K, N), "f16", 5)
+    eye = f16(np.eye(K))
+    np.testing.assert_array_equal(orc.gemm_bias_act(eye, B, None), orc.decode(B))
+    perm = np.random.default_rng(3).permutation(K)
+    P = f16(np.eye(K)[perm])
+    np.testing.assert_array_equal(orc.gemm_bias_act(P, B, None), orc.decode(B)[perm])
+    # right-multiplication by a permutation permutes columns
+    A = synth.random_bits((12, K), "f16", 6)
+    Q = f16(np.eye(K)[:, perm])
+    np.testing.assert_array_equal(orc.gemm_bias_act(A, Q, None), orc.decode(A)[:, perm])
+
+
+def test_zero_matrix_gives_activation_of_bias_per_column(orc):
+    M, N, K = 5, 9, 16
+    Z = f16(np.zeros((M, K)))
+    B = synth.random_bits((K, N), "f16", 8)
+    bias = synth.random_bits((N,), "f16", 9)
+    bv = orc.decode(bias)
+    for act in ("none", "relu", "sigmoid", "gelu"):
+        got = orc.gemm_bias_act(Z, B, bias, act)
+        want = np.broadcast_to(orc.act(bv, act), (M, N))
+        np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(orc.gemm_bias_act(Z, B, None, "gelu"), 0.0)
+    # K == 0: the empty sum
+    got = orc.gemm_bias_act(np.zeros((M, 0), np.uint16), np.zeros((0, N), np.uint16), bias)
+    np.testing.assert_array_equal(got, np.broadcast_to(bv, (M, N)))
+
+
+def test_rank_one_closed_form(orc):
+    M, N, K = 7, 11, 40
+    a = np.arange(M) - 3.0
+    b = np.arange(N) * 0.5 - 2.0
+    A = f16(np.repeat(a[:, None], K, axis=1))
+    B = f16(np.repeat(b[None, :], K, axis=0))
+    np.testing.assert_array_equal(orc.gemm_bias_act(A, B, None), K * np.outer(a, b))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_exact_integers_match_integer_matmul(orc, dtype):
+    rng = np.random.default_rng(21)
+    M, N, K = 37, 29, 301
+    Ai = rng.integers(-2, 3, (M, K))
+    Bi = rng.integers(-2, 3, (K, N))
+    biasi = rng.integers(-8, 9, N)
+    to = (lambda v: f16(v)) if dtype == "f16" else (lambda v: synth.to_bits(v.astype(np.float32), "bf16"))
+    got = orc.gemm_bias_act(to(Ai), to(Bi), to(biasi), "none", dtype)
+    np.testing.assert_array_equal(got, (Ai @ Bi + biasi).astype(np.float64))
+    relu = orc.gemm_bias_act(to(Ai), to(Bi), to(biasi), "relu", dtype)
+    np.testing.assert_array_equal(relu, np.maximum(Ai @ Bi + biasi, 0).astype(np.float64))
+
+
+def test_linearity_in_A(orc):
+    rng = np.random.default_rng(4)
+    A1 = rng.integers(-3, 4, (9, 20))
+    A2 = rng.integers(-3, 4, (9, 20))
+    B = f16(rng.integers(-3, 4, (20, 13)))
+    np.testing.assert_array_equal(orc.gemm_bias_act(f16(A1 + A2), B, None),
+                                  orc.gemm_bias_act(f16(A1), B, None)
+                                  + orc.gemm_bias_act(f16(A2), B, None))
+
+
+def test_transpose_identity(orc):
+    A = synth.random_bits((19, 33), "f16", 12)
+    B = synth.random_bits((33, 26), "f16", 13)
+    C = orc.gemm_bias_act(A, B, None)
+    Ct = orc.gemm_bias_act(np.ascontiguousarray(B.T), np.ascontiguousarray(A.T), None)
+    np.testing.assert_array_equal(C, Ct.T)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_mid_size_against_numpy_float64_matmul(orc, dtype):
+    M, N, K = 96, 80, 130
+    A = synth.random_bits((M, K), dtype, 31)
+    B = synth.random_bits((K, N), dtype, 32)
+    bias = synth.random_bits((N,), dtype, 33)
+    Av, Bv, bv = orc.decode(A, dtype), orc.decode(B, dtype), orc.decode(bias, dtype)
+    got, S = orc.gemm_bias_act(A, B, bias, "none", dtype, with_abs=True)
+    ref = Av @ Bv + bv
+    assert np.all(np.abs(got - ref) <= 2 * (K + 1) * 2.0 ** -53 * S)
+    np.testing.assert_allclose(S, np.abs(Av) @ np.abs(Bv) + np.abs(bv), rtol=1e-13)
+    # the epilogue is applied per element after the sum
+    for act in ("relu", "sigmoid", "gelu"):
+        np.testing.assert_array_equal(orc.gemm_bias_act(A, B, bias, act, dtype),
+                                      orc.act(got, act))
+
+
+def test_sampled_rows_equal_full_rows(orc):
+    w = synth.WORKLOADS["c1_gelu"]
+    A, B, bias = synth.make_inputs(w, M=300, N=64, K=96)
+    full = orc.gemm_bias_act(A, B, bias, "gelu")
+    rows = synth.sample_rows(300, 20, seed=1)
+    np.testing.assert_array_equal(orc.gemm_bias_act(A, B, bias, "gelu", rows=rows), full[rows])
+
+
+def test_thread_count_does_not_change_bits(orc):
+    A = synth.random_bits((70, 64), "bf16", 41)
+    B = synth.random_bits((64, 50), "bf16", 42)
+    r1 = orc.gemm_bias_act(A, B, None, "gelu", "bf16", nthreads=1)
+    r7 = orc.gemm_bias_act(A, B, None, "gelu", "bf16", nthreads=7)
+    np.testing.assert_array_equal(r1, r7)
+
+
+def test_oracle_rejects_bad_arguments(orc):
+    A = np.zeros((4, 5), np.uint16)
+    with pytest.raises(ValueError):
+        orc.gemm_bias_act(A, np.zeros((6, 3), np.uint16), None)
+    with pytest.raises(ValueError):
+        orc.gemm_bias_act(A, np.zeros((5, 3), np.uint16), np.zeros(4, np.uint16))
+    with pytest.raises(ValueError):
+        orc.gemm_bias_act(A, np.zeros((5, 3), np.uint16), None, rows=[4])
+
+
+# -------------------------------------------------------- unfused half --
+
+def test_bias_act_oracle_elementwise(orc):
+    X = synth.random_bits((33, 24), "f16", 51, scale=3.0)
+    bias = synth.random_bits((24,), "f16", 52)
+    xv, bv = orc.decode(X), orc.decode(bias)
+    for act in ("none", "relu", "sigmoid", "gelu"):
+        got = orc.bias_act(X, bias, act)
+        z = xv + bv
+        if act == "none":
+            want = z
+        elif act == "relu":
+            want = np.maximum(z, 0)
+        elif act == "sigmoid":
+            want = np.array([float(1 / (1 + mpmath.exp(-mpmath.mpf(v)))) for v in z.ravel()])
+        else:
+            want = np.array([float(mpmath.mpf(v) * mpmath.ncdf(v)) for v in z.ravel()])
+        np.testing.assert_allclose(got.ravel(), np.ravel(want), rtol=1e-14, atol=1e-300)
+    np.testing.assert_array_equal(orc.bias_act(X, None, "none"), xv)
+
+
+# ------------------------------------------------------ tolerance checker --
+
+def test_ulp_out_values():
+    np.testing.assert_array_equal(compare.ulp_out([1.0, 1.5, 2.0, 1000.0, 0.0, 2.0 ** -20], "f16"),
+                                  [2.0 ** -10, 2.0 ** -10, 2.0 ** -9, 0.5, 2.0 ** -24, 2.0 ** -24])
+    np.testing.assert_array_equal(compare.ulp_out([1.0, 3.0, 0.0], "bf16"),
+                                  [2.0 ** -7, 2.0 ** -6, 2.0 ** -133])
+
+
+def test_checker_flags_planted_errors():
+    rng = np.random.default_rng(0)
+    R = rng.standard_normal((64, 64)) * 8
+    C = np.asarray(R).astype(np.float16).astype(np.float64)
+    S = np.abs(R) + 1
+    ok = compare.check(C, R, K=64, dtype="f16", act=0, S=S)
+    assert ok["ok"] and ok["strict_ok"] and ok["max_ulp"] <= 0.5
+    bad = C.copy()
+    bad[3, 5] += 4 * compare.ulp_out(R[3, 5], "f16") + 0.01   # one element off
+    rep = compare.check(bad, R, K=64, dtype="f16", act=0, S=S)
+    assert not rep["strict_ok"] and rep["worst"]["index"] == [3, 5]
+    swapped = C[:, ::-1]                                       # columns mixed up
+    assert not compare.check(swapped, R, K=64, dtype="f16")["ok"]
+    nan = C.copy()
+    nan[0, 0] = np.nan
+    assert not compare.check(nan, R, K=64, dtype="f16")["ok"]
+
+
+# ---------------------------------------------------------- generators --
+
+def test_generators_are_deterministic_and_shaped():
+    w = synth.WORKLOADS["c4_relu"]
+    a1, b1, c1 = synth.make_inputs(w, M=64, N=72, K=40)
+    a2, b2, c2 = synth.make_inputs(w, M=64, N=72, K=40)
+    assert a1.shape == (64, 40) and b1.shape == (40, 72) and c1.shape == (72,)
+    assert np.array_equal(a1, a2) and np.array_equal(b1, b2) and np.array_equal(c1, c2)
+    v = a1.view(np.float16).astype(np.float64)
+    assert v.min() >= -1 and v.max() <= 1
+
+
+def test_generator_moments(orc):
+    w = synth.WORKLOADS["c5_gelu"]
+    A, B, bias = synth.make_inputs(w, M=256, N=512, K=4096)
+    assert w.dtype == "bf16"
+    b = orc.decode(B, "bf16")
+    assert abs(b.std() - 1 / 64) < 2e-4 and abs(b.mean()) < 2e-4
+    assert abs(orc.decode(bias, "bf16").std() - math.sqrt(0.02)) < 0.01
+    a = orc.decode(A, "bf16")
+    assert abs(a.std() - 1) < 0.01
+    w3 = synth.WORKLOADS["c3_gelu"]
+    A3, _, _ = synth.make_inputs(w3, M=128, N=8, K=1024)
+    assert abs(orc.decode(A3).std() - 1 / math.sqrt(2)) < 0.01
+
+
+def test_sample_rows():
+    r = synth.sample_rows(16384, 64, seed=5)
+    assert len(r) == 64 and len(set(r.tolist())) == 64
+    assert r[0] == 0 and r[-1] == 16383 and np.all(np.diff(r) > 0)
+    assert np.array_equal(synth.sample_rows(40, 64), np.arange(40))
