@@ -1,0 +1,246 @@
+"""Benchmark of the fused GEMM + bias + GELU on one MI355X.
+
+    python bench.py [--steps 50] [--warmup 10] [--workload c3_gelu] [--unfused]
+
+One step is one gemm_bias_act call over the whole workload (schedule choice,
+global->LDS loads, MFMA main loop, fused epilogue, store), with inputs already
+resident in HBM. W untimed steps, then K timed steps between two device
+synchronisations. Per-launch HIP events on the launch stream give the kernel's
+average duration (the roofline's "achieved") and the median, the pages' bench
+protocol (10 warmups, 50 reps, median latency by device events).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}   # dense, 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+METRIC = "TFLOP/s fused fp16 GEMM+bias+GELU at 4096³; % of MI355X fp16 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tiled_dense_gemm_bias_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".hip", ".hpp")):
+            h.update(fn.encode())
+            h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    rec = data.get(workload)
+    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    per = [s.elapsed_time(e) for s, e in ev]
+    return wall_ms, per
+
+
+def cpu_baseline(w, A, B, bias, got_bits, target_s=12.0):
+    """The fp64 oracle on a bounded sample of rows, timed on the host cores."""
+    import oracle
+    from oracle import compare
+    import synth
+
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    rows = synth.sample_rows(w.M, 16, seed=w.seed)
+    t0 = time.perf_counter()
+    oracle.gemm_bias_act(A, B, bias, w.act, w.dtype, rows=rows, nthreads=cores)
+    t_probe = time.perf_counter() - t0
+    n = int(min(w.M, max(16, 16 * target_s / max(t_probe, 1e-3))))
+    n = max(16, (n // cores) * cores if n > cores else n)
+    rows = synth.sample_rows(w.M, n, seed=w.seed)
+    t0 = time.perf_counter()
+    R, S = oracle.gemm_bias_act(A, B, bias, w.act, w.dtype, rows=rows, nthreads=cores,
+                                with_abs=True)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * w.N * w.K
+    rep = compare.check(oracle.decode(got_bits[rows], w.dtype), R, K=w.K, dtype=w.dtype,
+                        act=oracle.ACTS[w.act], S=S)
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d output rows of %dx%dx%d %s %s (fp64 triple loop, %.1f s)"
+                      % (len(rows), w.M, w.M, w.N, w.K, w.dtype, w.act, dt)}
+    parity = {k: rep[k] for k in ("ok", "strict_ok", "rel_frobenius", "max_abs", "max_ulp")}
+    parity["rows"] = len(rows)
+    return base, parity
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3_gelu")
+    ap.add_argument("--unfused", action="store_true", help="also time gemm + bias_act")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tune", action="store_true", help="autotune before timing")
+    ap.add_argument("--schedule", default=None, help="force bm,bn,bk,wm,wn[,raster,group_m]")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain device copy of the workload's C size (counter scaling)")
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1:
+        print("bench.py measures one GPU: this build runs the fused GEMM on a single MI355X "
+              "(no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import tiled_dense_gemm_bias_amd as gba
+
+    if not os.path.exists(gba.LIB_PATH):
+        from tiled_dense_gemm_bias_amd import build as gba_build
+        gba_build.build()
+
+    w = synth.WORKLOADS[a.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[bench] generating %s inputs %dx%dx%d %s" % (w.name, w.M, w.N, w.K, w.dtype))
+    A, B, bias = synth.make_inputs(w)
+    tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+
+    def dev_t(bits):
+        return None if bits is None else torch.from_numpy(bits.view(np.int16)).view(tdt).to(dev)
+
+    a_t, b_t, bias_t = dev_t(A), dev_t(B), dev_t(bias)
+    c_t = torch.empty((w.M, w.N), dtype=tdt, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if a.copy_calibration:
+        src = torch.empty((w.M, w.N), dtype=tdt, device=dev).fill_(1.0)
+        for _ in range(a.warmup + a.steps):
+            c_t.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: %d copies of %d bytes" % (a.warmup + a.steps,
+                                                                   c_t.numel() * 2))
+        return 0
+
+    if a.schedule:
+        f = [int(x) for x in a.schedule.split(",")]
+        keys = ["bm", "bn", "bk", "wm", "wn", "raster", "group_m"]
+        sched = dict(zip(keys, f))
+        sched.setdefault("raster", 1)
+        sched.setdefault("group_m", 4)
+        sched["stages"] = 2
+        gba.set_schedule(sched)
+    elif a.tune:
+        best, ms = gba.autotune(a_t, b_t, bias_t, c_t, w.act, all_groups=True)
+        log("[bench] autotune best %s %.4f ms" % (best, ms))
+    sched = gba.get_schedule(w.M, w.N, w.K, w.act, w.dtype)
+    log("[bench] schedule %s" % sched)
+
+    def step():
+        gba.gemm_bias_act(a_t, b_t, bias_t, c_t, w.act)
+
+    wall_ms, per = time_launches(step, a.steps, a.warmup, stream)
+    ms_per_step = wall_ms / a.steps
+    kern_avg = sum(per) / len(per)
+    kern_med = statistics.median(per)
+    flops = float(w.flops)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kern_avg * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[w.dtype]
+    alg_bytes = (w.M * w.K + w.K * w.N + w.M * w.N + (w.N if w.bias else 0)) * 2
+    log("[bench] %d steps: %.4f ms/step wall, kernel avg %.4f ms, median %.4f ms -> %.1f TFLOP/s"
+        " (%.1f%% of peak)" % (a.steps, ms_per_step, kern_avg, kern_med, achieved,
+                               100 * achieved / peak))
+    got_bits = c_t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": "%s: C = %s(A.B + bias), M=%d N=%d K=%d, %s in/out, fp32 accumulate"
+                               % (w.name, w.act, w.M, w.N, w.K, w.dtype),
+                   "M": w.M, "N": w.N, "K": w.K, "act": w.act, "bias": w.bias,
+                   "schedule": sched, "flop_model": "2*M*N*K (epilogue not counted)"},
+        "median_ms": round(kern_med, 5),
+        "pct_of_peak": round(100 * achieved / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(w.name),
+                     "algorithmic_bytes": alg_bytes, "kernel_avg_ms": round(kern_avg, 5)},
+    }
+
+    if a.unfused:
+        t_t = torch.empty_like(c_t)
+        y_t = torch.empty_like(c_t)
+        _, per_g = time_launches(lambda: gba.gemm(a_t, b_t, t_t), a.steps, a.warmup, stream)
+        _, per_b = time_launches(lambda: gba.bias_act(t_t, bias_t, y_t, w.act), a.steps,
+                                 a.warmup, stream)
+        g_ms, b_ms = statistics.median(per_g), statistics.median(per_b)
+        ba_bytes = 2 * w.M * w.N * 2 + (w.N * 2 if w.bias else 0)
+        out["unfused"] = {
+            "gemm_ms": round(g_ms, 5), "bias_act_ms": round(b_ms, 5),
+            "total_ms": round(g_ms + b_ms, 5), "fused_ms": round(kern_med, 5),
+            "speedup_fused": round((g_ms + b_ms) / kern_med, 3),
+            "bias_act_GBps": round(ba_bytes / (b_ms * 1e-3) / 1e9, 1),
+            "bias_act_frac_hbm_peak": round(ba_bytes / (b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "hbm_bytes_saved": 2 * w.M * w.N * 2,
+        }
+        log("[bench] unfused: gemm %.4f ms + bias_act %.4f ms (%.0f GB/s) vs fused %.4f ms"
+            % (g_ms, b_ms, out["unfused"]["bias_act_GBps"], kern_med))
+
+    if not a.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a row sample")
+        base, parity = cpu_baseline(w, A, B, bias, got_bits)
+        out["cpu_baseline"] = base
+        out["parity_sampled"] = parity
+        log("[bench] cpu baseline %.4f TFLOP/s on %d threads; parity %s"
+            % (base["value"], base["cores"], parity))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

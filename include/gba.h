@@ -1,0 +1,145 @@
+/*
+ * gba.h -- C ABI of the MI355X (gfx950) fused GEMM + bias + activation library.
+ *
+ * The operation is the tiled GEMM of "writing-tilelang-kernels" (skillsmp.com),
+ * sections "Kernel Anatomy" and "GEMM (Minimal)": A is (M,K), B is (K,N), C is
+ * (M,N), all row-major, fp16 inputs, float accumulator in registers, one write
+ * of C. "TileLang: Write, Autotune, and Ship Fused Tensor-Core Kernels from
+ * Python" (saipien.org), section "Why tile-level control matters", adds the
+ * fused epilogue: a bias add and an activation applied while the accumulator
+ * is still in registers, so the M x N intermediate never goes back to HBM.
+ *
+ * Conventions shared by every entry point:
+ *   - All array arguments are DEVICE pointers owned by the caller. The library
+ *     allocates nothing on the compute path and keeps no pointer after a call.
+ *   - Layouts are dense row-major with leading dimensions K (A), N (B, C, X, Y).
+ *   - dtype (gba_dtype) applies to A, B, bias and C alike; accumulation is fp32.
+ *   - Pointers must be 16-byte aligned, and K and N multiples of 8 (the 16-byte
+ *     row-alignment rule of "writing-tilelang-kernels", Common Pitfalls);
+ *     otherwise GBA_ERR_ALIGN. M is arbitrary.
+ *   - M == 0 or N == 0: nothing to do, GBA_OK, no launch. K == 0: the empty
+ *     sum, C = act(bias) (or act(0)). Negative sizes: GBA_ERR_SHAPE.
+ *   - Argument errors are reported synchronously, before any launch. Work is
+ *     enqueued on the calling thread's stream (gba_set_stream) and runs
+ *     asynchronously; a device fault surfaces at the caller's next sync.
+ *   - A launch failure returns GBA_ERR_HIP; gba_last_hip_error() gives the code.
+ *   - The device must be gfx950 (MI355X/MI350X); otherwise GBA_ERR_DEVICE.
+ */
+#ifndef GBA_H
+#define GBA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GBA_DTYPE_F16 = 0, GBA_DTYPE_BF16 = 1 } gba_dtype;
+
+/* Epilogue activations. ReLU and sigmoid: "writing-tilelang-kernels",
+ * Pre-flight Checklist ("ReLU/sigmoid epilogue after GEMM") and Key API
+ * Patterns (T.max, T.sigmoid). GELU: "TileLang: Write, Autotune, and Ship Fused
+ * Tensor-Core Kernels from Python", Why tile-level control matters; this
+ * library uses the erf form, GELU(z) = z * Phi(z) = 0.5 z (1 + erf(z/sqrt2)). */
+typedef enum {
+    GBA_ACT_NONE = 0,
+    GBA_ACT_RELU = 1,    /* max(z, 0) */
+    GBA_ACT_SIGMOID = 2, /* 1 / (1 + exp(-z)) */
+    GBA_ACT_GELU = 3     /* z * Phi(z), erf form */
+} gba_act;
+
+typedef enum {
+    GBA_OK = 0,
+    GBA_ERR_NULL = 1,     /* a required pointer is NULL */
+    GBA_ERR_SHAPE = 2,    /* negative or too-large size */
+    GBA_ERR_DTYPE = 3,    /* dtype not a gba_dtype */
+    GBA_ERR_ACT = 4,      /* act not a gba_act */
+    GBA_ERR_ALIGN = 5,    /* pointer not 16-byte aligned, or K / N not a multiple of 8 */
+    GBA_ERR_ALIAS = 6,    /* output overlaps an input it may not overlap */
+    GBA_ERR_DEVICE = 7,   /* no HIP device, or not gfx950 */
+    GBA_ERR_HIP = 8,      /* a HIP runtime call failed; see gba_last_hip_error() */
+    GBA_ERR_SCHEDULE = 9, /* schedule not among the compiled-in ones */
+    GBA_ERR_CACHE = 10    /* schedule cache could not be written (tuning still done) */
+} gba_status;
+
+/* A GEMM schedule: one compiled-in kernel instance plus its launch mapping.
+ * bm x bn is the output tile of one workgroup, bk the K depth of one LDS stage,
+ * wm x wn the grid of 64-lane waves over the tile, stages the LDS ring depth.
+ * raster 0 maps workgroup ids to tiles row by row; raster 1 first gathers the
+ * tiles each of the 8 XCDs runs into one contiguous block, then walks them in
+ * groups of group_m tile rows so that neighbouring workgroups share A and B
+ * panels in that XCD's L2 ("use_swizzle ... L2 cache locality",
+ * "writing-tilelang-kernels", Key API Patterns). */
+typedef struct {
+    int32_t bm, bn, bk;
+    int32_t wm, wn;
+    int32_t stages;
+    int32_t raster;
+    int32_t group_m;
+} gba_schedule;
+
+/* C = act(A.B + bias).
+ * A: [M,K], B: [K,N], bias: [N] or NULL (no bias), C: [M,N], all `dtype`.
+ * act: gba_act. C must not overlap A, B or bias (GBA_ERR_ALIAS). */
+int gemm_bias_act(const void *A, const void *B, const void *bias, void *C, int64_t M,
+                  int64_t N, int64_t K, int act, int dtype);
+
+/* C = A.B rounded to `dtype`: the first kernel of the unfused pair used as the
+ * HBM-traffic baseline ("TileLang: Write, Autotune, and Ship Fused Tensor-Core
+ * Kernels from Python", Why tile-level control matters: fused vs unfused,
+ * intermediate M x N round trip of 2*M*N*2 bytes). Same rules as gemm_bias_act. */
+int gemm(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype);
+
+/* Y = act(X + bias) elementwise over [M,N]: the second kernel of the unfused
+ * pair (an elementwise 2-D kernel, cf. the "Elementwise (2D)" template of
+ * "writing-tilelang-kernels", Quick Templates). X and Y: [M,N]; bias: [N] or
+ * NULL. Y may equal X exactly (in place) but may not partially overlap it;
+ * Y may not overlap bias. */
+int bias_act(const void *X, const void *bias, void *Y, int64_t M, int64_t N, int act,
+             int dtype);
+
+/* Stream for this thread's later calls (a hipStream_t); NULL = default stream. */
+int gba_set_stream(void *hip_stream);
+
+/* Force a schedule for this thread's later GEMM calls (NULL: back to the cache
+ * or the built-in heuristic). GBA_ERR_SCHEDULE if no compiled-in kernel has
+ * this (bm, bn, bk, wm, wn, stages), or raster/group_m are out of range. */
+int gba_set_schedule(const gba_schedule *s);
+
+/* The schedule a gemm_bias_act call with these arguments would use now. */
+int gba_get_schedule(int64_t M, int64_t N, int64_t K, int act, int dtype, gba_schedule *out);
+
+/* Compiled-in kernel instances: count, and the i-th one (raster/group_m are
+ * their defaults). */
+int gba_num_schedules(void);
+int gba_list_schedule(int i, gba_schedule *out);
+
+/* Autotuner ("TileLang: Write, Autotune, and Ship Fused Tensor-Core Kernels from
+ * Python", section Autotuning): for every compiled-in instance whose LDS ring
+ * (bm*bk + bk*bn) * 2 * stages fits the 160 KiB LDS of a CU, and each raster
+ * variant, run 10 untimed and 50 timed launches on the caller's buffers, keep
+ * the median time, and pick the fastest. The winner is stored in the on-disk
+ * schedule cache ($GBA_CACHE_DIR, default ~/.cache/gba; disabled by
+ * GBA_DISABLE_CACHE=1) under the key (arch, CU count, library version, dtype,
+ * act, M, N, K), and is used by later calls. C holds the winner's result on
+ * return. flags: bit 0 = also try every raster group size in {1,2,4,8,16}.
+ * best / best_ms may be NULL. Synchronous: it waits for its own launches.
+ * Returns GBA_ERR_CACHE (with best filled) if the cache file could not be
+ * written. */
+int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_t M,
+                 int64_t N, int64_t K, int act, int dtype, int flags, gba_schedule *best,
+                 double *best_ms);
+
+/* Device-side epilogue probe: y[i] = act(z[i]) in fp32, computed by the same
+ * device function the GEMM epilogue uses. z, y: device float arrays of n. */
+int gba_epilogue_probe(const float *z, float *y, int64_t n, int act);
+
+const char *gba_status_string(int status);
+int gba_last_hip_error(void);
+const char *gba_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GBA_H */

@@ -1,0 +1,355 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Bars:
+  * exact-input cases (integer or short-mantissa entries whose every fp32
+    partial sum is exact): bitwise equal to the oracle's rounded result, for
+    every compiled-in schedule, ragged shapes included;
+  * random cases: relative Frobenius <= 2e-2 and |C-R| <= 1e-2*sqrt(K)/64 +
+    1e-2*|R| per element (oracle/compare.py), plus the stricter
+    accumulation-aware 1-ulp gate;
+  * full workload sizes: 64 sampled rows, in the launch configuration the
+    benchmark times (the library's own schedule choice).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import compare
+import synth
+import tiled_dense_gemm_bias_amd as gba
+from tests.gpu_util import empty, say, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+ACTS = ["none", "relu", "sigmoid", "gelu"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    gba.set_schedule(None)
+
+
+def run_gpu(A, B, bias, act, dtype, sched=None):
+    import torch
+    M, K = A.shape
+    N = B.shape[1]
+    a, b, bb = to_dev(A, dtype), to_dev(B, dtype), to_dev(bias, dtype)
+    c = empty((M, N), dtype, fill_bits=0x7E00)   # NaN sentinel: every element must be written
+    gba.set_schedule(sched)
+    try:
+        gba.gemm_bias_act(a, b, bb, c, act)
+    finally:
+        gba.set_schedule(None)
+    torch.cuda.synchronize()
+    return to_bits(c)
+
+
+def schedules():
+    return gba.list_schedules()
+
+
+def sched_id(s):
+    return "%dx%dx%d_w%dx%d" % (s["bm"], s["bn"], s["bk"], s["wm"], s["wn"])
+
+
+# ---------------------------------------------------------- bit-exact ----
+
+def int_inputs(M, N, K, dtype, seed, lo=-1, hi=1, bias=True):
+    rng = np.random.default_rng(seed)
+    enc = (lambda v: v.astype(np.float16).view(np.uint16)) if dtype == "f16" else \
+        (lambda v: synth.to_bits(v.astype(np.float32), "bf16"))
+    A = enc(rng.integers(lo, hi + 1, (M, K)).astype(np.float64))
+    B = enc(rng.integers(lo, hi + 1, (K, N)).astype(np.float64))
+    bv = enc(rng.integers(-8, 9, N).astype(np.float64)) if bias else None
+    return A, B, bv
+
+
+EXACT_SHAPES = [(256, 256, 256), (1, 8, 8), (37, 40, 24), (129, 136, 72), (300, 264, 1000),
+                (520, 776, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", EXACT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_exact_integer_gemm_is_bitwise_for_every_schedule(shape, dtype):
+    M, N, K = shape
+    A, B, bias = int_inputs(M, N, K, dtype, seed=M + N + K)
+    R = oracle.gemm_bias_act(A, B, bias, "none", dtype)
+    want = oracle.encode(R, dtype)
+    for s in schedules():
+        for raster in (0, 1):
+            sch = dict(s, raster=raster)
+            say("exact", shape, dtype, sched_id(s), "raster", raster)
+            got = run_gpu(A, B, bias, "none", dtype, sched=sch)
+            bad = np.argwhere(got != want)
+            assert bad.size == 0, "%s %s: %d mismatches, first %s" % (
+                sched_id(s), raster, len(bad), bad[:3].tolist())
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_exact_relu_epilogue_bitwise(dtype):
+    A, B, bias = int_inputs(200, 136, 520, dtype, seed=9)
+    want = oracle.encode(oracle.gemm_bias_act(A, B, bias, "relu", dtype), dtype)
+    say("exact relu", dtype)
+    assert np.array_equal(run_gpu(A, B, bias, "relu", dtype), want)
+
+
+def test_rounding_is_nearest_even_on_exact_sums():
+    # A in {0, +-1, +-1/2, +-1/4}, B multiples of 2^-10 below 4 in magnitude: every
+    # product is a multiple of 2^-12 and every partial sum stays exact in fp32,
+    # but the totals need rounding to fp16 -- the result is unique.
+    rng = np.random.default_rng(77)
+    M, N, K = 160, 192, 512
+    A = rng.choice([0.0, 1.0, -1.0, 0.5, -0.5, 0.25, -0.25], size=(M, K))
+    B = rng.integers(-4095, 4096, size=(K, N)) / 1024.0
+    Ab = A.astype(np.float16).view(np.uint16)
+    Bb = B.astype(np.float16).view(np.uint16)
+    assert np.array_equal(Bb.view(np.float16).astype(np.float64), B)
+    want = oracle.encode(oracle.gemm_bias_act(Ab, Bb, None, "none", "f16"), "f16")
+    for s in schedules():
+        say("rne", sched_id(s))
+        got = run_gpu(Ab, Bb, None, "none", "f16", sched=dict(s))
+        assert np.array_equal(got, want), sched_id(s)
+
+
+# ----------------------------------------------------- random parity ----
+
+def check_random(A, B, bias, act, dtype, got_bits, rows=None):
+    R, S = oracle.gemm_bias_act(A, B, bias, act, dtype, rows=rows, with_abs=True)
+    C = oracle.decode(got_bits if rows is None else got_bits[rows], dtype)
+    rep = compare.check(C, R, K=A.shape[1], dtype=dtype, act=oracle.ACTS[act], S=S)
+    assert rep["ok"], rep
+    assert rep["strict_ok"], rep
+    return rep
+
+
+@pytest.mark.parametrize("name", ["c1_plain", "c1_gelu", "c2_plain", "c4_relu", "c4_sigmoid"])
+def test_workloads_full_check(name):
+    w = synth.WORKLOADS[name]
+    A, B, bias = synth.make_inputs(w)
+    say("workload", name)
+    got = run_gpu(A, B, bias, w.act, w.dtype)
+    check_random(A, B, bias, w.act, w.dtype, got)
+
+
+def test_c2_at_the_pages_default_tile():
+    # 128x128x32 tiles, 4 waves: the pages' default GEMM starting point.
+    w = synth.WORKLOADS["c2_plain"]
+    A, B, bias = synth.make_inputs(w)
+    sch = {"bm": 128, "bn": 128, "bk": 32, "wm": 2, "wn": 2, "stages": 2, "raster": 1,
+           "group_m": 8}
+    say("c2 128x128x32")
+    check_random(A, B, bias, "none", "f16", run_gpu(A, B, bias, "none", "f16", sched=sch))
+
+
+@pytest.mark.parametrize("name,M,N,K", [("c3_gelu", 512, 768, 4096), ("c5_gelu", 384, 1024, 4096)])
+def test_reduced_size_full_check(name, M, N, K):
+    w = synth.WORKLOADS[name]
+    A, B, bias = synth.make_inputs(w, M=M, N=N, K=K)
+    say("reduced", name, M, N, K)
+    check_random(A, B, bias, w.act, w.dtype, run_gpu(A, B, bias, w.act, w.dtype))
+
+
+@pytest.mark.parametrize("name", ["c3_gelu", "c5_gelu"])
+def test_full_size_sampled_rows(name):
+    w = synth.WORKLOADS[name]
+    A, B, bias = synth.make_inputs(w)
+    rows = synth.sample_rows(w.M, 64, seed=w.seed)
+    say("full", name, gba.get_schedule(w.M, w.N, w.K, w.act, w.dtype))
+    got = run_gpu(A, B, bias, w.act, w.dtype)
+    check_random(A, B, bias, w.act, w.dtype, got, rows=rows)
+    # no element may be left unwritten (the NaN sentinel) or non-finite
+    expmask = 0x7C00 if w.dtype == "f16" else 0x7F80
+    assert not np.any((got & expmask) == expmask)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ACTS)
+def test_every_schedule_ragged_random(act, dtype):
+    M, N, K = 300, 264, 136
+    A = synth.random_bits((M, K), dtype, 1)
+    B = synth.random_bits((K, N), dtype, 2, scale=0.25)
+    bias = synth.random_bits((N,), dtype, 3)
+    R, S = oracle.gemm_bias_act(A, B, bias, act, dtype, with_abs=True)
+    for s in schedules():
+        say("ragged", act, dtype, sched_id(s))
+        got = run_gpu(A, B, bias, act, dtype, sched=dict(s))
+        rep = compare.check(oracle.decode(got, dtype), R, K=K, dtype=dtype,
+                            act=oracle.ACTS[act], S=S)
+        assert rep["ok"] and rep["strict_ok"], (sched_id(s), rep)
+
+
+def test_no_bias_and_k_tail():
+    for (M, N, K) in [(64, 64, 8), (65, 72, 40), (257, 264, 264)]:
+        A = synth.random_bits((M, K), "f16", M)
+        B = synth.random_bits((K, N), "f16", N)
+        say("nobias", M, N, K)
+        check_random(A, B, None, "gelu", "f16", run_gpu(A, B, None, "gelu", "f16"))
+
+
+# ----------------------------------------------------------- edges ----
+
+def test_degenerate_shapes():
+    import torch
+    dt = "f16"
+    bias = synth.random_bits((16,), dt, 5)
+    # K == 0: the empty sum, C = act(bias)
+    for act in ACTS:
+        say("k0", act)
+        got = run_gpu(np.zeros((5, 0), np.uint16), np.zeros((0, 16), np.uint16), bias, act, dt)
+        want = oracle.encode(np.broadcast_to(oracle.act(oracle.decode(bias), act), (5, 16)), dt)
+        assert np.array_equal(got, want), act
+    # M == 0 / N == 0: no work, no error
+    a = torch.zeros(0, 8, dtype=torch.float16, device="cuda")
+    b = torch.zeros(8, 16, dtype=torch.float16, device="cuda")
+    gba.gemm_bias_act(a, b, None, torch.zeros(0, 16, dtype=torch.float16, device="cuda"), "gelu")
+    gba.gemm(b.t().contiguous()[:0], b, torch.zeros(0, 16, dtype=torch.float16, device="cuda"))
+    # single row / column-chunk
+    A = synth.random_bits((1, 8), dt, 1)
+    B = synth.random_bits((8, 8), dt, 2)
+    check_random(A, B, None, "none", dt, run_gpu(A, B, None, "none", dt))
+
+
+def test_writes_stay_inside_C():
+    import torch
+    M, N, K = 133, 200, 96
+    A = synth.random_bits((M, K), "f16", 1)
+    B = synth.random_bits((K, N), "f16", 2)
+    guard = 4096
+    buf = torch.full((M * N + 2 * guard,), 7.0, dtype=torch.float16, device="cuda")
+    c = buf[guard:guard + M * N].view(M, N)
+    say("guard band")
+    gba.gemm_bias_act(to_dev(A, "f16"), to_dev(B, "f16"), None, c, "none")
+    torch.cuda.synchronize()
+    assert bool((buf[:guard] == 7.0).all()) and bool((buf[guard + M * N:] == 7.0).all())
+    check_random(A, B, None, "none", "f16", to_bits(c))
+
+
+def test_run_to_run_bitwise_determinism():
+    w = synth.WORKLOADS["c4_sigmoid"]
+    A, B, bias = synth.make_inputs(w)
+    say("determinism")
+    r1 = run_gpu(A, B, bias, w.act, w.dtype)
+    r2 = run_gpu(A, B, bias, w.act, w.dtype)
+    assert np.array_equal(r1, r2)
+
+
+def test_non_default_stream():
+    import torch
+    A = synth.random_bits((256, 512), "bf16", 1)
+    B = synth.random_bits((512, 384), "bf16", 2)
+    bias = synth.random_bits((384,), "bf16", 3)
+    s = torch.cuda.Stream()
+    a, b, bb = to_dev(A, "bf16"), to_dev(B, "bf16"), to_dev(bias, "bf16")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        c = empty((256, 384), "bf16")
+        say("stream")
+        gba.gemm_bias_act(a, b, bb, c, "gelu")
+    s.synchronize()
+    check_random(A, B, bias, "gelu", "bf16", to_bits(c))
+
+
+# ---------------------------------------------------- unfused pair ----
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ACTS)
+def test_bias_act_against_oracle_on_its_input(act, dtype):
+    import torch
+    M, N = 333, 1032
+    X = synth.random_bits((M, N), dtype, 11, scale=4.0)
+    bias = synth.random_bits((N,), dtype, 12)
+    x, bb = to_dev(X, dtype), to_dev(bias, dtype)
+    y = empty((M, N), dtype, fill_bits=0x7E00)
+    say("bias_act", act, dtype)
+    gba.bias_act(x, bb, y, act)
+    torch.cuda.synchronize()
+    R = oracle.bias_act(X, bias, act, dtype)
+    got = oracle.decode(to_bits(y), dtype)
+    # one fp32 add, the activation, one rounding: within 1 ulp of the exact value
+    err = np.abs(got - R)
+    assert np.all(err <= compare.ulp_out(R, dtype) + 2.0 ** -22), float(err.max())
+    # in place
+    gba.bias_act(x, bb, x, act)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(x), to_bits(y))
+
+
+def test_unfused_pair_matches_oracle_and_fused():
+    import torch
+    w = synth.WORKLOADS["c4_relu"]
+    A, B, bias = synth.make_inputs(w, M=700, N=1024, K=1000)
+    a, b, bb = to_dev(A, "f16"), to_dev(B, "f16"), to_dev(bias, "f16")
+    for act in ("relu", "sigmoid", "gelu"):
+        t = empty((700, 1024), "f16")
+        y = empty((700, 1024), "f16")
+        f = empty((700, 1024), "f16")
+        say("unfused", act)
+        gba.gemm(a, b, t)
+        gba.bias_act(t, bb, y, act)
+        gba.gemm_bias_act(a, b, bb, f, act)
+        torch.cuda.synchronize()
+        T = to_bits(t)
+        check_random(A, B, None, "none", "f16", T)
+        # second kernel pinned on the intermediate it actually read
+        Ry = oracle.bias_act(T, bias, act, "f16")
+        Y = oracle.decode(to_bits(y), "f16")
+        assert np.all(np.abs(Y - Ry) <= compare.ulp_out(Ry, "f16") + 2.0 ** -22)
+        # the unfused result carries one extra rounding of the intermediate
+        check_random(A, B, bias, act, "f16", to_bits(f))
+        rep = compare.check(Y, oracle.decode(to_bits(f), "f16"), K=1000, dtype="f16")
+        assert rep["ok"], rep
+
+
+# ------------------------------------------------------ epilogue code ----
+
+@pytest.mark.parametrize("act", ACTS)
+def test_epilogue_device_functions_on_dense_grid(act):
+    import torch
+    z = np.concatenate([np.linspace(-12, 12, 200001), np.geomspace(1e-6, 80, 4000)])
+    z = np.concatenate([z, -z]).astype(np.float32)
+    zt = torch.from_numpy(z).cuda()
+    yt = torch.empty_like(zt)
+    say("epilogue", act)
+    gba.epilogue_probe(zt, yt, act)
+    torch.cuda.synchronize()
+    y = yt.cpu().numpy().astype(np.float64)
+    ref = oracle.act(z.astype(np.float64), act)
+    err = np.abs(y - ref)
+    if act in ("none", "relu"):
+        assert np.array_equal(y, ref)
+    elif act == "sigmoid":
+        # hardware exp2 and reciprocal, each within a couple of fp32 ulps
+        assert np.all(err <= 1e-6 * np.abs(ref) + 1e-37), float((err / np.abs(ref)).max())
+    else:
+        # erfc fit with fractional error < 1.2e-7, evaluated in fp32
+        assert np.all(err <= 2e-6 * np.abs(ref) + 1e-37), float((err / (np.abs(ref) + 1e-30)).max())
+
+
+# ------------------------------------------------------------ tuner ----
+
+def test_autotune_writes_cache_and_is_used(tmp_path, monkeypatch):
+    import json
+    import torch
+    monkeypatch.setenv("GBA_CACHE_DIR", str(tmp_path))
+    M, N, K = 512, 512, 256
+    A = synth.random_bits((M, K), "f16", 1)
+    B = synth.random_bits((K, N), "f16", 2)
+    bias = synth.random_bits((N,), "f16", 3)
+    a, b, bb = to_dev(A, "f16"), to_dev(B, "f16"), to_dev(bias, "f16")
+    c = empty((M, N), "f16")
+    say("autotune")
+    best, ms = gba.autotune(a, b, bb, c, "gelu")
+    torch.cuda.synchronize()
+    assert ms > 0
+    check_random(A, B, bias, "gelu", "f16", to_bits(c))
+    data = json.load(open(tmp_path / "schedules.json"))
+    assert data["format"] == "gba-schedule-cache" and data["version"] == 1
+    keys = [e["key"] for e in data["entries"]]
+    assert any(k.endswith("|f16|gelu|512|512|256") for k in keys)
+    assert gba.get_schedule(M, N, K, "gelu", "f16") == best

@@ -1,0 +1,262 @@
+"""Python binding of libgba, the gfx950 fused GEMM + bias + activation library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libgba.so (see include/gba.h for the C ABI). PyTorch supplies device
+memory and the current stream. There is no fallback: if libgba.so is missing
+or the device is not a gfx950, the calls raise.
+
+    import torch, tiled_dense_gemm_bias_amd as gba
+    c = torch.empty(M, N, dtype=torch.float16, device="cuda")
+    gba.gemm_bias_act(a, b, bias, c, act="gelu")     # c = gelu(a @ b + bias)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgba.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "gba.h")
+
+ACTS = {"none": 0, "relu": 1, "sigmoid": 2, "gelu": 3}
+STATUS = {
+    0: "GBA_OK", 1: "GBA_ERR_NULL", 2: "GBA_ERR_SHAPE", 3: "GBA_ERR_DTYPE", 4: "GBA_ERR_ACT",
+    5: "GBA_ERR_ALIGN", 6: "GBA_ERR_ALIAS", 7: "GBA_ERR_DEVICE", 8: "GBA_ERR_HIP",
+    9: "GBA_ERR_SCHEDULE", 10: "GBA_ERR_CACHE",
+}
+SCHED_FIELDS = ("bm", "bn", "bk", "wm", "wn", "stages", "raster", "group_m")
+
+
+class GbaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (what, STATUS.get(status, status),
+                                                 _lib().gba_status_string(status).decode()))
+
+
+class Schedule(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in SCHED_FIELDS]
+
+    def as_dict(self) -> dict:
+        return {f: int(getattr(self, f)) for f in SCHED_FIELDS}
+
+    @classmethod
+    def from_dict(cls, d: dict) -> "Schedule":
+        s = cls()
+        defaults = {"stages": 2, "raster": 1, "group_m": 4}
+        for f in SCHED_FIELDS:
+            setattr(s, f, int(d.get(f, defaults.get(f, 0))))
+        return s
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libgba.so is not built; run: python -m tiled_dense_gemm_bias_amd.build")
+        lib = ctypes.CDLL(LIB_PATH)
+        p, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        sig = {
+            "gemm_bias_act": [p, p, p, p, i64, i64, i64, ci, ci],
+            "gemm": [p, p, p, i64, i64, i64, ci],
+            "bias_act": [p, p, p, i64, i64, ci, ci],
+            "gba_set_stream": [p],
+            "gba_set_schedule": [ctypes.POINTER(Schedule)],
+            "gba_get_schedule": [i64, i64, i64, ci, ci, ctypes.POINTER(Schedule)],
+            "gba_num_schedules": [],
+            "gba_list_schedule": [ci, ctypes.POINTER(Schedule)],
+            "gba_autotune": [p, p, p, p, i64, i64, i64, ci, ci, ci, ctypes.POINTER(Schedule),
+                             ctypes.POINTER(ctypes.c_double)],
+            "gba_epilogue_probe": [p, p, i64, ci],
+            "gba_status_string": [ci],
+            "gba_last_hip_error": [],
+            "gba_version": [],
+        }
+        for name, args in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ci
+        lib.gba_status_string.restype = ctypes.c_char_p
+        lib.gba_version.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def lib():
+    """The raw ctypes handle of libgba.so (C ABI of include/gba.h)."""
+    return _lib()
+
+
+def header_functions() -> list:
+    """Names of the functions include/gba.h declares."""
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def version() -> str:
+    return _lib().gba_version().decode()
+
+
+# ------------------------------------------------------------- helpers ----
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return 0
+    if t.dtype == torch.bfloat16:
+        return 1
+    raise TypeError("gba supports float16 and bfloat16 tensors, got %s" % t.dtype)
+
+
+def _check_dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("gba works on device tensors; got a %s tensor" % t.device)
+        if not t.is_contiguous():
+            raise ValueError("gba needs contiguous row-major tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors on different devices: %s and %s" % (dev, t.device))
+    return dev
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _act(act) -> int:
+    if isinstance(act, str):
+        return ACTS[act]
+    return int(act)
+
+
+def _call(fn_name: str, dev, *args):
+    torch = _torch()
+    with torch.cuda.device(dev):
+        lib = _lib()
+        lib.gba_set_stream(ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+        st = getattr(lib, fn_name)(*args)
+    if st != 0:
+        raise GbaError(st, fn_name)
+
+
+# ---------------------------------------------------------------- API ----
+
+def gemm_bias_act(a, b, bias, c, act="gelu"):
+    """c[M,N] = act(a[M,K] @ b[K,N] + bias[N]); bias may be None. Returns c."""
+    dev = _check_dev(a, b, bias, c)
+    dt = _dtype_code(a)
+    for t in (b, bias, c):
+        if t is not None and _dtype_code(t) != dt:
+            raise TypeError("all operands must share one dtype")
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K or tuple(c.shape) != (M, N) or (bias is not None and tuple(bias.shape) != (N,)):
+        raise ValueError("shape mismatch: a%s b%s bias%s c%s" % (
+            tuple(a.shape), tuple(b.shape), None if bias is None else tuple(bias.shape),
+            tuple(c.shape)))
+    _call("gemm_bias_act", dev, _ptr(a), _ptr(b), _ptr(bias), _ptr(c), M, N, K, _act(act), dt)
+    return c
+
+
+def gemm(a, b, c):
+    """c[M,N] = a[M,K] @ b[K,N], rounded to the operand dtype. Returns c."""
+    dev = _check_dev(a, b, c)
+    dt = _dtype_code(a)
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K or tuple(c.shape) != (M, N) or _dtype_code(b) != dt or _dtype_code(c) != dt:
+        raise ValueError("shape or dtype mismatch")
+    _call("gemm", dev, _ptr(a), _ptr(b), _ptr(c), M, N, K, dt)
+    return c
+
+
+def bias_act(x, bias, y, act="gelu"):
+    """y[M,N] = act(x[M,N] + bias[N]) elementwise; y may be x. Returns y."""
+    dev = _check_dev(x, bias, y)
+    dt = _dtype_code(x)
+    M, N = x.shape
+    if tuple(y.shape) != (M, N) or (bias is not None and tuple(bias.shape) != (N,)):
+        raise ValueError("shape mismatch")
+    if _dtype_code(y) != dt or (bias is not None and _dtype_code(bias) != dt):
+        raise TypeError("all operands must share one dtype")
+    _call("bias_act", dev, _ptr(x), _ptr(bias), _ptr(y), M, N, _act(act), dt)
+    return y
+
+
+def epilogue_probe(z, y, act="gelu"):
+    """y = act(z) on float32 device tensors, by the GEMM epilogue's device code."""
+    torch = _torch()
+    dev = _check_dev(z, y)
+    if z.dtype != torch.float32 or y.dtype != torch.float32 or z.numel() != y.numel():
+        raise ValueError("epilogue_probe takes two float32 tensors of one size")
+    _call("gba_epilogue_probe", dev, _ptr(z), _ptr(y), z.numel(), _act(act))
+    return y
+
+
+def set_schedule(sched: Optional[dict]) -> None:
+    """Force a schedule (dict of SCHED_FIELDS) for this thread; None clears it."""
+    lib = _lib()
+    if sched is None:
+        st = lib.gba_set_schedule(None)
+    else:
+        s = Schedule.from_dict(sched)
+        st = lib.gba_set_schedule(ctypes.byref(s))
+    if st != 0:
+        raise GbaError(st, "gba_set_schedule")
+
+
+def get_schedule(M: int, N: int, K: int, act="gelu", dtype="f16") -> dict:
+    s = Schedule()
+    st = _lib().gba_get_schedule(M, N, K, _act(act), 0 if dtype in ("f16", "float16") else 1,
+                                 ctypes.byref(s))
+    if st != 0:
+        raise GbaError(st, "gba_get_schedule")
+    return s.as_dict()
+
+
+def list_schedules() -> list:
+    lib = _lib()
+    out = []
+    for i in range(lib.gba_num_schedules()):
+        s = Schedule()
+        lib.gba_list_schedule(i, ctypes.byref(s))
+        out.append(s.as_dict())
+    return out
+
+
+def autotune(a, b, bias, c, act="gelu", all_groups: bool = False):
+    """Time every compiled-in schedule on these buffers; cache and return the best.
+
+    Returns (schedule dict, median ms). c holds the winner's result.
+    """
+    dev = _check_dev(a, b, bias, c)
+    dt = _dtype_code(a)
+    M, K = a.shape
+    N = b.shape[1]
+    best = Schedule()
+    ms = ctypes.c_double()
+    torch = _torch()
+    with torch.cuda.device(dev):
+        lib = _lib()
+        lib.gba_set_stream(ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+        st = lib.gba_autotune(_ptr(a), _ptr(b), _ptr(bias), _ptr(c), M, N, K, _act(act), dt,
+                              1 if all_groups else 0, ctypes.byref(best), ctypes.byref(ms))
+    if st not in (0, 10):
+        raise GbaError(st, "gba_autotune")
+    return best.as_dict(), ms.value

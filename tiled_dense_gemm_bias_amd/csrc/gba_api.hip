@@ -1,0 +1,571 @@
+// C ABI of the fused GEMM + bias + activation library (declared in gba.h):
+// argument checks, device check, schedule choice (forced, on-disk cache, or
+// heuristic), kernel launch, the autotuner and its schedule cache.
+#include <errno.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+#include <sys/stat.h>
+#include <unistd.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "gba.h"
+#include "gba_kernels.hpp"
+#include "gba_registry.hpp"
+
+#define GBA_VERSION_STRING "0.1.0"
+
+namespace gba {
+extern const ScheduleEntry s_256x256x64_w2x2;
+extern const ScheduleEntry s_256x256x64_w2x4;
+extern const ScheduleEntry s_256x128x64_w2x2;
+extern const ScheduleEntry s_128x256x64_w2x2;
+extern const ScheduleEntry s_128x128x64_w2x2;
+extern const ScheduleEntry s_128x128x32_w2x2;
+}  // namespace gba
+
+namespace {
+
+using gba::ScheduleEntry;
+
+const ScheduleEntry *const kTable[] = {
+    &gba::s_256x256x64_w2x2, &gba::s_256x256x64_w2x4, &gba::s_256x128x64_w2x2,
+    &gba::s_128x256x64_w2x2, &gba::s_128x128x64_w2x2, &gba::s_128x128x32_w2x2,
+};
+constexpr int kNumTable = sizeof(kTable) / sizeof(kTable[0]);
+constexpr long long kLdsBytes = 160 * 1024;
+
+thread_local hipStream_t t_stream = nullptr;
+thread_local bool t_forced = false;
+thread_local gba_schedule t_forced_sched;
+thread_local int t_last_hip = 0;
+
+bool log_enabled() {
+    static int v = -1;
+    if (v < 0) {
+        const char *e = getenv("GBA_LOG");
+        v = (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
+    }
+    return v == 1;
+}
+
+int hip_fail(hipError_t e) {
+    t_last_hip = (int)e;
+    return GBA_ERR_HIP;
+}
+
+// ------------------------------------------------------------- device ----
+
+struct DeviceInfo {
+    bool checked = false;
+    bool ok = false;
+    int cus = 0;
+    std::string arch;
+};
+
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+// GBA_OK when the current device is a gfx950; fills *info.
+int current_device(const DeviceInfo **info) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        t_last_hip = (int)e;
+        return GBA_ERR_DEVICE;
+    }
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DeviceInfo &d = g_dev[dev];
+    if (!d.checked) {
+        hipDeviceProp_t p;
+        e = hipGetDeviceProperties(&p, dev);
+        d.checked = true;
+        if (e == hipSuccess) {
+            d.arch = p.gcnArchName;
+            d.cus = p.multiProcessorCount;
+            d.ok = d.arch.compare(0, 6, "gfx950") == 0;
+        } else {
+            (void)hipGetLastError();
+            t_last_hip = (int)e;
+        }
+        if (log_enabled())
+            fprintf(stderr, "[gba] device %d arch=%s cus=%d supported=%d\n", dev, d.arch.c_str(),
+                    d.cus, (int)d.ok);
+    }
+    *info = &d;
+    return d.ok ? GBA_OK : GBA_ERR_DEVICE;
+}
+
+// ------------------------------------------------------------ argument checks --
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
+    if (!a || !b || an == 0 || bn == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+int check_enums(int act, int dtype) {
+    if (dtype != GBA_DTYPE_F16 && dtype != GBA_DTYPE_BF16) return GBA_ERR_DTYPE;
+    if (act < GBA_ACT_NONE || act > GBA_ACT_GELU) return GBA_ERR_ACT;
+    return GBA_OK;
+}
+
+// Shared checks of the GEMM entry points. *nothing is set when there is no work.
+int check_gemm_args(const void *A, const void *B, const void *bias, const void *C, int64_t M,
+                    int64_t N, int64_t K, int act, int dtype, bool *nothing) {
+    int s = check_enums(act, dtype);
+    if (s) return s;
+    if (M < 0 || N < 0 || K < 0) return GBA_ERR_SHAPE;
+    // 32-bit tile arithmetic inside the kernel: per-tile offsets stay below 2^31.
+    if (M > 0x7fffffffLL || N > (1LL << 24) || K > (1LL << 23)) return GBA_ERR_SHAPE;
+    *nothing = (M == 0 || N == 0);
+    if (*nothing) return GBA_OK;
+    if (!C) return GBA_ERR_NULL;
+    if (K > 0 && (!A || !B)) return GBA_ERR_NULL;
+    if ((K % 8) || (N % 8)) return GBA_ERR_ALIGN;
+    if (!aligned16(C) || (A && !aligned16(A)) || (B && !aligned16(B)) ||
+        (bias && !aligned16(bias)))
+        return GBA_ERR_ALIGN;
+    const size_t cb = (size_t)M * N * 2;
+    if (overlaps(C, cb, A, (size_t)M * K * 2) || overlaps(C, cb, B, (size_t)K * N * 2) ||
+        overlaps(C, cb, bias, (size_t)N * 2))
+        return GBA_ERR_ALIAS;
+    return GBA_OK;
+}
+
+// ------------------------------------------------------------ schedules ----
+
+int find_entry(const gba_schedule &s) {
+    for (int i = 0; i < kNumTable; ++i) {
+        const gba_schedule &t = kTable[i]->sched;
+        if (t.bm == s.bm && t.bn == s.bn && t.bk == s.bk && t.wm == s.wm && t.wn == s.wn &&
+            t.stages == s.stages)
+            return i;
+    }
+    return -1;
+}
+
+bool sched_valid(const gba_schedule &s) {
+    if (find_entry(s) < 0) return false;
+    if (s.raster != 0 && s.raster != 1) return false;
+    if (s.group_m < 1 || s.group_m > 64) return false;
+    return true;
+}
+
+long long lds_bytes(const gba_schedule &s) {
+    return (long long)(s.bm * s.bk + s.bk * s.bn) * 2 * s.stages;
+}
+
+// Built-in choice when neither a forced schedule nor a cached one applies:
+// the largest tile that still gives every CU about one tile.
+gba_schedule heuristic(int64_t M, int64_t N, int cus) {
+    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    const int64_t want = (int64_t)cus * 9 / 10;
+    const ScheduleEntry *e;
+    if (tiles(256, 256) >= want)
+        e = &gba::s_256x256x64_w2x2;
+    else if (tiles(256, 128) >= want)
+        e = M >= N ? &gba::s_256x128x64_w2x2 : &gba::s_128x256x64_w2x2;
+    else
+        e = &gba::s_128x128x64_w2x2;
+    return e->sched;
+}
+
+// ------------------------------------------------------------ disk cache ----
+
+const char *kDtName[2] = {"f16", "bf16"};
+const char *kActName[4] = {"none", "relu", "sigmoid", "gelu"};
+
+struct CacheRec {
+    gba_schedule s;
+    double ms;
+};
+
+std::mutex g_cache_mu;
+bool g_cache_loaded = false;
+std::unordered_map<std::string, CacheRec> g_cache;
+
+bool cache_disabled() {
+    const char *e = getenv("GBA_DISABLE_CACHE");
+    return e && *e && strcmp(e, "0") != 0;
+}
+
+std::string cache_dir() {
+    const char *d = getenv("GBA_CACHE_DIR");
+    if (d && *d) return d;
+    const char *h = getenv("HOME");
+    return std::string(h && *h ? h : "/tmp") + "/.cache/gba";
+}
+
+std::string cache_file() { return cache_dir() + "/schedules.json"; }
+
+std::string cache_key(const DeviceInfo &d, int dtype, int act, int64_t M, int64_t N, int64_t K) {
+    char buf[256];
+    snprintf(buf, sizeof buf, "%s|%d|%s|%s|%s|%lld|%lld|%lld", d.arch.c_str(), d.cus,
+             GBA_VERSION_STRING, kDtName[dtype], kActName[act], (long long)M, (long long)N,
+             (long long)K);
+    return buf;
+}
+
+bool json_int(const char *line, const char *name, int *out) {
+    char pat[64];
+    snprintf(pat, sizeof pat, "\"%s\":", name);
+    const char *p = strstr(line, pat);
+    if (!p) return false;
+    p += strlen(pat);
+    char *end;
+    long v = strtol(p, &end, 10);
+    if (end == p) return false;
+    *out = (int)v;
+    return true;
+}
+
+// One entry per line: {"key": "...", "bm": 256, ..., "ms": 0.08}. Lines that do
+// not parse, or a file of another format version, are ignored.
+void cache_load_locked() {
+    if (g_cache_loaded) return;
+    g_cache_loaded = true;
+    if (cache_disabled()) return;
+    FILE *f = fopen(cache_file().c_str(), "r");
+    if (!f) return;
+    char line[1024];
+    bool header_ok = false;
+    while (fgets(line, sizeof line, f)) {
+        if (strstr(line, "\"format\": \"gba-schedule-cache\"") && strstr(line, "\"version\": 1"))
+            header_ok = true;
+        if (!header_ok) continue;
+        const char *k = strstr(line, "\"key\": \"");
+        if (!k) continue;
+        k += 8;
+        const char *ke = strchr(k, '"');
+        if (!ke) continue;
+        CacheRec r;
+        r.s.stages = 2;
+        if (!json_int(line, "bm", &r.s.bm) || !json_int(line, "bn", &r.s.bn) ||
+            !json_int(line, "bk", &r.s.bk) || !json_int(line, "wm", &r.s.wm) ||
+            !json_int(line, "wn", &r.s.wn) || !json_int(line, "stages", &r.s.stages) ||
+            !json_int(line, "raster", &r.s.raster) || !json_int(line, "group_m", &r.s.group_m))
+            continue;
+        const char *m = strstr(line, "\"ms\":");
+        r.ms = m ? atof(m + 5) : 0.0;
+        if (!sched_valid(r.s)) continue;
+        g_cache[std::string(k, ke)] = r;
+    }
+    fclose(f);
+}
+
+int mkdir_p(const std::string &path) {
+    std::string cur;
+    for (size_t i = 0; i < path.size(); ++i) {
+        cur += path[i];
+        if ((path[i] == '/' && i > 0) || i + 1 == path.size()) {
+            if (mkdir(cur.c_str(), 0755) != 0 && errno != EEXIST) return -1;
+        }
+    }
+    return 0;
+}
+
+// Rewrites the whole file through a temporary and a rename, so a reader never
+// sees a half-written cache.
+int cache_save_locked() {
+    if (cache_disabled()) return GBA_OK;
+    const std::string dir = cache_dir();
+    if (mkdir_p(dir) != 0) return GBA_ERR_CACHE;
+    const std::string fn = cache_file();
+    char tmpn[64];
+    snprintf(tmpn, sizeof tmpn, ".tmp.%d", (int)getpid());
+    const std::string tmp = fn + tmpn;
+    FILE *f = fopen(tmp.c_str(), "w");
+    if (!f) return GBA_ERR_CACHE;
+    fprintf(f, "{\"format\": \"gba-schedule-cache\", \"version\": 1, \"entries\": [\n");
+    std::vector<std::string> keys;
+    for (auto &kv : g_cache) keys.push_back(kv.first);
+    std::sort(keys.begin(), keys.end());
+    for (size_t i = 0; i < keys.size(); ++i) {
+        const CacheRec &r = g_cache[keys[i]];
+        fprintf(f,
+                "{\"key\": \"%s\", \"bm\": %d, \"bn\": %d, \"bk\": %d, \"wm\": %d, \"wn\": %d, "
+                "\"stages\": %d, \"raster\": %d, \"group_m\": %d, \"ms\": %.6f}%s\n",
+                keys[i].c_str(), r.s.bm, r.s.bn, r.s.bk, r.s.wm, r.s.wn, r.s.stages, r.s.raster,
+                r.s.group_m, r.ms, i + 1 < keys.size() ? "," : "");
+    }
+    fprintf(f, "]}\n");
+    const bool ok = fflush(f) == 0;
+    fclose(f);
+    if (!ok || rename(tmp.c_str(), fn.c_str()) != 0) {
+        unlink(tmp.c_str());
+        return GBA_ERR_CACHE;
+    }
+    return GBA_OK;
+}
+
+gba_schedule choose(const DeviceInfo &d, int64_t M, int64_t N, int64_t K, int act, int dtype,
+                    const char **why) {
+    if (t_forced) {
+        *why = "forced";
+        return t_forced_sched;
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        cache_load_locked();
+        auto it = g_cache.find(cache_key(d, dtype, act, M, N, K));
+        if (it != g_cache.end()) {
+            *why = "cache";
+            return it->second.s;
+        }
+    }
+    *why = "heuristic";
+    return heuristic(M, N, d.cus);
+}
+
+int launch(const gba_schedule &s, const void *A, const void *B, const void *bias, void *C,
+           int64_t M, int64_t N, int64_t K, int act, int dtype) {
+    const int i = find_entry(s);
+    if (i < 0) return GBA_ERR_SCHEDULE;
+    hipError_t e = kTable[i]->fn[dtype][act](A, B, bias, C, (int)M, (int)N, (int)K, s.raster,
+                                            s.group_m, t_stream);
+    return e == hipSuccess ? GBA_OK : hip_fail(e);
+}
+
+int gemm_common(const void *A, const void *B, const void *bias, void *C, int64_t M, int64_t N,
+                int64_t K, int act, int dtype) {
+    bool nothing = false;
+    int s = check_gemm_args(A, B, bias, C, M, N, K, act, dtype, &nothing);
+    if (s || nothing) return s;
+    const DeviceInfo *d;
+    s = current_device(&d);
+    if (s) return s;
+    const char *why = "";
+    const gba_schedule sch = choose(*d, M, N, K, act, dtype, &why);
+    if (log_enabled())
+        fprintf(stderr, "[gba] M=%lld N=%lld K=%lld act=%s dtype=%s -> %dx%dx%d w%dx%d r%d g%d (%s)\n",
+                (long long)M, (long long)N, (long long)K, kActName[act], kDtName[dtype], sch.bm,
+                sch.bn, sch.bk, sch.wm, sch.wn, sch.raster, sch.group_m, why);
+    return launch(sch, A, B, bias, C, M, N, K, act, dtype);
+}
+
+template <int DT, int ACT>
+hipError_t launch_bias_act_t(const void *X, const void *bias, void *Y, int M, int N,
+                             hipStream_t st) {
+    const int cpr = N / 8;
+    const int gx = (cpr + 255) / 256;
+    // Enough workgroups to keep every CU busy several times over; each thread
+    // then walks rows with a 4-row unroll.
+    int gy = (M + 3) / 4;
+    const int max_y = std::max(1, 4096 / gx);
+    if (gy > max_y) gy = max_y;
+    hipLaunchKernelGGL((gba::bias_act_kernel<DT, ACT>), dim3(gx, gy), dim3(256), 0, st,
+                       (const uint16_t *)X, (const uint16_t *)bias, (uint16_t *)Y, M, N);
+    return hipGetLastError();
+}
+
+using BiasActFn = hipError_t (*)(const void *, const void *, void *, int, int, hipStream_t);
+const BiasActFn kBiasAct[2][4] = {
+    {launch_bias_act_t<0, 0>, launch_bias_act_t<0, 1>, launch_bias_act_t<0, 2>, launch_bias_act_t<0, 3>},
+    {launch_bias_act_t<1, 0>, launch_bias_act_t<1, 1>, launch_bias_act_t<1, 2>, launch_bias_act_t<1, 3>},
+};
+
+}  // namespace
+
+// =================================================================== C ABI ===
+
+extern "C" {
+
+const char *gba_version(void) { return GBA_VERSION_STRING; }
+
+const char *gba_status_string(int s) {
+    switch (s) {
+    case GBA_OK: return "ok";
+    case GBA_ERR_NULL: return "null pointer";
+    case GBA_ERR_SHAPE: return "bad shape";
+    case GBA_ERR_DTYPE: return "bad dtype";
+    case GBA_ERR_ACT: return "bad activation";
+    case GBA_ERR_ALIGN: return "misaligned pointer, or K or N not a multiple of 8";
+    case GBA_ERR_ALIAS: return "output overlaps an input";
+    case GBA_ERR_DEVICE: return "no gfx950 device";
+    case GBA_ERR_HIP: return "HIP runtime error";
+    case GBA_ERR_SCHEDULE: return "unknown schedule";
+    case GBA_ERR_CACHE: return "schedule cache not writable";
+    default: return "unknown status";
+    }
+}
+
+int gba_last_hip_error(void) { return t_last_hip; }
+
+int gba_set_stream(void *s) {
+    t_stream = (hipStream_t)s;
+    return GBA_OK;
+}
+
+int gba_set_schedule(const gba_schedule *s) {
+    if (!s) {
+        t_forced = false;
+        return GBA_OK;
+    }
+    if (!sched_valid(*s)) return GBA_ERR_SCHEDULE;
+    t_forced_sched = *s;
+    t_forced = true;
+    return GBA_OK;
+}
+
+int gba_num_schedules(void) { return kNumTable; }
+
+int gba_list_schedule(int i, gba_schedule *out) {
+    if (i < 0 || i >= kNumTable) return GBA_ERR_SCHEDULE;
+    if (!out) return GBA_ERR_NULL;
+    *out = kTable[i]->sched;
+    return GBA_OK;
+}
+
+int gba_get_schedule(int64_t M, int64_t N, int64_t K, int act, int dtype, gba_schedule *out) {
+    if (!out) return GBA_ERR_NULL;
+    int s = check_enums(act, dtype);
+    if (s) return s;
+    if (M < 0 || N < 0 || K < 0) return GBA_ERR_SHAPE;
+    const DeviceInfo *d;
+    s = current_device(&d);
+    if (s) return s;
+    const char *why;
+    *out = choose(*d, M, N, K, act, dtype, &why);
+    return GBA_OK;
+}
+
+int gemm_bias_act(const void *A, const void *B, const void *bias, void *C, int64_t M, int64_t N,
+                  int64_t K, int act, int dtype) {
+    return gemm_common(A, B, bias, C, M, N, K, act, dtype);
+}
+
+int gemm(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype) {
+    return gemm_common(A, B, nullptr, C, M, N, K, GBA_ACT_NONE, dtype);
+}
+
+int bias_act(const void *X, const void *bias, void *Y, int64_t M, int64_t N, int act,
+             int dtype) {
+    int s = check_enums(act, dtype);
+    if (s) return s;
+    if (M < 0 || N < 0 || M > 0x7fffffffLL || N > (1LL << 30)) return GBA_ERR_SHAPE;
+    if (M == 0 || N == 0) return GBA_OK;
+    if (!X || !Y) return GBA_ERR_NULL;
+    if (N % 8) return GBA_ERR_ALIGN;
+    if (!aligned16(X) || !aligned16(Y) || (bias && !aligned16(bias))) return GBA_ERR_ALIGN;
+    const size_t nb = (size_t)M * N * 2;
+    if (X != Y && overlaps(X, nb, Y, nb)) return GBA_ERR_ALIAS;
+    if (overlaps(Y, nb, bias, (size_t)N * 2)) return GBA_ERR_ALIAS;
+    const DeviceInfo *d;
+    s = current_device(&d);
+    if (s) return s;
+    hipError_t e = kBiasAct[dtype][act](X, bias, Y, (int)M, (int)N, t_stream);
+    return e == hipSuccess ? GBA_OK : hip_fail(e);
+}
+
+int gba_epilogue_probe(const float *z, float *y, int64_t n, int act) {
+    if (act < GBA_ACT_NONE || act > GBA_ACT_GELU) return GBA_ERR_ACT;
+    if (n < 0) return GBA_ERR_SHAPE;
+    if (n == 0) return GBA_OK;
+    if (!z || !y) return GBA_ERR_NULL;
+    const DeviceInfo *d;
+    int s = current_device(&d);
+    if (s) return s;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    switch (act) {
+    case 0: hipLaunchKernelGGL(gba::epilogue_probe_kernel<0>, dim3(blocks), dim3(256), 0, t_stream, z, y, (long long)n); break;
+    case 1: hipLaunchKernelGGL(gba::epilogue_probe_kernel<1>, dim3(blocks), dim3(256), 0, t_stream, z, y, (long long)n); break;
+    case 2: hipLaunchKernelGGL(gba::epilogue_probe_kernel<2>, dim3(blocks), dim3(256), 0, t_stream, z, y, (long long)n); break;
+    default: hipLaunchKernelGGL(gba::epilogue_probe_kernel<3>, dim3(blocks), dim3(256), 0, t_stream, z, y, (long long)n); break;
+    }
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? GBA_OK : hip_fail(e);
+}
+
+int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_t M, int64_t N,
+                 int64_t K, int act, int dtype, int flags, gba_schedule *best_out,
+                 double *best_ms_out) {
+    bool nothing = false;
+    int s = check_gemm_args(A, B, bias, C, M, N, K, act, dtype, &nothing);
+    if (s) return s;
+    const DeviceInfo *d;
+    s = current_device(&d);
+    if (s) return s;
+    if (nothing) {
+        gba_schedule h = heuristic(M, N, d->cus);
+        if (best_out) *best_out = h;
+        if (best_ms_out) *best_ms_out = 0.0;
+        return GBA_OK;
+    }
+    std::vector<gba_schedule> cands;
+    const int groups_all[] = {1, 2, 4, 8, 16};
+    for (int i = 0; i < kNumTable; ++i) {
+        gba_schedule c = kTable[i]->sched;
+        if (lds_bytes(c) > kLdsBytes) continue;   // the pages' shared-memory filter
+        gba_schedule r0 = c;
+        r0.raster = 0;
+        cands.push_back(r0);
+        if (flags & 1) {
+            for (int g : groups_all) {
+                gba_schedule r1 = c;
+                r1.raster = 1;
+                r1.group_m = g;
+                cands.push_back(r1);
+            }
+        } else {
+            cands.push_back(c);
+        }
+    }
+    hipEvent_t ev[51];
+    for (auto &e : ev) {
+        hipError_t he = hipEventCreate(&e);
+        if (he != hipSuccess) return hip_fail(he);
+    }
+    double best_ms = 1e30;
+    gba_schedule best = cands[0];
+    int status = GBA_OK;
+    for (const gba_schedule &c : cands) {
+        for (int w = 0; w < 10 && status == GBA_OK; ++w)
+            status = launch(c, A, B, bias, C, M, N, K, act, dtype);
+        for (int r = 0; r < 50 && status == GBA_OK; ++r) {
+            hipEventRecord(ev[r], t_stream);
+            status = launch(c, A, B, bias, C, M, N, K, act, dtype);
+        }
+        if (status) break;
+        hipEventRecord(ev[50], t_stream);
+        hipError_t he = hipEventSynchronize(ev[50]);
+        if (he != hipSuccess) {
+            status = hip_fail(he);
+            break;
+        }
+        std::vector<float> t(50);
+        for (int r = 0; r < 50; ++r) hipEventElapsedTime(&t[r], ev[r], ev[r + 1]);
+        std::nth_element(t.begin(), t.begin() + 25, t.end());
+        const double med = t[25];
+        if (log_enabled())
+            fprintf(stderr, "[gba] tune %dx%dx%d w%dx%d r%d g%d: %.4f ms\n", c.bm, c.bn, c.bk,
+                    c.wm, c.wn, c.raster, c.group_m, med);
+        if (med < best_ms) {
+            best_ms = med;
+            best = c;
+        }
+    }
+    for (auto &e : ev) hipEventDestroy(e);
+    if (status) return status;
+    // Leave the winner's result in C.
+    status = launch(best, A, B, bias, C, M, N, K, act, dtype);
+    if (status) return status;
+    hipError_t he = hipStreamSynchronize(t_stream);
+    if (he != hipSuccess) return hip_fail(he);
+    if (best_out) *best_out = best;
+    if (best_ms_out) *best_ms_out = best_ms;
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    cache_load_locked();
+    g_cache[cache_key(*d, dtype, act, M, N, K)] = CacheRec{best, best_ms};
+    return cache_save_locked();
+}
+
+}  // extern "C"

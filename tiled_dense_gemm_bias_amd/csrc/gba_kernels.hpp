@@ -1,0 +1,402 @@
+// gfx950 kernels of the fused tiled GEMM C = act(A.B + bias).
+//
+// The computation is the tiled GEMM of "writing-tilelang-kernels" (Kernel
+// Anatomy): each workgroup owns one BM x BN tile of C, clears an fp32
+// accumulator held in registers, walks K in BK-deep slices staged through
+// on-chip memory, and writes its tile once. "TileLang: Write, Autotune, and Ship
+// Fused Tensor-Core Kernels from Python" (Why tile-level control matters) adds
+// the bias + activation epilogue applied to that register accumulator.
+//
+// CDNA4 mapping used here:
+//  * MFMA v_mfma_f32_32x32x16_{f16,bf16}: a 64-lane wave multiplies a 32x16 by a
+//    16x32 block into 16 fp32 accumulators per lane.
+//  * The MFMA's first operand is fed from B (rows n of B^T) and its second from
+//    A (columns m of A^T), so the 32x32 result block is C^T: lane l then holds
+//    C[m = l%32][n = 8i + 4(l/32) + j] in accumulator 4i+j, i.e. four adjacent
+//    columns of one row -- one 8-byte store per i.
+//  * LDS holds each stage as A[BM][BK] and B^T[BN][BK], both K-contiguous, in
+//    16-byte chunks; chunk c of row r sits at c ^ swz(r), which keeps both the
+//    loader's writes and the MFMA operand reads free of bank conflicts.
+//  * B is row-major [K,N] in HBM, so the loader transposes it on the way into
+//    LDS: each thread reads an 8(k) x 8(n) block as eight 16-byte row pieces and
+//    writes eight 16-byte column pieces, repacked with v_perm_b32.
+//  * Two LDS stages: the global loads of slice k+1 are in flight while slice k
+//    is multiplied; one barrier per slice.
+//  * Workgroup ids are remapped so that each of the 8 XCDs runs a contiguous
+//    block of tiles, walked in groups of group_m tile rows (L2 panel reuse).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gba {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Native 16-byte vector (HIP's u32x4 is a struct, whose copies defeat register promotion).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_SIGMOID = 2, ACT_GELU = 3 };
+
+constexpr int kNumXcd = 8;
+
+// ---------------------------------------------------------------- scalars --
+
+template <int DT>
+__device__ __forceinline__ float to_f32(uint32_t h) {
+    if constexpr (DT == DT_F16) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+    } else {
+        return __uint_as_float(h << 16);
+    }
+}
+
+// fp32 -> storage type, round to nearest even (v_cvt_f16_f32 / v_cvt_pk_bf16_f32).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    if constexpr (DT == DT_F16) {
+        uint32_t a = __builtin_bit_cast(uint16_t, (_Float16)lo);
+        uint32_t b = __builtin_bit_cast(uint16_t, (_Float16)hi);
+        return a | (b << 16);
+    } else {
+        uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
+        uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
+        return a | (b << 16);
+    }
+}
+
+// Activation on the fp32 accumulator.
+//  RELU:    max(z, 0).
+//  SIGMOID: 1 / (1 + 2^(-z log2 e)) with the hardware exp2 and reciprocal.
+//  GELU:    z * Phi(z), Phi(z) = erfc(-z/sqrt2) / 2. erfc(x), x >= 0, is the
+//           Chebyshev-fitted form of Press, Teukolsky, Vetterling & Flannery,
+//           "Numerical Recipes" (2nd ed., sec. 6.2, routine erfcc):
+//           erfc(x) = t exp(-x^2 + P(t)), t = 1 / (1 + x/2), with fractional
+//           error below 1.2e-7 for every x >= 0. Relative accuracy in the tail
+//           keeps z * Phi(z) accurate for large negative z as well.
+template <int ACT>
+__device__ __forceinline__ float act_fn(float z) {
+    if constexpr (ACT == ACT_RELU) {
+        return fmaxf(z, 0.0f);
+    } else if constexpr (ACT == ACT_SIGMOID) {
+        const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+        return __builtin_amdgcn_rcpf(1.0f + e);
+    } else if constexpr (ACT == ACT_GELU) {
+        const float x = fabsf(z) * 0.70710678118654752f;
+        const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, x, 1.0f));
+        float p = fmaf(t, 0.17087277f, -0.82215223f);
+        p = fmaf(t, p, 1.48851587f);
+        p = fmaf(t, p, -1.13520398f);
+        p = fmaf(t, p, 0.27886807f);
+        p = fmaf(t, p, -0.18628806f);
+        p = fmaf(t, p, 0.09678418f);
+        p = fmaf(t, p, 0.37409196f);
+        p = fmaf(t, p, 1.00002368f);
+        p = fmaf(t, p, -1.26551223f);
+        const float ec = t * __builtin_amdgcn_exp2f(fmaf(-x, x, p) * 1.4426950408889634f);
+        const float h = 0.5f * ec;                  // Phi(-|z|)
+        const float phi = z >= 0.0f ? 1.0f - h : h;
+        return z * phi;
+    } else {
+        return z;
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (DT == DT_F16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+}
+
+// Component d of a u32x4; d is a compile-time constant after unrolling.
+__device__ __forceinline__ uint32_t dword(const u32x4 &v, int d) {
+    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+}
+
+// ------------------------------------------------------------- tile order --
+
+// Bijection on [0, n): workgroup w runs on XCD w % 8 (round-robin dispatch);
+// return an index such that the workgroups of XCD x get one contiguous range.
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+    const int q = n / kNumXcd, r = n % kNumXcd;
+    const int x = w % kNumXcd, i = w / kNumXcd;
+    return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// Logical tile index -> (tile_m, tile_n), walking group_m tile rows at a time.
+__device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n, int group_m,
+                                             int &tm, int &tn) {
+    const int group_size = group_m * tiles_n;
+    const int g = t / group_size;
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int in_group = t - g * group_size;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}
+
+// ----------------------------------------------------------------- GEMM ----
+
+// Physical 16-byte chunk of logical chunk c in LDS row r. CH chunks per row;
+// rows that share a 128-byte bank window, and rows 8 apart, land on different
+// chunk slots, so 8 consecutive lanes never collide.
+template <int CH>
+__device__ __forceinline__ int swz(int r, int c) {
+    constexpr int RPW = 8 / CH;   // rows per 128-byte window
+    return c ^ (((r / RPW) ^ (r >> 3)) & (CH - 1));
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int DT, int ACT>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_bias_act_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+                     const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int M, int N,
+                     int K, int tiles_m, int tiles_n, int raster, int group_m) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int CH = BK / 8;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int A_CHUNKS = BM * CH;
+    constexpr int A_PER_T = A_CHUNKS / NT;
+    constexpr int B_SUB = (BK / 8) * (BN / 8);
+    constexpr int B_PER_T = (B_SUB + NT - 1) / NT;
+    static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+    static_assert(A_CHUNKS % NT == 0, "A slice must split evenly over the threads");
+    constexpr int STAGE = (BM + BN) * CH;   // u32x4 per stage
+    static_assert(2 * STAGE * 16 <= 160 * 1024, "LDS ring exceeds 160 KiB");
+
+    __shared__ u32x4 lds[2 * STAGE];
+
+    int tm, tn;
+    {
+        int t = blockIdx.x;
+        if (raster) t = xcd_remap(t, gridDim.x);
+        if (raster) {
+            grouped_tile(t, tiles_m, tiles_n, group_m, tm, tn);
+        } else {
+            tm = t / tiles_n;
+            tn = t % tiles_n;
+        }
+    }
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wid = tid >> 6;
+    const int wm = wid / WN, wn = wid % WN;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    u32x4 ra[A_PER_T];
+    u32x4 rb[B_PER_T][8];
+
+    auto load_slice = [&](int kt) {
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i) {
+            const int s = tid + i * NT;
+            const int r = s / CH, c = s % CH;
+            const int gm = m0 + r, gk = k0 + c * 8;
+            ra[i] = (gm < M && gk < K)
+                        ? *reinterpret_cast<const u32x4 *>(A + (size_t)gm * K + gk)
+                        : zero4;
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER_T; ++i) {
+            const int s = tid + i * NT;
+            if (B_SUB % NT == 0 || s < B_SUB) {
+                const int kb = s / (BN / 8), nb = s % (BN / 8);
+                const int gn = n0 + nb * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int gk = k0 + kb * 8 + e;
+                    rb[i][e] = (gk < K && gn < N)
+                                   ? *reinterpret_cast<const u32x4 *>(B + (size_t)gk * N + gn)
+                                   : zero4;
+                }
+            }
+        }
+    };
+
+    auto store_slice = [&](int st) {
+        u32x4 *As = lds + st * STAGE;
+        u32x4 *Bs = As + BM * CH;
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i) {
+            const int s = tid + i * NT;
+            const int r = s / CH, c = s % CH;
+            As[r * CH + swz<CH>(r, c)] = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER_T; ++i) {
+            const int s = tid + i * NT;
+            if (B_SUB % NT == 0 || s < B_SUB) {
+                const int kb = s / (BN / 8), nb = s % (BN / 8);
+                // rb[i][e] holds B[k = kb*8+e][n = nb*8 .. nb*8+7]; column j of the
+                // 8x8 block becomes row n = nb*8+j of B^T, eight k values.
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                    const int d = j >> 1;
+                    u32x4 t;
+                    t.x = __builtin_amdgcn_perm(dword(rb[i][1], d), dword(rb[i][0], d), sel);
+                    t.y = __builtin_amdgcn_perm(dword(rb[i][3], d), dword(rb[i][2], d), sel);
+                    t.z = __builtin_amdgcn_perm(dword(rb[i][5], d), dword(rb[i][4], d), sel);
+                    t.w = __builtin_amdgcn_perm(dword(rb[i][7], d), dword(rb[i][6], d), sel);
+                    const int n = nb * 8 + j;
+                    Bs[n * CH + swz<CH>(n, kb)] = t;
+                }
+            }
+        }
+    };
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+        for (int b = 0; b < FM; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
+
+    auto compute_slice = [&](int st) {
+        const u32x4 *As = lds + st * STAGE;
+        const u32x4 *Bs = As + BM * CH;
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int c = 2 * kk + lhalf;
+            u32x4 af[FM], bf[FN];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int r = wm * WTM + fm * 32 + lrow;
+                af[fm] = As[r * CH + swz<CH>(r, c)];
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int n = wn * WTN + fn * 32 + lrow;
+                bf[fn] = Bs[n * CH + swz<CH>(n, c)];
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    acc[fn][fm] = mfma32x32x16<DT>(bf[fn], af[fm], acc[fn][fm]);
+        }
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    if (nk > 0) {
+        load_slice(0);
+        store_slice(0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int st = kt & 1;
+        if (kt + 1 < nk) load_slice(kt + 1);
+        compute_slice(st);
+        if (kt + 1 < nk) store_slice(st ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: + bias[n], activation, round once, masked 8-byte stores.
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = n0 + wn * WTN + fn * 32 + i * 8 + lhalf * 4;
+            if (n >= N) continue;
+            float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+            if (bias) {
+                const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n);
+                b0 = to_f32<DT>(bb.x & 0xffffu);
+                b1 = to_f32<DT>(bb.x >> 16);
+                b2 = to_f32<DT>(bb.y & 0xffffu);
+                b3 = to_f32<DT>(bb.y >> 16);
+            }
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int m = m0 + wm * WTM + fm * 32 + lrow;
+                if (m >= M) continue;
+                const f32x16 &a = acc[fn][fm];
+                u32x2 o;
+                o.x = pack2<DT>(act_fn<ACT>(a[4 * i + 0] + b0), act_fn<ACT>(a[4 * i + 1] + b1));
+                o.y = pack2<DT>(act_fn<ACT>(a[4 * i + 2] + b2), act_fn<ACT>(a[4 * i + 3] + b3));
+                *reinterpret_cast<u32x2 *>(C + (size_t)m * N + n) = o;
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int DT, int ACT>
+hipError_t launch_gemm(const void *A, const void *B, const void *bias, void *C, int M, int N,
+                       int K, int raster, int group_m, hipStream_t stream) {
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const long long grid = (long long)tiles_m * tiles_n;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_bias_act_kernel<BM, BN, BK, WM, WN, DT, ACT>), dim3((unsigned)grid),
+                       dim3(WM * WN * 64), 0, stream, (const uint16_t *)A, (const uint16_t *)B,
+                       (const uint16_t *)bias, (uint16_t *)C, M, N, K, tiles_m, tiles_n, raster,
+                       group_m < 1 ? 1 : group_m);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------- bias_act ----
+
+// Y[r][c] = act(X[r][c] + bias[c]). Each thread owns one 8-column chunk of a
+// row (its bias chunk is loaded once) and strides down the rows; a wave's
+// 16-byte accesses are contiguous within a row.
+template <int DT, int ACT>
+__global__ void __launch_bounds__(256)
+bias_act_kernel(const uint16_t *X, const uint16_t *__restrict__ bias, uint16_t *Y, int M,
+                int N) {
+    const int cpr = N / 8;
+    const int chunk = blockIdx.x * 256 + threadIdx.x;
+    if (chunk >= cpr) return;
+    float bv[8];
+    if (bias) {
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(bias + chunk * 8);
+        const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bv[2 * e] = to_f32<DT>(w[e] & 0xffffu);
+            bv[2 * e + 1] = to_f32<DT>(w[e] >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[e] = 0.0f;
+    }
+    constexpr int U = 4;
+    for (int r0 = blockIdx.y * U; r0 < M; r0 += gridDim.y * U) {
+        u32x4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (r0 + u < M)
+                x[u] = *reinterpret_cast<const u32x4 *>(X + (size_t)(r0 + u) * N + chunk * 8);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (r0 + u >= M) continue;
+            const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = pack2<DT>(act_fn<ACT>(to_f32<DT>(w[e] & 0xffffu) + bv[2 * e]),
+                                 act_fn<ACT>(to_f32<DT>(w[e] >> 16) + bv[2 * e + 1]));
+            u32x4 y = {o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<u32x4 *>(Y + (size_t)(r0 + u) * N + chunk * 8) = y;
+        }
+    }
+}
+
+template <int ACT>
+__global__ void __launch_bounds__(256) epilogue_probe_kernel(const float *z, float *y, long long n) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) y[i] = act_fn<ACT>(z[i]);
+}
+
+}  // namespace gba

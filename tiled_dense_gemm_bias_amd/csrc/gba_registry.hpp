@@ -1,0 +1,52 @@
+// Table entry for one compiled-in GEMM schedule: its shape and the launchers of
+// its eight (dtype x activation) kernel instances.
+#pragma once
+
+#include "gba.h"
+#include "gba_kernels.hpp"
+
+namespace gba {
+
+using GemmLaunchFn = hipError_t (*)(const void *, const void *, const void *, void *, int, int,
+                                    int, int, int, hipStream_t);
+
+struct ScheduleEntry {
+    gba_schedule sched;      // raster / group_m hold the defaults
+    GemmLaunchFn fn[2][4];   // [dtype][act]
+};
+
+}  // namespace gba
+
+#define GBA_KERNEL_INST_(BM, BN, BK, WM, WN, DT, ACT)                                       \
+    template __global__ void gba::gemm_bias_act_kernel<BM, BN, BK, WM, WN, DT, ACT>(          \
+        const uint16_t *__restrict__, const uint16_t *__restrict__, const uint16_t *__restrict__, \
+        uint16_t *__restrict__, int, int, int, int, int, int, int);
+
+#define GBA_KERNEL_INSTS_(BM, BN, BK, WM, WN)                                                  \
+    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 0, 0)                                                 \
+    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 0, 1)                                                 \
+    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 0, 2)                                                 \
+    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 0, 3)                                                 \
+    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 1, 0)                                                 \
+    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 1, 1)                                                 \
+    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 1, 2)                                                 \
+    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 1, 3)
+
+#define GBA_LAUNCHERS_(BM, BN, BK, WM, WN, DT)                                              \
+    {gba::launch_gemm<BM, BN, BK, WM, WN, DT, 0>, gba::launch_gemm<BM, BN, BK, WM, WN, DT, 1>, \
+     gba::launch_gemm<BM, BN, BK, WM, WN, DT, 2>, gba::launch_gemm<BM, BN, BK, WM, WN, DT, 3>}
+
+// Instantiates the eight kernels (device and host passes) and, in the host
+// pass only, defines gba::NAME with external linkage for the host registry.
+#ifdef __HIP_DEVICE_COMPILE__
+#define GBA_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, GROUP_M) GBA_KERNEL_INSTS_(BM, BN, BK, WM, WN)
+#else
+#define GBA_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, GROUP_M)                               \
+    GBA_KERNEL_INSTS_(BM, BN, BK, WM, WN)                                                   \
+    namespace gba {                                                                         \
+    extern const ScheduleEntry NAME;                                                        \
+    const ScheduleEntry NAME = {{BM, BN, BK, WM, WN, 2, 1, GROUP_M},                        \
+                                {GBA_LAUNCHERS_(BM, BN, BK, WM, WN, 0),                     \
+                                 GBA_LAUNCHERS_(BM, BN, BK, WM, WN, 1)}};                   \
+    }
+#endif

@@ -1,0 +1,4 @@
+// Kernel instances of the 128x256x64 tile, 2x2 waves.
+#include "gba_registry.hpp"
+
+GBA_SCHEDULE_ENTRY(s_128x256x64_w2x2, 128, 256, 64, 2, 2, 4)
