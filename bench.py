@@ -115,7 +115,7 @@ def main(argv=None) -> int:
     ap.add_argument("--unfused", action="store_true", help="also time gemm + bias_act")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tune", action="store_true", help="autotune before timing")
-    ap.add_argument("--schedule", default=None, help="force bm,bn,bk,wm,wn[,raster,group_m]")
+    ap.add_argument("--schedule", default=None, help="force bm,bn,bk,wm,wn,stages,kernel,loaders,spread[,raster,group_m]")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain device copy of the workload's C size (counter scaling)")
     a = ap.parse_args(argv)
@@ -158,11 +158,11 @@ def main(argv=None) -> int:
 
     if a.schedule:
         f = [int(x) for x in a.schedule.split(",")]
-        keys = ["bm", "bn", "bk", "wm", "wn", "raster", "group_m"]
+        keys = ["bm", "bn", "bk", "wm", "wn", "stages", "kernel", "loaders", "spread", "raster",
+                "group_m"]
         sched = dict(zip(keys, f))
         sched.setdefault("raster", 1)
         sched.setdefault("group_m", 4)
-        sched["stages"] = 2
         gba.set_schedule(sched)
     elif a.tune:
         best, ms = gba.autotune(a_t, b_t, bias_t, c_t, w.act, all_groups=True)

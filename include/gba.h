@@ -18,7 +18,8 @@
  *     row-alignment rule of "writing-tilelang-kernels", Common Pitfalls);
  *     otherwise GBA_ERR_ALIGN. M is arbitrary.
  *   - M == 0 or N == 0: nothing to do, GBA_OK, no launch. K == 0: the empty
- *     sum, C = act(bias) (or act(0)). Negative sizes: GBA_ERR_SHAPE.
+ *     sum, C = act(bias) (or act(0)). Negative sizes, or K > 2^21, N > 2^23,
+ *     M > 2^31 - 1 (the kernels' 32-bit tile offsets): GBA_ERR_SHAPE.
  *   - Argument errors are reported synchronously, before any launch. Work is
  *     enqueued on the calling thread's stream (gba_set_stream) and runs
  *     asynchronously; a device fault surfaces at the caller's next sync.
@@ -69,13 +70,22 @@ typedef enum {
  * tiles each of the 8 XCDs runs into one contiguous block, then walks them in
  * groups of group_m tile rows so that neighbouring workgroups share A and B
  * panels in that XCD's L2 ("use_swizzle ... L2 cache locality",
- * "writing-tilelang-kernels", Key API Patterns). */
+ * "writing-tilelang-kernels", Key API Patterns). kernel selects the main-loop
+ * design: 0 = tiles staged through registers into LDS (B transposed on the
+ * way), 1 = direct global->LDS loads into a `stages`-deep ring with transposing
+ * LDS reads for B, 2 = the same with every instruction of a 16-deep MFMA step
+ * placed by hand: global->LDS loads (issued by the first `loaders` waves, spread
+ * over `spread` steps) and the next step's LDS reads between the MFMAs.
+ * loaders and spread are 0 for kernels 0 and 1. */
 typedef struct {
     int32_t bm, bn, bk;
     int32_t wm, wn;
     int32_t stages;
     int32_t raster;
     int32_t group_m;
+    int32_t kernel;
+    int32_t loaders;
+    int32_t spread;
 } gba_schedule;
 
 /* C = act(A.B + bias).
@@ -103,7 +113,8 @@ int gba_set_stream(void *hip_stream);
 
 /* Force a schedule for this thread's later GEMM calls (NULL: back to the cache
  * or the built-in heuristic). GBA_ERR_SCHEDULE if no compiled-in kernel has
- * this (bm, bn, bk, wm, wn, stages), or raster/group_m are out of range. */
+ * this (bm, bn, bk, wm, wn, stages, kernel, loaders, spread), or raster/group_m
+ * are out of range. */
 int gba_set_schedule(const gba_schedule *s);
 
 /* The schedule a gemm_bias_act call with these arguments would use now. */

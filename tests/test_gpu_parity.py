@@ -55,7 +55,8 @@ def schedules():
 
 
 def sched_id(s):
-    return "%dx%dx%d_w%dx%d" % (s["bm"], s["bn"], s["bk"], s["wm"], s["wn"])
+    return "k%d_%dx%dx%d_w%dx%d_s%d_l%d_p%d" % (s["kernel"], s["bm"], s["bn"], s["bk"], s["wm"],
+                                                s["wn"], s["stages"], s["loaders"], s["spread"])
 
 
 # ---------------------------------------------------------- bit-exact ----
@@ -143,7 +144,7 @@ def test_c2_at_the_pages_default_tile():
     w = synth.WORKLOADS["c2_plain"]
     A, B, bias = synth.make_inputs(w)
     sch = {"bm": 128, "bn": 128, "bk": 32, "wm": 2, "wn": 2, "stages": 2, "raster": 1,
-           "group_m": 8}
+           "group_m": 8, "kernel": 0, "loaders": 0, "spread": 0}
     say("c2 128x128x32")
     check_random(A, B, bias, "none", "f16", run_gpu(A, B, bias, "none", "f16", sched=sch))
 
@@ -330,11 +331,11 @@ def test_epilogue_device_functions_on_dense_grid(act):
         bound = (1e-6 + np.abs(z) * 1.2e-7) * np.abs(ref) + 1e-37
         assert np.all(err <= bound), float((err / bound).max())
     else:
-        # erfc fit with fractional error < 1.2e-7, evaluated in fp32; the exp of
-        # -z^2/2 + P(t) is conditioned like the sigmoid's: the fp32 roundings of
-        # |z|/sqrt2 (twice, through the square), of the fma and of the log2(e)
-        # scaling each move the result by about (z^2/2) 2^-24, relative.
-        bound = (2e-6 + 0.5 * z.astype(np.float64) ** 2 * 6 * 2.0 ** -24) * np.abs(ref) + 1e-37
+        # erfc fit with fractional error < 1e-5 (tests/test_gelu_fit.py), evaluated
+        # in fp32; the exp2 of Q2(t) - z^2 log2(e)/2 is conditioned like the
+        # sigmoid's: the fp32 roundings of |z|^2 and of the fma move the result by
+        # about (z^2/2) 2^-24 each, relative.
+        bound = (1.2e-5 + 0.5 * z.astype(np.float64) ** 2 * 6 * 2.0 ** -24) * np.abs(ref) + 1e-37
         assert np.all(err <= bound), float((err / bound).max())
 
 

@@ -26,7 +26,8 @@ STATUS = {
     5: "GBA_ERR_ALIGN", 6: "GBA_ERR_ALIAS", 7: "GBA_ERR_DEVICE", 8: "GBA_ERR_HIP",
     9: "GBA_ERR_SCHEDULE", 10: "GBA_ERR_CACHE",
 }
-SCHED_FIELDS = ("bm", "bn", "bk", "wm", "wn", "stages", "raster", "group_m")
+SCHED_FIELDS = ("bm", "bn", "bk", "wm", "wn", "stages", "raster", "group_m", "kernel", "loaders",
+                "spread")
 
 
 class GbaError(RuntimeError):
@@ -45,7 +46,7 @@ class Schedule(ctypes.Structure):
     @classmethod
     def from_dict(cls, d: dict) -> "Schedule":
         s = cls()
-        defaults = {"stages": 2, "raster": 1, "group_m": 4}
+        defaults = {"stages": 2, "raster": 1, "group_m": 4, "kernel": 2, "loaders": 4, "spread": 2}
         for f in SCHED_FIELDS:
             setattr(s, f, int(d.get(f, defaults.get(f, 0))))
         return s

@@ -22,11 +22,15 @@
 
 namespace gba {
 extern const ScheduleEntry s_256x256x64_w2x2;
-extern const ScheduleEntry s_256x256x64_w2x4;
-extern const ScheduleEntry s_256x128x64_w2x2;
-extern const ScheduleEntry s_128x256x64_w2x2;
-extern const ScheduleEntry s_128x128x64_w2x2;
 extern const ScheduleEntry s_128x128x32_w2x2;
+extern const ScheduleEntry d_256x256x64_w2x2_s2;
+extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p2;
+extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p1;
+extern const ScheduleEntry i_256x256x32_w2x2_s4_l4_p1;
+extern const ScheduleEntry i_256x256x64_w2x4_s2_l8_p2;
+extern const ScheduleEntry i_256x128x64_w2x2_s3_l4_p2;
+extern const ScheduleEntry i_128x256x64_w2x2_s3_l4_p2;
+extern const ScheduleEntry i_128x128x64_w2x2_s3_l4_p2;
 }  // namespace gba
 
 namespace {
@@ -34,8 +38,15 @@ namespace {
 using gba::ScheduleEntry;
 
 const ScheduleEntry *const kTable[] = {
-    &gba::s_256x256x64_w2x2, &gba::s_256x256x64_w2x4, &gba::s_256x128x64_w2x2,
-    &gba::s_128x256x64_w2x2, &gba::s_128x128x64_w2x2, &gba::s_128x128x32_w2x2,
+    // interleaved direct-to-LDS kernels (the default family)
+    &gba::i_256x256x64_w2x2_s2_l4_p2, &gba::i_256x256x64_w2x2_s2_l4_p1,
+    &gba::i_256x256x32_w2x2_s4_l4_p1, &gba::i_256x256x64_w2x4_s2_l8_p2,
+    &gba::i_256x128x64_w2x2_s3_l4_p2, &gba::i_128x256x64_w2x2_s3_l4_p2,
+    &gba::i_128x128x64_w2x2_s3_l4_p2,
+    // direct-to-LDS kernel with compiler-scheduled steps
+    &gba::d_256x256x64_w2x2_s2,
+    // register-staged kernels, incl. the 128x128x32 starting tile
+    &gba::s_256x256x64_w2x2, &gba::s_128x128x32_w2x2,
 };
 constexpr int kNumTable = sizeof(kTable) / sizeof(kTable[0]);
 constexpr long long kLdsBytes = 160 * 1024;
@@ -124,8 +135,9 @@ int check_gemm_args(const void *A, const void *B, const void *bias, const void *
     int s = check_enums(act, dtype);
     if (s) return s;
     if (M < 0 || N < 0 || K < 0) return GBA_ERR_SHAPE;
-    // 32-bit tile arithmetic inside the kernel: per-tile offsets stay below 2^31.
-    if (M > 0x7fffffffLL || N > (1LL << 24) || K > (1LL << 23)) return GBA_ERR_SHAPE;
+    // 32-bit buffer offsets inside the kernels: a tile's byte offsets (256 rows of
+    // A, 64 rows of B) stay below 2^31.
+    if (M > 0x7fffffffLL || N > (1LL << 23) || K > (1LL << 21)) return GBA_ERR_SHAPE;
     *nothing = (M == 0 || N == 0);
     if (*nothing) return GBA_OK;
     if (!C) return GBA_ERR_NULL;
@@ -147,7 +159,8 @@ int find_entry(const gba_schedule &s) {
     for (int i = 0; i < kNumTable; ++i) {
         const gba_schedule &t = kTable[i]->sched;
         if (t.bm == s.bm && t.bn == s.bn && t.bk == s.bk && t.wm == s.wm && t.wn == s.wn &&
-            t.stages == s.stages)
+            t.stages == s.stages && t.kernel == s.kernel && t.loaders == s.loaders &&
+            t.spread == s.spread)
             return i;
     }
     return -1;
@@ -171,11 +184,11 @@ gba_schedule heuristic(int64_t M, int64_t N, int cus) {
     const int64_t want = (int64_t)cus * 9 / 10;
     const ScheduleEntry *e;
     if (tiles(256, 256) >= want)
-        e = &gba::s_256x256x64_w2x2;
+        e = &gba::i_256x256x64_w2x2_s2_l4_p2;
     else if (tiles(256, 128) >= want)
-        e = M >= N ? &gba::s_256x128x64_w2x2 : &gba::s_128x256x64_w2x2;
+        e = M >= N ? &gba::i_256x128x64_w2x2_s3_l4_p2 : &gba::i_128x256x64_w2x2_s3_l4_p2;
     else
-        e = &gba::s_128x128x64_w2x2;
+        e = &gba::i_128x128x64_w2x2_s3_l4_p2;
     return e->sched;
 }
 
@@ -249,10 +262,15 @@ void cache_load_locked() {
         if (!ke) continue;
         CacheRec r;
         r.s.stages = 2;
+        r.s.kernel = 0;
+        r.s.loaders = 0;
+        r.s.spread = 0;
         if (!json_int(line, "bm", &r.s.bm) || !json_int(line, "bn", &r.s.bn) ||
             !json_int(line, "bk", &r.s.bk) || !json_int(line, "wm", &r.s.wm) ||
             !json_int(line, "wn", &r.s.wn) || !json_int(line, "stages", &r.s.stages) ||
-            !json_int(line, "raster", &r.s.raster) || !json_int(line, "group_m", &r.s.group_m))
+            !json_int(line, "raster", &r.s.raster) || !json_int(line, "group_m", &r.s.group_m) ||
+            !json_int(line, "kernel", &r.s.kernel) || !json_int(line, "loaders", &r.s.loaders) ||
+            !json_int(line, "spread", &r.s.spread))
             continue;
         const char *m = strstr(line, "\"ms\":");
         r.ms = m ? atof(m + 5) : 0.0;
@@ -293,9 +311,11 @@ int cache_save_locked() {
         const CacheRec &r = g_cache[keys[i]];
         fprintf(f,
                 "{\"key\": \"%s\", \"bm\": %d, \"bn\": %d, \"bk\": %d, \"wm\": %d, \"wn\": %d, "
-                "\"stages\": %d, \"raster\": %d, \"group_m\": %d, \"ms\": %.6f}%s\n",
+                "\"stages\": %d, \"raster\": %d, \"group_m\": %d, \"kernel\": %d, "
+                "\"loaders\": %d, \"spread\": %d, \"ms\": %.6f}%s\n",
                 keys[i].c_str(), r.s.bm, r.s.bn, r.s.bk, r.s.wm, r.s.wn, r.s.stages, r.s.raster,
-                r.s.group_m, r.ms, i + 1 < keys.size() ? "," : "");
+                r.s.group_m, r.s.kernel, r.s.loaders, r.s.spread, r.ms,
+                i + 1 < keys.size() ? "," : "");
     }
     fprintf(f, "]}\n");
     const bool ok = fflush(f) == 0;
@@ -346,9 +366,10 @@ int gemm_common(const void *A, const void *B, const void *bias, void *C, int64_t
     const char *why = "";
     const gba_schedule sch = choose(*d, M, N, K, act, dtype, &why);
     if (log_enabled())
-        fprintf(stderr, "[gba] M=%lld N=%lld K=%lld act=%s dtype=%s -> %dx%dx%d w%dx%d r%d g%d (%s)\n",
-                (long long)M, (long long)N, (long long)K, kActName[act], kDtName[dtype], sch.bm,
-                sch.bn, sch.bk, sch.wm, sch.wn, sch.raster, sch.group_m, why);
+        fprintf(stderr,
+                "[gba] M=%lld N=%lld K=%lld act=%s dtype=%s -> k%d %dx%dx%d w%dx%d s%d r%d g%d (%s)\n",
+                (long long)M, (long long)N, (long long)K, kActName[act], kDtName[dtype], sch.kernel,
+                sch.bm, sch.bn, sch.bk, sch.wm, sch.wn, sch.stages, sch.raster, sch.group_m, why);
     return launch(sch, A, B, bias, C, M, N, K, act, dtype);
 }
 
@@ -546,8 +567,8 @@ int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_
         std::nth_element(t.begin(), t.begin() + 25, t.end());
         const double med = t[25];
         if (log_enabled())
-            fprintf(stderr, "[gba] tune %dx%dx%d w%dx%d r%d g%d: %.4f ms\n", c.bm, c.bn, c.bk,
-                    c.wm, c.wn, c.raster, c.group_m, med);
+            fprintf(stderr, "[gba] tune k%d %dx%dx%d w%dx%d s%d r%d g%d: %.4f ms\n", c.kernel,
+                    c.bm, c.bn, c.bk, c.wm, c.wn, c.stages, c.raster, c.group_m, med);
         if (med < best_ms) {
             best_ms = med;
             best = c;

@@ -71,12 +71,14 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 // Activation on the fp32 accumulator.
 //  RELU:    max(z, 0).
 //  SIGMOID: 1 / (1 + 2^(-z log2 e)) with the hardware exp2 and reciprocal.
-//  GELU:    z * Phi(z), Phi(z) = erfc(-z/sqrt2) / 2. erfc(x), x >= 0, is the
-//           Chebyshev-fitted form of Press, Teukolsky, Vetterling & Flannery,
-//           "Numerical Recipes" (2nd ed., sec. 6.2, routine erfcc):
-//           erfc(x) = t exp(-x^2 + P(t)), t = 1 / (1 + x/2), with fractional
-//           error below 1.2e-7 for every x >= 0. Relative accuracy in the tail
-//           keeps z * Phi(z) accurate for large negative z as well.
+//  GELU:    z * Phi(z), written as max(z, 0) - |z| Phi(-|z|) (Phi(z) = 1 - Phi(-z)),
+//           with Phi(-|z|) = erfc(x) / 2, x = |z| / sqrt 2, from the form of Press,
+//           Teukolsky, Vetterling & Flannery, "Numerical Recipes" (2nd ed., sec.
+//           6.2): erfc(x) = t exp(-x^2 + Q(t)), t = 1 / (1 + x/2). Q here is a
+//           degree-5 fit (tiled_dense_gemm_bias_amd/gelu_fit.py) with fractional
+//           error below 8e-6 for x in [0, 9.5]; log2(e) and the factor 1/2 are
+//           folded into its coefficients. The error is relative, so z * Phi(z)
+//           stays accurate deep in the negative tail (bf16 outputs reach 1e-38).
 template <int ACT>
 __device__ __forceinline__ float act_fn(float z) {
     if constexpr (ACT == ACT_RELU) {
@@ -85,21 +87,15 @@ __device__ __forceinline__ float act_fn(float z) {
         const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
         return __builtin_amdgcn_rcpf(1.0f + e);
     } else if constexpr (ACT == ACT_GELU) {
-        const float x = fabsf(z) * 0.70710678118654752f;
-        const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, x, 1.0f));
-        float p = fmaf(t, 0.17087277f, -0.82215223f);
-        p = fmaf(t, p, 1.48851587f);
-        p = fmaf(t, p, -1.13520398f);
-        p = fmaf(t, p, 0.27886807f);
-        p = fmaf(t, p, -0.18628806f);
-        p = fmaf(t, p, 0.09678418f);
-        p = fmaf(t, p, 0.37409196f);
-        p = fmaf(t, p, 1.00002368f);
-        p = fmaf(t, p, -1.26551223f);
-        const float ec = t * __builtin_amdgcn_exp2f(fmaf(-x, x, p) * 1.4426950408889634f);
-        const float h = 0.5f * ec;                  // Phi(-|z|)
-        const float phi = z >= 0.0f ? 1.0f - h : h;
-        return z * phi;
+        const float az = fabsf(z);
+        const float t = __builtin_amdgcn_rcpf(fmaf(az, 0.35355339059327373f, 1.0f));
+        float q = fmaf(t, 0.3300653100013733f, -1.023119330406189f);
+        q = fmaf(t, q, 0.6845195889472961f);
+        q = fmaf(t, q, 0.3670990467071533f);
+        q = fmaf(t, q, 1.468679428100586f);
+        q = fmaf(t, q, -2.827233076095581f);
+        const float h = t * __builtin_amdgcn_exp2f(fmaf(az * az, -0.7213475204444817f, q));
+        return fmaf(-az, h, fmaxf(z, 0.0f));
     } else {
         return z;
     }

@@ -4,6 +4,8 @@
 
 #include "gba.h"
 #include "gba_kernels.hpp"
+#include "gemm_v2.hpp"
+#include "gemm_v3.hpp"
 
 namespace gba {
 
@@ -45,8 +47,79 @@ struct ScheduleEntry {
     GBA_KERNEL_INSTS_(BM, BN, BK, WM, WN)                                                   \
     namespace gba {                                                                         \
     extern const ScheduleEntry NAME;                                                        \
-    const ScheduleEntry NAME = {{BM, BN, BK, WM, WN, 2, 1, GROUP_M},                        \
+    const ScheduleEntry NAME = {{BM, BN, BK, WM, WN, 2, 1, GROUP_M, 0, 0, 0},                     \
                                 {GBA_LAUNCHERS_(BM, BN, BK, WM, WN, 0),                     \
                                  GBA_LAUNCHERS_(BM, BN, BK, WM, WN, 1)}};                   \
+    }
+#endif
+
+// ---- direct-to-LDS kernel (gemm_v2.hpp) ----
+#define GBA_V2_INST_(BM, BN, BK, WM, WN, S, DT, ACT)                                          \
+    template __global__ void gba::gemm_v2_kernel<BM, BN, BK, WM, WN, S, DT, ACT>(             \
+        const uint16_t *__restrict__, const uint16_t *__restrict__, const uint16_t *__restrict__, \
+        uint16_t *__restrict__, int, int, int, int, int, int, int);
+
+#define GBA_V2_INSTS_(BM, BN, BK, WM, WN, S)                                                   \
+    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 0)                                                  \
+    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 1)                                                  \
+    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 2)                                                  \
+    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 3)                                                  \
+    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 0)                                                  \
+    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 1)                                                  \
+    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 2)                                                  \
+    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 3)
+
+#define GBA_V2_LAUNCHERS_(BM, BN, BK, WM, WN, S, DT)                                           \
+    {gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 0>,                                        \
+     gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 1>,                                        \
+     gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 2>,                                        \
+     gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 3>}
+
+#ifdef __HIP_DEVICE_COMPILE__
+#define GBA_V2_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, S, GROUP_M) GBA_V2_INSTS_(BM, BN, BK, WM, WN, S)
+#else
+#define GBA_V2_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, S, GROUP_M)                          \
+    GBA_V2_INSTS_(BM, BN, BK, WM, WN, S)                                                     \
+    namespace gba {                                                                          \
+    extern const ScheduleEntry NAME;                                                         \
+    const ScheduleEntry NAME = {{BM, BN, BK, WM, WN, S, 1, GROUP_M, 1, 0, 0},                      \
+                                {GBA_V2_LAUNCHERS_(BM, BN, BK, WM, WN, S, 0),                \
+                                 GBA_V2_LAUNCHERS_(BM, BN, BK, WM, WN, S, 1)}};              \
+    }
+#endif
+
+// ---- interleaved direct-to-LDS kernel (gemm_v3.hpp) ----
+#define GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, DT, ACT)                                   \
+    template __global__ void gba::gemm_v3_kernel<BM, BN, BK, WM, WN, S, L, SP, DT, ACT>(      \
+        const uint16_t *__restrict__, const uint16_t *__restrict__, const uint16_t *__restrict__, \
+        uint16_t *__restrict__, int, int, int, int, int, int, int);
+
+#define GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP)                                            \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 0)                                           \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 1)                                           \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 2)                                           \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 3)                                           \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 0)                                           \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 1)                                           \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 2)                                           \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 3)
+
+#define GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, DT)                                    \
+    {gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, DT, 0>,                                 \
+     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, DT, 1>,                                 \
+     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, DT, 2>,                                 \
+     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, DT, 3>}
+
+#ifdef __HIP_DEVICE_COMPILE__
+#define GBA_V3_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, S, L, SP, GROUP_M)                   \
+    GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP)
+#else
+#define GBA_V3_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, S, L, SP, GROUP_M)                   \
+    GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP)                                              \
+    namespace gba {                                                                          \
+    extern const ScheduleEntry NAME;                                                         \
+    const ScheduleEntry NAME = {{BM, BN, BK, WM, WN, S, 1, GROUP_M, 2, L, SP},               \
+                                {GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, 0),         \
+                                 GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, 1)}};       \
     }
 #endif

@@ -1,0 +1,280 @@
+// Interleaved direct-to-LDS GEMM kernel for gfx950.
+//
+// Same tiles, LDS layouts and epilogue as gemm_v2.hpp; the difference is the
+// order in which a wave issues its instructions. Moving a slice from HBM/L2 into
+// LDS takes the CU's address path about as long as half of the slice's MFMA
+// work, and a wave that issues all its direct-to-LDS loads back to back stalls
+// in issue for that whole time. Here every MFMA step (16 K deep) is written out
+// as a fixed sequence: one MFMA, then the next step's fragment reads and this
+// slice's share of global->LDS loads, then the next MFMA, ... so the matrix core
+// keeps running while the loads drain.
+//
+//  * The loads of slice t+STAGES are spread over SPREAD MFMA steps: the one
+//    right after the barrier that frees their stage, and the first SPREAD-1
+//    steps of the next slice. All of them are issued before the next barrier,
+//    so every wait is "all but the (STAGES-2) newest slices".
+//  * Only the first LDW waves issue global->LDS loads; with LDW < waves, the
+//    other waves on the same SIMDs keep issuing MFMAs while the loaders wait
+//    on the address path.
+//  * Slices past the end of K are still "loaded" with every lane out of range
+//    (zeros, no memory access), which keeps the wait counts uniform.
+#pragma once
+
+#include "gemm_v2.hpp"
+
+namespace gba {
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int DT, int ACT>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+               const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int M, int N, int K,
+               int tiles_m, int tiles_n, int raster, int group_m) {
+    constexpr int NW = WM * WN;
+    constexpr int NTL = LDW * 64;         // loader threads
+    constexpr int CHA = BK / 8;
+    constexpr int CHB = BN / 8;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int NMF = FM * FN;          // MFMAs per 16-deep step
+    constexpr int NPF = FM + 2 * FN;      // fragment reads per step
+    constexpr int KK = BK / 16;
+    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
+    constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    constexpr int A_LD = BM * CHA / NTL;
+    constexpr int B_LD = BK * CHB / NTL;
+    constexpr int LD = A_LD + B_LD;       // loads per loader thread per slice
+    constexpr int LD_STEP = (LD + SPREAD - 1) / SPREAD;
+    static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+    static_assert(BN >= 128, "B swizzle needs at least 16 chunks per row");
+    static_assert(LDW >= 1 && LDW <= NW && NW % LDW == 0, "loader waves");
+    static_assert((BM * CHA) % NTL == 0 && (BK * CHB) % NTL == 0, "slices split evenly");
+    static_assert(STAGES >= 2 && STAGES * STAGE_BYTES <= 160 * 1024, "LDS ring too large");
+    static_assert(STAGES * LD < 64, "vmcnt range");
+    static_assert(SPREAD >= 1 && SPREAD <= KK, "loads must be issued before the next barrier");
+    static_assert(LD_STEP <= NMF, "at most one load per MFMA");
+
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+
+    int tm, tn;
+    {
+        int t = blockIdx.x;
+        if (raster) {
+            t = xcd_remap(t, gridDim.x);
+            grouped_tile(t, tiles_m, tiles_n, group_m, tm, tn);
+        } else {
+            tm = t / tiles_n;
+            tn = t % tiles_n;
+        }
+    }
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wid = tid >> 6;
+    const int wm = wid / WN, wn = wid % WN;
+    const int nk = (K + BK - 1) / BK;
+    const int wid_s = __builtin_amdgcn_readfirstlane(wid);
+    const bool loader = (LDW == NW) || wid_s < LDW;
+    const int rows_a = min(M - m0, BM);
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(GBA_LDS void *)smem;
+
+    // Loader lanes' byte offsets within a slice (row r, logical chunk c), fixed
+    // for the whole K loop; the slice's K offset goes into the descriptor base.
+    uint32_t off[LD];
+    int a_k[A_LD];
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+        const int s = i * NTL + tid;
+        const int r = s / CHA, p = s % CHA;
+        const int c = swz<CHA>(r, p);
+        a_k[i] = c * 8;
+        off[i] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)c * 16u;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+        const int s = i * NTL + tid;
+        const int r = s / CHB, p = s % CHB;
+        const int c = p ^ (((r & 3) * 2 + ((r >> 3) & 1) * 8) & (CHB - 1));
+        off[A_LD + i] = n0 + c * 8 < N ? (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u
+                                       : kOobOffset;
+    }
+
+    // Descriptors and LDS targets of one slice (slices at or past nk read nothing).
+    struct SliceDma {
+        __amdgpu_buffer_rsrc_t ra, rb;
+        uint32_t la, lb;
+        int k0;
+    };
+    auto slice_dma = [&](int kt) {
+        SliceDma d;
+        const int stage = kt % STAGES;
+        d.la = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(stage * STAGE_BYTES + wid_s * 64 * 16));
+        d.lb = d.la + A_BYTES;
+        d.k0 = kt * BK;
+        const bool live = d.k0 < K;
+        const uint32_t bytes_a =
+            live ? (uint32_t)rows_a * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u;
+        d.ra = make_rsrc(A + (size_t)m0 * K + (live ? d.k0 : 0), bytes_a);
+        const uint32_t bytes_b = live ? (uint32_t)min(K - d.k0, BK) * (uint32_t)N * 2u : 0u;
+        d.rb = make_rsrc(B + (size_t)(live ? d.k0 : 0) * N + n0, bytes_b);
+        return d;
+    };
+    auto dma_one = [&](const SliceDma &d, int i) {
+        if (i < A_LD) {
+            const uint32_t o = d.k0 + a_k[i] < K ? off[i] : kOobOffset;
+            buffer_load_lds16(d.ra, o, d.la + i * NTL * 16);
+        } else {
+            buffer_load_lds16(d.rb, off[i], d.lb + (i - A_LD) * NTL * 16);
+        }
+    };
+
+    // Fragment reads for MFMA step kk of a stage.
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    const int tg = lane >> 4, tj = lane & 15;
+    int a_row_off[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) a_row_off[fm] = (wm * WTM + fm * 32 + lrow) * (BK * 2);
+    auto a_addr = [&](int fm, int kk) -> int {
+        const int r = wm * WTM + fm * 32 + lrow;
+        return a_row_off[fm] + swz<CHA>(r, 2 * kk + lhalf) * 16;
+    };
+    auto b_addr = [&](int fn, int kk, int h) -> int {
+        const int k = kk * 16 + 8 * (tg >> 1) + 4 * h + (tj >> 2);
+        const int n = wn * WTN + fn * 32 + 16 * (tg & 1) + 4 * (tj & 3);
+        const int c = (n >> 3) ^ (((k & 3) * 2 + ((k >> 3) & 1) * 8) & (CHB - 1));
+        return A_BYTES + k * (BN * 2) + c * 16 + (n & 4) * 2;
+    };
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+        for (int b = 0; b < FM; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
+
+    u32x4 fa[2][FM];
+    i16x4 fbl[2][FN], fbh[2][FN];
+    auto read_one = [&](int buf, const char *base, int kk, int r) {
+        if (r < FM) {
+            fa[buf][r] = *reinterpret_cast<const u32x4 *>(base + a_addr(r, kk));
+        } else {
+            const int fn = (r - FM) >> 1, h = (r - FM) & 1;
+            const i16x4 v =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((GBA_LDS i16x4 *)(base + b_addr(fn, kk, h)));
+            if (h)
+                fbh[buf][fn] = v;
+            else
+                fbl[buf][fn] = v;
+        }
+    };
+
+    // One MFMA step: NMF MFMAs on buffer `cur`, with the next step's fragment
+    // reads (into cur^1, from `pf_base` step pf_kk) and, when `dma` is set, `nd`
+    // loads of slice `d` starting at load index `d0` woven in between.
+    auto step = [&](int cur, const char *pf_base, int pf_kk, bool dma, const SliceDma &d, int d0,
+                    int nd) {
+        constexpr int every = NMF / (LD_STEP > 0 ? LD_STEP : 1);
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+            const int fn = q / FM, fm = q % FM;
+            const u32x4 bop = __builtin_bit_cast(
+                u32x4, __builtin_shufflevector(fbl[cur][fn], fbh[cur][fn], 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[fn][fm] = mfma32x32x16<DT>(bop, fa[cur][fm], acc[fn][fm]);
+            if (q < NPF) read_one(cur ^ 1, pf_base, pf_kk, q);
+            if (dma && q % every == 0 && q / every < nd) dma_one(d, d0 + q / every);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r = NMF; r < NPF; ++r) read_one(cur ^ 1, pf_base, pf_kk, r);
+    };
+
+    // Prologue: slices 0 .. STAGES-2 requested in full and the first LD_STEP
+    // loads of slice STAGES-1 (the rest follow in slice 0's first steps, as in
+    // the steady state); slice 0 waited for.
+    if (loader) {
+#pragma unroll
+        for (int s = 0; s < STAGES; ++s) {
+            const SliceDma d = slice_dma(s);
+#pragma unroll
+            for (int i = 0; i < (s + 1 < STAGES ? LD : LD_STEP); ++i) dma_one(d, i);
+        }
+    }
+    wait_vmcnt<(STAGES - 2) * LD + LD_STEP>();
+    block_barrier();
+#pragma unroll
+    for (int r = 0; r < NPF; ++r) read_one(0, smem, 0, r);
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const char *cur_base = smem + (kt % STAGES) * STAGE_BYTES;
+        const char *nxt_base = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
+        const SliceDma dprev = slice_dma(kt - 1 + STAGES);   // its loads LD_STEP.. go here
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int cur = kk & 1;
+            if (kk + 1 < KK) {
+                const int first = (kk + 1) * LD_STEP;
+                const int nd = kk + 1 < SPREAD ? min(LD_STEP, LD - first) : 0;
+                if (loader)
+                    step(cur, cur_base, kk + 1, nd > 0, dprev, first, nd);
+                else
+                    step(cur, cur_base, kk + 1, false, dprev, first, 0);
+            } else {
+                // Publish slice kt+1 (own loads landed, own reads of slice kt
+                // returned; then the same for all waves) and recycle slice kt's
+                // stage for slice kt+STAGES.
+                wait_vmcnt_lgkm0<(STAGES - 2) * LD>();
+                block_barrier();
+                const SliceDma dnew = slice_dma(kt + STAGES);
+                if (loader)
+                    step(cur, nxt_base, 0, true, dnew, 0, min(LD_STEP, LD));
+                else
+                    step(cur, nxt_base, 0, false, dnew, 0, 0);
+            }
+        }
+    }
+    // No direct-to-LDS write may outlive the workgroup's LDS.
+    wait_vmcnt<0>();
+
+    // Epilogue: + bias[n], activation, round once, masked 8-byte stores.
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = n0 + wn * WTN + fn * 32 + i * 8 + lhalf * 4;
+            if (n >= N) continue;
+            float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+            if (bias) {
+                const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n);
+                b0 = to_f32<DT>(bb.x & 0xffffu);
+                b1 = to_f32<DT>(bb.x >> 16);
+                b2 = to_f32<DT>(bb.y & 0xffffu);
+                b3 = to_f32<DT>(bb.y >> 16);
+            }
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int m = m0 + wm * WTM + fm * 32 + lrow;
+                if (m >= M) continue;
+                const f32x16 &a = acc[fn][fm];
+                u32x2 o;
+                o.x = pack2<DT>(act_fn<ACT>(a[4 * i + 0] + b0), act_fn<ACT>(a[4 * i + 1] + b1));
+                o.y = pack2<DT>(act_fn<ACT>(a[4 * i + 2] + b2), act_fn<ACT>(a[4 * i + 3] + b3));
+                *reinterpret_cast<u32x2 *>(C + (size_t)m * N + n) = o;
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int DT, int ACT>
+hipError_t launch_gemm_v3(const void *A, const void *B, const void *bias, void *C, int M, int N,
+                          int K, int raster, int group_m, hipStream_t stream) {
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const long long grid = (long long)tiles_m * tiles_n;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, BK, WM, WN, STAGES, LDW, SPREAD, DT, ACT>),
+                       dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream, (const uint16_t *)A,
+                       (const uint16_t *)B, (const uint16_t *)bias, (uint16_t *)C, M, N, K, tiles_m,
+                       tiles_n, raster, group_m < 1 ? 1 : group_m);
+    return hipGetLastError();
+}
+
+}  // namespace gba
