@@ -73,10 +73,11 @@ typedef enum {
  * "writing-tilelang-kernels", Key API Patterns). kernel selects the main-loop
  * design: 0 = tiles staged through registers into LDS (B transposed on the
  * way), 1 = direct global->LDS loads into a `stages`-deep ring with transposing
- * LDS reads for B, 2 = the same with every instruction of a 16-deep MFMA step
- * placed by hand: global->LDS loads (issued by the first `loaders` waves, spread
- * over `spread` steps) and the next step's LDS reads between the MFMAs.
- * loaders and spread are 0 for kernels 0 and 1. */
+ * LDS reads for B, 2 = the same with every instruction of an MFMA step placed
+ * by hand: global->LDS loads (issued by the first `loaders` waves, spread over
+ * `spread` steps) and the next step's LDS reads between the MFMAs, using
+ * 32x32x16 MFMAs; 3 = kernel 2 with 16x16x32 MFMAs (the default: same work, less
+ * power, so higher sustained clocks). loaders and spread are 0 for kernels 0, 1. */
 typedef struct {
     int32_t bm, bn, bk;
     int32_t wm, wn;

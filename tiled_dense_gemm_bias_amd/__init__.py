@@ -46,7 +46,7 @@ class Schedule(ctypes.Structure):
     @classmethod
     def from_dict(cls, d: dict) -> "Schedule":
         s = cls()
-        defaults = {"stages": 2, "raster": 1, "group_m": 4, "kernel": 2, "loaders": 4, "spread": 2}
+        defaults = {"stages": 2, "raster": 1, "group_m": 4, "kernel": 3, "loaders": 4, "spread": 1}
         for f in SCHED_FIELDS:
             setattr(s, f, int(d.get(f, defaults.get(f, 0))))
         return s

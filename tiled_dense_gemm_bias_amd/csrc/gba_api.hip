@@ -24,13 +24,13 @@ namespace gba {
 extern const ScheduleEntry s_256x256x64_w2x2;
 extern const ScheduleEntry s_128x128x32_w2x2;
 extern const ScheduleEntry d_256x256x64_w2x2_s2;
-extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p2;
-extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p1;
-extern const ScheduleEntry i_256x256x32_w2x2_s4_l4_p1;
-extern const ScheduleEntry i_256x256x64_w2x4_s2_l8_p2;
-extern const ScheduleEntry i_256x128x64_w2x2_s3_l4_p2;
-extern const ScheduleEntry i_128x256x64_w2x2_s3_l4_p2;
-extern const ScheduleEntry i_128x128x64_w2x2_s3_l4_p2;
+extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p1_m32;
+extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p2_m32;
+extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p1_m16;
+extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p2_m16;
+extern const ScheduleEntry i_256x128x64_w2x2_s3_l4_p1_m16;
+extern const ScheduleEntry i_128x256x64_w2x2_s3_l4_p1_m16;
+extern const ScheduleEntry i_128x128x64_w2x2_s3_l4_p1_m16;
 }  // namespace gba
 
 namespace {
@@ -38,11 +38,12 @@ namespace {
 using gba::ScheduleEntry;
 
 const ScheduleEntry *const kTable[] = {
-    // interleaved direct-to-LDS kernels (the default family)
-    &gba::i_256x256x64_w2x2_s2_l4_p2, &gba::i_256x256x64_w2x2_s2_l4_p1,
-    &gba::i_256x256x32_w2x2_s4_l4_p1, &gba::i_256x256x64_w2x4_s2_l8_p2,
-    &gba::i_256x128x64_w2x2_s3_l4_p2, &gba::i_128x256x64_w2x2_s3_l4_p2,
-    &gba::i_128x128x64_w2x2_s3_l4_p2,
+    // interleaved direct-to-LDS kernels with 16x16x32 MFMAs (the default family)
+    &gba::i_256x256x64_w2x2_s2_l4_p1_m16, &gba::i_256x256x64_w2x2_s2_l4_p2_m16,
+    &gba::i_256x128x64_w2x2_s3_l4_p1_m16, &gba::i_128x256x64_w2x2_s3_l4_p1_m16,
+    &gba::i_128x128x64_w2x2_s3_l4_p1_m16,
+    // the same with 32x32x16 MFMAs
+    &gba::i_256x256x64_w2x2_s2_l4_p1_m32, &gba::i_256x256x64_w2x2_s2_l4_p2_m32,
     // direct-to-LDS kernel with compiler-scheduled steps
     &gba::d_256x256x64_w2x2_s2,
     // register-staged kernels, incl. the 128x128x32 starting tile
@@ -184,11 +185,11 @@ gba_schedule heuristic(int64_t M, int64_t N, int cus) {
     const int64_t want = (int64_t)cus * 9 / 10;
     const ScheduleEntry *e;
     if (tiles(256, 256) >= want)
-        e = &gba::i_256x256x64_w2x2_s2_l4_p2;
+        e = &gba::i_256x256x64_w2x2_s2_l4_p1_m16;
     else if (tiles(256, 128) >= want)
-        e = M >= N ? &gba::i_256x128x64_w2x2_s3_l4_p2 : &gba::i_128x256x64_w2x2_s3_l4_p2;
+        e = M >= N ? &gba::i_256x128x64_w2x2_s3_l4_p1_m16 : &gba::i_128x256x64_w2x2_s3_l4_p1_m16;
     else
-        e = &gba::i_128x128x64_w2x2_s3_l4_p2;
+        e = &gba::i_128x128x64_w2x2_s3_l4_p1_m16;
     return e->sched;
 }
 

@@ -89,37 +89,38 @@ struct ScheduleEntry {
 #endif
 
 // ---- interleaved direct-to-LDS kernel (gemm_v3.hpp) ----
-#define GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, DT, ACT)                                   \
-    template __global__ void gba::gemm_v3_kernel<BM, BN, BK, WM, WN, S, L, SP, DT, ACT>(      \
+#define GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, DT, ACT)                               \
+    template __global__ void gba::gemm_v3_kernel<BM, BN, BK, WM, WN, S, L, SP, MS, DT, ACT>(  \
         const uint16_t *__restrict__, const uint16_t *__restrict__, const uint16_t *__restrict__, \
         uint16_t *__restrict__, int, int, int, int, int, int, int);
 
-#define GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP)                                            \
-    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 0)                                           \
-    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 1)                                           \
-    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 2)                                           \
-    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 3)                                           \
-    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 0)                                           \
-    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 1)                                           \
-    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 2)                                           \
-    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 3)
+#define GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP, MS)                                        \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 0, 0)                                       \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 0, 1)                                       \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 0, 2)                                       \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 0, 3)                                       \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 1, 0)                                       \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 1, 1)                                       \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 1, 2)                                       \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 1, 3)
 
-#define GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, DT)                                    \
-    {gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, DT, 0>,                                 \
-     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, DT, 1>,                                 \
-     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, DT, 2>,                                 \
-     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, DT, 3>}
+#define GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, MS, DT)                                \
+    {gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, MS, DT, 0>,                             \
+     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, MS, DT, 1>,                             \
+     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, MS, DT, 2>,                             \
+     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, MS, DT, 3>}
 
+// kernel id 2: 32x32x16 MFMAs; kernel id 3: 16x16x32 MFMAs.
 #ifdef __HIP_DEVICE_COMPILE__
-#define GBA_V3_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, S, L, SP, GROUP_M)                   \
-    GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP)
+#define GBA_V3_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, S, L, SP, MS, GROUP_M)               \
+    GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP, MS)
 #else
-#define GBA_V3_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, S, L, SP, GROUP_M)                   \
-    GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP)                                              \
+#define GBA_V3_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, S, L, SP, MS, GROUP_M)               \
+    GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP, MS)                                          \
     namespace gba {                                                                          \
     extern const ScheduleEntry NAME;                                                         \
-    const ScheduleEntry NAME = {{BM, BN, BK, WM, WN, S, 1, GROUP_M, 2, L, SP},               \
-                                {GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, 0),         \
-                                 GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, 1)}};       \
+    const ScheduleEntry NAME = {{BM, BN, BK, WM, WN, S, 1, GROUP_M, MS == 32 ? 2 : 3, L, SP}, \
+                                {GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, MS, 0),     \
+                                 GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, MS, 1)}};   \
     }
 #endif

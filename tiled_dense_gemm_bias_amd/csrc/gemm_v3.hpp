@@ -4,7 +4,7 @@
 // order in which a wave issues its instructions. Moving a slice from HBM/L2 into
 // LDS takes the CU's address path about as long as half of the slice's MFMA
 // work, and a wave that issues all its direct-to-LDS loads back to back stalls
-// in issue for that whole time. Here every MFMA step (16 K deep) is written out
+// in issue for that whole time. Here every MFMA step is written out
 // as a fixed sequence: one MFMA, then the next step's fragment reads and this
 // slice's share of global->LDS loads, then the next MFMA, ... so the matrix core
 // keeps running while the loads drain.
@@ -24,7 +24,36 @@
 
 namespace gba {
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int DT, int ACT>
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int MS> struct Acc;
+template <> struct Acc<32> { typedef f32x16 type; static constexpr int n = 16; };
+template <> struct Acc<16> { typedef f32x4 type; static constexpr int n = 4; };
+
+// v_mfma_f32_16x16x32_{f16,bf16}: lane l holds row/column l % 16 and K chunk
+// l / 16 of the operands; the 16x16 result gives lane l column l % 16, rows
+// 4 (l / 16) .. +3 -- with B^T as the first operand, four adjacent n of row m.
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (DT == DT_F16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+}
+
+// XOR (in 16-byte chunks) of k row r of a B stage. The transposing reads of one
+// instruction touch k rows r0 + {0..3} + 8 {0..3} at one 32-byte column pair;
+// the even XOR moves each of those rows to its own pair slot.
+template <int CHB>
+__device__ __forceinline__ int bswz(int r) {
+    return (2 * (r & 3) + 8 * ((r >> 3) & 3)) & (CHB - 1);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int MS, int DT,
+          int ACT>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int M, int N, int K,
@@ -34,17 +63,23 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     constexpr int CHA = BK / 8;
     constexpr int CHB = BN / 8;
     constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int NMF = FM * FN;          // MFMAs per 16-deep step
+    constexpr int BD = MS;                // MFMA output block: BD x BD
+    constexpr int KS = MS == 32 ? 16 : 32;  // K depth of one MFMA
+    constexpr int NI = MS == 32 ? 4 : 1;  // 4-column groups per lane and block
+    constexpr int FM = WTM / BD, FN = WTN / BD;
+    constexpr int NMF = FM * FN;          // MFMAs per step
     constexpr int NPF = FM + 2 * FN;      // fragment reads per step
-    constexpr int KK = BK / 16;
+    constexpr int KK = BK / KS;           // steps per slice
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
     constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     constexpr int A_LD = BM * CHA / NTL;
     constexpr int B_LD = BK * CHB / NTL;
     constexpr int LD = A_LD + B_LD;       // loads per loader thread per slice
     constexpr int LD_STEP = (LD + SPREAD - 1) / SPREAD;
+    static_assert(MS == 32 || MS == 16, "MFMA 32x32x16 or 16x16x32");
     static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+    static_assert(KK % 2 == 0, "fragment buffers alternate within a slice");
+    static_assert(WTM % BD == 0 && WTN % BD == 0, "wave tile must be whole MFMA blocks");
     static_assert(BN >= 128, "B swizzle needs at least 16 chunks per row");
     static_assert(LDW >= 1 && LDW <= NW && NW % LDW == 0, "loader waves");
     static_assert((BM * CHA) % NTL == 0 && (BK * CHB) % NTL == 0, "slices split evenly");
@@ -92,7 +127,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     for (int i = 0; i < B_LD; ++i) {
         const int s = i * NTL + tid;
         const int r = s / CHB, p = s % CHB;
-        const int c = p ^ (((r & 3) * 2 + ((r >> 3) & 1) * 8) & (CHB - 1));
+        const int c = p ^ bswz<CHB>(r);
         off[A_LD + i] = n0 + c * 8 < N ? (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u
                                        : kOobOffset;
     }
@@ -127,29 +162,33 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     };
 
     // Fragment reads for MFMA step kk of a stage.
-    const int lrow = lane & 31, lhalf = lane >> 5;
+    const int lhalf = lane >> 5;
     const int tg = lane >> 4, tj = lane & 15;
-    int a_row_off[FM];
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) a_row_off[fm] = (wm * WTM + fm * 32 + lrow) * (BK * 2);
+    // A operand of block fm: lane l holds row (l % BD) of the block, K chunk
+    // (KS/8) kk + l / BD. B^T operand of block fn: lane l holds column (l % BD),
+    // the same K chunk, gathered by two transposing reads of four k rows each.
+    const int lrow_b = lane % BD, lchunk = lane / BD;
     auto a_addr = [&](int fm, int kk) -> int {
-        const int r = wm * WTM + fm * 32 + lrow;
-        return a_row_off[fm] + swz<CHA>(r, 2 * kk + lhalf) * 16;
+        const int r = wm * WTM + fm * BD + lrow_b;
+        return r * (BK * 2) + swz<CHA>(r, (KS / 8) * kk + lchunk) * 16;
     };
     auto b_addr = [&](int fn, int kk, int h) -> int {
-        const int k = kk * 16 + 8 * (tg >> 1) + 4 * h + (tj >> 2);
-        const int n = wn * WTN + fn * 32 + 16 * (tg & 1) + 4 * (tj & 3);
-        const int c = (n >> 3) ^ (((k & 3) * 2 + ((k >> 3) & 1) * 8) & (CHB - 1));
+        const int k = MS == 32 ? kk * 16 + 8 * (tg >> 1) + 4 * h + (tj >> 2)
+                               : kk * 32 + 8 * tg + 4 * h + (tj >> 2);
+        const int n = MS == 32 ? wn * WTN + fn * 32 + 16 * (tg & 1) + 4 * (tj & 3)
+                               : wn * WTN + fn * 16 + 4 * (tj & 3);
+        const int c = (n >> 3) ^ bswz<CHB>(k);
         return A_BYTES + k * (BN * 2) + c * 16 + (n & 4) * 2;
     };
 
-    f32x16 acc[FN][FM];
+    using AccT = typename Acc<MS>::type;
+    AccT acc[FN][FM];
 #pragma unroll
     for (int a = 0; a < FN; ++a)
 #pragma unroll
         for (int b = 0; b < FM; ++b)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
+            for (int e = 0; e < Acc<MS>::n; ++e) acc[a][b][e] = 0.0f;
 
     u32x4 fa[2][FM];
     i16x4 fbl[2][FN], fbh[2][FN];
@@ -178,7 +217,10 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             const int fn = q / FM, fm = q % FM;
             const u32x4 bop = __builtin_bit_cast(
                 u32x4, __builtin_shufflevector(fbl[cur][fn], fbh[cur][fn], 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[fn][fm] = mfma32x32x16<DT>(bop, fa[cur][fm], acc[fn][fm]);
+            if constexpr (MS == 32)
+                acc[fn][fm] = mfma32x32x16<DT>(bop, fa[cur][fm], acc[fn][fm]);
+            else
+                acc[fn][fm] = mfma16x16x32<DT>(bop, fa[cur][fm], acc[fn][fm]);
             if (q < NPF) read_one(cur ^ 1, pf_base, pf_kk, q);
             if (dma && q % every == 0 && q / every < nd) dma_one(d, d0 + q / every);
             __builtin_amdgcn_sched_barrier(0);
@@ -238,8 +280,9 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int n = n0 + wn * WTN + fn * 32 + i * 8 + lhalf * 4;
+        for (int i = 0; i < NI; ++i) {
+            const int n = n0 + wn * WTN + fn * BD +
+                          (MS == 32 ? i * 8 + lhalf * 4 : 4 * (lane >> 4));
             if (n >= N) continue;
             float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
             if (bias) {
@@ -251,9 +294,9 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             }
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
-                const int m = m0 + wm * WTM + fm * 32 + lrow;
+                const int m = m0 + wm * WTM + fm * BD + lrow_b;
                 if (m >= M) continue;
-                const f32x16 &a = acc[fn][fm];
+                const AccT &a = acc[fn][fm];
                 u32x2 o;
                 o.x = pack2<DT>(act_fn<ACT>(a[4 * i + 0] + b0), act_fn<ACT>(a[4 * i + 1] + b1));
                 o.y = pack2<DT>(act_fn<ACT>(a[4 * i + 2] + b2), act_fn<ACT>(a[4 * i + 3] + b3));
@@ -263,14 +306,15 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int DT, int ACT>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int MS, int DT,
+          int ACT>
 hipError_t launch_gemm_v3(const void *A, const void *B, const void *bias, void *C, int M, int N,
                           int K, int raster, int group_m, hipStream_t stream) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const long long grid = (long long)tiles_m * tiles_n;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, BK, WM, WN, STAGES, LDW, SPREAD, DT, ACT>),
+    hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, BK, WM, WN, STAGES, LDW, SPREAD, MS, DT, ACT>),
                        dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream, (const uint16_t *)A,
                        (const uint16_t *)B, (const uint16_t *)bias, (uint16_t *)C, M, N, K, tiles_m,
                        tiles_n, raster, group_m < 1 ? 1 : group_m);
