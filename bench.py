@@ -1,6 +1,6 @@
 """Benchmark of the fused GEMM + bias + GELU on one MI355X.
 
-    python bench.py [--steps 50] [--warmup 100] [--workload c3_gelu] [--unfused]
+    python bench.py [--steps 50] [--warmup 300] [--workload c3_gelu] [--unfused]
 
 One step is one gemm_bias_act call over the whole workload (schedule choice,
 global->LDS loads, MFMA main loop, fused epilogue, store), with inputs already
@@ -9,9 +9,10 @@ synchronisations. Per-launch HIP events on the launch stream give the kernel's
 average duration (the roofline's "achieved") and the median latency by device
 events, as the pages' bench helper reports it.
 
-The default W is 100, not the pages' 10: an MI355X coming out of idle raises
-its clocks over roughly the first 100 launches of this kernel (~13 ms); with 10
-warmups the timed steps still sit in that ramp (about 13% slower).
+The default W is 300, not the pages' 10: an MI355X coming out of idle raises
+its clocks over the first ~300 launches of this kernel (~40 ms). Measured per
+100-launch window from cold at 4096^3: 0.149, 0.125, 0.122, then 0.120 ms
+flat through 1500 launches. With 10 warmups the timed steps sit in the ramp.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -64,20 +65,23 @@ def measured_traffic(workload: str):
 
 
 def time_launches(fn, steps, warmup, stream):
+    """W untimed calls, then K timed ones. One event is recorded on the launch
+    stream before each timed call and one after the last, so the K per-launch
+    durations are back-to-back intervals: each holds one kernel plus the
+    dispatch gap before the next."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    for s, e in ev:
-        s.record(stream)
+    for i in range(steps):
+        ev[i].record(stream)
         fn()
-        e.record(stream)
+    ev[steps].record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    per = [s.elapsed_time(e) for s, e in ev]
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     return wall_ms, per
 
 
@@ -114,7 +118,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="c3_gelu")
     ap.add_argument("--unfused", action="store_true", help="also time gemm + bias_act")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -174,9 +178,7 @@ def main(argv=None) -> int:
     sched = gba.get_schedule(w.M, w.N, w.K, w.act, w.dtype)
     log("[bench] schedule %s" % sched)
 
-    def step():
-        gba.gemm_bias_act(a_t, b_t, bias_t, c_t, w.act)
-
+    step = gba.bind_gemm_bias_act(a_t, b_t, bias_t, c_t, w.act)
     wall_ms, per = time_launches(step, a.steps, a.warmup, stream)
     ms_per_step = wall_ms / a.steps
     kern_avg = sum(per) / len(per)

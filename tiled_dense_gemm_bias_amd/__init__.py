@@ -175,6 +175,38 @@ def gemm_bias_act(a, b, bias, c, act="gelu"):
     return c
 
 
+def bind_gemm_bias_act(a, b, bias, c, act="gelu"):
+    """Check and marshal the arguments once; return a no-argument callable that
+    enqueues c = act(a @ b + bias) on the stream current now (one C call per
+    invocation). For tight loops such as benchmarks; the tensors must stay alive
+    and unchanged in shape while the callable is used."""
+    dev = _check_dev(a, b, bias, c)
+    dt = _dtype_code(a)
+    for t in (b, bias, c):
+        if t is not None and _dtype_code(t) != dt:
+            raise TypeError("all operands must share one dtype")
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K or tuple(c.shape) != (M, N) or (bias is not None and tuple(bias.shape) != (N,)):
+        raise ValueError("shape mismatch")
+    torch = _torch()
+    lib = _lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    args = (_ptr(a), _ptr(b), _ptr(bias), _ptr(c), M, N, K, _act(act), dt)
+    fn = lib.gemm_bias_act
+    set_stream = lib.gba_set_stream
+    set_stream(stream)
+
+    def launch():
+        st = fn(*args)
+        if st != 0:
+            raise GbaError(st, "gemm_bias_act")
+
+    if torch.cuda.current_device() != dev.index:
+        raise ValueError("bind on the tensors' device (torch.cuda.set_device first)")
+    return launch
+
+
 def gemm(a, b, c):
     """c[M,N] = a[M,K] @ b[K,N], rounded to the operand dtype. Returns c."""
     dev = _check_dev(a, b, c)
