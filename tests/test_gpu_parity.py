@@ -331,11 +331,13 @@ def test_epilogue_device_functions_on_dense_grid(act):
         bound = (1e-6 + np.abs(z) * 1.2e-7) * np.abs(ref) + 1e-37
         assert np.all(err <= bound), float((err / bound).max())
     else:
-        # erfc fit with fractional error < 1e-5 (tests/test_gelu_fit.py), evaluated
-        # in fp32; the exp2 of Q2(t) - z^2 log2(e)/2 is conditioned like the
-        # sigmoid's: the fp32 roundings of |z|^2 and of the fma move the result by
-        # about (z^2/2) 2^-24 each, relative.
-        bound = (1.2e-5 + 0.5 * z.astype(np.float64) ** 2 * 6 * 2.0 ** -24) * np.abs(ref) + 1e-37
+        # Phi(-|z|) = 2^Q(|z|) with fractional error < 8e-6 on |z| <= 6
+        # (tests/test_gelu_fit.py); the fp32 Horner steps round Q (|Q| <= 30 there)
+        # by a few ulp, which moves 2^Q by about 1e-6 per ulp relative. Past |z| = 6
+        # the correction term is below 6e-9 absolute, far under the 2^-20 floor of
+        # the fused GEMM's element-wise check.
+        zz = np.abs(z.astype(np.float64))
+        bound = 1.2e-5 * np.abs(ref) + np.where(zz > 6.0, 1e-8, 0.0) + 1e-37
         assert np.all(err <= bound), float((err / bound).max())
 
 

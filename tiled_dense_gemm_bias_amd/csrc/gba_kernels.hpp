@@ -72,13 +72,11 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 //  RELU:    max(z, 0).
 //  SIGMOID: 1 / (1 + 2^(-z log2 e)) with the hardware exp2 and reciprocal.
 //  GELU:    z * Phi(z), written as max(z, 0) - |z| Phi(-|z|) (Phi(z) = 1 - Phi(-z)),
-//           with Phi(-|z|) = erfc(x) / 2, x = |z| / sqrt 2, from the form of Press,
-//           Teukolsky, Vetterling & Flannery, "Numerical Recipes" (2nd ed., sec.
-//           6.2): erfc(x) = t exp(-x^2 + Q(t)), t = 1 / (1 + x/2). Q here is a
-//           degree-5 fit (tiled_dense_gemm_bias_amd/gelu_fit.py) with fractional
-//           error below 8e-6 for x in [0, 9.5]; log2(e) and the factor 1/2 are
-//           folded into its coefficients. The error is relative, so z * Phi(z)
-//           stays accurate deep in the negative tail (bf16 outputs reach 1e-38).
+//           with Phi(-x) = 2^Q(x): Q is a degree-7 polynomial fitted to
+//           log2 Phi(-x) on [0, 6] (tiled_dense_gemm_bias_amd/gelu_fit.py), with
+//           fractional error below 8e-6 there. Its leading coefficient is
+//           negative, so past 6 the correction term |z| 2^Q(|z|) falls below
+//           6e-9 and keeps falling. Seven fma and one exp2, no division.
 template <int ACT>
 __device__ __forceinline__ float act_fn(float z) {
     if constexpr (ACT == ACT_RELU) {
@@ -88,14 +86,14 @@ __device__ __forceinline__ float act_fn(float z) {
         return __builtin_amdgcn_rcpf(1.0f + e);
     } else if constexpr (ACT == ACT_GELU) {
         const float az = fabsf(z);
-        const float t = __builtin_amdgcn_rcpf(fmaf(az, 0.35355339059327373f, 1.0f));
-        float q = fmaf(t, 0.3300653100013733f, -1.023119330406189f);
-        q = fmaf(t, q, 0.6845195889472961f);
-        q = fmaf(t, q, 0.3670990467071533f);
-        q = fmaf(t, q, 1.468679428100586f);
-        q = fmaf(t, q, -2.827233076095581f);
-        const float h = t * __builtin_amdgcn_exp2f(fmaf(az * az, -0.7213475204444817f, q));
-        return fmaf(-az, h, fmaxf(z, 0.0f));
+        float q = fmaf(az, -1.8348076764596044e-06f, 6.15982135059312e-05f);
+        q = fmaf(az, q, -0.0009305241401307285f);
+        q = fmaf(az, q, 0.008507887832820415f);
+        q = fmaf(az, q, -0.05396006256341934f);
+        q = fmaf(az, q, -0.4584644138813019f);
+        q = fmaf(az, q, -1.1512510776519775f);
+        q = fmaf(az, q, -0.9999952912330627f);
+        return fmaf(-az, __builtin_amdgcn_exp2f(q), fmaxf(z, 0.0f));
     } else {
         return z;
     }

@@ -44,6 +44,18 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     }
 }
 
+// Physical 16-byte chunk of logical chunk c in row r of an A stage. With the
+// 16x16x32 operand pattern (lane l reads row l % 16 of a block, chunk l / 16)
+// a plain XOR with r mod 8 keeps ds_read_b128 free of bank conflicts on gfx950
+// (measured with SQ_LDS_BANK_CONFLICT); the 32x32x16 pattern keeps swz<>.
+template <int MS, int CHA>
+__device__ __forceinline__ int aswz(int r, int c) {
+    if constexpr (MS == 16)
+        return c ^ (r & (CHA - 1));
+    else
+        return swz<CHA>(r, c);
+}
+
 // XOR (in 16-byte chunks) of k row r of a B stage. The transposing reads of one
 // instruction touch k rows r0 + {0..3} + 8 {0..3} at one 32-byte column pair;
 // the even XOR moves each of those rows to its own pair slot.
@@ -119,7 +131,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     for (int i = 0; i < A_LD; ++i) {
         const int s = i * NTL + tid;
         const int r = s / CHA, p = s % CHA;
-        const int c = swz<CHA>(r, p);
+        const int c = aswz<MS, CHA>(r, p);
         a_k[i] = c * 8;
         off[i] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)c * 16u;
     }
@@ -170,7 +182,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const int lrow_b = lane % BD, lchunk = lane / BD;
     auto a_addr = [&](int fm, int kk) -> int {
         const int r = wm * WTM + fm * BD + lrow_b;
-        return r * (BK * 2) + swz<CHA>(r, (KS / 8) * kk + lchunk) * 16;
+        return r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * kk + lchunk) * 16;
     };
     auto b_addr = [&](int fn, int kk, int h) -> int {
         const int k = MS == 32 ? kk * 16 + 8 * (tg >> 1) + 4 * h + (tj >> 2)
