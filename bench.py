@@ -41,25 +41,44 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# Sources each kernel family is compiled from (the schedule table and host code
+# are left out: they do not change what a launch of the kernel does).
+KERNEL_HEADERS = {0: ["gba_kernels.hpp"],
+                  1: ["gba_kernels.hpp", "gemm_v2.hpp"],
+                  2: ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp"],
+                  3: ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp"]}
+
+
+def instance_file(s: dict) -> str:
+    """The csrc file that instantiates schedule s."""
+    if s["kernel"] in (2, 3):
+        return "v3_%dx%dx%d_w%dx%d_s%d_l%d_p%d_m%d.hip" % (
+            s["bm"], s["bn"], s["bk"], s["wm"], s["wn"], s["stages"], s["loaders"], s["spread"],
+            32 if s["kernel"] == 2 else 16)
+    if s["kernel"] == 1:
+        return "v2_%dx%dx%d_w%dx%d_s%d.hip" % (s["bm"], s["bn"], s["bk"], s["wm"], s["wn"], s["stages"])
+    return "inst_%dx%dx%d_w%dx%d.hip" % (s["bm"], s["bn"], s["bk"], s["wm"], s["wn"])
+
+
+def kernel_source_hash(sched: dict) -> str:
+    """sha256 over the sources of the kernel that schedule `sched` launches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_dense_gemm_bias_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
-        if fn.endswith((".hip", ".hpp")):
-            h.update(fn.encode())
-            h.update(open(os.path.join(csrc, fn), "rb").read())
+    for fn in KERNEL_HEADERS[sched["kernel"]] + [instance_file(sched)]:
+        h.update(fn.encode())
+        h.update(open(os.path.join(csrc, fn), "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, sched: dict):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources; else None."""
+    were taken on the current sources of the kernel `sched` launches; else None."""
     try:
         data = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     rec = data.get(workload)
-    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+    if not rec or rec.get("kernel_hash") != kernel_source_hash(sched):
         return None
     return rec.get("bytes_per_launch")
 
@@ -214,7 +233,7 @@ def main(argv=None) -> int:
         "pct_of_peak": round(100 * achieved / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(w.name),
+                     "traffic": measured_traffic(w.name, sched),
                      "algorithmic_bytes": alg_bytes, "kernel_avg_ms": round(kern_avg, 5)},
     }
 
