@@ -54,18 +54,18 @@ __device__ __forceinline__ float to_f32(uint32_t h) {
     }
 }
 
-// fp32 -> storage type, round to nearest even (v_cvt_f16_f32 / v_cvt_pk_bf16_f32).
+// fp32 pair -> storage type, round to nearest even, in one v_cvt_pk_f16_f32 /
+// v_cvt_pk_bf16_f32 (gfx950); lo lands in the low half.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    if constexpr (DT == DT_F16) {
-        uint32_t a = __builtin_bit_cast(uint16_t, (_Float16)lo);
-        uint32_t b = __builtin_bit_cast(uint16_t, (_Float16)hi);
-        return a | (b << 16);
-    } else {
-        uint32_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
-        uint32_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
-        return a | (b << 16);
-    }
+    const f32x2 v = {lo, hi};
+    if constexpr (DT == DT_F16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Activation on the fp32 accumulator.

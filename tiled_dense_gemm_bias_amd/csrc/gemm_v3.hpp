@@ -22,6 +22,8 @@
 
 #include "gemm_v2.hpp"
 
+#include <type_traits>
+
 namespace gba {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -288,34 +290,50 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // No direct-to-LDS write may outlive the workgroup's LDS.
     wait_vmcnt<0>();
 
-    // Epilogue: + bias[n], activation, round once, masked 8-byte stores.
+    // Epilogue: + bias[n], activation, round once, 8-byte stores. Addresses are a
+    // 32-bit byte offset from the tile's corner (row pitch N*2, at most 2^32 for
+    // N <= 2^23); rows and columns are masked only in edge tiles. Lane l holds
+    // row (l % BD) of block fm and, per 4-column group i, columns c0(i) .. +3.
+    char *const Ct = reinterpret_cast<char *>(C + (size_t)m0 * N + n0);
+    const int mrow = wm * WTM + lrow_b;
+    auto col0 = [&](int fn, int i) {
+        return wn * WTN + fn * BD + (MS == 32 ? i * 8 + lhalf * 4 : 4 * (lane >> 4));
+    };
+    const uint32_t lane_off = ((uint32_t)mrow * (uint32_t)N + (uint32_t)col0(0, 0)) * 2u;
+    const bool full = m0 + BM <= M && n0 + BN <= N;
+    auto store_all = [&](auto masked) {
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
+        for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int n = n0 + wn * WTN + fn * BD +
-                          (MS == 32 ? i * 8 + lhalf * 4 : 4 * (lane >> 4));
-            if (n >= N) continue;
-            float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
-            if (bias) {
-                const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n);
-                b0 = to_f32<DT>(bb.x & 0xffffu);
-                b1 = to_f32<DT>(bb.x >> 16);
-                b2 = to_f32<DT>(bb.y & 0xffffu);
-                b3 = to_f32<DT>(bb.y >> 16);
-            }
+            for (int i = 0; i < NI; ++i) {
+                const int cn = col0(fn, i);
+                if (masked && n0 + cn >= N) continue;
+                float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+                if (bias) {
+                    const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n0 + cn);
+                    b0 = to_f32<DT>(bb.x & 0xffffu);
+                    b1 = to_f32<DT>(bb.x >> 16);
+                    b2 = to_f32<DT>(bb.y & 0xffffu);
+                    b3 = to_f32<DT>(bb.y >> 16);
+                }
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int m = m0 + wm * WTM + fm * BD + lrow_b;
-                if (m >= M) continue;
-                const AccT &a = acc[fn][fm];
-                u32x2 o;
-                o.x = pack2<DT>(act_fn<ACT>(a[4 * i + 0] + b0), act_fn<ACT>(a[4 * i + 1] + b1));
-                o.y = pack2<DT>(act_fn<ACT>(a[4 * i + 2] + b2), act_fn<ACT>(a[4 * i + 3] + b3));
-                *reinterpret_cast<u32x2 *>(C + (size_t)m * N + n) = o;
+                for (int fm = 0; fm < FM; ++fm) {
+                    if (masked && m0 + mrow + fm * BD >= M) continue;
+                    const AccT &a = acc[fn][fm];
+                    u32x2 o;
+                    o.x = pack2<DT>(act_fn<ACT>(a[4 * i + 0] + b0), act_fn<ACT>(a[4 * i + 1] + b1));
+                    o.y = pack2<DT>(act_fn<ACT>(a[4 * i + 2] + b2), act_fn<ACT>(a[4 * i + 3] + b3));
+                    const uint32_t off = lane_off + (uint32_t)(fm * BD) * (uint32_t)N * 2u +
+                                         (uint32_t)(cn - col0(0, 0)) * 2u;
+                    *reinterpret_cast<u32x2 *>(Ct + off) = o;
+                }
             }
         }
-    }
+    };
+    if (full)
+        store_all(std::false_type{});
+    else
+        store_all(std::true_type{});
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int MS, int DT,
