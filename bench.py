@@ -46,11 +46,14 @@ def log(*a):
 KERNEL_HEADERS = {0: ["gba_kernels.hpp"],
                   1: ["gba_kernels.hpp", "gemm_v2.hpp"],
                   2: ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp"],
-                  3: ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp"]}
+                  3: ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp"],
+                  4: ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp", "gemm_v5.hpp"]}
 
 
 def instance_file(s: dict) -> str:
     """The csrc file that instantiates schedule s."""
+    if s["kernel"] == 4:
+        return "v5_%dx%dx%d_w%dx%d_persistent.hip" % (s["bm"], s["bn"], s["bk"], s["wm"], s["wn"])
     if s["kernel"] in (2, 3):
         return "v3_%dx%dx%d_w%dx%d_s%d_l%d_p%d_m%d.hip" % (
             s["bm"], s["bn"], s["bk"], s["wm"], s["wn"], s["stages"], s["loaders"], s["spread"],

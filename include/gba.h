@@ -77,7 +77,12 @@ typedef enum {
  * by hand: global->LDS loads (issued by the first `loaders` waves, spread over
  * `spread` steps) and the next step's LDS reads between the MFMAs, using
  * 32x32x16 MFMAs; 3 = kernel 2 with 16x16x32 MFMAs (the default: same work, less
- * power, so higher sustained clocks). loaders and spread are 0 for kernels 0, 1. */
+ * power, so higher sustained clocks); 4 = kernel 3 run persistently: one
+ * workgroup per CU walks tiles w, w + G, ... (G = min(tiles, CUs)) as one stream
+ * of K slices, so the next tile's first slices load during the current tile's
+ * last steps and epilogue (the built-in choice when there are more tiles than
+ * CUs; with K <= bk it runs as kernel 3). loaders and spread are 0 for kernels
+ * 0, 1. */
 typedef struct {
     int32_t bm, bn, bk;
     int32_t wm, wn;

@@ -92,6 +92,43 @@ def test_exact_integer_gemm_is_bitwise_for_every_schedule(shape, dtype):
                 sched_id(s), raster, len(bad), bad[:3].tolist())
 
 
+PERSISTENT = dict(bm=256, bn=256, bk=64, wm=2, wn=2, stages=2, raster=1, group_m=4, kernel=4,
+                  loaders=4, spread=1)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("K", [128, 192, 1000])
+def test_persistent_kernel_streams_many_tiles_bitwise(K, dtype):
+    # 17 x 17 = 289 tiles of 256 x 256 on a 256-CU grid: some workgroups run two
+    # tiles, so the next tile's first slices are loaded inside the previous
+    # tile's K loop. K = 128: two slices per tile (the shortest stream); K = 192:
+    # an odd count, so the ring stage of slice 0 alternates from tile to tile;
+    # K = 1000: a ragged last slice. Ragged M and N tiles too.
+    M, N = 4100, 4200
+    A, B, bias = int_inputs(M, N, K, dtype, seed=K + 7)
+    want = oracle.encode(oracle.gemm_bias_act(A, B, bias, "none", dtype, nthreads=16), dtype)
+    for raster in (0, 1):
+        say("persistent exact", K, dtype, "raster", raster)
+        got = run_gpu(A, B, bias, "none", dtype, sched=dict(PERSISTENT, raster=raster))
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, "raster %d: %d mismatches, first %s" % (raster, len(bad),
+                                                                      bad[:3].tolist())
+
+
+def test_persistent_kernel_random_gelu_and_short_k():
+    A = synth.random_bits((4100, 520), "bf16", 31)
+    B = synth.random_bits((520, 4200), "bf16", 32, scale=1 / 16)
+    bias = synth.random_bits((4200,), "bf16", 33)
+    say("persistent random gelu")
+    got = run_gpu(A, B, bias, "gelu", "bf16", sched=PERSISTENT)
+    check_random(A, B, bias, "gelu", "bf16", got, rows=synth.sample_rows(4100, 64, seed=3))
+    # K <= 64 (one slice per tile) runs as the non-persistent kernel with the same tile
+    A, B, bias = int_inputs(600, 520, 64, "f16", seed=5)
+    want = oracle.encode(oracle.gemm_bias_act(A, B, bias, "none", "f16"), "f16")
+    say("persistent K=64")
+    assert np.array_equal(run_gpu(A, B, bias, "none", "f16", sched=PERSISTENT), want)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_exact_relu_epilogue_bitwise(dtype):
     A, B, bias = int_inputs(200, 136, 520, dtype, seed=9)

@@ -31,6 +31,7 @@ extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p2_m16;
 extern const ScheduleEntry i_256x128x64_w2x2_s3_l4_p1_m16;
 extern const ScheduleEntry i_128x256x64_w2x2_s3_l4_p1_m16;
 extern const ScheduleEntry i_128x128x64_w2x2_s3_l4_p1_m16;
+extern const ScheduleEntry p_256x256x64_w2x2;
 }  // namespace gba
 
 namespace {
@@ -42,6 +43,8 @@ const ScheduleEntry *const kTable[] = {
     &gba::i_256x256x64_w2x2_s2_l4_p1_m16, &gba::i_256x256x64_w2x2_s2_l4_p2_m16,
     &gba::i_256x128x64_w2x2_s3_l4_p1_m16, &gba::i_128x256x64_w2x2_s3_l4_p1_m16,
     &gba::i_128x128x64_w2x2_s3_l4_p1_m16,
+    // persistent version of the first: one workgroup per CU walks its tiles
+    &gba::p_256x256x64_w2x2,
     // the same with 32x32x16 MFMAs
     &gba::i_256x256x64_w2x2_s2_l4_p1_m32, &gba::i_256x256x64_w2x2_s2_l4_p2_m32,
     // direct-to-LDS kernel with compiler-scheduled steps
@@ -184,7 +187,9 @@ gba_schedule heuristic(int64_t M, int64_t N, int cus) {
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     const int64_t want = (int64_t)cus * 9 / 10;
     const ScheduleEntry *e;
-    if (tiles(256, 256) >= want)
+    if (tiles(256, 256) > cus)
+        e = &gba::p_256x256x64_w2x2;   // several tiles per CU: stream them
+    else if (tiles(256, 256) >= want)
         e = &gba::i_256x256x64_w2x2_s2_l4_p1_m16;
     else if (tiles(256, 128) >= want)
         e = M >= N ? &gba::i_256x128x64_w2x2_s3_l4_p1_m16 : &gba::i_128x256x64_w2x2_s3_l4_p1_m16;
@@ -347,8 +352,12 @@ gba_schedule choose(const DeviceInfo &d, int64_t M, int64_t N, int64_t K, int ac
     return heuristic(M, N, d.cus);
 }
 
-int launch(const gba_schedule &s, const void *A, const void *B, const void *bias, void *C,
+int launch(const gba_schedule &s0, const void *A, const void *B, const void *bias, void *C,
            int64_t M, int64_t N, int64_t K, int act, int dtype) {
+    gba_schedule s = s0;
+    // The persistent kernel streams at least two K slices per tile; with one,
+    // its non-persistent twin (same tile, kernel 3) does the same work.
+    if (s.kernel == 4 && K <= s.bk) s.kernel = 3;
     const int i = find_entry(s);
     if (i < 0) return GBA_ERR_SCHEDULE;
     hipError_t e = kTable[i]->fn[dtype][act](A, B, bias, C, (int)M, (int)N, (int)K, s.raster,

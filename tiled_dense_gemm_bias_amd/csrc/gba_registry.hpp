@@ -6,6 +6,7 @@
 #include "gba_kernels.hpp"
 #include "gemm_v2.hpp"
 #include "gemm_v3.hpp"
+#include "gemm_v5.hpp"
 
 namespace gba {
 
@@ -122,5 +123,38 @@ struct ScheduleEntry {
     const ScheduleEntry NAME = {{BM, BN, BK, WM, WN, S, 1, GROUP_M, MS == 32 ? 2 : 3, L, SP}, \
                                 {GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, MS, 0),     \
                                  GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, MS, 1)}};   \
+    }
+#endif
+
+// ---- persistent interleaved kernel (gemm_v5.hpp), kernel id 4 ----
+#define GBA_V5_INST_(BM, BN, WM, WN, DT, ACT)                                                 \
+    template __global__ void gba::gemm_v5_kernel<BM, BN, WM, WN, DT, ACT>(                    \
+        const uint16_t *__restrict__, const uint16_t *__restrict__, const uint16_t *__restrict__, \
+        uint16_t *__restrict__, int, int, int, int, int, int, int);
+
+#define GBA_V5_INSTS_(BM, BN, WM, WN)                                                          \
+    GBA_V5_INST_(BM, BN, WM, WN, 0, 0)                                                         \
+    GBA_V5_INST_(BM, BN, WM, WN, 0, 1)                                                         \
+    GBA_V5_INST_(BM, BN, WM, WN, 0, 2)                                                         \
+    GBA_V5_INST_(BM, BN, WM, WN, 0, 3)                                                         \
+    GBA_V5_INST_(BM, BN, WM, WN, 1, 0)                                                         \
+    GBA_V5_INST_(BM, BN, WM, WN, 1, 1)                                                         \
+    GBA_V5_INST_(BM, BN, WM, WN, 1, 2)                                                         \
+    GBA_V5_INST_(BM, BN, WM, WN, 1, 3)
+
+#define GBA_V5_LAUNCHERS_(BM, BN, WM, WN, DT)                                                  \
+    {gba::launch_gemm_v5<BM, BN, WM, WN, DT, 0>, gba::launch_gemm_v5<BM, BN, WM, WN, DT, 1>,   \
+     gba::launch_gemm_v5<BM, BN, WM, WN, DT, 2>, gba::launch_gemm_v5<BM, BN, WM, WN, DT, 3>}
+
+#ifdef __HIP_DEVICE_COMPILE__
+#define GBA_V5_SCHEDULE_ENTRY(NAME, BM, BN, WM, WN, GROUP_M) GBA_V5_INSTS_(BM, BN, WM, WN)
+#else
+#define GBA_V5_SCHEDULE_ENTRY(NAME, BM, BN, WM, WN, GROUP_M)                                   \
+    GBA_V5_INSTS_(BM, BN, WM, WN)                                                              \
+    namespace gba {                                                                            \
+    extern const ScheduleEntry NAME;                                                           \
+    const ScheduleEntry NAME = {{BM, BN, 64, WM, WN, 2, 1, GROUP_M, 4, WM * WN, 1},            \
+                                {GBA_V5_LAUNCHERS_(BM, BN, WM, WN, 0),                         \
+                                 GBA_V5_LAUNCHERS_(BM, BN, WM, WN, 1)}};                       \
     }
 #endif

@@ -1,0 +1,313 @@
+// Persistent variant of the interleaved 16x16x32 GEMM kernel (gemm_v3.hpp).
+//
+// One workgroup per CU walks its tiles (t = w, w + G, w + 2G, ... in raster
+// order, G = grid size) as one stream of 64-deep K slices through the same
+// two-stage LDS ring. The loads of stream position p + 2 are issued in the
+// last MFMA step of position p, exactly as in gemm_v3, except that positions
+// past a tile's last slice are the next tile's first slices. So when a tile's
+// main loop ends, the next tile's slice 0 is already in LDS (published by the
+// last barrier) and its slice 1 is in flight; both land while the epilogue
+// (bias, activation, rounding, stores) runs, and the next main loop starts
+// without the pipeline fill of a fresh workgroup. Tiles, LDS layouts,
+// fragments, MFMA order and epilogue are gemm_v3's (results are bit-identical).
+#pragma once
+
+#include "gemm_v3.hpp"
+
+namespace gba {
+
+template <int BM, int BN, int WM, int WN, int DT, int ACT>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+               const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int M, int N, int K,
+               int tiles_m, int tiles_n, int raster, int group_m) {
+    constexpr int BK = 64, MS = 16, BD = 16, KS = 32, KK = BK / KS;
+    constexpr int NW = WM * WN, NT = NW * 64;
+    constexpr int CHA = BK / 8, CHB = BN / 8;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / BD, FN = WTN / BD;
+    constexpr int NMF = FM * FN, NPF = FM + 2 * FN;
+    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
+    constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    constexpr int A_LD = BM * CHA / NT, B_LD = BK * CHB / NT, LD = A_LD + B_LD;
+    constexpr int EVERY = NMF / LD;
+    static_assert(KK == 2, "two MFMA steps per slice");
+    static_assert(WTM % BD == 0 && WTN % BD == 0, "wave tile must be whole MFMA blocks");
+    static_assert(BN >= 128, "B swizzle needs at least 16 chunks per row");
+    static_assert((BM * CHA) % NT == 0 && (BK * CHB) % NT == 0, "slices split evenly");
+    static_assert(2 * STAGE_BYTES <= 160 * 1024, "LDS ring too large");
+    static_assert(2 * LD < 64 && NMF % LD == 0 && NPF <= NMF, "step layout");
+    // Needs at least two K slices (K > 64): the launcher uses gemm_v3 below that.
+
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wid = tid >> 6;
+    const int wm = wid / WN, wn = wid % WN;
+    const int nk = (K + BK - 1) / BK;
+    const int T = tiles_m * tiles_n;
+    const int G = gridDim.x;
+    const int wid_s = __builtin_amdgcn_readfirstlane(wid);
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(GBA_LDS void *)smem;
+    // Position of this workgroup inside every round of G tiles.
+    const int slot = raster ? xcd_remap(blockIdx.x, G) : (int)blockIdx.x;
+
+    // Tile of round r: index r*G + slot in raster order (-1 past the last tile).
+    struct Tile {
+        int m0, n0, rows;
+    };
+    auto tile_of = [&](int r, Tile &t) -> bool {
+        const int idx = r * G + slot;
+        if (idx >= T) return false;
+        int tm, tn;
+        if (raster) {
+            grouped_tile(idx, tiles_m, tiles_n, group_m, tm, tn);
+        } else {
+            tm = idx / tiles_n;
+            tn = idx % tiles_n;
+        }
+        t.m0 = tm * BM;
+        t.n0 = tn * BN;
+        t.rows = min(M - t.m0, BM);
+        return true;
+    };
+
+    // Loader offsets within a slice (independent of the tile). Load i of a
+    // thread fills LDS chunk s = i*NT + tid of the A (B) part. For A that is row
+    // 32i + tid/8, logical chunk c_a = (tid%8) ^ (row%8), the same for every i;
+    // for B, k row 8i + tid/32 and logical chunk c_b(i) = c_b(0) ^ 8(i%4)
+    // (the B swizzle's row/8 term). So a handful of registers describe them all.
+    static_assert(NT == 256 && CHA == 8 && CHB == 32, "loader mapping written for 256 threads, BK 64, BN 256");
+    const int c_a = (tid & 7) ^ ((tid >> 3) & 7);
+    const uint32_t a_base = (uint32_t)(tid >> 3) * (uint32_t)K * 2u + (uint32_t)c_a * 16u;
+    const int c_b0 = (tid & 31) ^ bswz<CHB>(tid >> 5);
+    const uint32_t b_row = (uint32_t)(tid >> 5) * (uint32_t)N * 2u;
+    // Loads of slice kt of tile t (live) into stage `stage`; a dead slice reads
+    // nothing (every lane out of range) but keeps the wait counts uniform.
+    struct SliceDma {
+        __amdgpu_buffer_rsrc_t ra, rb;
+        uint32_t la, lb;
+        int k0, n0;
+    };
+    auto slice_dma = [&](const Tile &t, bool live, int kt, int stage) {
+        SliceDma d;
+        d.la = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(stage * STAGE_BYTES + wid_s * 64 * 16));
+        d.lb = d.la + A_BYTES;
+        d.k0 = live ? kt * BK : K;
+        d.n0 = live ? t.n0 : N;
+        d.ra = make_rsrc(A + (live ? (size_t)t.m0 * K + d.k0 : 0),
+                         live ? (uint32_t)t.rows * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u);
+        d.rb = make_rsrc(B + (live ? (size_t)d.k0 * N + t.n0 : 0),
+                         live ? (uint32_t)min(K - d.k0, BK) * (uint32_t)N * 2u : 0u);
+        return d;
+    };
+    // `kx`, `nx`: K and N re-read opaquely in each slice, so that the per-load
+    // row offsets (multiples of 64 K and 16 N bytes) are recomputed where used
+    // rather than held in scalar registers for the whole loop.
+    auto dma_one = [&](const SliceDma &d, int i, uint32_t kx, uint32_t nx) {
+        if (i < A_LD) {
+            const uint32_t o = d.k0 + c_a * 8 < K ? a_base + (uint32_t)(i * 64) * kx : kOobOffset;
+            buffer_load_lds16(d.ra, o, d.la + i * NT * 16);
+        } else {
+            const int j = i - A_LD;
+            const int c = c_b0 ^ (8 * (j & 3));
+            const uint32_t o = d.n0 + c * 8 < N
+                                   ? b_row + (uint32_t)(j * 16) * nx + (uint32_t)c * 16u
+                                   : kOobOffset;
+            buffer_load_lds16(d.rb, o, d.lb + j * NT * 16);
+        }
+    };
+
+    // Fragments (as gemm_v3 with 16x16x32 MFMAs). A block fm, step kk: lane l
+    // reads row wm*WTM + 16 fm + l%16, logical chunk 4 kk + l/16, stored at
+    // chunk ^ (row % 8); row % 8 = l % 8, so the address is a per-kk lane base
+    // plus 16 fm rows (the ds_read offset field). B^T block fn, step kk, half
+    // h: k row 32 kk + 8 (l/16) + 4 h + (l%16)/4 and columns n = wn*WTN + 16 fn
+    // + 4 (l%4); its swizzle term depends only on the lane, and 16 fn columns
+    // only flip chunk bits 1..3, so the address is a per-fn lane base plus the
+    // k-row offset of kk and h.
+    const int tg = lane >> 4, tj = lane & 15;
+    uint32_t fa_base[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        const int r = wm * WTM + tj;
+        fa_base[kk] = (uint32_t)(r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * kk + tg) * 16);
+    }
+    uint32_t fb_base[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        const int k = 8 * tg + (tj >> 2);
+        const int n = wn * WTN + fn * 16 + 4 * (tj & 3);
+        const int c = (n >> 3) ^ bswz<CHB>(k);
+        fb_base[fn] = (uint32_t)(A_BYTES + k * (BN * 2) + c * 16 + (n & 4) * 2);
+    }
+    auto a_addr = [&](int fm, int kk) -> uint32_t { return fa_base[kk] + fm * BD * (BK * 2); };
+    auto b_addr = [&](int fn, int kk, int h) -> uint32_t {
+        return fb_base[fn] + (32 * kk + 4 * h) * (BN * 2);
+    };
+
+    f32x4 acc[FN][FM];
+    u32x4 fa[2][FM];
+    i16x4 fbl[2][FN], fbh[2][FN];
+    auto read_one = [&](int buf, const char *base, int kk, int r) {
+        if (r < FM) {
+            fa[buf][r] = *reinterpret_cast<const u32x4 *>(base + a_addr(r, kk));
+        } else {
+            const int fn = (r - FM) >> 1, h = (r - FM) & 1;
+            const i16x4 v =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((GBA_LDS i16x4 *)(base + b_addr(fn, kk, h)));
+            if (h)
+                fbh[buf][fn] = v;
+            else
+                fbl[buf][fn] = v;
+        }
+    };
+    // One MFMA step on buffer `cur`; `reads`: the next step's fragments (from
+    // `pf_base` step pf_kk); `dma`: all LD loads of slice d, one per EVERY MFMAs.
+    auto step = [&](int cur, bool reads, const char *pf_base, int pf_kk, bool dma,
+                    const SliceDma &d, uint32_t kx, uint32_t nx) {
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+            const int fn = q / FM, fm = q % FM;
+            const u32x4 bop = __builtin_bit_cast(
+                u32x4, __builtin_shufflevector(fbl[cur][fn], fbh[cur][fn], 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[fn][fm] = mfma16x16x32<DT>(bop, fa[cur][fm], acc[fn][fm]);
+            if (reads && q < NPF) read_one(cur ^ 1, pf_base, pf_kk, q);
+            if (dma && q % EVERY == 0) dma_one(d, q / EVERY, kx, nx);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    Tile cur_t;
+    if (!tile_of(0, cur_t)) return;   // more workgroups than tiles: nothing to do
+
+    // Prologue: slices 0 and 1 of the first tile; slice 0 waited for and
+    // published, and its first fragments read.
+    {
+        const SliceDma d0 = slice_dma(cur_t, true, 0, 0), d1 = slice_dma(cur_t, true, 1, 1);
+#pragma unroll
+        for (int i = 0; i < LD; ++i) dma_one(d0, i, (uint32_t)K, (uint32_t)N);
+#pragma unroll
+        for (int i = 0; i < LD; ++i) dma_one(d1, i, (uint32_t)K, (uint32_t)N);
+    }
+    wait_vmcnt<LD>();
+    block_barrier();
+#pragma unroll
+    for (int q = 0; q < NPF; ++q) read_one(0, smem, 0, q);
+
+    const int mrow = wm * WTM + tj;
+    int stage0 = 0;   // stage of the current tile's slice 0
+    for (int r = 0;; ++r) {
+#pragma unroll
+        for (int a = 0; a < FN; ++a)
+#pragma unroll
+            for (int b = 0; b < FM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Tile nxt_t;
+        const bool nxt_live = tile_of(r + 1, nxt_t);
+        if (!nxt_live) nxt_t = cur_t;
+
+        // Slice kt: step 0 reads its kk=1 fragments; the barrier publishes stream
+        // position kt+1 (the next tile's slice 0 after the last slice) and frees
+        // kt's stage; step 1 loads position kt+2 into it and reads position
+        // kt+1's kk=0 fragments.
+        for (int kt = 0; kt < nk; ++kt) {
+            const int sc = (stage0 + kt) & 1;
+            const char *cur_base = smem + sc * STAGE_BYTES;
+            const char *nxt_base = smem + (sc ^ 1) * STAGE_BYTES;
+            uint32_t kx = (uint32_t)K, nx = (uint32_t)N;
+            asm volatile("" : "+s"(kx), "+s"(nx));
+            step(0, true, cur_base, 1, false, SliceDma{}, kx, nx);
+            wait_vmcnt_lgkm0<0>();
+            block_barrier();
+            const bool here = kt + 2 < nk;
+            const SliceDma dn = slice_dma(here ? cur_t : nxt_t, here || nxt_live,
+                                          here ? kt + 2 : kt + 2 - nk, sc);
+            step(1, true, nxt_base, 0, true, dn, kx, nx);
+        }
+
+        // Epilogue of this tile while the next tile's first slices land. The
+        // scheduling fences keep the next tile's fragment reads and the epilogue
+        // apart (mixing them would hold both register sets live at once).
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        {
+            char *const Ct = reinterpret_cast<char *>(C + (size_t)cur_t.m0 * N + cur_t.n0);
+            int c0 = wn * WTN + 4 * tg, mr = mrow;
+            asm volatile("" : "+v"(mr));
+            uint32_t lane_off = ((uint32_t)mr * (uint32_t)N + (uint32_t)c0) * 2u;
+            uint32_t pitch16 = (uint32_t)N * (2u * BD);   // bytes between row blocks fm
+            // Opaque to the optimiser: otherwise the per-store offsets, columns and
+            // bias addresses derived from these are hoisted out of the tile loop
+            // and held in registers across the main loop.
+            asm volatile("" : "+v"(lane_off), "+v"(c0), "+s"(pitch16));
+            const bool full = cur_t.m0 + BM <= M && cur_t.n0 + BN <= N;
+            auto store_all = [&](auto masked) {
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    const int cn = c0 + fn * BD;
+                    if (masked && cur_t.n0 + cn >= N) continue;
+                    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+                    if (bias) {
+                        const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + cur_t.n0 + cn);
+                        b0 = to_f32<DT>(bb.x & 0xffffu);
+                        b1 = to_f32<DT>(bb.x >> 16);
+                        b2 = to_f32<DT>(bb.y & 0xffffu);
+                        b3 = to_f32<DT>(bb.y >> 16);
+                    }
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm) {
+                        if (masked && cur_t.m0 + mr + fm * BD >= M) continue;
+                        const f32x4 &a = acc[fn][fm];
+                        u32x2 o;
+                        o.x = pack2<DT>(act_fn<ACT>(a[0] + b0), act_fn<ACT>(a[1] + b1));
+                        o.y = pack2<DT>(act_fn<ACT>(a[2] + b2), act_fn<ACT>(a[3] + b3));
+                        const uint32_t offs = lane_off + (uint32_t)fm * pitch16 + (uint32_t)(fn * BD) * 2u;
+                        *reinterpret_cast<u32x2 *>(Ct + offs) = o;
+                    }
+                    // One column group at a time: the next tile's first
+                    // fragments are live here, so the scheduler may not
+                    // interleave the whole tile's epilogue.
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            if (full)
+                store_all(std::false_type{});
+            else
+                store_all(std::true_type{});
+        }
+
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        stage0 = (stage0 + nk) & 1;
+        if (!nxt_live) break;
+        cur_t = nxt_t;
+    }
+    // No direct-to-LDS write may outlive the workgroup's LDS.
+    wait_vmcnt<0>();
+}
+
+// Grid: one workgroup per CU (two 64 KiB stages fill the LDS), or fewer when
+// there are fewer tiles. K must exceed 64 (at least two K slices per tile): the
+// library sends K <= 64 to gemm_v3 with the same tile.
+template <int BM, int BN, int WM, int WN, int DT, int ACT>
+hipError_t launch_gemm_v5(const void *A, const void *B, const void *bias, void *C, int M, int N,
+                          int K, int raster, int group_m, hipStream_t stream) {
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const long long tiles = (long long)tiles_m * tiles_n;
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (K <= 64) return hipErrorInvalidValue;   // needs two K slices; see the note above
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int grid = (int)(tiles < cus ? tiles : cus);
+    hipLaunchKernelGGL((gemm_v5_kernel<BM, BN, WM, WN, DT, ACT>), dim3((unsigned)grid),
+                       dim3(WM * WN * 64), 0, stream, (const uint16_t *)A, (const uint16_t *)B,
+                       (const uint16_t *)bias, (uint16_t *)C, M, N, K, tiles_m, tiles_n, raster,
+                       group_m < 1 ? 1 : group_m);
+    return hipGetLastError();
+}
+
+}  // namespace gba
