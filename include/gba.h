@@ -80,8 +80,8 @@ typedef enum {
  * power, so higher sustained clocks); 4 = kernel 3 run persistently: one
  * workgroup per CU walks tiles w, w + G, ... (G = min(tiles, CUs)) as one stream
  * of K slices, so the next tile's first slices load during the current tile's
- * last steps and epilogue (the built-in choice when there are more tiles than
- * CUs; with K <= bk it runs as kernel 3). loaders and spread are 0 for kernels
+ * last steps and epilogue (the built-in choice for 256x256 tiles; with K <= bk
+ * it runs as kernel 3). loaders and spread are 0 for kernels
  * 0, 1. */
 typedef struct {
     int32_t bm, bn, bk;
