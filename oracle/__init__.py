@@ -14,6 +14,8 @@ file's header for the pages and sections each step follows:
     from Python", Why tile-level control matters (bias add + GELU on the
     accumulator); ReLU / sigmoid from "writing-tilelang-kernels", Pre-flight
     Checklist and Key API Patterns.
+  - transpose_B (same page, Key API Patterns): the second operand stored (N, K)
+    and used as its transpose (``transpose_b=True``).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against facts
 that do not come from the oracle itself (closed forms, exact rational brute
@@ -77,8 +79,9 @@ class Oracle:
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
         ci = ctypes.c_int
-        lib.oracle_gemm_bias_act.argtypes = [p, p, p, p, p, i64, i64, i64, ci, ci, p, i64, ci]
-        lib.oracle_gemm_bias_act.restype = ci
+        for name in ("oracle_gemm_bias_act", "oracle_gemm_bias_act_nt"):
+            getattr(lib, name).argtypes = [p, p, p, p, p, i64, i64, i64, ci, ci, p, i64, ci]
+            getattr(lib, name).restype = ci
         lib.oracle_bias_act.argtypes = [p, p, p, i64, i64, ci, ci]
         lib.oracle_bias_act.restype = ci
         for name in ("oracle_decode", "oracle_encode", "oracle_act"):
@@ -88,16 +91,17 @@ class Oracle:
         self.path = path
 
     def gemm_bias_act(self, A, B, bias, act="none", dtype="f16", rows=None, nthreads=0,
-                      with_abs=False):
+                      with_abs=False, transpose_b=False):
         """fp64 act(A.B + bias) for the given rows (all rows when rows is None).
 
-        A: uint16 bits [M, K]; B: uint16 bits [K, N]; bias: uint16 bits [N] or None.
+        A: uint16 bits [M, K]; B: uint16 bits [K, N], or [N, K] with transpose_b
+        (the product is then A.B^T); bias: uint16 bits [N] or None.
         Returns out[len(rows) or M, N] float64, plus sum_k |A_ik B_kj| + |bias_j|
         when with_abs is set.
         """
         A, B = _bits(A), _bits(B)
         M, K = A.shape
-        K2, N = B.shape
+        N, K2 = B.shape if transpose_b else B.shape[::-1]
         if K2 != K:
             raise ValueError("inner dimensions differ: A is %s, B is %s" % (A.shape, B.shape))
         if bias is not None:
@@ -108,9 +112,9 @@ class Oracle:
         nrows = M if r is None else r.shape[0]
         out = np.empty((nrows, N), dtype=np.float64)
         absout = np.empty((nrows, N), dtype=np.float64) if with_abs else None
-        rc = self._lib.oracle_gemm_bias_act(_ptr(A), _ptr(B), _ptr(bias), _ptr(out),
-                                            _ptr(absout), M, N, K, _act(act), _dt(dtype),
-                                            _ptr(r), 0 if r is None else nrows, int(nthreads))
+        fn = self._lib.oracle_gemm_bias_act_nt if transpose_b else self._lib.oracle_gemm_bias_act
+        rc = fn(_ptr(A), _ptr(B), _ptr(bias), _ptr(out), _ptr(absout), M, N, K, _act(act),
+                _dt(dtype), _ptr(r), 0 if r is None else nrows, int(nthreads))
         if rc != 0:
             raise ValueError("oracle_gemm_bias_act rejected its arguments")
         return (out, absout) if with_abs else out

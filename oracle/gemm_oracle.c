@@ -16,6 +16,10 @@
  *     program is the plain product A @ B.
  *   - Same page, "Pre-flight Checklist" and "Key API Patterns": the fused
  *     epilogues are ReLU (max) and sigmoid.
+ *   - Same page, "Key API Patterns": the tile GEMM takes a transpose_B flag.
+ *     With it, the second operand is given as an (N,K) row-major array W and
+ *     the product is A times its transpose: s[i][j] = sum_k A[i][k] * W[j][k]
+ *     (oracle_gemm_bias_act_nt).
  *
  * The oracle is the mathematical definition written out, in fp64:
  *     s[i][j] = sum_{k<K} A[i][k] * B[k][j]        (each product exact in fp64)
@@ -165,13 +169,18 @@ static void *gemm_worker(void *p) {
 typedef struct {
     const uint16_t *B;
     double *Bd;
-    int64_t lo, hi;
-    int dtype;
+    int64_t lo, hi, N, K;
+    int dtype, b_nk;
 } dec_job;
 
+/* Bd[k][j] = the (k, j) entry of the second operand: B[k][j] when B is stored
+ * (K,N), W[j][k] when it is stored (N,K) (transpose_B). */
 static void *dec_worker(void *p) {
     dec_job *d = (dec_job *)p;
-    for (int64_t t = d->lo; t < d->hi; ++t) d->Bd[t] = dec(d->dtype, d->B[t]);
+    for (int64_t t = d->lo; t < d->hi; ++t) {
+        const int64_t k = t / d->N, j = t % d->N;
+        d->Bd[t] = dec(d->dtype, d->b_nk ? d->B[j * d->K + k] : d->B[t]);
+    }
     return NULL;
 }
 
@@ -189,10 +198,9 @@ static int pick_threads(int nthreads, int64_t work_items) {
  * + |bias[c]|, the magnitude that bounds any fp32 summation's rounding error.
  * Returns 0, or -1 on a bad argument.
  */
-int oracle_gemm_bias_act(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
-                         double *out, double *absout, int64_t M, int64_t N, int64_t K,
-                         int act, int dtype, const int64_t *rows, int64_t nrows,
-                         int nthreads) {
+static int gemm_impl(const uint16_t *A, const uint16_t *B, int b_nk, const uint16_t *bias,
+                     double *out, double *absout, int64_t M, int64_t N, int64_t K, int act,
+                     int dtype, const int64_t *rows, int64_t nrows, int nthreads) {
     if (M < 0 || N < 0 || K < 0 || act < 0 || act > 3 || (dtype != OR_F16 && dtype != OR_BF16))
         return -1;
     if (!rows) nrows = M;
@@ -208,7 +216,8 @@ int oracle_gemm_bias_act(const uint16_t *A, const uint16_t *B, const uint16_t *b
         pthread_t th[256];
         dec_job dj[256];
         for (int t = 0; t < T; ++t) {
-            dj[t].B = B; dj[t].Bd = Bd; dj[t].dtype = dtype;
+            dj[t].B = B; dj[t].Bd = Bd; dj[t].dtype = dtype; dj[t].b_nk = b_nk;
+            dj[t].N = N; dj[t].K = K;
             dj[t].lo = (K * N) * t / T; dj[t].hi = (K * N) * (t + 1) / T;
             pthread_create(&th[t], NULL, dec_worker, &dj[t]);
         }
@@ -226,6 +235,22 @@ int oracle_gemm_bias_act(const uint16_t *A, const uint16_t *B, const uint16_t *b
     for (int t = 0; t < T; ++t) pthread_join(th[t], NULL);
     free(Bd);
     return 0;
+}
+
+/* B stored (K,N): out = act(A.B + bias). */
+int oracle_gemm_bias_act(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
+                         double *out, double *absout, int64_t M, int64_t N, int64_t K,
+                         int act, int dtype, const int64_t *rows, int64_t nrows,
+                         int nthreads) {
+    return gemm_impl(A, B, 0, bias, out, absout, M, N, K, act, dtype, rows, nrows, nthreads);
+}
+
+/* W stored (N,K) (transpose_B): out[r][c] = act(sum_k A[i][k]*W[c][k] + bias[c]). */
+int oracle_gemm_bias_act_nt(const uint16_t *A, const uint16_t *W, const uint16_t *bias,
+                            double *out, double *absout, int64_t M, int64_t N, int64_t K,
+                            int act, int dtype, const int64_t *rows, int64_t nrows,
+                            int nthreads) {
+    return gemm_impl(A, W, 1, bias, out, absout, M, N, K, act, dtype, rows, nrows, nthreads);
 }
 
 /* out[i][j] = act(X[i][j] + bias[j]) in fp64: the elementwise second half of the

@@ -35,6 +35,8 @@ MUTANTS = {
     "round_truncates": ("double r = rint(a / q);", "double r = floor(a / q);"),
     "round_half_up": ("double r = rint(a / q);", "double r = floor(a / q + 0.5);"),
     "abs_sum_signed": ("aacc[c] += aa * fabs(brow[c]);", "aacc[c] += aa * brow[c];"),
+    "transpose_b_reads_kn": ("d->b_nk ? d->B[j * d->K + k] : d->B[t]",
+                             "d->b_nk ? d->B[k * d->N + j] : d->B[t]"),
     "second_operand_row": ("const double *brow = j->Bd + k * N;",
                            "const double *brow = j->Bd + (K - 1 - k) * N;"),
 }

@@ -266,6 +266,42 @@ def test_gemm_equals_exact_rational_sum(orc, dtype, shape):
             assert S[i, j] == pytest.approx(float(sabs + abs(Fraction(bv[j]))), rel=1e-14)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 5, 7), (7, 4, 9), (4, 3, 33)])
+def test_transpose_b_equals_exact_rational_sum(orc, dtype, shape):
+    # transpose_B: the second operand is stored (N, K) and enters as its transpose
+    M, N, K = shape
+    A = synth.random_bits((M, K), dtype, 110 + M)
+    W = synth.random_bits((N, K), dtype, 210 + N)
+    bias = synth.random_bits((N,), dtype, 310 + K)
+    Av, Wv, bv = orc.decode(A, dtype), orc.decode(W, dtype), orc.decode(bias, dtype)
+    exact = _fraction_gemm(Av, Wv.T, bv)
+    got, S = orc.gemm_bias_act(A, W, bias, "none", dtype, with_abs=True, transpose_b=True)
+    for i in range(M):
+        for j in range(N):
+            bound = (K + 1) * 2.0 ** -53 * S[i, j]
+            assert abs(Fraction(got[i, j]) - exact[i, j]) <= Fraction(bound), (i, j)
+
+
+def test_transpose_b_identity_permutation_and_integers(orc):
+    K = 40
+    A = synth.random_bits((12, K), "f16", 14)
+    eye = f16(np.eye(K))
+    np.testing.assert_array_equal(orc.gemm_bias_act(A, eye, None, transpose_b=True), orc.decode(A))
+    # W = P (rows permuted): column j of the result is column perm[j] of A
+    perm = np.random.default_rng(5).permutation(K)
+    P = f16(np.eye(K)[perm])
+    np.testing.assert_array_equal(orc.gemm_bias_act(A, P, None, transpose_b=True),
+                                  orc.decode(A)[:, perm])
+    rng = np.random.default_rng(22)
+    M, N, K = 23, 31, 77
+    Ai, Wi, bi = rng.integers(-3, 4, (M, K)), rng.integers(-3, 4, (N, K)), rng.integers(-9, 10, N)
+    for act in ("none", "relu"):
+        got = orc.gemm_bias_act(f16(Ai), f16(Wi), f16(bi), act, transpose_b=True)
+        want = Ai @ Wi.T + bi
+        np.testing.assert_array_equal(got, np.maximum(want, 0) if act == "relu" else want)
+
+
 def test_identity_and_permutation(orc):
     K, N = 48, 40
     B = synth.random_bits((K, N), "f16", 5)
