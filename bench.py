@@ -1,6 +1,7 @@
 """Benchmark of the fused GEMM + bias + GELU on one MI355X.
 
     python bench.py [--steps 50] [--warmup 300] [--workload c3_gelu] [--unfused]
+                    [--transpose-b]
 
 One step is one gemm_bias_act call over the whole workload (schedule choice,
 global->LDS loads, MFMA main loop, fused epilogue, store), with inputs already
@@ -107,7 +108,7 @@ def time_launches(fn, steps, warmup, stream):
     return wall_ms, per
 
 
-def cpu_baseline(w, A, B, bias, got_bits, target_s=12.0):
+def cpu_baseline(w, A, B, bias, got_bits, target_s=12.0, transpose_b=False):
     """The fp64 oracle on a bounded sample of rows, timed on the host cores."""
     import oracle
     from oracle import compare
@@ -116,14 +117,15 @@ def cpu_baseline(w, A, B, bias, got_bits, target_s=12.0):
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     rows = synth.sample_rows(w.M, 16, seed=w.seed)
     t0 = time.perf_counter()
-    oracle.gemm_bias_act(A, B, bias, w.act, w.dtype, rows=rows, nthreads=cores)
+    oracle.gemm_bias_act(A, B, bias, w.act, w.dtype, rows=rows, nthreads=cores,
+                         transpose_b=transpose_b)
     t_probe = time.perf_counter() - t0
     n = int(min(w.M, max(16, 16 * target_s / max(t_probe, 1e-3))))
     n = max(16, (n // cores) * cores if n > cores else n)
     rows = synth.sample_rows(w.M, n, seed=w.seed)
     t0 = time.perf_counter()
     R, S = oracle.gemm_bias_act(A, B, bias, w.act, w.dtype, rows=rows, nthreads=cores,
-                                with_abs=True)
+                                with_abs=True, transpose_b=transpose_b)
     dt = time.perf_counter() - t0
     flops = 2.0 * len(rows) * w.N * w.K
     rep = compare.check(oracle.decode(got_bits[rows], w.dtype), R, K=w.K, dtype=w.dtype,
@@ -143,6 +145,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="c3_gelu")
     ap.add_argument("--unfused", action="store_true", help="also time gemm + bias_act")
+    ap.add_argument("--transpose-b", action="store_true",
+                    help="B stored [N,K] (transpose_B): time gemm_bias_act_nt on the same numbers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tune", action="store_true", help="autotune before timing")
     ap.add_argument("--schedule", default=None, help="force bm,bn,bk,wm,wn,stages,kernel,loaders,spread[,raster,group_m]")
@@ -168,6 +172,10 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     log("[bench] generating %s inputs %dx%dx%d %s" % (w.name, w.M, w.N, w.K, w.dtype))
     A, B, bias = synth.make_inputs(w)
+    tb = a.transpose_b
+    if tb:
+        B = np.ascontiguousarray(B.T)   # the same operand, stored as the [N,K] weight W
+    wl_key = w.name + ("_nt" if tb else "")
     tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
 
     def dev_t(bits):
@@ -195,12 +203,12 @@ def main(argv=None) -> int:
         sched.setdefault("group_m", 4)
         gba.set_schedule(sched)
     elif a.tune:
-        best, ms = gba.autotune(a_t, b_t, bias_t, c_t, w.act, all_groups=True)
+        best, ms = gba.autotune(a_t, b_t, bias_t, c_t, w.act, all_groups=True, transpose_b=tb)
         log("[bench] autotune best %s %.4f ms" % (best, ms))
-    sched = gba.get_schedule(w.M, w.N, w.K, w.act, w.dtype)
-    log("[bench] schedule %s" % sched)
+    sched = gba.get_schedule(w.M, w.N, w.K, w.act, w.dtype, transpose_b=tb)
+    log("[bench] schedule %s%s" % (sched, " (B stored [N,K])" if tb else ""))
 
-    step = gba.bind_gemm_bias_act(a_t, b_t, bias_t, c_t, w.act)
+    step = gba.bind_gemm_bias_act(a_t, b_t, bias_t, c_t, w.act, transpose_b=tb)
     wall_ms, per = time_launches(step, a.steps, a.warmup, stream)
     ms_per_step = wall_ms / a.steps
     kern_avg = sum(per) / len(per)
@@ -228,22 +236,25 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": "%s: C = %s(A.B + bias), M=%d N=%d K=%d, %s in/out, fp32 accumulate"
-                               % (w.name, w.act, w.M, w.N, w.K, w.dtype),
+        "config": {"workload": "%s: C = %s(A.%s + bias), M=%d N=%d K=%d, %s in/out, fp32 accumulate"
+                               % (wl_key, w.act, "W^T, W stored [N,K]" if tb else "B", w.M, w.N,
+                                  w.K, w.dtype),
                    "M": w.M, "N": w.N, "K": w.K, "act": w.act, "bias": w.bias,
+                   "b_layout": "NK (transpose_B)" if tb else "KN",
                    "schedule": sched, "flop_model": "2*M*N*K (epilogue not counted)"},
         "median_ms": round(kern_med, 5),
         "pct_of_peak": round(100 * achieved / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(w.name, sched),
+                     "traffic": measured_traffic(wl_key, sched),
                      "algorithmic_bytes": alg_bytes, "kernel_avg_ms": round(kern_avg, 5)},
     }
 
     if a.unfused:
         t_t = torch.empty_like(c_t)
         y_t = torch.empty_like(c_t)
-        _, per_g = time_launches(lambda: gba.gemm(a_t, b_t, t_t), a.steps, a.warmup, stream)
+        _, per_g = time_launches(lambda: gba.gemm(a_t, b_t, t_t, transpose_b=tb), a.steps,
+                                 a.warmup, stream)
         _, per_b = time_launches(lambda: gba.bias_act(t_t, bias_t, y_t, w.act), a.steps,
                                  a.warmup, stream)
         g_ms, b_ms = statistics.median(per_g), statistics.median(per_b)
@@ -261,7 +272,7 @@ def main(argv=None) -> int:
 
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a row sample")
-        base, parity = cpu_baseline(w, A, B, bias, got_bits)
+        base, parity = cpu_baseline(w, A, B, bias, got_bits, transpose_b=tb)
         out["cpu_baseline"] = base
         out["parity_sampled"] = parity
         log("[bench] cpu baseline %.4f TFLOP/s on %d threads; parity %s"

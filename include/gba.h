@@ -12,7 +12,8 @@
  * Conventions shared by every entry point:
  *   - All array arguments are DEVICE pointers owned by the caller. The library
  *     allocates nothing on the compute path and keeps no pointer after a call.
- *   - Layouts are dense row-major with leading dimensions K (A), N (B, C, X, Y).
+ *   - Layouts are dense row-major with leading dimensions K (A, and W of the
+ *     _nt calls), N (B, C, X, Y).
  *   - dtype (gba_dtype) applies to A, B, bias and C alike; accumulation is fp32.
  *   - Pointers must be 16-byte aligned, and K and N multiples of 8 (the 16-byte
  *     row-alignment rule of "writing-tilelang-kernels", Common Pitfalls);
@@ -114,6 +115,21 @@ int gemm(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
 int bias_act(const void *X, const void *bias, void *Y, int64_t M, int64_t N, int act,
              int dtype);
 
+/* C = act(A.W^T + bias) with the second operand stored as W: [N,K] row-major
+ * (K-contiguous rows, the layout of a linear layer's weight): the transpose_B
+ * form of the tile GEMM ("writing-tilelang-kernels", Key API Patterns,
+ * T.gemm(..., transpose_B=True)). A: [M,K], bias: [N] or NULL, C: [M,N].
+ * Everything else as gemm_bias_act: same dtype rule, the 16-byte alignment rule
+ * with K and N multiples of 8, same errors; C may not overlap A, W or bias.
+ * Kernels 3 and 4 have this path; a forced schedule of another kernel makes the
+ * call return GBA_ERR_SCHEDULE. The result is bitwise that of gemm_bias_act on
+ * the same schedule with B = W^T. */
+int gemm_bias_act_nt(const void *A, const void *W, const void *bias, void *C, int64_t M,
+                     int64_t N, int64_t K, int act, int dtype);
+
+/* C = A.W^T rounded to `dtype`, W: [N,K] (gemm with transpose_B). */
+int gemm_nt(const void *A, const void *W, void *C, int64_t M, int64_t N, int64_t K, int dtype);
+
 /* Stream for this thread's later calls (a hipStream_t); NULL = default stream. */
 int gba_set_stream(void *hip_stream);
 
@@ -123,8 +139,16 @@ int gba_set_stream(void *hip_stream);
  * are out of range. */
 int gba_set_schedule(const gba_schedule *s);
 
-/* The schedule a gemm_bias_act call with these arguments would use now. */
+/* The schedule a gemm_bias_act (gemm_bias_act_nt) call with these arguments
+ * would use now. */
 int gba_get_schedule(int64_t M, int64_t N, int64_t K, int act, int dtype, gba_schedule *out);
+int gba_get_schedule_nt(int64_t M, int64_t N, int64_t K, int act, int dtype, gba_schedule *out);
+
+/* gba_autotune flags. */
+enum {
+    GBA_TUNE_ALL_GROUPS = 1,   /* also try every raster group size in {1,2,4,8,16} */
+    GBA_TUNE_TRANSPOSE_B = 2   /* tune gemm_bias_act_nt: B is W, stored [N,K] */
+};
 
 /* Compiled-in kernel instances: count, and the i-th one (raster/group_m are
  * their defaults). */
@@ -132,14 +156,15 @@ int gba_num_schedules(void);
 int gba_list_schedule(int i, gba_schedule *out);
 
 /* Autotuner ("TileLang: Write, Autotune, and Ship Fused Tensor-Core Kernels from
- * Python", section Autotuning): for every compiled-in instance whose LDS ring
+ * Python", section Autotuning): for every compiled-in instance (with a
+ * transpose_B path when GBA_TUNE_TRANSPOSE_B is set) whose LDS ring
  * (bm*bk + bk*bn) * 2 * stages fits the 160 KiB LDS of a CU, and each raster
  * variant, run 10 untimed and 50 timed launches on the caller's buffers, keep
  * the median time, and pick the fastest. The winner is stored in the on-disk
  * schedule cache ($GBA_CACHE_DIR, default ~/.cache/gba; disabled by
  * GBA_DISABLE_CACHE=1) under the key (arch, CU count, library version, dtype,
- * act, M, N, K), and is used by later calls. C holds the winner's result on
- * return. flags: bit 0 = also try every raster group size in {1,2,4,8,16}.
+ * act, B layout, M, N, K), and is used by later calls. C holds the winner's
+ * result on return. flags: GBA_TUNE_* bits.
  * best / best_ms may be NULL. Synchronous: it waits for its own launches.
  * Returns GBA_ERR_CACHE (with best filled) if the cache file could not be
  * written. */

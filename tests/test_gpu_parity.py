@@ -433,5 +433,5 @@ def test_autotune_writes_cache_and_is_used(tmp_path, monkeypatch):
     data = json.load(open(tmp_path / "schedules.json"))
     assert data["format"] == "gba-schedule-cache" and data["version"] == 1
     keys = [e["key"] for e in data["entries"]]
-    assert any(k.endswith("|f16|gelu|512|512|256") for k in keys)
+    assert any(k.endswith("|f16|gelu|nn|512|512|256") for k in keys)
     assert gba.get_schedule(M, N, K, "gelu", "f16") == best

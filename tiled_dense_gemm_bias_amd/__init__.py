@@ -65,10 +65,13 @@ def _lib():
         sig = {
             "gemm_bias_act": [p, p, p, p, i64, i64, i64, ci, ci],
             "gemm": [p, p, p, i64, i64, i64, ci],
+            "gemm_bias_act_nt": [p, p, p, p, i64, i64, i64, ci, ci],
+            "gemm_nt": [p, p, p, i64, i64, i64, ci],
             "bias_act": [p, p, p, i64, i64, ci, ci],
             "gba_set_stream": [p],
             "gba_set_schedule": [ctypes.POINTER(Schedule)],
             "gba_get_schedule": [i64, i64, i64, ci, ci, ctypes.POINTER(Schedule)],
+            "gba_get_schedule_nt": [i64, i64, i64, ci, ci, ctypes.POINTER(Schedule)],
             "gba_num_schedules": [],
             "gba_list_schedule": [ci, ctypes.POINTER(Schedule)],
             "gba_autotune": [p, p, p, p, i64, i64, i64, ci, ci, ci, ctypes.POINTER(Schedule),
@@ -158,64 +161,65 @@ def _call(fn_name: str, dev, *args):
 
 # ---------------------------------------------------------------- API ----
 
-def gemm_bias_act(a, b, bias, c, act="gelu"):
-    """c[M,N] = act(a[M,K] @ b[K,N] + bias[N]); bias may be None. Returns c."""
-    dev = _check_dev(a, b, bias, c)
+def _gemm_shapes(a, b, bias, c, transpose_b):
+    """(dtype code, M, N, K) after the dtype and shape checks of the GEMM calls.
+    b is [K,N], or [N,K] with transpose_b."""
     dt = _dtype_code(a)
     for t in (b, bias, c):
         if t is not None and _dtype_code(t) != dt:
             raise TypeError("all operands must share one dtype")
     M, K = a.shape
-    K2, N = b.shape
+    N, K2 = tuple(b.shape) if transpose_b else tuple(b.shape)[::-1]
     if K2 != K or tuple(c.shape) != (M, N) or (bias is not None and tuple(bias.shape) != (N,)):
-        raise ValueError("shape mismatch: a%s b%s bias%s c%s" % (
-            tuple(a.shape), tuple(b.shape), None if bias is None else tuple(bias.shape),
-            tuple(c.shape)))
-    _call("gemm_bias_act", dev, _ptr(a), _ptr(b), _ptr(bias), _ptr(c), M, N, K, _act(act), dt)
+        raise ValueError("shape mismatch: a%s b%s%s bias%s c%s" % (
+            tuple(a.shape), tuple(b.shape), " (transpose_b)" if transpose_b else "",
+            None if bias is None else tuple(bias.shape), tuple(c.shape)))
+    return dt, M, N, K
+
+
+def gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False):
+    """c[M,N] = act(a[M,K] @ b[K,N] + bias[N]); bias may be None. Returns c.
+
+    transpose_b: b is stored [N,K] (a linear layer's weight) and c = act(a @ b.T + bias)."""
+    dev = _check_dev(a, b, bias, c)
+    dt, M, N, K = _gemm_shapes(a, b, bias, c, transpose_b)
+    _call("gemm_bias_act_nt" if transpose_b else "gemm_bias_act", dev, _ptr(a), _ptr(b),
+          _ptr(bias), _ptr(c), M, N, K, _act(act), dt)
     return c
 
 
-def bind_gemm_bias_act(a, b, bias, c, act="gelu"):
+def bind_gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False):
     """Check and marshal the arguments once; return a no-argument callable that
-    enqueues c = act(a @ b + bias) on the stream current now (one C call per
-    invocation). For tight loops such as benchmarks; the tensors must stay alive
-    and unchanged in shape while the callable is used."""
+    enqueues c = act(a @ b + bias) (a @ b.T with transpose_b) on the stream
+    current now (one C call per invocation). For tight loops such as benchmarks;
+    the tensors must stay alive and unchanged in shape while the callable is used."""
     dev = _check_dev(a, b, bias, c)
-    dt = _dtype_code(a)
-    for t in (b, bias, c):
-        if t is not None and _dtype_code(t) != dt:
-            raise TypeError("all operands must share one dtype")
-    M, K = a.shape
-    K2, N = b.shape
-    if K2 != K or tuple(c.shape) != (M, N) or (bias is not None and tuple(bias.shape) != (N,)):
-        raise ValueError("shape mismatch")
+    dt, M, N, K = _gemm_shapes(a, b, bias, c, transpose_b)
     torch = _torch()
     lib = _lib()
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     args = (_ptr(a), _ptr(b), _ptr(bias), _ptr(c), M, N, K, _act(act), dt)
-    fn = lib.gemm_bias_act
+    name = "gemm_bias_act_nt" if transpose_b else "gemm_bias_act"
+    fn = getattr(lib, name)
     set_stream = lib.gba_set_stream
     set_stream(stream)
 
     def launch():
         st = fn(*args)
         if st != 0:
-            raise GbaError(st, "gemm_bias_act")
+            raise GbaError(st, name)
 
     if torch.cuda.current_device() != dev.index:
         raise ValueError("bind on the tensors' device (torch.cuda.set_device first)")
     return launch
 
 
-def gemm(a, b, c):
-    """c[M,N] = a[M,K] @ b[K,N], rounded to the operand dtype. Returns c."""
+def gemm(a, b, c, transpose_b=False):
+    """c[M,N] = a[M,K] @ b[K,N] (a @ b.T for b [N,K] with transpose_b), rounded to
+    the operand dtype. Returns c."""
     dev = _check_dev(a, b, c)
-    dt = _dtype_code(a)
-    M, K = a.shape
-    K2, N = b.shape
-    if K2 != K or tuple(c.shape) != (M, N) or _dtype_code(b) != dt or _dtype_code(c) != dt:
-        raise ValueError("shape or dtype mismatch")
-    _call("gemm", dev, _ptr(a), _ptr(b), _ptr(c), M, N, K, dt)
+    dt, M, N, K = _gemm_shapes(a, b, None, c, transpose_b)
+    _call("gemm_nt" if transpose_b else "gemm", dev, _ptr(a), _ptr(b), _ptr(c), M, N, K, dt)
     return c
 
 
@@ -254,10 +258,10 @@ def set_schedule(sched: Optional[dict]) -> None:
         raise GbaError(st, "gba_set_schedule")
 
 
-def get_schedule(M: int, N: int, K: int, act="gelu", dtype="f16") -> dict:
+def get_schedule(M: int, N: int, K: int, act="gelu", dtype="f16", transpose_b=False) -> dict:
     s = Schedule()
-    st = _lib().gba_get_schedule(M, N, K, _act(act), 0 if dtype in ("f16", "float16") else 1,
-                                 ctypes.byref(s))
+    fn = _lib().gba_get_schedule_nt if transpose_b else _lib().gba_get_schedule
+    st = fn(M, N, K, _act(act), 0 if dtype in ("f16", "float16") else 1, ctypes.byref(s))
     if st != 0:
         raise GbaError(st, "gba_get_schedule")
     return s.as_dict()
@@ -273,15 +277,16 @@ def list_schedules() -> list:
     return out
 
 
-def autotune(a, b, bias, c, act="gelu", all_groups: bool = False):
+TUNE_ALL_GROUPS, TUNE_TRANSPOSE_B = 1, 2
+
+
+def autotune(a, b, bias, c, act="gelu", all_groups: bool = False, transpose_b=False):
     """Time every compiled-in schedule on these buffers; cache and return the best.
 
     Returns (schedule dict, median ms). c holds the winner's result.
     """
     dev = _check_dev(a, b, bias, c)
-    dt = _dtype_code(a)
-    M, K = a.shape
-    N = b.shape[1]
+    dt, M, N, K = _gemm_shapes(a, b, bias, c, transpose_b)
     best = Schedule()
     ms = ctypes.c_double()
     torch = _torch()
@@ -289,7 +294,9 @@ def autotune(a, b, bias, c, act="gelu", all_groups: bool = False):
         lib = _lib()
         lib.gba_set_stream(ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
         st = lib.gba_autotune(_ptr(a), _ptr(b), _ptr(bias), _ptr(c), M, N, K, _act(act), dt,
-                              1 if all_groups else 0, ctypes.byref(best), ctypes.byref(ms))
+                              (TUNE_ALL_GROUPS if all_groups else 0)
+                              | (TUNE_TRANSPOSE_B if transpose_b else 0),
+                              ctypes.byref(best), ctypes.byref(ms))
     if st not in (0, 10):
         raise GbaError(st, "gba_autotune")
     return best.as_dict(), ms.value

@@ -18,7 +18,7 @@
 #include "gba_kernels.hpp"
 #include "gba_registry.hpp"
 
-#define GBA_VERSION_STRING "0.1.0"
+#define GBA_VERSION_STRING "0.2.0"
 
 namespace gba {
 extern const ScheduleEntry s_256x256x64_w2x2;
@@ -226,11 +226,13 @@ std::string cache_dir() {
 
 std::string cache_file() { return cache_dir() + "/schedules.json"; }
 
-std::string cache_key(const DeviceInfo &d, int dtype, int act, int64_t M, int64_t N, int64_t K) {
+// tb: B stored (N,K) (transpose_B), "nt" in the key; else "nn".
+std::string cache_key(const DeviceInfo &d, int dtype, int act, bool tb, int64_t M, int64_t N,
+                      int64_t K) {
     char buf[256];
-    snprintf(buf, sizeof buf, "%s|%d|%s|%s|%s|%lld|%lld|%lld", d.arch.c_str(), d.cus,
-             GBA_VERSION_STRING, kDtName[dtype], kActName[act], (long long)M, (long long)N,
-             (long long)K);
+    snprintf(buf, sizeof buf, "%s|%d|%s|%s|%s|%s|%lld|%lld|%lld", d.arch.c_str(), d.cus,
+             GBA_VERSION_STRING, kDtName[dtype], kActName[act], tb ? "nt" : "nn", (long long)M,
+             (long long)N, (long long)K);
     return buf;
 }
 
@@ -334,7 +336,7 @@ int cache_save_locked() {
 }
 
 gba_schedule choose(const DeviceInfo &d, int64_t M, int64_t N, int64_t K, int act, int dtype,
-                    const char **why) {
+                    bool tb, const char **why) {
     if (t_forced) {
         *why = "forced";
         return t_forced_sched;
@@ -342,7 +344,7 @@ gba_schedule choose(const DeviceInfo &d, int64_t M, int64_t N, int64_t K, int ac
     {
         std::lock_guard<std::mutex> lk(g_cache_mu);
         cache_load_locked();
-        auto it = g_cache.find(cache_key(d, dtype, act, M, N, K));
+        auto it = g_cache.find(cache_key(d, dtype, act, tb, M, N, K));
         if (it != g_cache.end()) {
             *why = "cache";
             return it->second.s;
@@ -352,21 +354,27 @@ gba_schedule choose(const DeviceInfo &d, int64_t M, int64_t N, int64_t K, int ac
     return heuristic(M, N, d.cus);
 }
 
+// The instance of schedule s for (dtype, act, B layout), or null.
+gba::GemmLaunchFn launcher(const gba_schedule &s, int dtype, int act, bool tb) {
+    const int i = find_entry(s);
+    if (i < 0) return nullptr;
+    return tb ? kTable[i]->tb[dtype][act] : kTable[i]->fn[dtype][act];
+}
+
 int launch(const gba_schedule &s0, const void *A, const void *B, const void *bias, void *C,
-           int64_t M, int64_t N, int64_t K, int act, int dtype) {
+           int64_t M, int64_t N, int64_t K, int act, int dtype, bool tb) {
     gba_schedule s = s0;
     // The persistent kernel streams at least two K slices per tile; with one,
     // its non-persistent twin (same tile, kernel 3) does the same work.
     if (s.kernel == 4 && K <= s.bk) s.kernel = 3;
-    const int i = find_entry(s);
-    if (i < 0) return GBA_ERR_SCHEDULE;
-    hipError_t e = kTable[i]->fn[dtype][act](A, B, bias, C, (int)M, (int)N, (int)K, s.raster,
-                                            s.group_m, t_stream);
+    const gba::GemmLaunchFn f = launcher(s, dtype, act, tb);
+    if (!f) return GBA_ERR_SCHEDULE;   // unknown, or no transpose_B path in this kernel
+    hipError_t e = f(A, B, bias, C, (int)M, (int)N, (int)K, s.raster, s.group_m, t_stream);
     return e == hipSuccess ? GBA_OK : hip_fail(e);
 }
 
 int gemm_common(const void *A, const void *B, const void *bias, void *C, int64_t M, int64_t N,
-                int64_t K, int act, int dtype) {
+                int64_t K, int act, int dtype, bool tb) {
     bool nothing = false;
     int s = check_gemm_args(A, B, bias, C, M, N, K, act, dtype, &nothing);
     if (s || nothing) return s;
@@ -374,13 +382,15 @@ int gemm_common(const void *A, const void *B, const void *bias, void *C, int64_t
     s = current_device(&d);
     if (s) return s;
     const char *why = "";
-    const gba_schedule sch = choose(*d, M, N, K, act, dtype, &why);
+    const gba_schedule sch = choose(*d, M, N, K, act, dtype, tb, &why);
     if (log_enabled())
         fprintf(stderr,
-                "[gba] M=%lld N=%lld K=%lld act=%s dtype=%s -> k%d %dx%dx%d w%dx%d s%d r%d g%d (%s)\n",
-                (long long)M, (long long)N, (long long)K, kActName[act], kDtName[dtype], sch.kernel,
-                sch.bm, sch.bn, sch.bk, sch.wm, sch.wn, sch.stages, sch.raster, sch.group_m, why);
-    return launch(sch, A, B, bias, C, M, N, K, act, dtype);
+                "[gba] M=%lld N=%lld K=%lld act=%s dtype=%s B=%s -> k%d %dx%dx%d w%dx%d s%d r%d g%d "
+                "(%s)\n",
+                (long long)M, (long long)N, (long long)K, kActName[act], kDtName[dtype],
+                tb ? "NK" : "KN", sch.kernel, sch.bm, sch.bn, sch.bk, sch.wm, sch.wn, sch.stages,
+                sch.raster, sch.group_m, why);
+    return launch(sch, A, B, bias, C, M, N, K, act, dtype, tb);
 }
 
 template <int DT, int ACT>
@@ -456,7 +466,8 @@ int gba_list_schedule(int i, gba_schedule *out) {
     return GBA_OK;
 }
 
-int gba_get_schedule(int64_t M, int64_t N, int64_t K, int act, int dtype, gba_schedule *out) {
+static int get_schedule(int64_t M, int64_t N, int64_t K, int act, int dtype, bool tb,
+                        gba_schedule *out) {
     if (!out) return GBA_ERR_NULL;
     int s = check_enums(act, dtype);
     if (s) return s;
@@ -465,17 +476,34 @@ int gba_get_schedule(int64_t M, int64_t N, int64_t K, int act, int dtype, gba_sc
     s = current_device(&d);
     if (s) return s;
     const char *why;
-    *out = choose(*d, M, N, K, act, dtype, &why);
+    *out = choose(*d, M, N, K, act, dtype, tb, &why);
     return GBA_OK;
+}
+
+int gba_get_schedule(int64_t M, int64_t N, int64_t K, int act, int dtype, gba_schedule *out) {
+    return get_schedule(M, N, K, act, dtype, false, out);
+}
+
+int gba_get_schedule_nt(int64_t M, int64_t N, int64_t K, int act, int dtype, gba_schedule *out) {
+    return get_schedule(M, N, K, act, dtype, true, out);
 }
 
 int gemm_bias_act(const void *A, const void *B, const void *bias, void *C, int64_t M, int64_t N,
                   int64_t K, int act, int dtype) {
-    return gemm_common(A, B, bias, C, M, N, K, act, dtype);
+    return gemm_common(A, B, bias, C, M, N, K, act, dtype, false);
 }
 
 int gemm(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype) {
-    return gemm_common(A, B, nullptr, C, M, N, K, GBA_ACT_NONE, dtype);
+    return gemm_common(A, B, nullptr, C, M, N, K, GBA_ACT_NONE, dtype, false);
+}
+
+int gemm_bias_act_nt(const void *A, const void *W, const void *bias, void *C, int64_t M,
+                     int64_t N, int64_t K, int act, int dtype) {
+    return gemm_common(A, W, bias, C, M, N, K, act, dtype, true);
+}
+
+int gemm_nt(const void *A, const void *W, void *C, int64_t M, int64_t N, int64_t K, int dtype) {
+    return gemm_common(A, W, nullptr, C, M, N, K, GBA_ACT_NONE, dtype, true);
 }
 
 int bias_act(const void *X, const void *bias, void *Y, int64_t M, int64_t N, int act,
@@ -525,6 +553,7 @@ int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_
     const DeviceInfo *d;
     s = current_device(&d);
     if (s) return s;
+    const bool tb = (flags & GBA_TUNE_TRANSPOSE_B) != 0;
     if (nothing) {
         gba_schedule h = heuristic(M, N, d->cus);
         if (best_out) *best_out = h;
@@ -536,10 +565,11 @@ int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_
     for (int i = 0; i < kNumTable; ++i) {
         gba_schedule c = kTable[i]->sched;
         if (lds_bytes(c) > kLdsBytes) continue;   // the pages' shared-memory filter
+        if (tb && !kTable[i]->tb[0][0]) continue;   // no transpose_B path
         gba_schedule r0 = c;
         r0.raster = 0;
         cands.push_back(r0);
-        if (flags & 1) {
+        if (flags & GBA_TUNE_ALL_GROUPS) {
             for (int g : groups_all) {
                 gba_schedule r1 = c;
                 r1.raster = 1;
@@ -560,10 +590,10 @@ int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_
     int status = GBA_OK;
     for (const gba_schedule &c : cands) {
         for (int w = 0; w < 10 && status == GBA_OK; ++w)
-            status = launch(c, A, B, bias, C, M, N, K, act, dtype);
+            status = launch(c, A, B, bias, C, M, N, K, act, dtype, tb);
         for (int r = 0; r < 50 && status == GBA_OK; ++r) {
             hipEventRecord(ev[r], t_stream);
-            status = launch(c, A, B, bias, C, M, N, K, act, dtype);
+            status = launch(c, A, B, bias, C, M, N, K, act, dtype, tb);
         }
         if (status) break;
         hipEventRecord(ev[50], t_stream);
@@ -587,7 +617,7 @@ int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_
     for (auto &e : ev) hipEventDestroy(e);
     if (status) return status;
     // Leave the winner's result in C.
-    status = launch(best, A, B, bias, C, M, N, K, act, dtype);
+    status = launch(best, A, B, bias, C, M, N, K, act, dtype, tb);
     if (status) return status;
     hipError_t he = hipStreamSynchronize(t_stream);
     if (he != hipSuccess) return hip_fail(he);
@@ -595,7 +625,7 @@ int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_
     if (best_ms_out) *best_ms_out = best_ms;
     std::lock_guard<std::mutex> lk(g_cache_mu);
     cache_load_locked();
-    g_cache[cache_key(*d, dtype, act, M, N, K)] = CacheRec{best, best_ms};
+    g_cache[cache_key(*d, dtype, act, tb, M, N, K)] = CacheRec{best, best_ms};
     return cache_save_locked();
 }
 

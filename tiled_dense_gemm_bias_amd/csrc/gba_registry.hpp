@@ -1,5 +1,6 @@
 // Table entry for one compiled-in GEMM schedule: its shape and the launchers of
-// its eight (dtype x activation) kernel instances.
+// its (dtype x activation) kernel instances, for B stored (K,N) and, where the
+// kernel has that path, for B stored (N,K) (transpose_B).
 #pragma once
 
 #include "gba.h"
@@ -15,7 +16,8 @@ using GemmLaunchFn = hipError_t (*)(const void *, const void *, const void *, vo
 
 struct ScheduleEntry {
     gba_schedule sched;      // raster / group_m hold the defaults
-    GemmLaunchFn fn[2][4];   // [dtype][act]
+    GemmLaunchFn fn[2][4];   // [dtype][act], B stored (K,N)
+    GemmLaunchFn tb[2][4];   // [dtype][act], B stored (N,K); null without that path
 };
 
 }  // namespace gba
@@ -111,7 +113,30 @@ struct ScheduleEntry {
      gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, MS, DT, 2>,                             \
      gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, MS, DT, 3>}
 
-// kernel id 2: 32x32x16 MFMAs; kernel id 3: 16x16x32 MFMAs.
+// transpose_B instances (16x16x32 MFMAs only)
+#define GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, DT, ACT)                                  \
+    template __global__ void gba::gemm_v3_kernel<BM, BN, BK, WM, WN, S, L, SP, 16, DT, ACT, true>( \
+        const uint16_t *__restrict__, const uint16_t *__restrict__, const uint16_t *__restrict__, \
+        uint16_t *__restrict__, int, int, int, int, int, int, int);
+
+#define GBA_V3T_INSTS_(BM, BN, BK, WM, WN, S, L, SP)                                           \
+    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 0)                                          \
+    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 1)                                          \
+    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 2)                                          \
+    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 3)                                          \
+    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 0)                                          \
+    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 1)                                          \
+    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 2)                                          \
+    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 3)
+
+#define GBA_V3T_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, DT)                                   \
+    {gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, 16, DT, 0, true>,                        \
+     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, 16, DT, 1, true>,                        \
+     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, 16, DT, 2, true>,                        \
+     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, 16, DT, 3, true>}
+
+// kernel id 2: 32x32x16 MFMAs (B stored (K,N) only); kernel id 3: 16x16x32
+// MFMAs, both B layouts (GBA_V3_SCHEDULE_ENTRY_TB).
 #ifdef __HIP_DEVICE_COMPILE__
 #define GBA_V3_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, S, L, SP, MS, GROUP_M)               \
     GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP, MS)
@@ -126,25 +151,45 @@ struct ScheduleEntry {
     }
 #endif
 
+#ifdef __HIP_DEVICE_COMPILE__
+#define GBA_V3_SCHEDULE_ENTRY_TB(NAME, BM, BN, BK, WM, WN, S, L, SP, GROUP_M)                 \
+    GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP, 16)                                          \
+    GBA_V3T_INSTS_(BM, BN, BK, WM, WN, S, L, SP)
+#else
+#define GBA_V3_SCHEDULE_ENTRY_TB(NAME, BM, BN, BK, WM, WN, S, L, SP, GROUP_M)                 \
+    GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP, 16)                                          \
+    GBA_V3T_INSTS_(BM, BN, BK, WM, WN, S, L, SP)                                             \
+    namespace gba {                                                                          \
+    extern const ScheduleEntry NAME;                                                         \
+    const ScheduleEntry NAME = {{BM, BN, BK, WM, WN, S, 1, GROUP_M, 3, L, SP},                \
+                                {GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, 16, 0),     \
+                                 GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, 16, 1)},    \
+                                {GBA_V3T_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, 0),        \
+                                 GBA_V3T_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, 1)}};      \
+    }
+#endif
+
 // ---- persistent interleaved kernel (gemm_v5.hpp), kernel id 4 ----
-#define GBA_V5_INST_(BM, BN, WM, WN, DT, ACT)                                                 \
-    template __global__ void gba::gemm_v5_kernel<BM, BN, WM, WN, DT, ACT>(                    \
+#define GBA_V5_INST_(BM, BN, WM, WN, DT, ACT, TB)                                             \
+    template __global__ void gba::gemm_v5_kernel<BM, BN, WM, WN, DT, ACT, TB>(                \
         const uint16_t *__restrict__, const uint16_t *__restrict__, const uint16_t *__restrict__, \
         uint16_t *__restrict__, int, int, int, int, int, int, int);
 
-#define GBA_V5_INSTS_(BM, BN, WM, WN)                                                          \
-    GBA_V5_INST_(BM, BN, WM, WN, 0, 0)                                                         \
-    GBA_V5_INST_(BM, BN, WM, WN, 0, 1)                                                         \
-    GBA_V5_INST_(BM, BN, WM, WN, 0, 2)                                                         \
-    GBA_V5_INST_(BM, BN, WM, WN, 0, 3)                                                         \
-    GBA_V5_INST_(BM, BN, WM, WN, 1, 0)                                                         \
-    GBA_V5_INST_(BM, BN, WM, WN, 1, 1)                                                         \
-    GBA_V5_INST_(BM, BN, WM, WN, 1, 2)                                                         \
-    GBA_V5_INST_(BM, BN, WM, WN, 1, 3)
+#define GBA_V5_INSTS1_(BM, BN, WM, WN, TB)                                                     \
+    GBA_V5_INST_(BM, BN, WM, WN, 0, 0, TB)                                                     \
+    GBA_V5_INST_(BM, BN, WM, WN, 0, 1, TB)                                                     \
+    GBA_V5_INST_(BM, BN, WM, WN, 0, 2, TB)                                                     \
+    GBA_V5_INST_(BM, BN, WM, WN, 0, 3, TB)                                                     \
+    GBA_V5_INST_(BM, BN, WM, WN, 1, 0, TB)                                                     \
+    GBA_V5_INST_(BM, BN, WM, WN, 1, 1, TB)                                                     \
+    GBA_V5_INST_(BM, BN, WM, WN, 1, 2, TB)                                                     \
+    GBA_V5_INST_(BM, BN, WM, WN, 1, 3, TB)
 
-#define GBA_V5_LAUNCHERS_(BM, BN, WM, WN, DT)                                                  \
-    {gba::launch_gemm_v5<BM, BN, WM, WN, DT, 0>, gba::launch_gemm_v5<BM, BN, WM, WN, DT, 1>,   \
-     gba::launch_gemm_v5<BM, BN, WM, WN, DT, 2>, gba::launch_gemm_v5<BM, BN, WM, WN, DT, 3>}
+#define GBA_V5_INSTS_(BM, BN, WM, WN) GBA_V5_INSTS1_(BM, BN, WM, WN, false) GBA_V5_INSTS1_(BM, BN, WM, WN, true)
+
+#define GBA_V5_LAUNCHERS_(BM, BN, WM, WN, DT, TB)                                              \
+    {gba::launch_gemm_v5<BM, BN, WM, WN, DT, 0, TB>, gba::launch_gemm_v5<BM, BN, WM, WN, DT, 1, TB>, \
+     gba::launch_gemm_v5<BM, BN, WM, WN, DT, 2, TB>, gba::launch_gemm_v5<BM, BN, WM, WN, DT, 3, TB>}
 
 #ifdef __HIP_DEVICE_COMPILE__
 #define GBA_V5_SCHEDULE_ENTRY(NAME, BM, BN, WM, WN, GROUP_M) GBA_V5_INSTS_(BM, BN, WM, WN)
@@ -154,7 +199,9 @@ struct ScheduleEntry {
     namespace gba {                                                                            \
     extern const ScheduleEntry NAME;                                                           \
     const ScheduleEntry NAME = {{BM, BN, 64, WM, WN, 2, 1, GROUP_M, 4, WM * WN, 1},            \
-                                {GBA_V5_LAUNCHERS_(BM, BN, WM, WN, 0),                         \
-                                 GBA_V5_LAUNCHERS_(BM, BN, WM, WN, 1)}};                       \
+                                {GBA_V5_LAUNCHERS_(BM, BN, WM, WN, 0, false),                  \
+                                 GBA_V5_LAUNCHERS_(BM, BN, WM, WN, 1, false)},                 \
+                                {GBA_V5_LAUNCHERS_(BM, BN, WM, WN, 0, true),                   \
+                                 GBA_V5_LAUNCHERS_(BM, BN, WM, WN, 1, true)}};                 \
     }
 #endif

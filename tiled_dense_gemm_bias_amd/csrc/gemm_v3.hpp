@@ -18,6 +18,11 @@
 //    on the address path.
 //  * Slices past the end of K are still "loaded" with every lane out of range
 //    (zeros, no memory access), which keeps the wait counts uniform.
+//
+// TB (transpose_B): B is given as an (N,K) row-major array W and the product is
+// A.W^T. W's tile then has A's shape and layout (BN rows of BK K-contiguous
+// values, the same chunk XOR), is loaded like A, and its MFMA operand is read
+// like A's with ds_read_b128 -- no transposing reads. 16x16x32 MFMAs only.
 #pragma once
 
 #include "gemm_v2.hpp"
@@ -67,7 +72,7 @@ __device__ __forceinline__ int bswz(int r) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int MS, int DT,
-          int ACT>
+          int ACT, bool TB = false>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int M, int N, int K,
@@ -82,21 +87,23 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     constexpr int NI = MS == 32 ? 4 : 1;  // 4-column groups per lane and block
     constexpr int FM = WTM / BD, FN = WTN / BD;
     constexpr int NMF = FM * FN;          // MFMAs per step
-    constexpr int NPF = FM + 2 * FN;      // fragment reads per step
+    constexpr int NPF = FM + (TB ? 1 : 2) * FN;   // fragment reads per step
     constexpr int KK = BK / KS;           // steps per slice
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
     constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     constexpr int A_LD = BM * CHA / NTL;
-    constexpr int B_LD = BK * CHB / NTL;
+    constexpr int B_LD = TB ? BN * CHA / NTL : BK * CHB / NTL;
     constexpr int LD = A_LD + B_LD;       // loads per loader thread per slice
     constexpr int LD_STEP = (LD + SPREAD - 1) / SPREAD;
     static_assert(MS == 32 || MS == 16, "MFMA 32x32x16 or 16x16x32");
     static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
     static_assert(KK % 2 == 0, "fragment buffers alternate within a slice");
     static_assert(WTM % BD == 0 && WTN % BD == 0, "wave tile must be whole MFMA blocks");
-    static_assert(BN >= 128, "B swizzle needs at least 16 chunks per row");
+    static_assert(TB || BN >= 128, "B swizzle needs at least 16 chunks per row");
+    static_assert(!TB || MS == 16, "transpose_B is written for 16x16x32 MFMAs");
     static_assert(LDW >= 1 && LDW <= NW && NW % LDW == 0, "loader waves");
-    static_assert((BM * CHA) % NTL == 0 && (BK * CHB) % NTL == 0, "slices split evenly");
+    static_assert((BM * CHA) % NTL == 0 && (B_LD * NTL == (TB ? BN * CHA : BK * CHB)),
+                  "slices split evenly");
     static_assert(STAGES >= 2 && STAGES * STAGE_BYTES <= 160 * 1024, "LDS ring too large");
     static_assert(STAGES * LD < 64, "vmcnt range");
     static_assert(SPREAD >= 1 && SPREAD <= KK, "loads must be issued before the next barrier");
@@ -123,27 +130,32 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const int wid_s = __builtin_amdgcn_readfirstlane(wid);
     const bool loader = (LDW == NW) || wid_s < LDW;
     const int rows_a = min(M - m0, BM);
+    const int rows_b = min(N - n0, BN);   // rows of W's tile (TB)
     const uint32_t smem_lds = (uint32_t)(uintptr_t)(GBA_LDS void *)smem;
 
     // Loader lanes' byte offsets within a slice (row r, logical chunk c), fixed
     // for the whole K loop; the slice's K offset goes into the descriptor base.
+    // K-contiguous tiles (A, and W when TB) also keep each load's first k.
+    constexpr int NKC = TB ? LD : A_LD;
     uint32_t off[LD];
-    int a_k[A_LD];
+    int a_k[NKC];
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-        const int s = i * NTL + tid;
+    for (int i = 0; i < NKC; ++i) {
+        const int s = (i < A_LD ? i : i - A_LD) * NTL + tid;
         const int r = s / CHA, p = s % CHA;
         const int c = aswz<MS, CHA>(r, p);
         a_k[i] = c * 8;
         off[i] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)c * 16u;
     }
+    if constexpr (!TB) {
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-        const int s = i * NTL + tid;
-        const int r = s / CHB, p = s % CHB;
-        const int c = p ^ bswz<CHB>(r);
-        off[A_LD + i] = n0 + c * 8 < N ? (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u
-                                       : kOobOffset;
+        for (int i = 0; i < B_LD; ++i) {
+            const int s = i * NTL + tid;
+            const int r = s / CHB, p = s % CHB;
+            const int c = p ^ bswz<CHB>(r);
+            off[A_LD + i] = n0 + c * 8 < N ? (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u
+                                           : kOobOffset;
+        }
     }
 
     // Descriptors and LDS targets of one slice (slices at or past nk read nothing).
@@ -162,14 +174,23 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         const uint32_t bytes_a =
             live ? (uint32_t)rows_a * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u;
         d.ra = make_rsrc(A + (size_t)m0 * K + (live ? d.k0 : 0), bytes_a);
-        const uint32_t bytes_b = live ? (uint32_t)min(K - d.k0, BK) * (uint32_t)N * 2u : 0u;
-        d.rb = make_rsrc(B + (size_t)(live ? d.k0 : 0) * N + n0, bytes_b);
+        if constexpr (TB) {
+            const uint32_t bytes_b =
+                live ? (uint32_t)rows_b * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u;
+            d.rb = make_rsrc(B + (size_t)n0 * K + (live ? d.k0 : 0), bytes_b);
+        } else {
+            const uint32_t bytes_b = live ? (uint32_t)min(K - d.k0, BK) * (uint32_t)N * 2u : 0u;
+            d.rb = make_rsrc(B + (size_t)(live ? d.k0 : 0) * N + n0, bytes_b);
+        }
         return d;
     };
     auto dma_one = [&](const SliceDma &d, int i) {
         if (i < A_LD) {
             const uint32_t o = d.k0 + a_k[i] < K ? off[i] : kOobOffset;
             buffer_load_lds16(d.ra, o, d.la + i * NTL * 16);
+        } else if constexpr (TB) {
+            const uint32_t o = d.k0 + a_k[i] < K ? off[i] : kOobOffset;
+            buffer_load_lds16(d.rb, o, d.lb + (i - A_LD) * NTL * 16);
         } else {
             buffer_load_lds16(d.rb, off[i], d.lb + (i - A_LD) * NTL * 16);
         }
@@ -194,6 +215,11 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         const int c = (n >> 3) ^ bswz<CHB>(k);
         return A_BYTES + k * (BN * 2) + c * 16 + (n & 4) * 2;
     };
+    // TB: W^T operand of block fn read like A's (row n of W's tile, K chunk).
+    auto w_addr = [&](int fn, int kk) -> int {
+        const int r = wn * WTN + fn * BD + lrow_b;
+        return A_BYTES + r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * kk + lchunk) * 16;
+    };
 
     using AccT = typename Acc<MS>::type;
     AccT acc[FN][FM];
@@ -206,9 +232,12 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 
     u32x4 fa[2][FM];
     i16x4 fbl[2][FN], fbh[2][FN];
+    u32x4 fw[2][FN];
     auto read_one = [&](int buf, const char *base, int kk, int r) {
         if (r < FM) {
             fa[buf][r] = *reinterpret_cast<const u32x4 *>(base + a_addr(r, kk));
+        } else if constexpr (TB) {
+            fw[buf][r - FM] = *reinterpret_cast<const u32x4 *>(base + w_addr(r - FM, kk));
         } else {
             const int fn = (r - FM) >> 1, h = (r - FM) & 1;
             const i16x4 v =
@@ -229,8 +258,12 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 #pragma unroll
         for (int q = 0; q < NMF; ++q) {
             const int fn = q / FM, fm = q % FM;
-            const u32x4 bop = __builtin_bit_cast(
-                u32x4, __builtin_shufflevector(fbl[cur][fn], fbh[cur][fn], 0, 1, 2, 3, 4, 5, 6, 7));
+            u32x4 bop;
+            if constexpr (TB)
+                bop = fw[cur][fn];
+            else
+                bop = __builtin_bit_cast(u32x4, __builtin_shufflevector(fbl[cur][fn], fbh[cur][fn],
+                                                                        0, 1, 2, 3, 4, 5, 6, 7));
             if constexpr (MS == 32)
                 acc[fn][fm] = mfma32x32x16<DT>(bop, fa[cur][fm], acc[fn][fm]);
             else
@@ -337,14 +370,14 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int MS, int DT,
-          int ACT>
+          int ACT, bool TB = false>
 hipError_t launch_gemm_v3(const void *A, const void *B, const void *bias, void *C, int M, int N,
                           int K, int raster, int group_m, hipStream_t stream) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const long long grid = (long long)tiles_m * tiles_n;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, BK, WM, WN, STAGES, LDW, SPREAD, MS, DT, ACT>),
+    hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, BK, WM, WN, STAGES, LDW, SPREAD, MS, DT, ACT, TB>),
                        dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream, (const uint16_t *)A,
                        (const uint16_t *)B, (const uint16_t *)bias, (uint16_t *)C, M, N, K, tiles_m,
                        tiles_n, raster, group_m < 1 ? 1 : group_m);

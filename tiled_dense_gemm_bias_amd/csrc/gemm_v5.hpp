@@ -10,13 +10,14 @@
 // (bias, activation, rounding, stores) runs, and the next main loop starts
 // without the pipeline fill of a fresh workgroup. Tiles, LDS layouts,
 // fragments, MFMA order and epilogue are gemm_v3's (results are bit-identical).
+// TB (transpose_B, B given as an (N,K) array W) is gemm_v3's TB layout.
 #pragma once
 
 #include "gemm_v3.hpp"
 
 namespace gba {
 
-template <int BM, int BN, int WM, int WN, int DT, int ACT>
+template <int BM, int BN, int WM, int WN, int DT, int ACT, bool TB = false>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int M, int N, int K,
@@ -26,15 +27,16 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     constexpr int CHA = BK / 8, CHB = BN / 8;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / BD, FN = WTN / BD;
-    constexpr int NMF = FM * FN, NPF = FM + 2 * FN;
+    constexpr int NMF = FM * FN, NPF = FM + (TB ? 1 : 2) * FN;
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
     constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    constexpr int A_LD = BM * CHA / NT, B_LD = BK * CHB / NT, LD = A_LD + B_LD;
+    constexpr int A_LD = BM * CHA / NT, B_LD = (TB ? BN * CHA : BK * CHB) / NT, LD = A_LD + B_LD;
     constexpr int EVERY = NMF / LD;
     static_assert(KK == 2, "two MFMA steps per slice");
     static_assert(WTM % BD == 0 && WTN % BD == 0, "wave tile must be whole MFMA blocks");
     static_assert(BN >= 128, "B swizzle needs at least 16 chunks per row");
-    static_assert((BM * CHA) % NT == 0 && (BK * CHB) % NT == 0, "slices split evenly");
+    static_assert((BM * CHA) % NT == 0 && B_LD * NT == (TB ? BN * CHA : BK * CHB),
+                  "slices split evenly");
     static_assert(2 * STAGE_BYTES <= 160 * 1024, "LDS ring too large");
     static_assert(2 * LD < 64 && NMF % LD == 0 && NPF <= NMF, "step layout");
     // Needs at least two K slices (K > 64): the launcher uses gemm_v3 below that.
@@ -54,7 +56,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 
     // Tile of round r: index r*G + slot in raster order (-1 past the last tile).
     struct Tile {
-        int m0, n0, rows;
+        int m0, n0, rows;   // rows: of A's tile (M edge)
     };
     auto tile_of = [&](int r, Tile &t) -> bool {
         const int idx = r * G + slot;
@@ -78,6 +80,8 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // for B, k row 8i + tid/32 and logical chunk c_b(i) = c_b(0) ^ 8(i%4)
     // (the B swizzle's row/8 term). So a handful of registers describe them all.
     static_assert(NT == 256 && CHA == 8 && CHB == 32, "loader mapping written for 256 threads, BK 64, BN 256");
+    // TB: W's tile is loaded like A's (BN = 256 rows of 64 k), with the same
+    // per-thread base.
     const int c_a = (tid & 7) ^ ((tid >> 3) & 7);
     const uint32_t a_base = (uint32_t)(tid >> 3) * (uint32_t)K * 2u + (uint32_t)c_a * 16u;
     const int c_b0 = (tid & 31) ^ bswz<CHB>(tid >> 5);
@@ -97,8 +101,13 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         d.n0 = live ? t.n0 : N;
         d.ra = make_rsrc(A + (live ? (size_t)t.m0 * K + d.k0 : 0),
                          live ? (uint32_t)t.rows * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u);
-        d.rb = make_rsrc(B + (live ? (size_t)d.k0 * N + t.n0 : 0),
-                         live ? (uint32_t)min(K - d.k0, BK) * (uint32_t)N * 2u : 0u);
+        if constexpr (TB)
+            d.rb = make_rsrc(B + (live ? (size_t)t.n0 * K + d.k0 : 0),
+                             live ? (uint32_t)min(N - t.n0, BN) * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u
+                                  : 0u);
+        else
+            d.rb = make_rsrc(B + (live ? (size_t)d.k0 * N + t.n0 : 0),
+                             live ? (uint32_t)min(K - d.k0, BK) * (uint32_t)N * 2u : 0u);
         return d;
     };
     // `kx`, `nx`: K and N re-read opaquely in each slice, so that the per-load
@@ -108,6 +117,10 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         if (i < A_LD) {
             const uint32_t o = d.k0 + c_a * 8 < K ? a_base + (uint32_t)(i * 64) * kx : kOobOffset;
             buffer_load_lds16(d.ra, o, d.la + i * NT * 16);
+        } else if constexpr (TB) {
+            const int j = i - A_LD;
+            const uint32_t o = d.k0 + c_a * 8 < K ? a_base + (uint32_t)(j * 64) * kx : kOobOffset;
+            buffer_load_lds16(d.rb, o, d.lb + j * NT * 16);
         } else {
             const int j = i - A_LD;
             const int c = c_b0 ^ (8 * (j & 3));
@@ -133,25 +146,39 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         const int r = wm * WTM + tj;
         fa_base[kk] = (uint32_t)(r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * kk + tg) * 16);
     }
-    uint32_t fb_base[FN];
+    // TB: W^T block fn, step kk: lane l reads row wn*WTN + 16 fn + l%16 of W's
+    // tile like A's (a per-kk lane base plus 16 fn rows).
+    constexpr int NFB = TB ? KK : FN;
+    uint32_t fb_base[NFB];
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-        const int k = 8 * tg + (tj >> 2);
-        const int n = wn * WTN + fn * 16 + 4 * (tj & 3);
-        const int c = (n >> 3) ^ bswz<CHB>(k);
-        fb_base[fn] = (uint32_t)(A_BYTES + k * (BN * 2) + c * 16 + (n & 4) * 2);
+    for (int f = 0; f < NFB; ++f) {
+        if constexpr (TB) {
+            const int r = wn * WTN + tj;
+            fb_base[f] = (uint32_t)(A_BYTES + r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * f + tg) * 16);
+        } else {
+            const int k = 8 * tg + (tj >> 2);
+            const int n = wn * WTN + f * 16 + 4 * (tj & 3);
+            const int c = (n >> 3) ^ bswz<CHB>(k);
+            fb_base[f] = (uint32_t)(A_BYTES + k * (BN * 2) + c * 16 + (n & 4) * 2);
+        }
     }
     auto a_addr = [&](int fm, int kk) -> uint32_t { return fa_base[kk] + fm * BD * (BK * 2); };
     auto b_addr = [&](int fn, int kk, int h) -> uint32_t {
-        return fb_base[fn] + (32 * kk + 4 * h) * (BN * 2);
+        if constexpr (TB)
+            return fb_base[kk] + fn * BD * (BK * 2);
+        else
+            return fb_base[fn] + (32 * kk + 4 * h) * (BN * 2);
     };
 
     f32x4 acc[FN][FM];
     u32x4 fa[2][FM];
     i16x4 fbl[2][FN], fbh[2][FN];
+    u32x4 fw[2][FN];
     auto read_one = [&](int buf, const char *base, int kk, int r) {
         if (r < FM) {
             fa[buf][r] = *reinterpret_cast<const u32x4 *>(base + a_addr(r, kk));
+        } else if constexpr (TB) {
+            fw[buf][r - FM] = *reinterpret_cast<const u32x4 *>(base + b_addr(r - FM, kk, 0));
         } else {
             const int fn = (r - FM) >> 1, h = (r - FM) & 1;
             const i16x4 v =
@@ -169,8 +196,12 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 #pragma unroll
         for (int q = 0; q < NMF; ++q) {
             const int fn = q / FM, fm = q % FM;
-            const u32x4 bop = __builtin_bit_cast(
-                u32x4, __builtin_shufflevector(fbl[cur][fn], fbh[cur][fn], 0, 1, 2, 3, 4, 5, 6, 7));
+            u32x4 bop;
+            if constexpr (TB)
+                bop = fw[cur][fn];
+            else
+                bop = __builtin_bit_cast(u32x4, __builtin_shufflevector(fbl[cur][fn], fbh[cur][fn],
+                                                                        0, 1, 2, 3, 4, 5, 6, 7));
             acc[fn][fm] = mfma16x16x32<DT>(bop, fa[cur][fm], acc[fn][fm]);
             if (reads && q < NPF) read_one(cur ^ 1, pf_base, pf_kk, q);
             if (dma && q % EVERY == 0) dma_one(d, q / EVERY, kx, nx);
@@ -289,7 +320,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 // Grid: one workgroup per CU (two 64 KiB stages fill the LDS), or fewer when
 // there are fewer tiles. K must exceed 64 (at least two K slices per tile): the
 // library sends K <= 64 to gemm_v3 with the same tile.
-template <int BM, int BN, int WM, int WN, int DT, int ACT>
+template <int BM, int BN, int WM, int WN, int DT, int ACT, bool TB = false>
 hipError_t launch_gemm_v5(const void *A, const void *B, const void *bias, void *C, int M, int N,
                           int K, int raster, int group_m, hipStream_t stream) {
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -303,7 +334,7 @@ hipError_t launch_gemm_v5(const void *A, const void *B, const void *bias, void *
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     const int grid = (int)(tiles < cus ? tiles : cus);
-    hipLaunchKernelGGL((gemm_v5_kernel<BM, BN, WM, WN, DT, ACT>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((gemm_v5_kernel<BM, BN, WM, WN, DT, ACT, TB>), dim3((unsigned)grid),
                        dim3(WM * WN * 64), 0, stream, (const uint16_t *)A, (const uint16_t *)B,
                        (const uint16_t *)bias, (uint16_t *)C, M, N, K, tiles_m, tiles_n, raster,
                        group_m < 1 ? 1 : group_m);
