@@ -13,7 +13,8 @@ file's header for the pages and sections each step follows:
   - Epilogue: "TileLang: Write, Autotune, and Ship Fused Tensor-Core Kernels
     from Python", Why tile-level control matters (bias add + GELU on the
     accumulator); ReLU / sigmoid from "writing-tilelang-kernels", Pre-flight
-    Checklist and Key API Patterns.
+    Checklist and Key API Patterns; softplus from the same page's Elementwise
+    (2D) template; the tanh form of GELU (Hendrycks and Gimpel, 2016).
   - transpose_B (same page, Key API Patterns): the second operand stored (N, K)
     and used as its transpose (``transpose_b=True``).
 
@@ -34,8 +35,9 @@ _SRC = os.path.join(_HERE, "gemm_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 F16, BF16 = 0, 1
-ACT_NONE, ACT_RELU, ACT_SIGMOID, ACT_GELU = 0, 1, 2, 3
-ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "sigmoid": ACT_SIGMOID, "gelu": ACT_GELU}
+ACT_NONE, ACT_RELU, ACT_SIGMOID, ACT_GELU, ACT_SOFTPLUS, ACT_GELU_TANH = 0, 1, 2, 3, 4, 5
+ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "sigmoid": ACT_SIGMOID, "gelu": ACT_GELU,
+        "softplus": ACT_SOFTPLUS, "gelu_tanh": ACT_GELU_TANH}
 DTYPES = {"f16": F16, "fp16": F16, "float16": F16, "bf16": BF16, "bfloat16": BF16}
 
 

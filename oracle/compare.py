@@ -25,8 +25,9 @@ REL_FRO_TOL = 2e-2
 RTOL = 1e-2
 
 # Largest slope of each activation: identity/ReLU 1, logistic 1/4,
-# z*Phi(z) has derivative Phi(z) + z*phi(z) <= 1.129 (max near z = 1.41).
-ACT_LIPSCHITZ = {0: 1.0, 1: 1.0, 2: 0.25, 3: 1.13}
+# z*Phi(z) has derivative Phi(z) + z*phi(z) <= 1.129 (max near z = 1.41),
+# softplus' derivative is the logistic (< 1), the tanh form of GELU <= 1.129.
+ACT_LIPSCHITZ = {0: 1.0, 1: 1.0, 2: 0.25, 3: 1.13, 4: 1.0, 5: 1.13}
 
 
 def atol_k(K: int) -> float:

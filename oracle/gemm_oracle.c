@@ -16,6 +16,11 @@
  *     program is the plain product A @ B.
  *   - Same page, "Pre-flight Checklist" and "Key API Patterns": the fused
  *     epilogues are ReLU (max) and sigmoid.
+ *   - Same page, "Quick Templates" (Elementwise 2D): softplus, log(1 + e^z),
+ *     evaluated in the float accumulator type.
+ *   - The tanh form of GELU, 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))
+ *     (Hendrycks and Gimpel, "Gaussian Error Linear Units", 2016), as the
+ *     second GELU variant next to the erf form the pages' GELU epilogue reads as.
  *   - Same page, "Key API Patterns": the tile GEMM takes a transpose_B flag.
  *     With it, the second operand is given as an (N,K) row-major array W and
  *     the product is A times its transpose: s[i][j] = sum_k A[i][k] * W[j][k]
@@ -25,7 +30,8 @@
  *     s[i][j] = sum_{k<K} A[i][k] * B[k][j]        (each product exact in fp64)
  *     z[i][j] = s[i][j] + bias[j]                  (bias[N], broadcast over rows)
  *     y[i][j] = act(z[i][j])
- * with act in { identity, max(z,0), 1/(1+exp(-z)), z*Phi(z) (erf form) }.
+ * with act in { identity, max(z,0), 1/(1+exp(-z)), z*Phi(z) (erf form),
+ * log(1+exp(z)), tanh-form GELU }.
  * The loop order is i, then k, then j; the sum over k for one (i,j) is formed
  * left to right in k. fp16/bf16 bit patterns are decoded by this file's own
  * decoders; the fp64 result can be rounded to fp16/bf16 by this file's own
@@ -44,7 +50,7 @@
 #include <unistd.h>
 
 enum { OR_F16 = 0, OR_BF16 = 1 };
-enum { OR_NONE = 0, OR_RELU = 1, OR_SIGMOID = 2, OR_GELU = 3 };
+enum { OR_NONE = 0, OR_RELU = 1, OR_SIGMOID = 2, OR_GELU = 3, OR_SOFTPLUS = 4, OR_GELU_TANH = 5 };
 
 /* ---- bit decoders (IEEE binary16 and bfloat16) ---------------------------- */
 
@@ -114,6 +120,18 @@ static double act_apply(int act, double z) {
     case OR_GELU:
         /* z * Phi(z); Phi(z) = 0.5 * (1 + erf(z/sqrt2)) = 0.5 * erfc(-z/sqrt2) */
         return 0.5 * z * erfc(-z / sqrt(2.0));
+    case OR_SOFTPLUS:
+        /* log(1 + e^z), written so that neither branch overflows or cancels:
+         * z + log(1 + e^-z) = log(e^z (1 + e^-z)) for z > 0. */
+        return z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z));
+    case OR_GELU_TANH: {
+        /* 0.5 z (1 + tanh(y)); for y < 0, 1 + tanh(y) = 2 e^(2y) / (1 + e^(2y))
+         * (no cancellation). */
+        const double y = sqrt(2.0 / 3.14159265358979323846) * (z + 0.044715 * z * z * z);
+        if (y >= 0.0) return 0.5 * z * (1.0 + tanh(y));
+        const double e = exp(2.0 * y);
+        return z * e / (1.0 + e);
+    }
     default:
         return z;
     }
@@ -201,7 +219,7 @@ static int pick_threads(int nthreads, int64_t work_items) {
 static int gemm_impl(const uint16_t *A, const uint16_t *B, int b_nk, const uint16_t *bias,
                      double *out, double *absout, int64_t M, int64_t N, int64_t K, int act,
                      int dtype, const int64_t *rows, int64_t nrows, int nthreads) {
-    if (M < 0 || N < 0 || K < 0 || act < 0 || act > 3 || (dtype != OR_F16 && dtype != OR_BF16))
+    if (M < 0 || N < 0 || K < 0 || act < 0 || act > 5 || (dtype != OR_F16 && dtype != OR_BF16))
         return -1;
     if (!rows) nrows = M;
     if (nrows == 0 || N == 0) return 0;
@@ -257,7 +275,7 @@ int oracle_gemm_bias_act_nt(const uint16_t *A, const uint16_t *W, const uint16_t
  * unfused pair, applied to the fp16/bf16 intermediate exactly as stored. */
 int oracle_bias_act(const uint16_t *X, const uint16_t *bias, double *out, int64_t M,
                     int64_t N, int act, int dtype) {
-    if (M < 0 || N < 0 || act < 0 || act > 3 || (dtype != OR_F16 && dtype != OR_BF16))
+    if (M < 0 || N < 0 || act < 0 || act > 5 || (dtype != OR_F16 && dtype != OR_BF16))
         return -1;
     for (int64_t i = 0; i < M; ++i)
         for (int64_t j = 0; j < N; ++j) {

@@ -28,6 +28,12 @@ MUTANTS = {
     "gelu_scale": ("erfc(-z / sqrt(2.0))", "erfc(-z / 2.0)"),
     "sigmoid_sign": ("return 1.0 / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(z));"),
     "sigmoid_neg_branch": ("return e / (1.0 + e);", "return 1.0 / (1.0 + e);"),
+    "softplus_drops_z": ("return z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z));",
+                         "return z > 0.0 ? log1p(exp(-z)) : log1p(exp(z));"),
+    "softplus_log_not_log1p": ("return z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z));",
+                               "return z > 0.0 ? z + log(exp(-z)) : log1p(exp(z));"),
+    "gelu_tanh_cubic_coeff": ("0.044715 * z * z * z", "0.04715 * z * z * z"),
+    "gelu_tanh_neg_branch": ("return z * e / (1.0 + e);", "return z / (1.0 + e);"),
     "leaky_relu": ("return z > 0.0 ? z : 0.0;", "return z > 0.0 ? z : 0.01 * z;"),
     "f16_exp_off_by_one": ("ldexp((double)(fr | 0x400), ex - 25)", "ldexp((double)(fr | 0x400), ex - 24)"),
     "f16_subnormal_scale": ("ldexp((double)fr, -24)", "ldexp((double)fr, -25)"),

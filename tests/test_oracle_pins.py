@@ -209,6 +209,38 @@ def test_relu_and_identity(orc):
     np.testing.assert_array_equal(orc.act(x, "none"), x)
 
 
+def test_softplus_closed_forms_and_mpmath(orc):
+    # the pages' elementwise template: log(1 + e^z)
+    assert orc.act([0.0], "softplus")[0] == pytest.approx(math.log(2.0), rel=1e-16)
+    assert orc.act([math.log(3.0)], "softplus")[0] == pytest.approx(2 * math.log(2.0), rel=1e-15)
+    assert orc.act([math.log(math.e - 1)], "softplus")[0] == pytest.approx(1.0, rel=1e-15)
+    x = np.concatenate([np.linspace(-60, 60, 2401), np.geomspace(1e-8, 700, 400)])
+    x = np.concatenate([x, -x])
+    sp = orc.act(x, "softplus")
+    ref = np.array([float(mpmath.log1p(mpmath.exp(mpmath.mpf(v)))) for v in x])
+    np.testing.assert_allclose(sp, ref, rtol=4e-16, atol=0)
+    # log(1+e^z) - log(1+e^-z) = z
+    np.testing.assert_allclose(sp - orc.act(-x, "softplus"), x, rtol=2e-16, atol=2e-16)
+
+
+def test_gelu_tanh_against_torch_and_identities(orc):
+    # the tanh form of GELU against an independent implementation (torch's CPU
+    # float64 gelu with approximate="tanh")
+    torch = pytest.importorskip("torch")
+    x = np.concatenate([np.linspace(-12, 12, 4801), np.geomspace(1e-8, 1e4, 400)])
+    x = np.concatenate([x, -x])
+    g = orc.act(x, "gelu_tanh")
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    # torch forms 0.5 z (1 + tanh(y)) directly, which cancels for z << 0: its
+    # absolute error there is up to |z| ulp(1)/2; the oracle avoids the cancellation.
+    assert np.all(np.abs(g - ref) <= 1e-14 * np.abs(ref) + 2.3e-16 * np.abs(x))
+    assert orc.act([0.0], "gelu_tanh")[0] == 0.0
+    # tanh is odd, so g(z) - g(-z) = z
+    np.testing.assert_allclose(g - orc.act(-x, "gelu_tanh"), x, rtol=1e-15, atol=1e-15)
+    # an approximation of z * Phi(z): within 1e-3 of the erf form everywhere
+    assert np.abs(g - orc.act(x, "gelu")).max() < 1e-3
+
+
 # ------------------------------------------------------------ GEMM core ----
 
 def _hand_gemm():
@@ -322,7 +354,7 @@ def test_zero_matrix_gives_activation_of_bias_per_column(orc):
     B = synth.random_bits((K, N), "f16", 8)
     bias = synth.random_bits((N,), "f16", 9)
     bv = orc.decode(bias)
-    for act in ("none", "relu", "sigmoid", "gelu"):
+    for act in ("none", "relu", "sigmoid", "gelu", "softplus", "gelu_tanh"):
         got = orc.gemm_bias_act(Z, B, bias, act)
         want = np.broadcast_to(orc.act(bv, act), (M, N))
         np.testing.assert_array_equal(got, want)
@@ -385,7 +417,7 @@ def test_mid_size_against_numpy_float64_matmul(orc, dtype):
     assert np.all(np.abs(got - ref) <= 2 * (K + 1) * 2.0 ** -53 * S)
     np.testing.assert_allclose(S, np.abs(Av) @ np.abs(Bv) + np.abs(bv), rtol=1e-13)
     # the epilogue is applied per element after the sum
-    for act in ("relu", "sigmoid", "gelu"):
+    for act in ("relu", "sigmoid", "gelu", "softplus", "gelu_tanh"):
         np.testing.assert_array_equal(orc.gemm_bias_act(A, B, bias, act, dtype),
                                       orc.act(got, act))
 
