@@ -42,12 +42,17 @@ typedef enum { GBA_DTYPE_F16 = 0, GBA_DTYPE_BF16 = 1 } gba_dtype;
  * Pre-flight Checklist ("ReLU/sigmoid epilogue after GEMM") and Key API
  * Patterns (T.max, T.sigmoid). GELU: "TileLang: Write, Autotune, and Ship Fused
  * Tensor-Core Kernels from Python", Why tile-level control matters; this
- * library uses the erf form, GELU(z) = z * Phi(z) = 0.5 z (1 + erf(z/sqrt2)). */
+ * library's GELU is the erf form, GELU(z) = z * Phi(z) = 0.5 z (1 + erf(z/sqrt2)).
+ * Softplus: the Elementwise (2D) template of "writing-tilelang-kernels", Quick
+ * Templates, log(1 + exp(z)) in the float accumulator type. GELU_TANH: the
+ * tanh form of GELU (Hendrycks and Gimpel, 2016). */
 typedef enum {
     GBA_ACT_NONE = 0,
-    GBA_ACT_RELU = 1,    /* max(z, 0) */
-    GBA_ACT_SIGMOID = 2, /* 1 / (1 + exp(-z)) */
-    GBA_ACT_GELU = 3     /* z * Phi(z), erf form */
+    GBA_ACT_RELU = 1,     /* max(z, 0) */
+    GBA_ACT_SIGMOID = 2,  /* 1 / (1 + exp(-z)) */
+    GBA_ACT_GELU = 3,     /* z * Phi(z), erf form */
+    GBA_ACT_SOFTPLUS = 4, /* log(1 + exp(z)) */
+    GBA_ACT_GELU_TANH = 5 /* 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) */
 } gba_act;
 
 typedef enum {

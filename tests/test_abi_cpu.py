@@ -81,7 +81,7 @@ def call(lib, A=P16, B=P16, bias=None, C=P16 * 64, M=64, N=64, K=64, act=0, dt=0
 
 def test_argument_errors_are_synchronous_and_precede_device_use(lib):
     assert call(lib, dt=2) == ERR_DTYPE
-    assert call(lib, act=4) == ERR_ACT
+    assert call(lib, act=6) == ERR_ACT
     assert call(lib, act=-1) == ERR_ACT
     assert call(lib, M=-1) == ERR_SHAPE
     assert call(lib, K=1 << 24) == ERR_SHAPE
@@ -100,7 +100,7 @@ def test_argument_errors_are_synchronous_and_precede_device_use(lib):
 
 def test_bias_act_argument_errors(lib):
     v = ctypes.c_void_p
-    assert lib.bias_act(v(P16), None, v(P16), 4, 8, 5, 0) == ERR_ACT
+    assert lib.bias_act(v(P16), None, v(P16), 4, 8, 6, 0) == ERR_ACT
     assert lib.bias_act(v(P16), None, v(P16), 4, 12, 0, 0) == ERR_ALIGN
     assert lib.bias_act(None, None, v(P16), 4, 8, 0, 0) == ERR_NULL
     assert lib.bias_act(v(P16), None, v(P16 + 16), 4, 8, 0, 0) == ERR_ALIAS   # partial overlap

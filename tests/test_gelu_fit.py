@@ -65,7 +65,7 @@ def test_q_keeps_falling_past_the_fit_range_in_float32():
 def test_kernel_constants_are_the_tested_ones():
     src = open(KERNELS_HPP).read()
     start = src.index("ACT == ACT_GELU")
-    body = src[start:src.index("} else {", start)]
+    body = src[start:src.index("} else", start)]
     consts = [float(v) for v in re.findall(r"(-?\d+\.\d+(?:e-?\d+)?)f", body)]
     # the eight Horner coefficients, then the 0 of max(z, 0)
     assert consts[:8] == gelu_fit.KERNEL_Q and consts[8:] == [0.0], consts

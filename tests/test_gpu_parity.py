@@ -23,7 +23,7 @@ from tests.gpu_util import empty, say, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
-ACTS = ["none", "relu", "sigmoid", "gelu"]
+ACTS = ["none", "relu", "sigmoid", "gelu", "softplus", "gelu_tanh"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -401,6 +401,23 @@ def test_epilogue_device_functions_on_dense_grid(act):
         # hardware exp2 and reciprocal, each within a couple of fp32 ulps, plus the
         # conditioning of exp: rounding z*log2(e) to fp32 moves e^-z by |z| 2^-24.
         bound = (1e-6 + np.abs(z) * 1.2e-7) * np.abs(ref) + 1e-37
+        assert np.all(err <= bound), float((err / bound).max())
+    elif act == "softplus":
+        # max(z,0) + log1p(e^-|z|): hardware exp2 (conditioning |z| 2^-24 on e^-|z|),
+        # log2 and reciprocal each within a few fp32 ulps, Kahan's log1p correction.
+        t = np.exp(-np.abs(z.astype(np.float64)))
+        bound = 2e-6 * np.abs(ref) + 1.2e-7 * np.abs(z) * t + 1e-37
+        assert np.all(err <= bound), float((err / bound).max())
+    elif act == "gelu_tanh":
+        # z / (1 + 2^a), a = -2 y log2 e formed in fp32: two float32 constants and
+        # three roundings (z^2, the fma, the product) give a relative error up to
+        # 5 2^-24 = 3e-7 in a, so 2^a moves by |a| ln2 3e-7 relative; then the
+        # hardware exp2 and reciprocal (a few ulp). Where 1 + 2^a passes 2^126 the
+        # reciprocal is below the smallest normal float and flushes to zero, so
+        # results below |z| 2^-126 (< 1e-36 on this grid) come out as -0.
+        zz = z.astype(np.float64)
+        a = 2 * np.sqrt(2 / np.pi) * np.log2(np.e) * np.abs(zz + 0.044715 * zz ** 3)
+        bound = (2e-6 + a * 3.0e-7) * np.abs(ref) + 1e-36
         assert np.all(err <= bound), float((err / bound).max())
     else:
         # Phi(-|z|) = 2^Q(|z|) with fractional error < 8e-6 on |z| <= 6

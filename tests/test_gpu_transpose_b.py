@@ -18,7 +18,7 @@ from tests.gpu_util import empty, say, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
-ACTS = ["none", "relu", "sigmoid", "gelu"]
+ACTS = ["none", "relu", "sigmoid", "gelu", "softplus", "gelu_tanh"]
 PERSISTENT = dict(bm=256, bn=256, bk=64, wm=2, wn=2, stages=2, raster=1, group_m=4, kernel=4,
                   loaders=4, spread=1)
 

@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgba.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "gba.h")
 
-ACTS = {"none": 0, "relu": 1, "sigmoid": 2, "gelu": 3}
+ACTS = {"none": 0, "relu": 1, "sigmoid": 2, "gelu": 3, "softplus": 4, "gelu_tanh": 5}
 STATUS = {
     0: "GBA_OK", 1: "GBA_ERR_NULL", 2: "GBA_ERR_SHAPE", 3: "GBA_ERR_DTYPE", 4: "GBA_ERR_ACT",
     5: "GBA_ERR_ALIGN", 6: "GBA_ERR_ALIAS", 7: "GBA_ERR_DEVICE", 8: "GBA_ERR_HIP",

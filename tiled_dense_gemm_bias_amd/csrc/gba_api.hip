@@ -129,7 +129,7 @@ bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
 
 int check_enums(int act, int dtype) {
     if (dtype != GBA_DTYPE_F16 && dtype != GBA_DTYPE_BF16) return GBA_ERR_DTYPE;
-    if (act < GBA_ACT_NONE || act > GBA_ACT_GELU) return GBA_ERR_ACT;
+    if (act < GBA_ACT_NONE || act > GBA_ACT_GELU_TANH) return GBA_ERR_ACT;
     return GBA_OK;
 }
 
@@ -201,7 +201,7 @@ gba_schedule heuristic(int64_t M, int64_t N, int cus) {
 // ------------------------------------------------------------ disk cache ----
 
 const char *kDtName[2] = {"f16", "bf16"};
-const char *kActName[4] = {"none", "relu", "sigmoid", "gelu"};
+const char *kActName[gba::kNumActs] = {"none", "relu", "sigmoid", "gelu", "softplus", "gelu_tanh"};
 
 struct CacheRec {
     gba_schedule s;
@@ -409,9 +409,11 @@ hipError_t launch_bias_act_t(const void *X, const void *bias, void *Y, int M, in
 }
 
 using BiasActFn = hipError_t (*)(const void *, const void *, void *, int, int, hipStream_t);
-const BiasActFn kBiasAct[2][4] = {
-    {launch_bias_act_t<0, 0>, launch_bias_act_t<0, 1>, launch_bias_act_t<0, 2>, launch_bias_act_t<0, 3>},
-    {launch_bias_act_t<1, 0>, launch_bias_act_t<1, 1>, launch_bias_act_t<1, 2>, launch_bias_act_t<1, 3>},
+const BiasActFn kBiasAct[2][gba::kNumActs] = {
+    {launch_bias_act_t<0, 0>, launch_bias_act_t<0, 1>, launch_bias_act_t<0, 2>, launch_bias_act_t<0, 3>,
+     launch_bias_act_t<0, 4>, launch_bias_act_t<0, 5>},
+    {launch_bias_act_t<1, 0>, launch_bias_act_t<1, 1>, launch_bias_act_t<1, 2>, launch_bias_act_t<1, 3>,
+     launch_bias_act_t<1, 4>, launch_bias_act_t<1, 5>},
 };
 
 }  // namespace
@@ -526,7 +528,7 @@ int bias_act(const void *X, const void *bias, void *Y, int64_t M, int64_t N, int
 }
 
 int gba_epilogue_probe(const float *z, float *y, int64_t n, int act) {
-    if (act < GBA_ACT_NONE || act > GBA_ACT_GELU) return GBA_ERR_ACT;
+    if (act < GBA_ACT_NONE || act > GBA_ACT_GELU_TANH) return GBA_ERR_ACT;
     if (n < 0) return GBA_ERR_SHAPE;
     if (n == 0) return GBA_OK;
     if (!z || !y) return GBA_ERR_NULL;
@@ -538,7 +540,9 @@ int gba_epilogue_probe(const float *z, float *y, int64_t n, int act) {
     case 0: hipLaunchKernelGGL(gba::epilogue_probe_kernel<0>, dim3(blocks), dim3(256), 0, t_stream, z, y, (long long)n); break;
     case 1: hipLaunchKernelGGL(gba::epilogue_probe_kernel<1>, dim3(blocks), dim3(256), 0, t_stream, z, y, (long long)n); break;
     case 2: hipLaunchKernelGGL(gba::epilogue_probe_kernel<2>, dim3(blocks), dim3(256), 0, t_stream, z, y, (long long)n); break;
-    default: hipLaunchKernelGGL(gba::epilogue_probe_kernel<3>, dim3(blocks), dim3(256), 0, t_stream, z, y, (long long)n); break;
+    case 3: hipLaunchKernelGGL(gba::epilogue_probe_kernel<3>, dim3(blocks), dim3(256), 0, t_stream, z, y, (long long)n); break;
+    case 4: hipLaunchKernelGGL(gba::epilogue_probe_kernel<4>, dim3(blocks), dim3(256), 0, t_stream, z, y, (long long)n); break;
+    default: hipLaunchKernelGGL(gba::epilogue_probe_kernel<5>, dim3(blocks), dim3(256), 0, t_stream, z, y, (long long)n); break;
     }
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? GBA_OK : hip_fail(e);

@@ -39,7 +39,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
-enum { ACT_NONE = 0, ACT_RELU = 1, ACT_SIGMOID = 2, ACT_GELU = 3 };
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_SIGMOID = 2, ACT_GELU = 3, ACT_SOFTPLUS = 4, ACT_GELU_TANH = 5 };
+constexpr int kNumActs = 6;
 
 constexpr int kNumXcd = 8;
 
@@ -77,6 +78,13 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 //           fractional error below 8e-6 there. Its leading coefficient is
 //           negative, so past 6 the correction term |z| 2^Q(|z|) falls below
 //           6e-9 and keeps falling. Seven fma and one exp2, no division.
+//  SOFTPLUS: log(1 + e^z) = max(z, 0) + log1p(t), t = e^-|z| in (0, 1]; log1p(t)
+//           as ln(u) * t / (u - 1) with u = 1 + t rounded (Kahan's correction:
+//           the rounding of u cancels to first order), t itself when u == 1.
+//  GELU_TANH: 0.5 z (1 + tanh(y)), y = sqrt(2/pi) (z + 0.044715 z^3), written as
+//           z / (1 + e^(-2y)) (1 + tanh(y) = 2 / (1 + e^(-2y))): one exp2 and one
+//           reciprocal. For z << 0, e^(-2y) overflows to +inf and the result is
+//           -0 (the true value is below 1e-30 in magnitude there).
 template <int ACT>
 __device__ __forceinline__ float act_fn(float z) {
     if constexpr (ACT == ACT_RELU) {
@@ -94,6 +102,17 @@ __device__ __forceinline__ float act_fn(float z) {
         q = fmaf(az, q, -1.1512510776519775f);
         q = fmaf(az, q, -0.9999952912330627f);
         return fmaf(-az, __builtin_amdgcn_exp2f(q), fmaxf(z, 0.0f));
+    } else if constexpr (ACT == ACT_SOFTPLUS) {
+        const float t = __builtin_amdgcn_exp2f(-fabsf(z) * 1.4426950408889634f);
+        const float u = 1.0f + t;
+        const float d = u - 1.0f;
+        const float lu = __builtin_amdgcn_logf(u) * 0.6931471824645996f;   // ln(u)
+        const float lp = d == 0.0f ? t : lu * (t * __builtin_amdgcn_rcpf(d));
+        return fmaxf(z, 0.0f) + lp;
+    } else if constexpr (ACT == ACT_GELU_TANH) {
+        // -2 y log2(e) = -z (c1 + c3 z^2), c1 = 2 sqrt(2/pi) log2(e), c3 = 0.044715 c1
+        const float a = -z * fmaf(z * z, 0.10294324159622192f, 2.302208185195923f);
+        return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a));
     } else {
         return z;
     }

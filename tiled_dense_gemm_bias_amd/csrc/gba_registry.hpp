@@ -16,8 +16,8 @@ using GemmLaunchFn = hipError_t (*)(const void *, const void *, const void *, vo
 
 struct ScheduleEntry {
     gba_schedule sched;      // raster / group_m hold the defaults
-    GemmLaunchFn fn[2][4];   // [dtype][act], B stored (K,N)
-    GemmLaunchFn tb[2][4];   // [dtype][act], B stored (N,K); null without that path
+    GemmLaunchFn fn[2][kNumActs];   // [dtype][act], B stored (K,N)
+    GemmLaunchFn tb[2][kNumActs];   // [dtype][act], B stored (N,K); null without that path
 };
 
 }  // namespace gba
@@ -32,17 +32,23 @@ struct ScheduleEntry {
     GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 0, 1)                                                 \
     GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 0, 2)                                                 \
     GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 0, 3)                                                 \
+    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 0, 4) \
+    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 0, 5) \
     GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 1, 0)                                                 \
     GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 1, 1)                                                 \
     GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 1, 2)                                                 \
-    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 1, 3)
+    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 1, 3)    \
+    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 1, 4) \
+    GBA_KERNEL_INST_(BM, BN, BK, WM, WN, 1, 5)
 
 #define GBA_LAUNCHERS_(BM, BN, BK, WM, WN, DT)                                              \
     {gba::launch_gemm<BM, BN, BK, WM, WN, DT, 0>, gba::launch_gemm<BM, BN, BK, WM, WN, DT, 1>, \
-     gba::launch_gemm<BM, BN, BK, WM, WN, DT, 2>, gba::launch_gemm<BM, BN, BK, WM, WN, DT, 3>}
+     gba::launch_gemm<BM, BN, BK, WM, WN, DT, 2>, gba::launch_gemm<BM, BN, BK, WM, WN, DT, 3>, \
+     gba::launch_gemm<BM, BN, BK, WM, WN, DT, 4>, gba::launch_gemm<BM, BN, BK, WM, WN, DT, 5>}
 
-// Instantiates the eight kernels (device and host passes) and, in the host
-// pass only, defines gba::NAME with external linkage for the host registry.
+// Instantiates the twelve kernels (2 dtypes x 6 activations; device and host
+// passes) and, in the host pass only, defines gba::NAME with external linkage
+// for the host registry. The other families below follow the same pattern.
 #ifdef __HIP_DEVICE_COMPILE__
 #define GBA_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, GROUP_M) GBA_KERNEL_INSTS_(BM, BN, BK, WM, WN)
 #else
@@ -67,16 +73,21 @@ struct ScheduleEntry {
     GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 1)                                                  \
     GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 2)                                                  \
     GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 3)                                                  \
+    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 4) \
+    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 5) \
     GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 0)                                                  \
     GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 1)                                                  \
     GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 2)                                                  \
-    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 3)
+    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 3)    \
+    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 4) \
+    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 5)
 
 #define GBA_V2_LAUNCHERS_(BM, BN, BK, WM, WN, S, DT)                                           \
     {gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 0>,                                        \
      gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 1>,                                        \
      gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 2>,                                        \
-     gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 3>}
+     gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 3>, \
+     gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 4>, gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 5>}
 
 #ifdef __HIP_DEVICE_COMPILE__
 #define GBA_V2_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, S, GROUP_M) GBA_V2_INSTS_(BM, BN, BK, WM, WN, S)
@@ -102,16 +113,21 @@ struct ScheduleEntry {
     GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 0, 1)                                       \
     GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 0, 2)                                       \
     GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 0, 3)                                       \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 0, 4) \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 0, 5) \
     GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 1, 0)                                       \
     GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 1, 1)                                       \
     GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 1, 2)                                       \
-    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 1, 3)
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 1, 3)    \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 1, 4) \
+    GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 1, 5)
 
 #define GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, MS, DT)                                \
     {gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, MS, DT, 0>,                             \
      gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, MS, DT, 1>,                             \
      gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, MS, DT, 2>,                             \
-     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, MS, DT, 3>}
+     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, MS, DT, 3>, \
+     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, MS, DT, 4>, gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, MS, DT, 5>}
 
 // transpose_B instances (16x16x32 MFMAs only)
 #define GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, DT, ACT)                                  \
@@ -124,16 +140,21 @@ struct ScheduleEntry {
     GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 1)                                          \
     GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 2)                                          \
     GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 3)                                          \
+    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 4) \
+    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 5) \
     GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 0)                                          \
     GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 1)                                          \
     GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 2)                                          \
-    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 3)
+    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 3)    \
+    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 4) \
+    GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, 5)
 
 #define GBA_V3T_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, DT)                                   \
     {gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, 16, DT, 0, true>,                        \
      gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, 16, DT, 1, true>,                        \
      gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, 16, DT, 2, true>,                        \
-     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, 16, DT, 3, true>}
+     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, 16, DT, 3, true>, \
+     gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, 16, DT, 4, true>, gba::launch_gemm_v3<BM, BN, BK, WM, WN, S, L, SP, 16, DT, 5, true>}
 
 // kernel id 2: 32x32x16 MFMAs (B stored (K,N) only); kernel id 3: 16x16x32
 // MFMAs, both B layouts (GBA_V3_SCHEDULE_ENTRY_TB).
@@ -180,16 +201,21 @@ struct ScheduleEntry {
     GBA_V5_INST_(BM, BN, WM, WN, 0, 1, TB)                                                     \
     GBA_V5_INST_(BM, BN, WM, WN, 0, 2, TB)                                                     \
     GBA_V5_INST_(BM, BN, WM, WN, 0, 3, TB)                                                     \
+    GBA_V5_INST_(BM, BN, WM, WN, 0, 4, TB) \
+    GBA_V5_INST_(BM, BN, WM, WN, 0, 5, TB) \
     GBA_V5_INST_(BM, BN, WM, WN, 1, 0, TB)                                                     \
     GBA_V5_INST_(BM, BN, WM, WN, 1, 1, TB)                                                     \
     GBA_V5_INST_(BM, BN, WM, WN, 1, 2, TB)                                                     \
-    GBA_V5_INST_(BM, BN, WM, WN, 1, 3, TB)
+    GBA_V5_INST_(BM, BN, WM, WN, 1, 3, TB)    \
+    GBA_V5_INST_(BM, BN, WM, WN, 1, 4, TB) \
+    GBA_V5_INST_(BM, BN, WM, WN, 1, 5, TB)
 
 #define GBA_V5_INSTS_(BM, BN, WM, WN) GBA_V5_INSTS1_(BM, BN, WM, WN, false) GBA_V5_INSTS1_(BM, BN, WM, WN, true)
 
 #define GBA_V5_LAUNCHERS_(BM, BN, WM, WN, DT, TB)                                              \
     {gba::launch_gemm_v5<BM, BN, WM, WN, DT, 0, TB>, gba::launch_gemm_v5<BM, BN, WM, WN, DT, 1, TB>, \
-     gba::launch_gemm_v5<BM, BN, WM, WN, DT, 2, TB>, gba::launch_gemm_v5<BM, BN, WM, WN, DT, 3, TB>}
+     gba::launch_gemm_v5<BM, BN, WM, WN, DT, 2, TB>, gba::launch_gemm_v5<BM, BN, WM, WN, DT, 3, TB>, \
+     gba::launch_gemm_v5<BM, BN, WM, WN, DT, 4, TB>, gba::launch_gemm_v5<BM, BN, WM, WN, DT, 5, TB>}
 
 #ifdef __HIP_DEVICE_COMPILE__
 #define GBA_V5_SCHEDULE_ENTRY(NAME, BM, BN, WM, WN, GROUP_M) GBA_V5_INSTS_(BM, BN, WM, WN)
