@@ -17,6 +17,10 @@ file's header for the pages and sections each step follows:
     (2D) template; the tanh form of GELU (Hendrycks and Gimpel, 2016).
   - transpose_B (same page, Key API Patterns): the second operand stored (N, K)
     and used as its transpose (``transpose_b=True``).
+  - 8-bit inputs ("tilelang" (skillsmp.com), Documentation Structure: the type
+    system lists float8_e4m3/e5m2, the GEMM examples an FP8 GEMM): OCP E4M3 /
+    E5M2 A and (N, K) W, one fp32 scale on the product, fp16/bf16 bias and
+    result (``gemm_bias_act_fp8``).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against facts
 that do not come from the oracle itself (closed forms, exact rational brute
@@ -39,6 +43,7 @@ ACT_NONE, ACT_RELU, ACT_SIGMOID, ACT_GELU, ACT_SOFTPLUS, ACT_GELU_TANH = 0, 1, 2
 ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "sigmoid": ACT_SIGMOID, "gelu": ACT_GELU,
         "softplus": ACT_SOFTPLUS, "gelu_tanh": ACT_GELU_TANH}
 DTYPES = {"f16": F16, "fp16": F16, "float16": F16, "bf16": BF16, "bfloat16": BF16}
+FP8 = {"e4m3": 0, "e5m2": 1}
 
 
 def build(force: bool = False, src: str = _SRC, out: str = _LIB) -> str:
@@ -84,6 +89,11 @@ class Oracle:
         for name in ("oracle_gemm_bias_act", "oracle_gemm_bias_act_nt"):
             getattr(lib, name).argtypes = [p, p, p, p, p, i64, i64, i64, ci, ci, p, i64, ci]
             getattr(lib, name).restype = ci
+        lib.oracle_gemm_bias_act_fp8_nt.argtypes = [p, p, p, p, p, i64, i64, i64,
+                                                    ctypes.c_double, ci, ci, ci, p, i64, ci]
+        lib.oracle_gemm_bias_act_fp8_nt.restype = ci
+        lib.oracle_decode_fp8.argtypes = [ci, p, p, i64]
+        lib.oracle_decode_fp8.restype = None
         lib.oracle_bias_act.argtypes = [p, p, p, i64, i64, ci, ci]
         lib.oracle_bias_act.restype = ci
         for name in ("oracle_decode", "oracle_encode", "oracle_act"):
@@ -120,6 +130,47 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_gemm_bias_act rejected its arguments")
         return (out, absout) if with_abs else out
+
+    def gemm_bias_act_fp8(self, A, W, bias, scale=1.0, act="none", fmt="e4m3", dtype="bf16",
+                          rows=None, nthreads=0, with_abs=False):
+        """fp64 act(scale * A.W^T + bias) with 8-bit inputs.
+
+        A: uint8 bits [M, K], W: uint8 bits [N, K], both in format fmt ("e4m3" or
+        "e5m2"); bias: uint16 bits [N] of dtype, or None; scale: the fp32
+        dequantization factor of the product. Returns out[len(rows) or M, N]
+        float64 (plus |scale| sum_k |A_ik W_jk| + |bias_j| with with_abs).
+        """
+        A = np.ascontiguousarray(A)
+        W = np.ascontiguousarray(W)
+        if A.dtype != np.uint8 or W.dtype != np.uint8:
+            raise TypeError("8-bit inputs are uint8 bit patterns")
+        M, K = A.shape
+        N, K2 = W.shape
+        if K2 != K:
+            raise ValueError("inner dimensions differ: A is %s, W is %s" % (A.shape, W.shape))
+        if bias is not None:
+            bias = _bits(bias)
+            if bias.shape != (N,):
+                raise ValueError("bias must have N=%d entries, got %s" % (N, bias.shape))
+        r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = M if r is None else r.shape[0]
+        out = np.empty((nrows, N), dtype=np.float64)
+        absout = np.empty((nrows, N), dtype=np.float64) if with_abs else None
+        rc = self._lib.oracle_gemm_bias_act_fp8_nt(
+            _ptr(A), _ptr(W), _ptr(bias), _ptr(out), _ptr(absout), M, N, K, float(scale),
+            _act(act), FP8[fmt] if isinstance(fmt, str) else int(fmt), _dt(dtype), _ptr(r),
+            0 if r is None else nrows, int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_gemm_bias_act_fp8_nt rejected its arguments")
+        return (out, absout) if with_abs else out
+
+    def decode_fp8(self, bits, fmt="e4m3"):
+        bits = np.ascontiguousarray(np.asarray(bits, dtype=np.uint8))
+        flat = bits.reshape(-1)
+        out = np.empty(flat.shape, dtype=np.float64)
+        self._lib.oracle_decode_fp8(FP8[fmt] if isinstance(fmt, str) else int(fmt), _ptr(flat),
+                                    _ptr(out), flat.size)
+        return out.reshape(bits.shape)
 
     def bias_act(self, X, bias, act="none", dtype="f16"):
         """fp64 act(X + bias) elementwise; X uint16 bits [M, N], bias [N] or None."""
@@ -177,6 +228,14 @@ def gemm_bias_act(*args, **kw):
 
 def bias_act(*args, **kw):
     return default().bias_act(*args, **kw)
+
+
+def gemm_bias_act_fp8(*args, **kw):
+    return default().gemm_bias_act_fp8(*args, **kw)
+
+
+def decode_fp8(*args, **kw):
+    return default().decode_fp8(*args, **kw)
 
 
 def decode(*args, **kw):

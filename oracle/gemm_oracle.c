@@ -21,6 +21,12 @@
  *   - The tanh form of GELU, 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))
  *     (Hendrycks and Gimpel, "Gaussian Error Linear Units", 2016), as the
  *     second GELU variant next to the erf form the pages' GELU epilogue reads as.
+ *   - 8-bit float inputs ("tilelang" (skillsmp.com), Documentation Structure:
+ *     the type system lists float8_e4m3/e5m2 and the GEMM examples an FP8
+ *     GEMM): A and the (N,K) operand W in one OCP 8-bit format, E4M3 or E5M2
+ *     ("OCP 8-bit Floating Point Specification (OFP8)", 2023), with one fp32
+ *     dequantization scale for the product: s = scale * sum_k A[i][k] * W[j][k];
+ *     bias and result in fp16/bf16 (oracle_gemm_bias_act_fp8_nt).
  *   - Same page, "Key API Patterns": the tile GEMM takes a transpose_B flag.
  *     With it, the second operand is given as an (N,K) row-major array W and
  *     the product is A times its transpose: s[i][j] = sum_k A[i][k] * W[j][k]
@@ -79,6 +85,46 @@ static double dec_bf16(uint16_t h) {
 }
 
 static double dec(int dtype, uint16_t h) { return dtype == OR_F16 ? dec_f16(h) : dec_bf16(h); }
+
+/* OCP E4M3: 1 sign, 4 exponent (bias 7), 3 fraction bits; no infinities,
+ * S.1111.111 is NaN, largest finite 448. */
+static double dec_e4m3(uint8_t x) {
+    int sign = x >> 7, ex = (x >> 3) & 0xf, fr = x & 0x7;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)fr, -9);                  /* subnormal: fr * 2^-9 */
+    else if (ex == 15 && fr == 7)
+        v = NAN;
+    else
+        v = ldexp((double)(fr | 0x8), ex - 10);     /* (8+fr) * 2^(ex-7-3) */
+    return sign ? -v : v;
+}
+
+/* OCP E5M2: 1 sign, 5 exponent (bias 15), 2 fraction bits; IEEE-style
+ * infinities and NaNs at exponent 31, largest finite 57344. */
+static double dec_e5m2(uint8_t x) {
+    int sign = x >> 7, ex = (x >> 2) & 0x1f, fr = x & 0x3;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)fr, -16);                 /* subnormal: fr * 2^-16 */
+    else if (ex == 31)
+        v = fr ? NAN : INFINITY;
+    else
+        v = ldexp((double)(fr | 0x4), ex - 17);     /* (4+fr) * 2^(ex-15-2) */
+    return sign ? -v : v;
+}
+
+/* Operand kinds: the two 16-bit types (their gba dtype codes) and the two
+ * 8-bit formats. */
+enum { OK_F16 = 0, OK_BF16 = 1, OK_E4M3 = 2, OK_E5M2 = 3 };
+
+static double dec_op(int kind, const void *base, int64_t idx) {
+    switch (kind) {
+    case OK_E4M3: return dec_e4m3(((const uint8_t *)base)[idx]);
+    case OK_E5M2: return dec_e5m2(((const uint8_t *)base)[idx]);
+    default: return dec(kind, ((const uint16_t *)base)[idx]);
+    }
+}
 
 /* ---- round-to-nearest-even encoders from fp64 ----------------------------- */
 /* man_bits: stored fraction bits; emin: smallest normal exponent; emax: largest. */
@@ -140,12 +186,14 @@ static double act_apply(int act, double z) {
 /* ---- the fused GEMM ------------------------------------------------------- */
 
 typedef struct {
-    const uint16_t *A, *bias;
+    const void *A;         /* operand kind a_kind */
+    const uint16_t *bias;  /* dtype */
     const double *Bd;      /* B decoded to fp64, K x N */
     double *out, *absout;
     const int64_t *rows;
     int64_t nrows, N, K;
-    int act, dtype;
+    int act, dtype, a_kind;
+    double scale;          /* multiplies the sum before the bias (1 for 16-bit inputs) */
     int64_t r0, r1;        /* this worker's slice of [0, nrows) */
 } gemm_job;
 
@@ -159,7 +207,7 @@ static void *gemm_worker(void *p) {
         for (int64_t c = 0; c < N; ++c) acc[c] = 0.0;
         if (aacc) for (int64_t c = 0; c < N; ++c) aacc[c] = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            const double a = dec(j->dtype, j->A[i * K + k]);
+            const double a = dec_op(j->a_kind, j->A, i * K + k);
             const double *brow = j->Bd + k * N;
             for (int64_t c = 0; c < N; ++c) acc[c] += a * brow[c];
             if (aacc) {
@@ -169,14 +217,14 @@ static void *gemm_worker(void *p) {
         }
         double *o = j->out + r * N;
         for (int64_t c = 0; c < N; ++c) {
-            double z = acc[c];
+            double z = j->scale * acc[c];
             if (j->bias) z += dec(j->dtype, j->bias[c]);
             o[c] = act_apply(j->act, z);
         }
         if (aacc) {
             double *ao = j->absout + r * N;
             for (int64_t c = 0; c < N; ++c)
-                ao[c] = aacc[c] + (j->bias ? fabs(dec(j->dtype, j->bias[c])) : 0.0);
+                ao[c] = fabs(j->scale) * aacc[c] + (j->bias ? fabs(dec(j->dtype, j->bias[c])) : 0.0);
         }
     }
     free(acc);
@@ -185,10 +233,10 @@ static void *gemm_worker(void *p) {
 }
 
 typedef struct {
-    const uint16_t *B;
+    const void *B;
     double *Bd;
     int64_t lo, hi, N, K;
-    int dtype, b_nk;
+    int b_kind, b_nk;
 } dec_job;
 
 /* Bd[k][j] = the (k, j) entry of the second operand: B[k][j] when B is stored
@@ -197,7 +245,7 @@ static void *dec_worker(void *p) {
     dec_job *d = (dec_job *)p;
     for (int64_t t = d->lo; t < d->hi; ++t) {
         const int64_t k = t / d->N, j = t % d->N;
-        d->Bd[t] = dec(d->dtype, d->b_nk ? d->B[j * d->K + k] : d->B[t]);
+        d->Bd[t] = dec_op(d->b_kind, d->B, d->b_nk ? j * d->K + k : t);
     }
     return NULL;
 }
@@ -216,11 +264,13 @@ static int pick_threads(int nthreads, int64_t work_items) {
  * + |bias[c]|, the magnitude that bounds any fp32 summation's rounding error.
  * Returns 0, or -1 on a bad argument.
  */
-static int gemm_impl(const uint16_t *A, const uint16_t *B, int b_nk, const uint16_t *bias,
-                     double *out, double *absout, int64_t M, int64_t N, int64_t K, int act,
-                     int dtype, const int64_t *rows, int64_t nrows, int nthreads) {
+static int gemm_impl(const void *A, const void *B, int op_kind, int b_nk, double scale,
+                     const uint16_t *bias, double *out, double *absout, int64_t M, int64_t N,
+                     int64_t K, int act, int dtype, const int64_t *rows, int64_t nrows,
+                     int nthreads) {
     if (M < 0 || N < 0 || K < 0 || act < 0 || act > 5 || (dtype != OR_F16 && dtype != OR_BF16))
         return -1;
+    if (op_kind < OK_F16 || op_kind > OK_E5M2 || !isfinite(scale)) return -1;
     if (!rows) nrows = M;
     if (nrows == 0 || N == 0) return 0;
     if (rows)
@@ -234,7 +284,7 @@ static int gemm_impl(const uint16_t *A, const uint16_t *B, int b_nk, const uint1
         pthread_t th[256];
         dec_job dj[256];
         for (int t = 0; t < T; ++t) {
-            dj[t].B = B; dj[t].Bd = Bd; dj[t].dtype = dtype; dj[t].b_nk = b_nk;
+            dj[t].B = B; dj[t].Bd = Bd; dj[t].b_kind = op_kind; dj[t].b_nk = b_nk;
             dj[t].N = N; dj[t].K = K;
             dj[t].lo = (K * N) * t / T; dj[t].hi = (K * N) * (t + 1) / T;
             pthread_create(&th[t], NULL, dec_worker, &dj[t]);
@@ -245,8 +295,8 @@ static int gemm_impl(const uint16_t *A, const uint16_t *B, int b_nk, const uint1
     pthread_t th[256];
     gemm_job jb[256];
     for (int t = 0; t < T; ++t) {
-        gemm_job g = {A, bias, Bd, out, absout, rows, nrows, N, K, act, dtype,
-                      nrows * t / T, nrows * (t + 1) / T};
+        gemm_job g = {A, bias, Bd, out, absout, rows, nrows, N, K, act, dtype, op_kind,
+                      scale, nrows * t / T, nrows * (t + 1) / T};
         jb[t] = g;
         pthread_create(&th[t], NULL, gemm_worker, &jb[t]);
     }
@@ -260,7 +310,8 @@ int oracle_gemm_bias_act(const uint16_t *A, const uint16_t *B, const uint16_t *b
                          double *out, double *absout, int64_t M, int64_t N, int64_t K,
                          int act, int dtype, const int64_t *rows, int64_t nrows,
                          int nthreads) {
-    return gemm_impl(A, B, 0, bias, out, absout, M, N, K, act, dtype, rows, nrows, nthreads);
+    return gemm_impl(A, B, dtype, 0, 1.0, bias, out, absout, M, N, K, act, dtype, rows, nrows,
+                     nthreads);
 }
 
 /* W stored (N,K) (transpose_B): out[r][c] = act(sum_k A[i][k]*W[c][k] + bias[c]). */
@@ -268,7 +319,20 @@ int oracle_gemm_bias_act_nt(const uint16_t *A, const uint16_t *W, const uint16_t
                             double *out, double *absout, int64_t M, int64_t N, int64_t K,
                             int act, int dtype, const int64_t *rows, int64_t nrows,
                             int nthreads) {
-    return gemm_impl(A, W, 1, bias, out, absout, M, N, K, act, dtype, rows, nrows, nthreads);
+    return gemm_impl(A, W, dtype, 1, 1.0, bias, out, absout, M, N, K, act, dtype, rows, nrows,
+                     nthreads);
+}
+
+/* 8-bit inputs, W stored (N,K): out[r][c] = act(scale * sum_k A[i][k]*W[c][k] + bias[c]),
+ * A and W in format fmt (0 = E4M3, 1 = E5M2), bias in dtype (fp16/bf16). absout
+ * receives |scale| sum_k |A[i][k]*W[c][k]| + |bias[c]|. */
+int oracle_gemm_bias_act_fp8_nt(const uint8_t *A, const uint8_t *W, const uint16_t *bias,
+                                double *out, double *absout, int64_t M, int64_t N, int64_t K,
+                                double scale, int act, int fmt, int dtype,
+                                const int64_t *rows, int64_t nrows, int nthreads) {
+    if (fmt != 0 && fmt != 1) return -1;
+    return gemm_impl(A, W, fmt == 0 ? OK_E4M3 : OK_E5M2, 1, scale, bias, out, absout, M, N, K,
+                     act, dtype, rows, nrows, nthreads);
 }
 
 /* out[i][j] = act(X[i][j] + bias[j]) in fp64: the elementwise second half of the
@@ -293,6 +357,10 @@ void oracle_decode(int dtype, const uint16_t *bits, double *out, int64_t n) {
 
 void oracle_encode(int dtype, const double *x, uint16_t *bits, int64_t n) {
     for (int64_t t = 0; t < n; ++t) bits[t] = enc(dtype, x[t]);
+}
+
+void oracle_decode_fp8(int fmt, const uint8_t *bits, double *out, int64_t n) {
+    for (int64_t t = 0; t < n; ++t) out[t] = fmt == 0 ? dec_e4m3(bits[t]) : dec_e5m2(bits[t]);
 }
 
 void oracle_act(int act, const double *z, double *out, int64_t n) {

@@ -34,6 +34,12 @@ MUTANTS = {
                                "return z > 0.0 ? z + log(exp(-z)) : log1p(exp(z));"),
     "gelu_tanh_cubic_coeff": ("0.044715 * z * z * z", "0.04715 * z * z * z"),
     "gelu_tanh_neg_branch": ("return z * e / (1.0 + e);", "return z / (1.0 + e);"),
+    "e4m3_exponent_bias": ("ldexp((double)(fr | 0x8), ex - 10)", "ldexp((double)(fr | 0x8), ex - 11)"),
+    "e4m3_nan_rule": ("else if (ex == 15 && fr == 7)", "else if (ex == 15)"),
+    "e5m2_hidden_bit": ("ldexp((double)(fr | 0x4), ex - 17)", "ldexp((double)(fr | 0x8), ex - 17)"),
+    "fp8_scale_dropped": ("double z = j->scale * acc[c];", "double z = acc[c];"),
+    "fp8_scale_on_bias": ("if (j->bias) z += dec(j->dtype, j->bias[c]);",
+                          "if (j->bias) z += j->scale * dec(j->dtype, j->bias[c]);"),
     "leaky_relu": ("return z > 0.0 ? z : 0.0;", "return z > 0.0 ? z : 0.01 * z;"),
     "f16_exp_off_by_one": ("ldexp((double)(fr | 0x400), ex - 25)", "ldexp((double)(fr | 0x400), ex - 24)"),
     "f16_subnormal_scale": ("ldexp((double)fr, -24)", "ldexp((double)fr, -25)"),
@@ -41,8 +47,7 @@ MUTANTS = {
     "round_truncates": ("double r = rint(a / q);", "double r = floor(a / q);"),
     "round_half_up": ("double r = rint(a / q);", "double r = floor(a / q + 0.5);"),
     "abs_sum_signed": ("aacc[c] += aa * fabs(brow[c]);", "aacc[c] += aa * brow[c];"),
-    "transpose_b_reads_kn": ("d->b_nk ? d->B[j * d->K + k] : d->B[t]",
-                             "d->b_nk ? d->B[k * d->N + j] : d->B[t]"),
+    "transpose_b_reads_kn": ("d->b_nk ? j * d->K + k : t", "d->b_nk ? k * d->N + j : t"),
     "second_operand_row": ("const double *brow = j->Bd + k * N;",
                            "const double *brow = j->Bd + (K - 1 - k) * N;"),
 }

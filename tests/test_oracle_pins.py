@@ -241,6 +241,68 @@ def test_gelu_tanh_against_torch_and_identities(orc):
     assert np.abs(g - orc.act(x, "gelu")).max() < 1e-3
 
 
+# ------------------------------------------------------------ 8-bit inputs --
+
+E4M3_KNOWN = {0x00: 0.0, 0x38: 1.0, 0xB8: -1.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9,
+              0x07: 7 * 2.0 ** -9, 0x40: 2.0, 0x3C: 1.5, 0x77: 240.0}
+E5M2_KNOWN = {0x00: 0.0, 0x3C: 1.0, 0xBC: -1.0, 0x7B: 57344.0, 0x04: 2.0 ** -14, 0x01: 2.0 ** -16,
+              0x7C: math.inf, 0xFC: -math.inf, 0x3E: 1.5, 0x40: 2.0}
+
+
+def test_fp8_decoders_known_values_and_every_pattern_against_torch(orc):
+    torch = pytest.importorskip("torch")
+    for fmt, known, tdt in (("e4m3", E4M3_KNOWN, torch.float8_e4m3fn),
+                            ("e5m2", E5M2_KNOWN, torch.float8_e5m2)):
+        bits = np.array(list(known), dtype=np.uint8)
+        assert list(orc.decode_fp8(bits, fmt)) == list(known.values()), fmt
+        allb = np.arange(256, dtype=np.uint16).astype(np.uint8)
+        ref = torch.from_numpy(allb).view(tdt).to(torch.float64).numpy()
+        got = orc.decode_fp8(allb, fmt)
+        np.testing.assert_array_equal(got, ref)
+    assert np.isnan(orc.decode_fp8(np.array([0x7F, 0xFF], np.uint8), "e4m3")).all()
+
+
+def _fp8_bits(rng, shape, fmt):
+    """Random finite 8-bit patterns of moderate magnitude."""
+    b = rng.integers(0, 256, size=shape).astype(np.uint8)
+    top = 0x70 if fmt == "e4m3" else 0x78      # cap the exponent: no NaN / inf
+    return (b & np.uint8(0x80)) | np.minimum(b & np.uint8(0x7F), np.uint8(top - 1))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 5, 7), (4, 3, 33)])
+def test_fp8_gemm_equals_exact_rational_sum(orc, fmt, shape):
+    M, N, K = shape
+    rng = np.random.default_rng(M * 100 + N * 10 + K)
+    A, W = _fp8_bits(rng, (M, K), fmt), _fp8_bits(rng, (N, K), fmt)
+    bias = synth.random_bits((N,), "bf16", 7)
+    scale = 0.375
+    Av, Wv, bv = orc.decode_fp8(A, fmt), orc.decode_fp8(W, fmt), orc.decode(bias, "bf16")
+    got, S = orc.gemm_bias_act_fp8(A, W, bias, scale, "none", fmt, "bf16", with_abs=True)
+    for i in range(M):
+        for j in range(N):
+            s = sum((Fraction(Av[i, k]) * Fraction(Wv[j, k]) for k in range(K)), Fraction(0))
+            exact = Fraction(scale) * s + Fraction(bv[j])
+            bound = (K + 2) * 2.0 ** -53 * S[i, j]
+            assert abs(Fraction(got[i, j]) - exact) <= Fraction(bound), (i, j)
+
+
+def test_fp8_integer_matmul_scale_and_bias_order(orc):
+    rng = np.random.default_rng(9)
+    M, N, K = 21, 19, 150
+    Ai, Wi = rng.integers(-4, 5, (M, K)), rng.integers(-4, 5, (N, K))
+    torch = pytest.importorskip("torch")
+    enc = lambda v: torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    A, W = enc(Ai), enc(Wi)
+    bi = rng.integers(-8, 9, N)
+    bias = f16(bi)
+    for scale in (1.0, 0.125, -3.0):
+        got = orc.gemm_bias_act_fp8(A, W, bias, scale, "none", "e4m3", "f16")
+        np.testing.assert_array_equal(got, scale * (Ai @ Wi.T) + bi)
+    relu = orc.gemm_bias_act_fp8(A, W, None, 0.5, "relu", "e4m3", "f16")
+    np.testing.assert_array_equal(relu, np.maximum(0.5 * (Ai @ Wi.T), 0))
+
+
 # ------------------------------------------------------------ GEMM core ----
 
 def _hand_gemm():
