@@ -6,9 +6,10 @@
 One step is one gemm_bias_act call over the whole workload (schedule choice,
 global->LDS loads, MFMA main loop, fused epilogue, store), with inputs already
 resident in HBM. W untimed steps, then K timed steps between two device
-synchronisations. Per-launch HIP events on the launch stream give the kernel's
-average duration (the roofline's "achieved") and the median latency by device
-events, as the pages' bench helper reports it.
+synchronisations. Two HIP events on the launch stream bracket the K timed
+launches and give the kernel's average launch duration (the roofline's
+"achieved"); a separate pass with an event per launch gives the median latency,
+as the pages' bench helper reports it.
 
 The default W is 300, not the pages' 10: an MI355X coming out of idle raises
 its clocks over the first ~300 launches of this kernel (~40 ms). Measured per
@@ -32,7 +33,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_MFMA_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}   # dense, 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_MFMA_TFLOPS = {"f16": 2516.6, "bf16": 2516.6,    # dense, 256 CU x 2.4 GHz x 4096 flop/clk
+                    "e4m3": 5033.2, "e5m2": 5033.2}    # dense fp8: twice the 16-bit rate
 PEAK_HBM_GBS = 8000.0
 METRIC = "TFLOP/s fused fp16 GEMM+bias+GELU at 4096³; % of MI355X fp16 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -48,11 +50,15 @@ KERNEL_HEADERS = {0: ["gba_kernels.hpp"],
                   1: ["gba_kernels.hpp", "gemm_v2.hpp"],
                   2: ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp"],
                   3: ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp"],
-                  4: ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp", "gemm_v5.hpp"]}
+                  4: ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp", "gemm_v5.hpp"],
+                  "f8": ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp", "gemm_v5.hpp",
+                         "gemm_f8.hpp"]}
 
 
 def instance_file(s: dict) -> str:
     """The csrc file that instantiates schedule s."""
+    if s["kernel"] == "f8":
+        return "f8_256x256x128_w2x2_persistent_%s.hip" % s["fmt"]
     if s["kernel"] == 4:
         return "v5_%dx%dx%d_w%dx%d_persistent.hip" % (s["bm"], s["bn"], s["bk"], s["wm"], s["wn"])
     if s["kernel"] in (2, 3):
@@ -88,51 +94,73 @@ def measured_traffic(workload: str, sched: dict):
 
 
 def time_launches(fn, steps, warmup, stream):
-    """W untimed calls, then K timed ones. One event is recorded on the launch
-    stream before each timed call and one after the last, so the K per-launch
-    durations are back-to-back intervals: each holds one kernel plus the
-    dispatch gap before the next."""
+    """W untimed calls, then K timed ones between two device synchronisations.
+
+    Returns (wall_ms, avg_ms, per):
+      wall_ms  host clock over the K timed calls (sync before and after);
+      avg_ms   average launch duration: two HIP events on the launch stream
+               bracket the K launches, divided by K (each launch's kernel plus
+               the dispatch gap before the next);
+      per      per-launch durations from a second, separate pass of K calls
+               with an event before each (for the median). An event record
+               between launches costs ~3 us on this device, so those intervals
+               run a little longer; they are not part of the timed region.
+    """
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    avg_ms = e0.elapsed_time(e1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     for i in range(steps):
         ev[i].record(stream)
         fn()
     ev[steps].record(stream)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    return wall_ms, per
+    return wall_ms, avg_ms, per
 
 
-def cpu_baseline(w, A, B, bias, got_bits, target_s=12.0, transpose_b=False):
-    """The fp64 oracle on a bounded sample of rows, timed on the host cores."""
+def cpu_baseline(w, A, B, bias, got_bits, target_s=12.0, transpose_b=False, scale=None):
+    """The fp64 oracle on a bounded sample of rows, timed on the host cores
+    (8-bit inputs when scale is given)."""
     import oracle
     from oracle import compare
     import synth
 
+    def run(rows, with_abs=False):
+        if scale is not None:
+            return oracle.gemm_bias_act_fp8(A, B, bias, scale, w.act, w.fmt, w.dtype, rows=rows,
+                                            nthreads=cores, with_abs=with_abs)
+        return oracle.gemm_bias_act(A, B, bias, w.act, w.dtype, rows=rows, nthreads=cores,
+                                    with_abs=with_abs, transpose_b=transpose_b)
+
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     rows = synth.sample_rows(w.M, 16, seed=w.seed)
     t0 = time.perf_counter()
-    oracle.gemm_bias_act(A, B, bias, w.act, w.dtype, rows=rows, nthreads=cores,
-                         transpose_b=transpose_b)
+    run(rows)
     t_probe = time.perf_counter() - t0
     n = int(min(w.M, max(16, 16 * target_s / max(t_probe, 1e-3))))
     n = max(16, (n // cores) * cores if n > cores else n)
     rows = synth.sample_rows(w.M, n, seed=w.seed)
     t0 = time.perf_counter()
-    R, S = oracle.gemm_bias_act(A, B, bias, w.act, w.dtype, rows=rows, nthreads=cores,
-                                with_abs=True, transpose_b=transpose_b)
+    R, S = run(rows, with_abs=True)
     dt = time.perf_counter() - t0
     flops = 2.0 * len(rows) * w.N * w.K
     rep = compare.check(oracle.decode(got_bits[rows], w.dtype), R, K=w.K, dtype=w.dtype,
                         act=oracle.ACTS[w.act], S=S)
     base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": "%d of %d output rows of %dx%dx%d %s %s (fp64 triple loop, %.1f s)"
-                      % (len(rows), w.M, w.M, w.N, w.K, w.dtype, w.act, dt)}
+                      % (len(rows), w.M, w.M, w.N, w.K,
+                         w.dtype if scale is None else w.fmt + "->" + w.dtype, w.act, dt)}
     parity = {k: rep[k] for k in ("ok", "strict_ok", "rel_frobenius", "max_abs", "max_ulp")}
     parity["rows"] = len(rows)
     return base, parity
@@ -167,12 +195,17 @@ def main(argv=None) -> int:
         from tiled_dense_gemm_bias_amd import build as gba_build
         gba_build.build()
 
-    w = synth.WORKLOADS[a.workload]
+    fp8 = a.workload in synth.FP8_WORKLOADS
+    w = synth.FP8_WORKLOADS[a.workload] if fp8 else synth.WORKLOADS[a.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log("[bench] generating %s inputs %dx%dx%d %s" % (w.name, w.M, w.N, w.K, w.dtype))
-    A, B, bias = synth.make_inputs(w)
-    tb = a.transpose_b
+    scale = None
+    if fp8:
+        A, B, bias, scale = synth.make_inputs_fp8(w)   # B is W [N,K]
+    else:
+        A, B, bias = synth.make_inputs(w)
+    tb = a.transpose_b and not fp8
     if tb:
         B = np.ascontiguousarray(B.T)   # the same operand, stored as the [N,K] weight W
     wl_key = w.name + ("_nt" if tb else "")
@@ -181,7 +214,11 @@ def main(argv=None) -> int:
     def dev_t(bits):
         return None if bits is None else torch.from_numpy(bits.view(np.int16)).view(tdt).to(dev)
 
-    a_t, b_t, bias_t = dev_t(A), dev_t(B), dev_t(bias)
+    if fp8:
+        a_t, b_t = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+        bias_t = dev_t(bias)
+    else:
+        a_t, b_t, bias_t = dev_t(A), dev_t(B), dev_t(bias)
     c_t = torch.empty((w.M, w.N), dtype=tdt, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -194,7 +231,7 @@ def main(argv=None) -> int:
                                                                    c_t.numel() * 2))
         return 0
 
-    if a.schedule:
+    if a.schedule and not fp8:
         f = [int(x) for x in a.schedule.split(",")]
         keys = ["bm", "bn", "bk", "wm", "wn", "stages", "kernel", "loaders", "spread", "raster",
                 "group_m"]
@@ -202,22 +239,26 @@ def main(argv=None) -> int:
         sched.setdefault("raster", 1)
         sched.setdefault("group_m", 4)
         gba.set_schedule(sched)
-    elif a.tune:
+    elif a.tune and not fp8:
         best, ms = gba.autotune(a_t, b_t, bias_t, c_t, w.act, all_groups=True, transpose_b=tb)
         log("[bench] autotune best %s %.4f ms" % (best, ms))
-    sched = gba.get_schedule(w.M, w.N, w.K, w.act, w.dtype, transpose_b=tb)
+    if fp8:
+        sched = {"kernel": "f8", "fmt": w.fmt, "bm": 256, "bn": 256, "bk": 128, "wm": 2, "wn": 2,
+                 "stages": 2, "raster": 1, "group_m": 4}
+        step = gba.bind_gemm_bias_act_fp8(a_t, b_t, bias_t, c_t, scale, w.act, w.fmt)
+    else:
+        sched = gba.get_schedule(w.M, w.N, w.K, w.act, w.dtype, transpose_b=tb)
+        step = gba.bind_gemm_bias_act(a_t, b_t, bias_t, c_t, w.act, transpose_b=tb)
     log("[bench] schedule %s%s" % (sched, " (B stored [N,K])" if tb else ""))
-
-    step = gba.bind_gemm_bias_act(a_t, b_t, bias_t, c_t, w.act, transpose_b=tb)
-    wall_ms, per = time_launches(step, a.steps, a.warmup, stream)
+    wall_ms, kern_avg, per = time_launches(step, a.steps, a.warmup, stream)
     ms_per_step = wall_ms / a.steps
-    kern_avg = sum(per) / len(per)
     kern_med = statistics.median(per)
     flops = float(w.flops)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_avg * 1e-3) / 1e12
-    peak = PEAK_MFMA_TFLOPS[w.dtype]
-    alg_bytes = (w.M * w.K + w.K * w.N + w.M * w.N + (w.N if w.bias else 0)) * 2
+    peak = PEAK_MFMA_TFLOPS[w.fmt if fp8 else w.dtype]
+    in_bytes = 1 if fp8 else 2
+    alg_bytes = (w.M * w.K + w.K * w.N) * in_bytes + (w.M * w.N + (w.N if w.bias else 0)) * 2
     log("[bench] %d steps: %.4f ms/step wall, kernel avg %.4f ms, median %.4f ms -> %.1f TFLOP/s"
         " (%.1f%% of peak)" % (a.steps, ms_per_step, kern_avg, kern_med, achieved,
                                100 * achieved / peak))
@@ -234,13 +275,16 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": ("fp8_" + w.fmt + "->" + w.dtype) if fp8 else w.dtype,
         "data": "synthetic",
-        "config": {"workload": "%s: C = %s(A.%s + bias), M=%d N=%d K=%d, %s in/out, fp32 accumulate"
-                               % (wl_key, w.act, "W^T, W stored [N,K]" if tb else "B", w.M, w.N,
-                                  w.K, w.dtype),
+        "config": {"workload": ("%s: C = %s(scale * A.W^T + bias), W stored [N,K], M=%d N=%d K=%d, "
+                                "%s in, %s out, fp32 accumulate"
+                                % (wl_key, w.act, w.M, w.N, w.K, w.fmt, w.dtype)) if fp8 else
+                               ("%s: C = %s(A.%s + bias), M=%d N=%d K=%d, %s in/out, fp32 accumulate"
+                                % (wl_key, w.act, "W^T, W stored [N,K]" if tb else "B", w.M, w.N,
+                                   w.K, w.dtype)),
                    "M": w.M, "N": w.N, "K": w.K, "act": w.act, "bias": w.bias,
-                   "b_layout": "NK (transpose_B)" if tb else "KN",
+                   "b_layout": "NK (transpose_B)" if (tb or fp8) else "KN",
                    "schedule": sched, "flop_model": "2*M*N*K (epilogue not counted)"},
         "median_ms": round(kern_med, 5),
         "pct_of_peak": round(100 * achieved / peak, 2),
@@ -250,29 +294,28 @@ def main(argv=None) -> int:
                      "algorithmic_bytes": alg_bytes, "kernel_avg_ms": round(kern_avg, 5)},
     }
 
-    if a.unfused:
+    if a.unfused and not fp8:
         t_t = torch.empty_like(c_t)
         y_t = torch.empty_like(c_t)
-        _, per_g = time_launches(lambda: gba.gemm(a_t, b_t, t_t, transpose_b=tb), a.steps,
-                                 a.warmup, stream)
-        _, per_b = time_launches(lambda: gba.bias_act(t_t, bias_t, y_t, w.act), a.steps,
-                                 a.warmup, stream)
-        g_ms, b_ms = statistics.median(per_g), statistics.median(per_b)
+        _, g_ms, _ = time_launches(lambda: gba.gemm(a_t, b_t, t_t, transpose_b=tb), a.steps,
+                                   a.warmup, stream)
+        _, b_ms, _ = time_launches(lambda: gba.bias_act(t_t, bias_t, y_t, w.act), a.steps,
+                                   a.warmup, stream)
         ba_bytes = 2 * w.M * w.N * 2 + (w.N * 2 if w.bias else 0)
         out["unfused"] = {
             "gemm_ms": round(g_ms, 5), "bias_act_ms": round(b_ms, 5),
-            "total_ms": round(g_ms + b_ms, 5), "fused_ms": round(kern_med, 5),
-            "speedup_fused": round((g_ms + b_ms) / kern_med, 3),
+            "total_ms": round(g_ms + b_ms, 5), "fused_ms": round(kern_avg, 5),
+            "speedup_fused": round((g_ms + b_ms) / kern_avg, 3),
             "bias_act_GBps": round(ba_bytes / (b_ms * 1e-3) / 1e9, 1),
             "bias_act_frac_hbm_peak": round(ba_bytes / (b_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "hbm_bytes_saved": 2 * w.M * w.N * 2,
         }
         log("[bench] unfused: gemm %.4f ms + bias_act %.4f ms (%.0f GB/s) vs fused %.4f ms"
-            % (g_ms, b_ms, out["unfused"]["bias_act_GBps"], kern_med))
+            % (g_ms, b_ms, out["unfused"]["bias_act_GBps"], kern_avg))
 
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a row sample")
-        base, parity = cpu_baseline(w, A, B, bias, got_bits, transpose_b=tb)
+        base, parity = cpu_baseline(w, A, B, bias, got_bits, transpose_b=tb, scale=scale)
         out["cpu_baseline"] = base
         out["parity_sampled"] = parity
         log("[bench] cpu baseline %.4f TFLOP/s on %d threads; parity %s"

@@ -135,6 +135,27 @@ int gemm_bias_act_nt(const void *A, const void *W, const void *bias, void *C, in
 /* C = A.W^T rounded to `dtype`, W: [N,K] (gemm with transpose_B). */
 int gemm_nt(const void *A, const void *W, void *C, int64_t M, int64_t N, int64_t K, int dtype);
 
+/* 8-bit float input formats (OCP OFP8): E4M3 (largest finite 448, no
+ * infinities) and E5M2 (largest finite 57344). */
+typedef enum { GBA_FP8_E4M3 = 0, GBA_FP8_E5M2 = 1 } gba_fp8_format;
+
+/* C = act(scale * A.W^T + bias) with 8-bit float inputs: the FP8 GEMM named
+ * in "tilelang" (skillsmp.com), Documentation Structure (float8_e4m3/e5m2 in
+ * the type system, an FP8 GEMM among the GEMM examples), with the fused
+ * epilogue of gemm_bias_act.
+ * A: [M,K] and W: [N,K] (the transpose_B layout), both 8-bit in format `fmt`
+ * (gba_fp8_format), row-major, K-contiguous; scale: the fp32 dequantization
+ * factor of the product (e.g. the product of the per-tensor scales of A and
+ * W), applied before the bias; bias: [N] or NULL and C: [M,N], both `dtype`
+ * (fp16/bf16). Accumulation is fp32 on the 16x16x128 8-bit matrix cores.
+ * K must be a multiple of 16 (16-byte rows) and N of 8; pointers 16-byte
+ * aligned (GBA_ERR_ALIGN). fmt not a gba_fp8_format: GBA_ERR_DTYPE. A
+ * non-finite scale: GBA_ERR_SHAPE. C may not overlap A, W or bias. One
+ * compiled-in schedule (persistent 256x256 tiles); forced schedules do not
+ * apply. Other rules as gemm_bias_act. */
+int gemm_bias_act_fp8_nt(const void *A, const void *W, const void *bias, void *C, int64_t M,
+                         int64_t N, int64_t K, float scale, int act, int fmt, int dtype);
+
 /* Stream for this thread's later calls (a hipStream_t); NULL = default stream. */
 int gba_set_stream(void *hip_stream);
 

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
 
-This module only draws random numbers and rounds them to fp16/bf16 bit
-patterns. It holds none of the GEMM or epilogue arithmetic, and it is the only
+This module only draws random numbers and rounds them to fp16/bf16 (or OCP
+8-bit float) bit patterns. It holds none of the GEMM or epilogue arithmetic, and it is the only
 code that both the HIP path's callers and the oracle's callers use.
 
 Recipe (one numpy PCG64 generator per workload, seeded from the workload):
@@ -9,7 +9,10 @@ Recipe (one numpy PCG64 generator per workload, seeded from the workload):
      N(0, v) means variance v (so std sqrt(v)); U(-1, 1) is uniform on [-1, 1);
   2. scale in float32;
   3. round to the storage type with round-to-nearest-even (numpy's float16
-     cast for fp16; the top-16-bit RNE rule for bf16).
+     cast for fp16; the top-16-bit RNE rule for bf16). 8-bit inputs are first
+     divided by a per-tensor scale amax / (largest finite value), then rounded
+     by torch's float8 conversion (nearest-even, saturated); the product of the
+     two scales is the GEMM's dequantization factor.
 """
 from __future__ import annotations
 
@@ -92,6 +95,71 @@ WORKLOADS = {
     "c5_gelu": Workload("c5_gelu", 16384, 14336, 4096, "bf16", "gelu", True, 5,
                         b_std=1 / math.sqrt(4096), bias_std=math.sqrt(0.02)),
 }
+
+
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+
+
+def f32_to_fp8_bits(x: np.ndarray, fmt: str) -> np.ndarray:
+    """float32 -> OCP 8-bit float bit patterns (torch's conversion: nearest, ties
+    to even), saturated to the format's largest finite value first."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = t.clamp(-FP8_MAX[fmt], FP8_MAX[fmt])
+    tdt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+    return t.to(tdt).view(torch.uint8).numpy()
+
+
+@dataclasses.dataclass(frozen=True)
+class Fp8Workload:
+    """A GEMM with 8-bit inputs: A [M,K] and W [N,K] in format fmt, each scaled
+    per tensor onto the format's range (s = amax / largest finite value), bias
+    and output in dtype; the product's dequantization factor is sA * sW."""
+    name: str
+    M: int
+    N: int
+    K: int
+    fmt: str                # "e4m3" | "e5m2"
+    dtype: str              # bias / output: "f16" | "bf16"
+    act: str
+    bias: bool
+    seed: int
+    a_std: float = 1.0
+    b_std: float = 1.0
+    bias_std: float = 1.0
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+# The 4096^3 and LLM-MLP workloads with E4M3 inputs (same draws as the 16-bit ones).
+FP8_WORKLOADS = {
+    "c3_fp8": Fp8Workload("c3_fp8", 4096, 4096, 4096, "e4m3", "f16", "gelu", True, 3,
+                          a_std=1 / math.sqrt(2), b_std=1 / math.sqrt(2)),
+    "c5_fp8": Fp8Workload("c5_fp8", 16384, 14336, 4096, "e4m3", "bf16", "gelu", True, 5,
+                          b_std=1 / math.sqrt(4096), bias_std=math.sqrt(0.02)),
+}
+
+
+def make_inputs_fp8(w: Fp8Workload, M: Optional[int] = None, N: Optional[int] = None,
+                    K: Optional[int] = None):
+    """Return (A, W, bias, scale): A uint8 [M,K], W uint8 [N,K] (format w.fmt), bias
+    uint16 [N] or None, scale the float32 product of the two per-tensor scales.
+    Draw order A, W, bias from one generator seeded by the workload."""
+    M = w.M if M is None else M
+    N = w.N if N is None else N
+    K = w.K if K is None else K
+    rng = np.random.default_rng(w.seed)
+    a = _draw(rng, (M, K), "normal", w.a_std)
+    b = _draw(rng, (N, K), "normal", w.b_std)
+    bias = to_bits(_draw(rng, (N,), "normal", w.bias_std), w.dtype) if w.bias else None
+    fmax = np.float32(FP8_MAX[w.fmt])
+    sa = np.float32(max(float(np.abs(a).max()), 1e-30)) / fmax
+    sb = np.float32(max(float(np.abs(b).max()), 1e-30)) / fmax
+    A = f32_to_fp8_bits(a / sa, w.fmt)
+    W = f32_to_fp8_bits(b / sb, w.fmt)
+    return A, W, bias, float(np.float32(sa * sb))
 
 
 def make_inputs(w: Workload, M: Optional[int] = None, N: Optional[int] = None,

@@ -98,6 +98,29 @@ def test_argument_errors_are_synchronous_and_precede_device_use(lib):
     assert call(lib, N=0, A=None, B=None) == OK
 
 
+def call8(lib, A=P16, W=P16, bias=None, C=P16 * 64, M=64, N=64, K=64, scale=1.0, act=0, fmt=0,
+          dt=0):
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gemm_bias_act_fp8_nt(v(A), v(W), v(bias), v(C), M, N, K, scale, act, fmt, dt)
+
+
+def test_fp8_argument_errors_precede_device_use(lib):
+    assert call8(lib, fmt=2) == ERR_DTYPE
+    assert call8(lib, dt=2) == ERR_DTYPE
+    assert call8(lib, act=6) == ERR_ACT
+    assert call8(lib, M=-1) == ERR_SHAPE
+    assert call8(lib, scale=float("inf")) == ERR_SHAPE
+    assert call8(lib, scale=float("nan")) == ERR_SHAPE
+    assert call8(lib, C=None) == ERR_NULL
+    assert call8(lib, W=None) == ERR_NULL
+    assert call8(lib, K=24) == ERR_ALIGN     # 8-bit rows must be whole 16-byte chunks
+    assert call8(lib, N=60) == ERR_ALIGN
+    assert call8(lib, A=P16 + 8) == ERR_ALIGN
+    assert call8(lib, C=P16 + 32) == ERR_ALIAS
+    assert call8(lib, M=0) == OK
+    assert call8(lib, N=0, A=None, W=None) == OK
+
+
 def test_bias_act_argument_errors(lib):
     v = ctypes.c_void_p
     assert lib.bias_act(v(P16), None, v(P16), 4, 8, 6, 0) == ERR_ACT

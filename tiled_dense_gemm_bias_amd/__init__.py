@@ -67,6 +67,7 @@ def _lib():
             "gemm": [p, p, p, i64, i64, i64, ci],
             "gemm_bias_act_nt": [p, p, p, p, i64, i64, i64, ci, ci],
             "gemm_nt": [p, p, p, i64, i64, i64, ci],
+            "gemm_bias_act_fp8_nt": [p, p, p, p, i64, i64, i64, ctypes.c_float, ci, ci, ci],
             "bias_act": [p, p, p, i64, i64, ci, ci],
             "gba_set_stream": [p],
             "gba_set_schedule": [ctypes.POINTER(Schedule)],
@@ -211,6 +212,73 @@ def bind_gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False):
 
     if torch.cuda.current_device() != dev.index:
         raise ValueError("bind on the tensors' device (torch.cuda.set_device first)")
+    return launch
+
+
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
+
+
+def _fp8_code(t, fmt) -> int:
+    torch = _torch()
+    if fmt is None:
+        if t.dtype == torch.float8_e4m3fn:
+            return 0
+        if t.dtype == torch.float8_e5m2:
+            return 1
+        raise TypeError("8-bit operands are float8_e4m3fn / float8_e5m2 tensors, or uint8 "
+                        "bit patterns with fmt given; got %s" % t.dtype)
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2):
+        raise TypeError("8-bit operand expected, got %s" % t.dtype)
+    return FP8_FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def gemm_bias_act_fp8(a, w, bias, c, scale=1.0, act="gelu", fmt=None):
+    """c[M,N] = act(scale * a[M,K] @ w[N,K].T + bias[N]) with 8-bit a and w.
+
+    a, w: float8_e4m3fn / float8_e5m2 tensors (or uint8 bit patterns with fmt
+    "e4m3" / "e5m2"), w stored [N,K]; bias (or None) and c: float16 or bfloat16.
+    scale: the fp32 dequantization factor of the product. Returns c."""
+    dev = _check_dev(a, w, bias, c)
+    fa, fw = _fp8_code(a, fmt), _fp8_code(w, fmt)
+    if fa != fw:
+        raise TypeError("a and w must share one 8-bit format")
+    dt = _dtype_code(c)
+    if bias is not None and _dtype_code(bias) != dt:
+        raise TypeError("bias and c must share one dtype")
+    M, K = a.shape
+    N, K2 = w.shape
+    if K2 != K or tuple(c.shape) != (M, N) or (bias is not None and tuple(bias.shape) != (N,)):
+        raise ValueError("shape mismatch: a%s w%s c%s" % (tuple(a.shape), tuple(w.shape),
+                                                          tuple(c.shape)))
+    _call("gemm_bias_act_fp8_nt", dev, _ptr(a), _ptr(w), _ptr(bias), _ptr(c), M, N, K,
+          float(scale), _act(act), fa, dt)
+    return c
+
+
+def bind_gemm_bias_act_fp8(a, w, bias, c, scale=1.0, act="gelu", fmt=None):
+    """bind_gemm_bias_act for the 8-bit-input call (same checks as gemm_bias_act_fp8)."""
+    dev = _check_dev(a, w, bias, c)
+    fa = _fp8_code(a, fmt)
+    if _fp8_code(w, fmt) != fa:
+        raise TypeError("a and w must share one 8-bit format")
+    dt = _dtype_code(c)
+    M, K = a.shape
+    N, K2 = w.shape
+    if K2 != K or tuple(c.shape) != (M, N) or (bias is not None and tuple(bias.shape) != (N,)):
+        raise ValueError("shape mismatch")
+    torch = _torch()
+    if torch.cuda.current_device() != dev.index:
+        raise ValueError("bind on the tensors' device (torch.cuda.set_device first)")
+    lib = _lib()
+    lib.gba_set_stream(ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    args = (_ptr(a), _ptr(w), _ptr(bias), _ptr(c), M, N, K, float(scale), _act(act), fa, dt)
+    fn = lib.gemm_bias_act_fp8_nt
+
+    def launch():
+        st = fn(*args)
+        if st != 0:
+            raise GbaError(st, "gemm_bias_act_fp8_nt")
+
     return launch
 
 

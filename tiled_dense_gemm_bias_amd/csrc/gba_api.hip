@@ -32,6 +32,8 @@ extern const ScheduleEntry i_256x128x64_w2x2_s3_l4_p1_m16;
 extern const ScheduleEntry i_128x256x64_w2x2_s3_l4_p1_m16;
 extern const ScheduleEntry i_128x128x64_w2x2_s3_l4_p1_m16;
 extern const ScheduleEntry p_256x256x64_w2x2;
+extern const F8LaunchFn f8_e4m3[2][kNumActs];
+extern const F8LaunchFn f8_e5m2[2][kNumActs];
 }  // namespace gba
 
 namespace {
@@ -431,7 +433,7 @@ const char *gba_status_string(int s) {
     case GBA_ERR_SHAPE: return "bad shape";
     case GBA_ERR_DTYPE: return "bad dtype";
     case GBA_ERR_ACT: return "bad activation";
-    case GBA_ERR_ALIGN: return "misaligned pointer, or K or N not a multiple of 8";
+    case GBA_ERR_ALIGN: return "misaligned pointer, or K or N not a multiple of 8 (K of 16 for 8-bit inputs)";
     case GBA_ERR_ALIAS: return "output overlaps an input";
     case GBA_ERR_DEVICE: return "no gfx950 device";
     case GBA_ERR_HIP: return "HIP runtime error";
@@ -524,6 +526,36 @@ int bias_act(const void *X, const void *bias, void *Y, int64_t M, int64_t N, int
     s = current_device(&d);
     if (s) return s;
     hipError_t e = kBiasAct[dtype][act](X, bias, Y, (int)M, (int)N, t_stream);
+    return e == hipSuccess ? GBA_OK : hip_fail(e);
+}
+
+int gemm_bias_act_fp8_nt(const void *A, const void *W, const void *bias, void *C, int64_t M,
+                         int64_t N, int64_t K, float scale, int act, int fmt, int dtype) {
+    int s = check_enums(act, dtype);
+    if (s) return s;
+    if (fmt != GBA_FP8_E4M3 && fmt != GBA_FP8_E5M2) return GBA_ERR_DTYPE;
+    if (M < 0 || N < 0 || K < 0) return GBA_ERR_SHAPE;
+    if (M > 0x7fffffffLL || N > (1LL << 23) || K > (1LL << 21)) return GBA_ERR_SHAPE;
+    if (!(scale == scale) || scale - scale != 0.0f) return GBA_ERR_SHAPE;   // NaN or inf
+    if (M == 0 || N == 0) return GBA_OK;
+    if (!C) return GBA_ERR_NULL;
+    if (K > 0 && (!A || !W)) return GBA_ERR_NULL;
+    if ((K % 16) || (N % 8)) return GBA_ERR_ALIGN;
+    if (!aligned16(C) || (A && !aligned16(A)) || (W && !aligned16(W)) || (bias && !aligned16(bias)))
+        return GBA_ERR_ALIGN;
+    const size_t cb = (size_t)M * N * 2;
+    if (overlaps(C, cb, A, (size_t)M * K) || overlaps(C, cb, W, (size_t)N * K) ||
+        overlaps(C, cb, bias, (size_t)N * 2))
+        return GBA_ERR_ALIAS;
+    const DeviceInfo *d;
+    s = current_device(&d);
+    if (s) return s;
+    const gba::F8LaunchFn f = (fmt == GBA_FP8_E4M3 ? gba::f8_e4m3 : gba::f8_e5m2)[dtype][act];
+    if (log_enabled())
+        fprintf(stderr, "[gba] fp8 M=%lld N=%lld K=%lld act=%s fmt=%s out=%s scale=%g\n",
+                (long long)M, (long long)N, (long long)K, kActName[act],
+                fmt == GBA_FP8_E4M3 ? "e4m3" : "e5m2", kDtName[dtype], (double)scale);
+    hipError_t e = f(A, W, bias, C, (int)M, (int)N, (int)K, scale, 1, 4, t_stream);
     return e == hipSuccess ? GBA_OK : hip_fail(e);
 }
 

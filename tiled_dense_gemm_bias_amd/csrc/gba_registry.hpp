@@ -8,6 +8,7 @@
 #include "gemm_v2.hpp"
 #include "gemm_v3.hpp"
 #include "gemm_v5.hpp"
+#include "gemm_f8.hpp"
 
 namespace gba {
 
@@ -229,5 +230,39 @@ struct ScheduleEntry {
                                  GBA_V5_LAUNCHERS_(BM, BN, WM, WN, 1, false)},                 \
                                 {GBA_V5_LAUNCHERS_(BM, BN, WM, WN, 0, true),                   \
                                  GBA_V5_LAUNCHERS_(BM, BN, WM, WN, 1, true)}};                 \
+    }
+#endif
+
+// ---- 8-bit-input persistent kernel (gemm_f8.hpp) ----
+namespace gba {
+using F8LaunchFn = hipError_t (*)(const void *, const void *, const void *, void *, int, int, int,
+                                  float, int, int, hipStream_t);
+}  // namespace gba
+
+#define GBA_F8_INST_(FMT, DT, ACT)                                                             \
+    template __global__ void gba::gemm_f8_kernel<FMT, DT, ACT>(                                \
+        const uint8_t *__restrict__, const uint8_t *__restrict__, const uint16_t *__restrict__, \
+        uint16_t *__restrict__, int, int, int, float, int, int, int, int);
+
+#define GBA_F8_INSTS_(FMT)                                                                     \
+    GBA_F8_INST_(FMT, 0, 0) GBA_F8_INST_(FMT, 0, 1) GBA_F8_INST_(FMT, 0, 2)                    \
+    GBA_F8_INST_(FMT, 0, 3) GBA_F8_INST_(FMT, 0, 4) GBA_F8_INST_(FMT, 0, 5)                    \
+    GBA_F8_INST_(FMT, 1, 0) GBA_F8_INST_(FMT, 1, 1) GBA_F8_INST_(FMT, 1, 2)                    \
+    GBA_F8_INST_(FMT, 1, 3) GBA_F8_INST_(FMT, 1, 4) GBA_F8_INST_(FMT, 1, 5)
+
+#define GBA_F8_LAUNCHERS_(FMT, DT)                                                             \
+    {gba::launch_gemm_f8<FMT, DT, 0>, gba::launch_gemm_f8<FMT, DT, 1>,                         \
+     gba::launch_gemm_f8<FMT, DT, 2>, gba::launch_gemm_f8<FMT, DT, 3>,                         \
+     gba::launch_gemm_f8<FMT, DT, 4>, gba::launch_gemm_f8<FMT, DT, 5>}
+
+// Defines gba::NAME[dtype][act] (host pass) for 8-bit format FMT.
+#ifdef __HIP_DEVICE_COMPILE__
+#define GBA_F8_ENTRY(NAME, FMT) GBA_F8_INSTS_(FMT)
+#else
+#define GBA_F8_ENTRY(NAME, FMT)                                                                \
+    GBA_F8_INSTS_(FMT)                                                                         \
+    namespace gba {                                                                            \
+    extern const F8LaunchFn NAME[2][kNumActs];                                                 \
+    const F8LaunchFn NAME[2][kNumActs] = {GBA_F8_LAUNCHERS_(FMT, 0), GBA_F8_LAUNCHERS_(FMT, 1)}; \
     }
 #endif

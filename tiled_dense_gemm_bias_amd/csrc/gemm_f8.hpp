@@ -1,0 +1,307 @@
+// Persistent GEMM with 8-bit float inputs: C = act(scale * A.W^T + bias), A
+// [M,K] and W [N,K] (the transpose_B layout) in OCP E4M3 or E5M2, bias and C
+// in fp16/bf16, fp32 accumulation, on gfx950's v_mfma_f32_16x16x128_f8f6f4.
+//
+// The tiles have the shape of the 16-bit transpose_B kernel's (gemm_v5.hpp): a
+// 256x256 output tile per workgroup, K slices of 128 bytes (here 128 values),
+// A's and W's tiles 256 rows of 8 16-byte chunks, loaded straight into a
+// two-stage LDS ring with buffer range checks zero-filling the edges. One MFMA
+// consumes a whole slice: lane l of a 16-row block holds row r = l % 16 and the
+// 32 bytes of logical chunks 2g, 2g+1 (g = l / 16), i.e. k = 32g .. 32g+31. The
+// matrix instruction pairs lane i + 16g of one operand with lane j + 16g of the
+// other, so every row must hand over its 32 bytes in the same order: the
+// swizzle moves whole 32-byte pairs, logical chunk c of row r at physical chunk
+// c ^ 2((r / 2) % 4). A lane's fragment is then one contiguous, aligned 32-byte
+// read from pair g ^ ((r / 2) % 4), and the 8 rows one read serves per cycle
+// hit 8 distinct bank groups.
+//
+// Each wave owns a 128x128 block: 8 x 8 MFMAs of 16x16 per slice, issued in two
+// steps by row-block halves:
+//   step 0: rows 0..3 x columns 0..7, reading this slice's A fragments 4..7;
+//   barrier (the next slice has landed; every wave is done with this one);
+//   step 1: rows 4..7 x columns 0..7, reading the next slice's A fragments
+//           0..3 and each W fragment right after its last use, and issuing
+//           the global->LDS loads two slices ahead into the stage just freed.
+// The slice stream runs across a workgroup's tiles as in gemm_v5.hpp: the next
+// tile's first two slices load during the current tile's last steps.
+#pragma once
+
+#include "gemm_v5.hpp"
+
+namespace gba {
+
+enum { FP8_E4M3 = 0, FP8_E5M2 = 1 };
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// acc += A.B on 16x16x128 8-bit blocks (cbsz/blgp 0: E4M3, 1: E5M2, for the
+// first and second operand). Issued as inline assembly with the accumulator
+// tied to the destination: the compiler's own form of this instruction does not
+// tie them, so each MFMA wrote a fresh register and the 64 accumulators of a
+// wave were copied around (and spilled) every slice. The compiler therefore
+// sees neither this instruction's latency nor its register hazards; the kernel
+// covers them itself (see hazard_gap below). The operands come from LDS reads,
+// whose waits the compiler places from the asm operands.
+// FIRST: the accumulator input is the constant 0 (the tile's first slice), so
+// every definition of an accumulator is one of these instructions and the
+// accumulators stay in AGPRs throughout.
+template <int FMT, bool FIRST>
+__device__ __forceinline__ void mfma16x16x128_f8(f32x4 &acc, const i32x8 &a, const i32x8 &b) {
+    if constexpr (FIRST) {
+        if constexpr (FMT == FP8_E4M3)
+            asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+        else
+            asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0 cbsz:1 blgp:1"
+                         : "=a"(acc)
+                         : "v"(a), "v"(b));
+    } else {
+        if constexpr (FMT == FP8_E4M3)
+            asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+        else
+            asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1"
+                         : "+a"(acc)
+                         : "v"(a), "v"(b));
+    }
+}
+
+// An accumulator as a VGPR value (the compiler copies it out of its AGPRs).
+__device__ __forceinline__ f32x4 acc_value(const f32x4 &acc) {
+    f32x4 v;
+    asm volatile("" : "=v"(v) : "0"(acc));
+    return v;
+}
+
+// 32 wait states: more than any matrix instruction needs between writing an
+// accumulator and a vector instruction reading it (at most 19, for 16 passes).
+__device__ __forceinline__ void hazard_gap() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int FMT, int DT, int ACT>
+__global__ void __launch_bounds__(256)
+gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
+               const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int M, int N, int K,
+               float scale, int tiles_m, int tiles_n, int raster, int group_m) {
+    constexpr int BM = 256, BN = 256, BK = 128;   // BK in values = bytes
+    constexpr int NT = 256, BD = 16;
+    constexpr int WTM = 128, WTN = 128, FM = 8, FN = 8, HM = FM / 2;
+    constexpr int A_BYTES = BM * BK, STAGE_BYTES = 2 * A_BYTES;
+    constexpr int A_LD = BM * 8 / NT, LD = 2 * A_LD;   // 16-byte loads per thread and slice
+
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wid = tid >> 6;
+    const int wm = wid >> 1, wn = wid & 1;
+    // At least two slices per tile (the stream below assumes it); for K <= 128
+    // the second is all zeros.
+    const int nk = max((K + BK - 1) / BK, 2);
+    const int T = tiles_m * tiles_n;
+    const int G = gridDim.x;
+    const int wid_s = __builtin_amdgcn_readfirstlane(wid);
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(GBA_LDS void *)smem;
+    const int slot = raster ? xcd_remap(blockIdx.x, G) : (int)blockIdx.x;
+
+    struct Tile {
+        int m0, n0;
+    };
+    auto tile_of = [&](int r, Tile &t) -> bool {
+        const int idx = r * G + slot;
+        if (idx >= T) return false;
+        int tm, tn;
+        if (raster) {
+            grouped_tile(idx, tiles_m, tiles_n, group_m, tm, tn);
+        } else {
+            tm = idx / tiles_n;
+            tn = idx % tiles_n;
+        }
+        t.m0 = tm * BM;
+        t.n0 = tn * BN;
+        return true;
+    };
+
+    // Load i of a thread fills row 32 i + tid/8 of A's (i < 8) or W's tile at
+    // physical chunk tid % 8, i.e. logical chunk (tid%8) ^ 2((row/2)%4), where
+    // (row/2) % 4 = (tid/16) % 4 for every i.
+    const int c_a = (tid & 7) ^ (2 * ((tid >> 4) & 3));
+    const uint32_t ld_base = (uint32_t)(tid >> 3) * (uint32_t)K + (uint32_t)c_a * 16u;
+    struct SliceDma {
+        __amdgpu_buffer_rsrc_t ra, rw;
+        uint32_t la;
+        int k0;
+    };
+    // Slice kt of tile t into stage `stage`; slices past K (or of no tile) read
+    // nothing: every lane is out of range and lands zeros, which keeps the wait
+    // counts uniform.
+    auto slice_dma = [&](const Tile &t, bool live, int kt, int stage) {
+        SliceDma d;
+        d.la = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(stage * STAGE_BYTES + wid_s * 64 * 16));
+        const bool any = live && kt * BK < K;
+        d.k0 = any ? kt * BK : K;
+        const uint32_t rows_a = (uint32_t)min(M - t.m0, BM), rows_w = (uint32_t)min(N - t.n0, BN);
+        d.ra = make_rsrc(A + (any ? (size_t)t.m0 * K + d.k0 : 0),
+                         any ? rows_a * (uint32_t)K - (uint32_t)d.k0 : 0u);
+        d.rw = make_rsrc(W + (any ? (size_t)t.n0 * K + d.k0 : 0),
+                         any ? rows_w * (uint32_t)K - (uint32_t)d.k0 : 0u);
+        return d;
+    };
+    auto dma_one = [&](const SliceDma &d, int i, uint32_t kx) {
+        const int j = i & (A_LD - 1);
+        const uint32_t o = d.k0 + c_a * 16 < K ? ld_base + (uint32_t)(j * 32) * kx : kOobOffset;
+        if (i < A_LD)
+            buffer_load_lds16(d.ra, o, d.la + j * NT * 16);
+        else
+            buffer_load_lds16(d.rw, o, d.la + A_BYTES + j * NT * 16);
+    };
+
+    // Fragment bases: lane l of block f reads row 16 f + l%16 of the wave's
+    // rows ((row/2) % 4 = (l/2) % 4), 32-byte pair (l/16) ^ ((l/2) % 4).
+    const int tg = lane >> 4, tj = lane & 15;
+    const uint32_t pair = (uint32_t)((tg ^ ((tj >> 1) & 3)) * 32);
+    const uint32_t ra_row = (uint32_t)(wm * WTM + tj) * BK + pair;
+    const uint32_t rw_row = (uint32_t)(A_BYTES + (wn * WTN + tj) * BK) + pair;
+    auto read_frag = [&](const char *base, uint32_t row0, int f) -> i32x8 {
+        return *reinterpret_cast<const i32x8 *>(base + row0 + f * BD * BK);
+    };
+
+    f32x4 acc[FN][FM];
+    i32x8 fa[2][HM];   // A fragments: [0] rows 0..3, [1] rows 4..7
+    i32x8 fw[FN];      // W fragments of the slice being multiplied
+
+    Tile cur_t;
+    if (!tile_of(0, cur_t)) return;
+
+    {
+        const SliceDma d0 = slice_dma(cur_t, true, 0, 0), d1 = slice_dma(cur_t, true, 1, 1);
+#pragma unroll
+        for (int i = 0; i < LD; ++i) dma_one(d0, i, (uint32_t)K);
+#pragma unroll
+        for (int i = 0; i < LD; ++i) dma_one(d1, i, (uint32_t)K);
+    }
+    wait_vmcnt<LD>();
+    block_barrier();
+#pragma unroll
+    for (int f = 0; f < HM; ++f) fa[0][f] = read_frag(smem, ra_row, f);
+#pragma unroll
+    for (int f = 0; f < FN; ++f) fw[f] = read_frag(smem, rw_row, f);
+
+    const int mrow = wm * WTM + tj;
+    int stage0 = 0;
+    for (int r = 0;; ++r) {
+        Tile nxt_t;
+        const bool nxt_live = tile_of(r + 1, nxt_t);
+        if (!nxt_live) nxt_t = cur_t;
+
+        // Slice kt of this tile (FIRST: kt == 0, whose MFMAs start from zero).
+        auto slice = [&](int kt, auto first) {
+            constexpr bool F = decltype(first)::value;
+            const int sc = (stage0 + kt) & 1;
+            const char *cur_base = smem + sc * STAGE_BYTES;
+            const char *nxt_base = smem + (sc ^ 1) * STAGE_BYTES;
+            uint32_t kx = (uint32_t)K;
+            asm volatile("" : "+s"(kx));
+            // step 0: rows 0..3; this slice's A fragments 4..7 are read meanwhile
+#pragma unroll
+            for (int q = 0; q < FN * HM; ++q) {
+                const int fn = q / HM, fm = q % HM;
+                mfma16x16x128_f8<FMT, F>(acc[fn][fm], fw[fn], fa[0][fm]);
+                if (q % 8 == 0) fa[1][q / 8] = read_frag(cur_base, ra_row, HM + q / 8);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wait_vmcnt_lgkm0<0>();
+            block_barrier();
+            const bool here = kt + 2 < nk;
+            const SliceDma dn = slice_dma(here ? cur_t : nxt_t, here || nxt_live,
+                                          here ? kt + 2 : kt + 2 - nk, sc);
+            // step 1: rows 4..7; the next slice's A fragments 0..3, each W
+            // fragment after its last MFMA here, and the loads two slices ahead
+#pragma unroll
+            for (int q = 0; q < FN * HM; ++q) {
+                const int fn = q / HM, fm = q % HM;
+                mfma16x16x128_f8<FMT, F>(acc[fn][HM + fm], fw[fn], fa[1][fm]);
+                if (q % 2 == 0) dma_one(dn, q / 2, kx);
+                if (fm == HM - 1) fw[fn] = read_frag(nxt_base, rw_row, fn);
+                if (q % 8 == 1) fa[0][q / 8] = read_frag(nxt_base, ra_row, q / 8);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        slice(0, std::true_type{});
+        for (int kt = 1; kt < nk; ++kt) slice(kt, std::false_type{});
+
+        // Epilogue while the next tile's first slices land: z = scale * acc + bias.
+        hazard_gap();   // the last MFMAs' results are complete before they are read
+        asm volatile("" ::: "memory");
+        {
+            char *const Ct = reinterpret_cast<char *>(C + (size_t)cur_t.m0 * N + cur_t.n0);
+            int c0 = wn * WTN + 4 * tg, mr = mrow;
+            asm volatile("" : "+v"(mr));
+            uint32_t lane_off = ((uint32_t)mr * (uint32_t)N + (uint32_t)c0) * 2u;
+            uint32_t pitch16 = (uint32_t)N * (2u * BD);
+            asm volatile("" : "+v"(lane_off), "+v"(c0), "+s"(pitch16));
+            const bool full = cur_t.m0 + BM <= M && cur_t.n0 + BN <= N;
+            auto store_all = [&](auto masked) {
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    const int cn = c0 + fn * BD;
+                    if (masked && cur_t.n0 + cn >= N) continue;
+                    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+                    if (bias) {
+                        const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + cur_t.n0 + cn);
+                        b0 = to_f32<DT>(bb.x & 0xffffu);
+                        b1 = to_f32<DT>(bb.x >> 16);
+                        b2 = to_f32<DT>(bb.y & 0xffffu);
+                        b3 = to_f32<DT>(bb.y >> 16);
+                    }
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm) {
+                        if (masked && cur_t.m0 + mr + fm * BD >= M) continue;
+                        const f32x4 a = acc_value(acc[fn][fm]);
+                        u32x2 o;
+                        o.x = pack2<DT>(act_fn<ACT>(fmaf(a[0], scale, b0)),
+                                        act_fn<ACT>(fmaf(a[1], scale, b1)));
+                        o.y = pack2<DT>(act_fn<ACT>(fmaf(a[2], scale, b2)),
+                                        act_fn<ACT>(fmaf(a[3], scale, b3)));
+                        const uint32_t offs = lane_off + (uint32_t)fm * pitch16 + (uint32_t)(fn * BD) * 2u;
+                        *reinterpret_cast<u32x2 *>(Ct + offs) = o;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            if (full)
+                store_all(std::false_type{});
+            else
+                store_all(std::true_type{});
+        }
+
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        stage0 = (stage0 + nk) & 1;
+        if (!nxt_live) break;
+        cur_t = nxt_t;
+    }
+    wait_vmcnt<0>();
+}
+
+// Grid: one workgroup per CU, or fewer when there are fewer tiles.
+template <int FMT, int DT, int ACT>
+hipError_t launch_gemm_f8(const void *A, const void *W, const void *bias, void *C, int M, int N,
+                          int K, float scale, int raster, int group_m, hipStream_t stream) {
+    const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+    const long long tiles = (long long)tiles_m * tiles_n;
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int grid = (int)(tiles < cus ? tiles : cus);
+    hipLaunchKernelGGL((gemm_f8_kernel<FMT, DT, ACT>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const uint8_t *)A, (const uint8_t *)W, (const uint16_t *)bias,
+                       (uint16_t *)C, M, N, K, scale, tiles_m, tiles_n, raster,
+                       group_m < 1 ? 1 : group_m);
+    return hipGetLastError();
+}
+
+}  // namespace gba
