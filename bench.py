@@ -21,6 +21,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -176,6 +177,8 @@ def main(argv=None) -> int:
     ap.add_argument("--transpose-b", action="store_true",
                     help="B stored [N,K] (transpose_B): time gemm_bias_act_nt on the same numbers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--act", default=None,
+                    help="replace the workload's activation (none, relu, sigmoid, gelu, softplus, gelu_tanh)")
     ap.add_argument("--tune", action="store_true", help="autotune before timing")
     ap.add_argument("--schedule", default=None, help="force bm,bn,bk,wm,wn,stages,kernel,loaders,spread[,raster,group_m]")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -197,6 +200,8 @@ def main(argv=None) -> int:
 
     fp8 = a.workload in synth.FP8_WORKLOADS
     w = synth.FP8_WORKLOADS[a.workload] if fp8 else synth.WORKLOADS[a.workload]
+    if a.act:
+        w = dataclasses.replace(w, act=a.act)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log("[bench] generating %s inputs %dx%dx%d %s" % (w.name, w.M, w.N, w.K, w.dtype))
@@ -208,7 +213,7 @@ def main(argv=None) -> int:
     tb = a.transpose_b and not fp8
     if tb:
         B = np.ascontiguousarray(B.T)   # the same operand, stored as the [N,K] weight W
-    wl_key = w.name + ("_nt" if tb else "")
+    wl_key = w.name + ("_nt" if tb else "") + ("_" + a.act if a.act else "")
     tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
 
     def dev_t(bits):
