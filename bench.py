@@ -174,6 +174,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="c3_gelu")
     ap.add_argument("--unfused", action="store_true", help="also time gemm + bias_act")
+    ap.add_argument("--workspace", action="store_true",
+                    help="pass a split-K workspace (gemm_bias_act_ex): shapes with fewer tiles "
+                         "than CUs split K")
     ap.add_argument("--transpose-b", action="store_true",
                     help="B stored [N,K] (transpose_B): time gemm_bias_act_nt on the same numbers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -253,7 +256,12 @@ def main(argv=None) -> int:
         step = gba.bind_gemm_bias_act_fp8(a_t, b_t, bias_t, c_t, scale, w.act, w.fmt)
     else:
         sched = gba.get_schedule(w.M, w.N, w.K, w.act, w.dtype, transpose_b=tb)
-        step = gba.bind_gemm_bias_act(a_t, b_t, bias_t, c_t, w.act, transpose_b=tb)
+        ws_t = None
+        if a.workspace:
+            nb = gba.workspace_size(w.M, w.N, w.K, w.act, w.dtype, transpose_b=tb)
+            ws_t = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+            sched = dict(sched, splits_workspace_bytes=nb)
+        step = gba.bind_gemm_bias_act(a_t, b_t, bias_t, c_t, w.act, transpose_b=tb, workspace=ws_t)
     log("[bench] schedule %s%s" % (sched, " (B stored [N,K])" if tb else ""))
     wall_ms, kern_avg, per = time_launches(step, a.steps, a.warmup, stream)
     ms_per_step = wall_ms / a.steps

@@ -30,6 +30,7 @@
 #ifndef GBA_H
 #define GBA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -134,6 +135,33 @@ int gemm_bias_act_nt(const void *A, const void *W, const void *bias, void *C, in
 
 /* C = A.W^T rounded to `dtype`, W: [N,K] (gemm with transpose_B). */
 int gemm_nt(const void *A, const void *W, void *C, int64_t M, int64_t N, int64_t K, int dtype);
+
+/* gemm_bias_act_ex flags. */
+enum { GBA_TRANSPOSE_B = 1 /* B is W, stored [N,K], as in gemm_bias_act_nt */ };
+
+/* gemm_bias_act (or, with GBA_TRANSPOSE_B, gemm_bias_act_nt) with an optional
+ * caller-owned device workspace for split-K. When the chosen schedule's tiles
+ * leave compute units idle and K is deep enough for the split to pay for its
+ * extra traffic (e.g. 256x256x4096: 4 tiles of 128x128 for 256 CUs; not
+ * 1024^3, where the fp32 partials' round trip costs more than it saves), K is
+ * split S ways: a first kernel writes the S fp32 partial sums
+ * [S][M][N] into the workspace, and a second adds them in split order and
+ * applies bias, act and the rounding (the fused epilogue, one pass over C).
+ * gba_workspace_size gives the bytes that enable the split (0: no split for
+ * this shape); a NULL or smaller workspace runs the one-kernel path. The
+ * workspace needs no initialisation and holds nothing between calls; it must
+ * be 16-byte aligned and overlap none of A, B, bias, C (GBA_ERR_ALIGN /
+ * GBA_ERR_ALIAS). Calls sharing a workspace must be ordered on one stream.
+ * The split changes the fp32 summation order, not the tolerance; results are
+ * deterministic. Unknown flag bits: GBA_ERR_SHAPE. */
+int gemm_bias_act_ex(const void *A, const void *B, const void *bias, void *C, int64_t M,
+                     int64_t N, int64_t K, int act, int dtype, int flags, void *workspace,
+                     size_t workspace_bytes);
+
+/* Workspace bytes gemm_bias_act_ex would use for these arguments (0 if it would
+ * not split), written to *bytes. */
+int gba_workspace_size(int64_t M, int64_t N, int64_t K, int act, int dtype, int flags,
+                       size_t *bytes);
 
 /* 8-bit float input formats (OCP OFP8): E4M3 (largest finite 448, no
  * infinities) and E5M2 (largest finite 57344). */

@@ -121,6 +121,22 @@ def test_fp8_argument_errors_precede_device_use(lib):
     assert call8(lib, N=0, A=None, W=None) == OK
 
 
+def test_ex_and_workspace_argument_errors_precede_device_use(lib):
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    ex = lambda flags=0, ws=None, nb=0, **kw: lib.gemm_bias_act_ex(
+        v(P16), v(P16), None, v(P16 * 64), 64, 64, 64, kw.get("act", 0), kw.get("dt", 0), flags,
+        v(ws), nb)
+    assert ex(flags=2) == ERR_SHAPE              # unknown flag bit
+    assert ex(act=6) == ERR_ACT
+    assert ex(ws=P16 * 200 + 8, nb=1 << 20) == ERR_ALIGN
+    assert ex(ws=P16 * 64 + 256, nb=1 << 20) == ERR_ALIAS   # overlaps C
+    size = ctypes.c_size_t(123)
+    assert lib.gba_workspace_size(64, 64, 64, 0, 0, 2, ctypes.byref(size)) == ERR_SHAPE
+    assert lib.gba_workspace_size(-1, 64, 64, 0, 0, 0, ctypes.byref(size)) == ERR_SHAPE
+    assert lib.gba_workspace_size(0, 64, 64, 0, 0, 0, ctypes.byref(size)) == OK and size.value == 0
+    assert lib.gba_workspace_size(64, 64, 64, 0, 0, 0, None) == ERR_NULL
+
+
 def test_bias_act_argument_errors(lib):
     v = ctypes.c_void_p
     assert lib.bias_act(v(P16), None, v(P16), 4, 8, 6, 0) == ERR_ACT

@@ -68,6 +68,8 @@ def _lib():
             "gemm_bias_act_nt": [p, p, p, p, i64, i64, i64, ci, ci],
             "gemm_nt": [p, p, p, i64, i64, i64, ci],
             "gemm_bias_act_fp8_nt": [p, p, p, p, i64, i64, i64, ctypes.c_float, ci, ci, ci],
+            "gemm_bias_act_ex": [p, p, p, p, i64, i64, i64, ci, ci, ci, p, ctypes.c_size_t],
+            "gba_workspace_size": [i64, i64, i64, ci, ci, ci, ctypes.POINTER(ctypes.c_size_t)],
             "bias_act": [p, p, p, i64, i64, ci, ci],
             "gba_set_stream": [p],
             "gba_set_schedule": [ctypes.POINTER(Schedule)],
@@ -178,18 +180,47 @@ def _gemm_shapes(a, b, bias, c, transpose_b):
     return dt, M, N, K
 
 
-def gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False):
+TRANSPOSE_B = 1
+
+
+def _ws_args(workspace):
+    if workspace is None:
+        return None, 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("the workspace is a contiguous device tensor")
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
+def gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False, workspace=None):
     """c[M,N] = act(a[M,K] @ b[K,N] + bias[N]); bias may be None. Returns c.
 
-    transpose_b: b is stored [N,K] (a linear layer's weight) and c = act(a @ b.T + bias)."""
+    transpose_b: b is stored [N,K] (a linear layer's weight) and c = act(a @ b.T + bias).
+    workspace: optional device tensor of workspace_size(...) bytes that lets
+    shapes with fewer tiles than CUs split K (gemm_bias_act_ex)."""
     dev = _check_dev(a, b, bias, c)
     dt, M, N, K = _gemm_shapes(a, b, bias, c, transpose_b)
+    if workspace is not None:
+        _check_dev(workspace)
+        ws, nb = _ws_args(workspace)
+        _call("gemm_bias_act_ex", dev, _ptr(a), _ptr(b), _ptr(bias), _ptr(c), M, N, K, _act(act),
+              dt, TRANSPOSE_B if transpose_b else 0, ws, nb)
+        return c
     _call("gemm_bias_act_nt" if transpose_b else "gemm_bias_act", dev, _ptr(a), _ptr(b),
           _ptr(bias), _ptr(c), M, N, K, _act(act), dt)
     return c
 
 
-def bind_gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False):
+def workspace_size(M: int, N: int, K: int, act="gelu", dtype="f16", transpose_b=False) -> int:
+    """Bytes of split-K workspace gemm_bias_act would use for this shape (0: no split)."""
+    out = ctypes.c_size_t()
+    st = _lib().gba_workspace_size(M, N, K, _act(act), 0 if dtype in ("f16", "float16") else 1,
+                                   TRANSPOSE_B if transpose_b else 0, ctypes.byref(out))
+    if st != 0:
+        raise GbaError(st, "gba_workspace_size")
+    return int(out.value)
+
+
+def bind_gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False, workspace=None):
     """Check and marshal the arguments once; return a no-argument callable that
     enqueues c = act(a @ b + bias) (a @ b.T with transpose_b) on the stream
     current now (one C call per invocation). For tight loops such as benchmarks;
@@ -201,6 +232,10 @@ def bind_gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False):
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     args = (_ptr(a), _ptr(b), _ptr(bias), _ptr(c), M, N, K, _act(act), dt)
     name = "gemm_bias_act_nt" if transpose_b else "gemm_bias_act"
+    if workspace is not None:
+        _check_dev(workspace)
+        args = args + ((TRANSPOSE_B if transpose_b else 0,) + _ws_args(workspace))
+        name = "gemm_bias_act_ex"
     fn = getattr(lib, name)
     set_stream = lib.gba_set_stream
     set_stream(stream)

@@ -375,16 +375,93 @@ int launch(const gba_schedule &s0, const void *A, const void *B, const void *bia
     return e == hipSuccess ? GBA_OK : hip_fail(e);
 }
 
+// Split-K factor for schedule s: > 1 only for schedules with a split-K first
+// pass, when their tiles leave CUs idle and the split pays for itself. Units
+// (tiles x splits) stay within the CU count, each split keeps at least two K
+// slices, at most 16 splits. Cost model (measured on MI355X with the 128x128
+// schedule): a K slice takes ~0.65 us per tile; the split adds the fp32
+// partials' round trip, 2 S M N 4 bytes at ~4 TB/s, and ~5 us for the second
+// kernel and its launch. Split only if that saves at least 15 %. (At 1024^3 it
+// does not: 19.6 us split against 14.3 us whole; at 256x256x4096 it does.)
+int split_count(const gba_schedule &s0, int64_t M, int64_t N, int64_t K, int cus, int dtype,
+                bool tb) {
+    gba_schedule s = s0;
+    if (s.kernel == 4 && K <= s.bk) s.kernel = 3;
+    const int i = find_entry(s);
+    if (i < 0 || !kTable[i]->part[dtype][tb ? 1 : 0] || K <= 0) return 1;
+    const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
+    const int64_t nk = (K + s.bk - 1) / s.bk;
+    int64_t smax = tiles > 0 ? cus / tiles : 1;
+    smax = std::min<int64_t>(smax, nk / 2);
+    smax = std::min<int64_t>(smax, 16);
+    const double t_slice = 0.65e-6, bw = 4.0e12, t_fixed = 5.0e-6;
+    const double whole = nk * t_slice;
+    int best = 1;
+    double best_t = whole;
+    for (int64_t S = 2; S <= smax; ++S) {
+        const double t = ((nk + S - 1) / S) * t_slice + 2.0 * S * (double)M * N * 4.0 / bw + t_fixed;
+        if (t < best_t) {
+            best_t = t;
+            best = (int)S;
+        }
+    }
+    return best_t < 0.85 * whole ? best : 1;
+}
+
+template <int DT, int ACT>
+hipError_t launch_splitk_reduce_t(const float *P, int S, const void *bias, void *C, int M, int N,
+                                  hipStream_t st) {
+    const int cpr = N / 8;
+    const int gx = (cpr + 255) / 256;
+    int gy = M;
+    const int max_y = std::max(1, 8192 / gx);
+    if (gy > max_y) gy = max_y;
+    hipLaunchKernelGGL((gba::splitk_reduce_kernel<DT, ACT>), dim3(gx, gy), dim3(256), 0, st, P, S,
+                       (const uint16_t *)bias, (uint16_t *)C, M, N);
+    return hipGetLastError();
+}
+
+using ReduceFn = hipError_t (*)(const float *, int, const void *, void *, int, int, hipStream_t);
+const ReduceFn kReduce[2][gba::kNumActs] = {
+    {launch_splitk_reduce_t<0, 0>, launch_splitk_reduce_t<0, 1>, launch_splitk_reduce_t<0, 2>,
+     launch_splitk_reduce_t<0, 3>, launch_splitk_reduce_t<0, 4>, launch_splitk_reduce_t<0, 5>},
+    {launch_splitk_reduce_t<1, 0>, launch_splitk_reduce_t<1, 1>, launch_splitk_reduce_t<1, 2>,
+     launch_splitk_reduce_t<1, 3>, launch_splitk_reduce_t<1, 4>, launch_splitk_reduce_t<1, 5>},
+};
+
 int gemm_common(const void *A, const void *B, const void *bias, void *C, int64_t M, int64_t N,
-                int64_t K, int act, int dtype, bool tb) {
+                int64_t K, int act, int dtype, bool tb, void *ws = nullptr, size_t ws_bytes = 0) {
     bool nothing = false;
     int s = check_gemm_args(A, B, bias, C, M, N, K, act, dtype, &nothing);
     if (s || nothing) return s;
+    if (ws) {
+        if (!aligned16(ws)) return GBA_ERR_ALIGN;
+        if (overlaps(ws, ws_bytes, A, (size_t)M * K * 2) || overlaps(ws, ws_bytes, B, (size_t)K * N * 2) ||
+            overlaps(ws, ws_bytes, bias, (size_t)N * 2) || overlaps(ws, ws_bytes, C, (size_t)M * N * 2))
+            return GBA_ERR_ALIAS;
+    }
     const DeviceInfo *d;
     s = current_device(&d);
     if (s) return s;
     const char *why = "";
     const gba_schedule sch = choose(*d, M, N, K, act, dtype, tb, &why);
+    if (ws) {
+        const int S = split_count(sch, M, N, K, d->cus, dtype, tb);
+        if (S > 1 && ws_bytes >= (size_t)S * (size_t)M * (size_t)N * 4u) {
+            if (log_enabled())
+                fprintf(stderr, "[gba] M=%lld N=%lld K=%lld act=%s dtype=%s -> split-K %d x k%d %dx%dx%d (%s)\n",
+                        (long long)M, (long long)N, (long long)K, kActName[act], kDtName[dtype], S,
+                        sch.kernel, sch.bm, sch.bn, sch.bk, why);
+            gba_schedule s3 = sch;
+            if (s3.kernel == 4 && K <= s3.bk) s3.kernel = 3;
+            const gba::PartialLaunchFn pf = kTable[find_entry(s3)]->part[dtype][tb ? 1 : 0];
+            hipError_t e = pf(A, B, (float *)ws, (int)M, (int)N, (int)K, S, s3.raster, s3.group_m,
+                              t_stream);
+            if (e != hipSuccess) return hip_fail(e);
+            e = kReduce[dtype][act]((const float *)ws, S, bias, C, (int)M, (int)N, t_stream);
+            return e == hipSuccess ? GBA_OK : hip_fail(e);
+        }
+    }
     if (log_enabled())
         fprintf(stderr,
                 "[gba] M=%lld N=%lld K=%lld act=%s dtype=%s B=%s -> k%d %dx%dx%d w%dx%d s%d r%d g%d "
@@ -508,6 +585,34 @@ int gemm_bias_act_nt(const void *A, const void *W, const void *bias, void *C, in
 
 int gemm_nt(const void *A, const void *W, void *C, int64_t M, int64_t N, int64_t K, int dtype) {
     return gemm_common(A, W, nullptr, C, M, N, K, GBA_ACT_NONE, dtype, true);
+}
+
+int gemm_bias_act_ex(const void *A, const void *B, const void *bias, void *C, int64_t M,
+                     int64_t N, int64_t K, int act, int dtype, int flags, void *workspace,
+                     size_t workspace_bytes) {
+    if (flags & ~GBA_TRANSPOSE_B) return GBA_ERR_SHAPE;
+    return gemm_common(A, B, bias, C, M, N, K, act, dtype, (flags & GBA_TRANSPOSE_B) != 0,
+                       workspace, workspace ? workspace_bytes : 0);
+}
+
+int gba_workspace_size(int64_t M, int64_t N, int64_t K, int act, int dtype, int flags,
+                       size_t *bytes) {
+    if (!bytes) return GBA_ERR_NULL;
+    *bytes = 0;
+    if (flags & ~GBA_TRANSPOSE_B) return GBA_ERR_SHAPE;
+    int s = check_enums(act, dtype);
+    if (s) return s;
+    if (M < 0 || N < 0 || K < 0) return GBA_ERR_SHAPE;
+    if (M == 0 || N == 0) return GBA_OK;
+    const DeviceInfo *d;
+    s = current_device(&d);
+    if (s) return s;
+    const bool tb = (flags & GBA_TRANSPOSE_B) != 0;
+    const char *why;
+    const gba_schedule sch = choose(*d, M, N, K, act, dtype, tb, &why);
+    const int S = split_count(sch, M, N, K, d->cus, dtype, tb);
+    if (S > 1) *bytes = (size_t)S * (size_t)M * (size_t)N * 4u;
+    return GBA_OK;
 }
 
 int bias_act(const void *X, const void *bias, void *Y, int64_t M, int64_t N, int act,

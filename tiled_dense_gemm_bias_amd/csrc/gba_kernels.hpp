@@ -37,6 +37,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // Native 16-byte vector (HIP's u32x4 is a struct, whose copies defeat register promotion).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_SIGMOID = 2, ACT_GELU = 3, ACT_SOFTPLUS = 4, ACT_GELU_TANH = 5 };
@@ -403,6 +404,49 @@ bias_act_kernel(const uint16_t *X, const uint16_t *__restrict__ bias, uint16_t *
             u32x4 y = {o[0], o[1], o[2], o[3]};
             *reinterpret_cast<u32x4 *>(Y + (size_t)(r0 + u) * N + chunk * 8) = y;
         }
+    }
+}
+
+// Split-K second pass: C[r][c] = act(sum_{s<S} P[s][r][c] + bias[c]), with P
+// the fp32 partial sums [S][M][N] of disjoint K ranges, added in s order (the
+// result does not depend on which partial was written first), then one
+// rounding. Thread layout as bias_act_kernel: one 8-column chunk per thread,
+// striding down the rows.
+template <int DT, int ACT>
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float *__restrict__ P, int S, const uint16_t *__restrict__ bias,
+                     uint16_t *__restrict__ C, int M, int N) {
+    const int cpr = N / 8;
+    const int chunk = blockIdx.x * 256 + threadIdx.x;
+    if (chunk >= cpr) return;
+    float bv[8];
+    if (bias) {
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(bias + chunk * 8);
+        const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bv[2 * e] = to_f32<DT>(w[e] & 0xffffu);
+            bv[2 * e + 1] = to_f32<DT>(w[e] >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[e] = 0.0f;
+    }
+    const size_t plane = (size_t)M * N;
+    for (int r = blockIdx.y; r < M; r += gridDim.y) {
+        const float *p = P + (size_t)r * N + chunk * 8;
+        f32x4 lo = *reinterpret_cast<const f32x4 *>(p);
+        f32x4 hi = *reinterpret_cast<const f32x4 *>(p + 4);
+        for (int s = 1; s < S; ++s) {
+            lo += *reinterpret_cast<const f32x4 *>(p + s * plane);
+            hi += *reinterpret_cast<const f32x4 *>(p + s * plane + 4);
+        }
+        u32x4 y;
+        y.x = pack2<DT>(act_fn<ACT>(lo[0] + bv[0]), act_fn<ACT>(lo[1] + bv[1]));
+        y.y = pack2<DT>(act_fn<ACT>(lo[2] + bv[2]), act_fn<ACT>(lo[3] + bv[3]));
+        y.z = pack2<DT>(act_fn<ACT>(hi[0] + bv[4]), act_fn<ACT>(hi[1] + bv[5]));
+        y.w = pack2<DT>(act_fn<ACT>(hi[2] + bv[6]), act_fn<ACT>(hi[3] + bv[7]));
+        *reinterpret_cast<u32x4 *>(C + (size_t)r * N + chunk * 8) = y;
     }
 }
 

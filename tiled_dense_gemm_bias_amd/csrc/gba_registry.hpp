@@ -14,11 +14,15 @@ namespace gba {
 
 using GemmLaunchFn = hipError_t (*)(const void *, const void *, const void *, void *, int, int,
                                     int, int, int, hipStream_t);
+// Split-K first pass: (A, B, part, M, N, K, splits, raster, group_m, stream).
+using PartialLaunchFn = hipError_t (*)(const void *, const void *, float *, int, int, int, int,
+                                       int, int, hipStream_t);
 
 struct ScheduleEntry {
     gba_schedule sched;      // raster / group_m hold the defaults
     GemmLaunchFn fn[2][kNumActs];   // [dtype][act], B stored (K,N)
     GemmLaunchFn tb[2][kNumActs];   // [dtype][act], B stored (N,K); null without that path
+    PartialLaunchFn part[2][2];     // split-K first pass [dtype][B stored (N,K)]; null if none
 };
 
 }  // namespace gba
@@ -107,7 +111,7 @@ struct ScheduleEntry {
 #define GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, DT, ACT)                               \
     template __global__ void gba::gemm_v3_kernel<BM, BN, BK, WM, WN, S, L, SP, MS, DT, ACT>(  \
         const uint16_t *__restrict__, const uint16_t *__restrict__, const uint16_t *__restrict__, \
-        uint16_t *__restrict__, int, int, int, int, int, int, int);
+        uint16_t *__restrict__, int, int, int, int, int, int, int, int, float *__restrict__);
 
 #define GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP, MS)                                        \
     GBA_V3_INST_(BM, BN, BK, WM, WN, S, L, SP, MS, 0, 0)                                       \
@@ -134,7 +138,26 @@ struct ScheduleEntry {
 #define GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, DT, ACT)                                  \
     template __global__ void gba::gemm_v3_kernel<BM, BN, BK, WM, WN, S, L, SP, 16, DT, ACT, true>( \
         const uint16_t *__restrict__, const uint16_t *__restrict__, const uint16_t *__restrict__, \
-        uint16_t *__restrict__, int, int, int, int, int, int, int);
+        uint16_t *__restrict__, int, int, int, int, int, int, int, int, float *__restrict__);
+
+// split-K first-pass instances: [dtype][B stored (N,K)]
+#define GBA_V3P_INST_(BM, BN, BK, WM, WN, S, L, SP, DT, TB)                                    \
+    template __global__ void                                                                  \
+    gba::gemm_v3_kernel<BM, BN, BK, WM, WN, S, L, SP, 16, DT, 0, TB, true>(                   \
+        const uint16_t *__restrict__, const uint16_t *__restrict__, const uint16_t *__restrict__, \
+        uint16_t *__restrict__, int, int, int, int, int, int, int, int, float *__restrict__);
+
+#define GBA_V3P_INSTS_(BM, BN, BK, WM, WN, S, L, SP)                                           \
+    GBA_V3P_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, false)                                      \
+    GBA_V3P_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, true)                                       \
+    GBA_V3P_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, false)                                      \
+    GBA_V3P_INST_(BM, BN, BK, WM, WN, S, L, SP, 1, true)
+
+#define GBA_V3P_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP)                                       \
+    {{gba::launch_gemm_v3_partial<BM, BN, BK, WM, WN, S, L, SP, 0, false>,                      \
+      gba::launch_gemm_v3_partial<BM, BN, BK, WM, WN, S, L, SP, 0, true>},                      \
+     {gba::launch_gemm_v3_partial<BM, BN, BK, WM, WN, S, L, SP, 1, false>,                      \
+      gba::launch_gemm_v3_partial<BM, BN, BK, WM, WN, S, L, SP, 1, true>}}
 
 #define GBA_V3T_INSTS_(BM, BN, BK, WM, WN, S, L, SP)                                           \
     GBA_V3T_INST_(BM, BN, BK, WM, WN, S, L, SP, 0, 0)                                          \
@@ -170,6 +193,28 @@ struct ScheduleEntry {
     const ScheduleEntry NAME = {{BM, BN, BK, WM, WN, S, 1, GROUP_M, MS == 32 ? 2 : 3, L, SP}, \
                                 {GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, MS, 0),     \
                                  GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, MS, 1)}};   \
+    }
+#endif
+
+// Both B layouts and the split-K first pass.
+#ifdef __HIP_DEVICE_COMPILE__
+#define GBA_V3_SCHEDULE_ENTRY_TBP(NAME, BM, BN, BK, WM, WN, S, L, SP, GROUP_M)                \
+    GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP, 16)                                          \
+    GBA_V3T_INSTS_(BM, BN, BK, WM, WN, S, L, SP)                                             \
+    GBA_V3P_INSTS_(BM, BN, BK, WM, WN, S, L, SP)
+#else
+#define GBA_V3_SCHEDULE_ENTRY_TBP(NAME, BM, BN, BK, WM, WN, S, L, SP, GROUP_M)                \
+    GBA_V3_INSTS_(BM, BN, BK, WM, WN, S, L, SP, 16)                                          \
+    GBA_V3T_INSTS_(BM, BN, BK, WM, WN, S, L, SP)                                             \
+    GBA_V3P_INSTS_(BM, BN, BK, WM, WN, S, L, SP)                                             \
+    namespace gba {                                                                          \
+    extern const ScheduleEntry NAME;                                                         \
+    const ScheduleEntry NAME = {{BM, BN, BK, WM, WN, S, 1, GROUP_M, 3, L, SP},                \
+                                {GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, 16, 0),     \
+                                 GBA_V3_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, 16, 1)},    \
+                                {GBA_V3T_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, 0),        \
+                                 GBA_V3T_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP, 1)},       \
+                                GBA_V3P_LAUNCHERS_(BM, BN, BK, WM, WN, S, L, SP)};           \
     }
 #endif
 

@@ -23,6 +23,11 @@
 // A.W^T. W's tile then has A's shape and layout (BN rows of BK K-contiguous
 // values, the same chunk XOR), is loaded like A, and its MFMA operand is read
 // like A's with ds_read_b128 -- no transposing reads. 16x16x32 MFMAs only.
+//
+// PARTIAL (split-K, first pass): the grid holds `splits` work units per tile;
+// unit s covers K slices [s nk / splits, (s+1) nk / splits) and writes its raw
+// fp32 sums to part[s][M][N] instead of running the epilogue. The second pass
+// (splitk_reduce_kernel) adds the partials in s order, then bias, act, rounding.
 #pragma once
 
 #include "gemm_v2.hpp"
@@ -30,8 +35,6 @@
 #include <type_traits>
 
 namespace gba {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int MS> struct Acc;
 template <> struct Acc<32> { typedef f32x16 type; static constexpr int n = 16; };
@@ -72,11 +75,12 @@ __device__ __forceinline__ int bswz(int r) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int MS, int DT,
-          int ACT, bool TB = false>
+          int ACT, bool TB = false, bool PARTIAL = false>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int M, int N, int K,
-               int tiles_m, int tiles_n, int raster, int group_m) {
+               int tiles_m, int tiles_n, int raster, int group_m, int splits,
+               float *__restrict__ part) {
     constexpr int NW = WM * WN;
     constexpr int NTL = LDW * 64;         // loader threads
     constexpr int CHA = BK / 8;
@@ -111,11 +115,17 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
 
-    int tm, tn;
+    static_assert(!PARTIAL || MS == 16, "split-K is written for 16x16x32 MFMAs");
+    int tm, tn, split = 0;
     {
         int t = blockIdx.x;
+        if (raster) t = xcd_remap(t, gridDim.x);
+        if constexpr (PARTIAL) {
+            // units of one split are contiguous, so each XCD walks whole tiles' panels
+            split = t / (tiles_m * tiles_n);
+            t -= split * (tiles_m * tiles_n);
+        }
         if (raster) {
-            t = xcd_remap(t, gridDim.x);
             grouped_tile(t, tiles_m, tiles_n, group_m, tm, tn);
         } else {
             tm = t / tiles_n;
@@ -126,7 +136,10 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
     const int wm = wid / WN, wn = wid % WN;
-    const int nk = (K + BK - 1) / BK;
+    // This unit's K slices: [kt0, kt0 + nk).
+    const int nk_all = (K + BK - 1) / BK;
+    const int kt0 = PARTIAL ? (int)((long long)split * nk_all / splits) : 0;
+    const int nk = PARTIAL ? (int)((long long)(split + 1) * nk_all / splits) - kt0 : nk_all;
     const int wid_s = __builtin_amdgcn_readfirstlane(wid);
     const bool loader = (LDW == NW) || wid_s < LDW;
     const int rows_a = min(M - m0, BM);
@@ -169,8 +182,8 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         const int stage = kt % STAGES;
         d.la = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(stage * STAGE_BYTES + wid_s * 64 * 16));
         d.lb = d.la + A_BYTES;
-        d.k0 = kt * BK;
-        const bool live = d.k0 < K;
+        d.k0 = (kt0 + kt) * BK;
+        const bool live = PARTIAL ? kt < nk : d.k0 < K;
         const uint32_t bytes_a =
             live ? (uint32_t)rows_a * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u;
         d.ra = make_rsrc(A + (size_t)m0 * K + (live ? d.k0 : 0), bytes_a);
@@ -323,6 +336,25 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // No direct-to-LDS write may outlive the workgroup's LDS.
     wait_vmcnt<0>();
 
+    if constexpr (PARTIAL) {
+        // Raw fp32 sums of this unit: lane l holds 4 adjacent n of one row m per
+        // block; 16-byte stores into part[split], masked at the M / N edges.
+        float *const Pt = part + (size_t)split * M * N + (size_t)m0 * N + n0;
+        const int prow = wm * WTM + (lane & 15);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int cn = wn * WTN + fn * BD + 4 * (lane >> 4);
+            if (n0 + cn >= N) continue;
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int r = prow + fm * BD;
+                if (m0 + r >= M) continue;
+                *reinterpret_cast<f32x4 *>(Pt + (size_t)r * N + cn) = acc[fn][fm];
+            }
+        }
+        return;
+    }
+
     // Epilogue: + bias[n], activation, round once, 8-byte stores. Addresses are a
     // 32-bit byte offset from the tile's corner (row pitch N*2, at most 2^32 for
     // N <= 2^23); rows and columns are masked only in edge tiles. Lane l holds
@@ -380,7 +412,24 @@ hipError_t launch_gemm_v3(const void *A, const void *B, const void *bias, void *
     hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, BK, WM, WN, STAGES, LDW, SPREAD, MS, DT, ACT, TB>),
                        dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream, (const uint16_t *)A,
                        (const uint16_t *)B, (const uint16_t *)bias, (uint16_t *)C, M, N, K, tiles_m,
-                       tiles_n, raster, group_m < 1 ? 1 : group_m);
+                       tiles_n, raster, group_m < 1 ? 1 : group_m, 1, (float *)nullptr);
+    return hipGetLastError();
+}
+
+// Split-K first pass: `splits` units per tile write fp32 partials to part
+// ([splits][M][N]); the epilogue runs in splitk_reduce_kernel.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int DT, bool TB>
+hipError_t launch_gemm_v3_partial(const void *A, const void *B, float *part, int M, int N, int K,
+                                  int splits, int raster, int group_m, hipStream_t stream) {
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const long long grid = (long long)tiles_m * tiles_n * splits;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL || splits < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(
+        (gemm_v3_kernel<BM, BN, BK, WM, WN, STAGES, LDW, SPREAD, 16, DT, ACT_NONE, TB, true>),
+        dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream, (const uint16_t *)A, (const uint16_t *)B,
+        (const uint16_t *)nullptr, (uint16_t *)nullptr, M, N, K, tiles_m, tiles_n, raster,
+        group_m < 1 ? 1 : group_m, splits, part);
     return hipGetLastError();
 }
 

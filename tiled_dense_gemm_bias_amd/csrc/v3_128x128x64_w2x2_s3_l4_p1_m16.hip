@@ -1,5 +1,6 @@
 // Interleaved direct-to-LDS kernel instances: 128x128x64 tile, 2x2 waves,
-// 3 LDS stages, 4 loader waves, loads spread over 1 MFMA step(s), 16x16x32 MFMAs.
+// 3 LDS stages, 4 loader waves, loads spread over 1 MFMA step(s), 16x16x32 MFMAs;
+// also the split-K first pass.
 #include "gba_registry.hpp"
 
-GBA_V3_SCHEDULE_ENTRY_TB(i_128x128x64_w2x2_s3_l4_p1_m16, 128, 128, 64, 2, 2, 3, 4, 1, 8)
+GBA_V3_SCHEDULE_ENTRY_TBP(i_128x128x64_w2x2_s3_l4_p1_m16, 128, 128, 64, 2, 2, 3, 4, 1, 8)
