@@ -1,0 +1,81 @@
+"""The transpose_B, 8-bit and split-K entry points captured into one HIP graph.
+
+None of them allocates, copies, fills or synchronises, so a caller can capture
+them. Replays, with eager work and device synchronisation between them and the
+captured inputs overwritten, must match eager calls bitwise.
+"""
+import numpy as np
+import pytest
+
+import synth
+import tiled_dense_gemm_bias_amd as gba
+from tests.gpu_util import empty, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def test_new_entry_points_replay_like_eager():
+    import torch
+    # transpose_B, bf16, 520 x 776 x 328
+    A1 = [synth.random_bits((520, 328), "bf16", s) for s in (1, 2)]
+    W1 = synth.random_bits((776, 328), "bf16", 3)
+    b1 = synth.random_bits((776,), "bf16", 4)
+    # 8-bit, 600 x 520 x 512
+    w8 = synth.Fp8Workload("g", 600, 520, 512, "e4m3", "f16", "gelu", True, 5)
+    A8a, W8, b8, sc = synth.make_inputs_fp8(w8)
+    A8b = synth.make_inputs_fp8(synth.Fp8Workload("g", 600, 520, 512, "e4m3", "f16", "gelu",
+                                                  True, 6))[0]
+    # split-K, f16, 256 x 384 x 4096
+    A3 = [synth.random_bits((256, 4096), "f16", s) for s in (7, 8)]
+    B3 = synth.random_bits((4096, 384), "f16", 9, scale=1 / 64)
+    b3 = synth.random_bits((384,), "f16", 10)
+    nb = gba.workspace_size(256, 384, 4096, "softplus", "f16")
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    a1 = [to_dev(x, "bf16") for x in A1]
+    a8 = [torch.from_numpy(x).cuda() for x in (A8a, A8b)]
+    a3 = [to_dev(x, "f16") for x in A3]
+    w1, bb1 = to_dev(W1, "bf16"), to_dev(b1, "bf16")
+    w8, bb8 = torch.from_numpy(W8).cuda(), to_dev(b8, "f16")
+    bm3, bb3 = to_dev(B3, "f16"), to_dev(b3, "f16")
+
+    def run_all(x1, x8, x3, c1, c8, c3):
+        gba.gemm_bias_act(x1, w1, bb1, c1, "gelu_tanh", transpose_b=True)
+        gba.gemm_bias_act_fp8(x8, w8, bb8, c8, sc, "gelu", "e4m3")
+        gba.gemm_bias_act(x3, bm3, bb3, c3, "softplus", workspace=ws)
+
+    refs = []
+    for i in range(2):
+        outs = (empty((520, 776), "bf16"), empty((600, 520), "f16"), empty((256, 384), "f16"))
+        run_all(a1[i], a8[i], a3[i], *outs)
+        refs.append(outs)
+    torch.cuda.synchronize()
+
+    src = (a1[0].clone(), a8[0].clone(), a3[0].clone())
+    outs = (empty((520, 776), "bf16"), empty((600, 520), "f16"), empty((256, 384), "f16"))
+    graph = torch.cuda.CUDAGraph()
+    say("graph capture: transpose_B, 8-bit, split-K")
+    with torch.cuda.graph(graph):
+        run_all(*src, *outs)
+    torch.cuda.synchronize()
+    for r in range(4):
+        i = r % 2
+        src[0].copy_(a1[i])
+        src[1].copy_(a8[i])
+        src[2].copy_(a3[i])
+        for o in outs:
+            o.fill_(0.0)
+        ws.fill_(255)   # the workspace carries nothing between calls
+        say("graph replay", r)
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, ref in zip(outs, refs[i]):
+            assert torch.equal(o.view(torch.int16), ref.view(torch.int16)), r
