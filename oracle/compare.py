@@ -52,11 +52,19 @@ def rel_frobenius(C: np.ndarray, R: np.ndarray) -> float:
     return float(num / den) if den > 0 else float(num)
 
 
-def check(C, R, K: int, dtype: str, act: int = 0, S=None) -> dict:
+# Accumulation coefficient of the stricter gate for 8-bit inputs: the 8-bit
+# matrix instruction's internal summation is not published; measured error per
+# unit of sum |a w scale| stays below 8.1e-6 at K <= 4096, so the gate is 2^-14.
+FP8_SUM_REL = 2.0 ** -14
+
+
+def check(C, R, K: int, dtype: str, act: int = 0, S=None, sum_rel=None) -> dict:
     """Compare device output C (float64 values) against oracle R.
 
     Returns a report dict; report["ok"] is the official verdict and
-    report["strict_ok"] the stricter gate (only when S is given).
+    report["strict_ok"] the stricter gate (only when S is given). sum_rel is
+    the gate's accumulation coefficient per unit of S; the default is the fp32
+    summation bound 2 sqrt(K+1) 2^-24.
     """
     C = np.asarray(C, dtype=np.float64)
     R = np.asarray(R, dtype=np.float64)
@@ -77,7 +85,8 @@ def check(C, R, K: int, dtype: str, act: int = 0, S=None) -> dict:
     rep["ok"] = finite and rf <= REL_FRO_TOL and rep["elem_violations"] == 0
     if S is not None:
         L = ACT_LIPSCHITZ[int(act)]
-        strict = ulp_out(R, dtype) + L * 2.0 * math.sqrt(K + 1) * 2.0 ** -24 * np.asarray(S) + 2.0 ** -20
+        rel = 2.0 * math.sqrt(K + 1) * 2.0 ** -24 if sum_rel is None else sum_rel
+        strict = ulp_out(R, dtype) + L * rel * np.asarray(S) + 2.0 ** -20
         bad = err > strict
         rep["strict_violations"] = int(np.count_nonzero(bad))
         if rep["strict_violations"]:

@@ -94,6 +94,10 @@ WORKLOADS = {
     # LLM-MLP shape, bf16: A ~ N(0,1), B ~ N(0,1/K), bias ~ N(0,0.02), erf-GELU.
     "c5_gelu": Workload("c5_gelu", 16384, 14336, 4096, "bf16", "gelu", True, 5,
                         b_std=1 / math.sqrt(4096), bias_std=math.sqrt(0.02)),
+    # The same MLP's down projection for a batch of 128 tokens: few output tiles,
+    # deep K (the split-K case); C5's distributions with K = 14336, bias, no act.
+    "mlp_down_m128": Workload("mlp_down_m128", 128, 4096, 14336, "bf16", "none", True, 6,
+                              b_std=1 / math.sqrt(14336), bias_std=math.sqrt(0.02)),
 }
 
 

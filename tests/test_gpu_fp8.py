@@ -21,9 +21,7 @@ pytestmark = pytest.mark.gpu
 
 ACTS = ["none", "relu", "sigmoid", "gelu", "softplus", "gelu_tanh"]
 
-# Largest |C - R| / sum_k |A W scale| measured over the random cases; the gate
-# below allows it with margin on top of the output rounding.
-FP8_SUM_REL = 2.0 ** -14
+FP8_SUM_REL = compare.FP8_SUM_REL
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -68,16 +66,14 @@ def check(A, W, bias, scale, act, fmt, dtype, got, rows=None, report=None):
     R, S = oracle.gemm_bias_act_fp8(A, W, bias, scale, act, fmt, dtype, rows=rows,
                                     with_abs=True, nthreads=16)
     C = oracle.decode(got if rows is None else got[rows], dtype)
-    rep = compare.check(C, R, K=A.shape[1], dtype=dtype, act=oracle.ACTS[act])
-    assert rep["ok"], rep
+    rep = compare.check(C, R, K=A.shape[1], dtype=dtype, act=oracle.ACTS[act], S=S,
+                        sum_rel=FP8_SUM_REL)
     err = np.abs(C - R)
-    L = compare.ACT_LIPSCHITZ[oracle.ACTS[act]]
-    gate = compare.ulp_out(R, dtype) + L * FP8_SUM_REL * S + 2.0 ** -20
     rel = float((np.maximum(err - compare.ulp_out(R, dtype), 0) / np.maximum(S, 1e-30)).max())
     say("fp8 max (|C-R| - ulp) / S = %.3g" % rel, "rel_fro %.3g" % rep["rel_frobenius"])
     if report is not None:
         report.append(rel)
-    assert np.all(err <= gate), rel
+    assert rep["ok"] and rep["strict_ok"], rep
     return rep
 
 
