@@ -31,6 +31,7 @@ extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p2_m16;
 extern const ScheduleEntry i_256x128x64_w2x2_s3_l4_p1_m16;
 extern const ScheduleEntry i_128x256x64_w2x2_s3_l4_p1_m16;
 extern const ScheduleEntry i_128x128x64_w2x2_s3_l4_p1_m16;
+extern const ScheduleEntry i_128x128x64_w2x2_s4_l4_p1_m16;
 extern const ScheduleEntry p_256x256x64_w2x2;
 extern const F8LaunchFn f8_e4m3[2][kNumActs];
 extern const F8LaunchFn f8_e5m2[2][kNumActs];
@@ -44,7 +45,7 @@ const ScheduleEntry *const kTable[] = {
     // interleaved direct-to-LDS kernels with 16x16x32 MFMAs (the default family)
     &gba::i_256x256x64_w2x2_s2_l4_p1_m16, &gba::i_256x256x64_w2x2_s2_l4_p2_m16,
     &gba::i_256x128x64_w2x2_s3_l4_p1_m16, &gba::i_128x256x64_w2x2_s3_l4_p1_m16,
-    &gba::i_128x128x64_w2x2_s3_l4_p1_m16,
+    &gba::i_128x128x64_w2x2_s3_l4_p1_m16, &gba::i_128x128x64_w2x2_s4_l4_p1_m16,
     // persistent version of the first: one workgroup per CU walks its tiles
     &gba::p_256x256x64_w2x2,
     // the same with 32x32x16 MFMAs
@@ -196,7 +197,7 @@ gba_schedule heuristic(int64_t M, int64_t N, int cus) {
     else if (tiles(256, 128) >= want)
         e = M >= N ? &gba::i_256x128x64_w2x2_s3_l4_p1_m16 : &gba::i_128x256x64_w2x2_s3_l4_p1_m16;
     else
-        e = &gba::i_128x128x64_w2x2_s3_l4_p1_m16;
+        e = &gba::i_128x128x64_w2x2_s4_l4_p1_m16;   // 4 stages: 10-20 % faster than 3 here
     return e->sched;
 }
 
