@@ -254,7 +254,13 @@ def main(argv=None) -> int:
     if fp8:
         sched = {"kernel": "f8", "fmt": w.fmt, "bm": 256, "bn": 256, "bk": 128, "wm": 2, "wn": 2,
                  "stages": 2, "raster": 1, "group_m": 4}
-        step = gba.bind_gemm_bias_act_fp8(a_t, b_t, bias_t, c_t, scale, w.act, w.fmt)
+        ws_t = None
+        if a.workspace:
+            nb = gba.workspace_size(w.M, w.N, w.K, w.act, w.dtype, fp8=True)
+            ws_t = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+            sched = dict(sched, splits_workspace_bytes=nb)
+        step = gba.bind_gemm_bias_act_fp8(a_t, b_t, bias_t, c_t, scale, w.act, w.fmt,
+                                          workspace=ws_t)
     else:
         sched = gba.get_schedule(w.M, w.N, w.K, w.act, w.dtype, transpose_b=tb)
         ws_t = None

@@ -136,8 +136,11 @@ int gemm_bias_act_nt(const void *A, const void *W, const void *bias, void *C, in
 /* C = A.W^T rounded to `dtype`, W: [N,K] (gemm with transpose_B). */
 int gemm_nt(const void *A, const void *W, void *C, int64_t M, int64_t N, int64_t K, int dtype);
 
-/* gemm_bias_act_ex flags. */
-enum { GBA_TRANSPOSE_B = 1 /* B is W, stored [N,K], as in gemm_bias_act_nt */ };
+/* gemm_bias_act_ex / gba_workspace_size flags. */
+enum {
+    GBA_TRANSPOSE_B = 1, /* B is W, stored [N,K], as in gemm_bias_act_nt */
+    GBA_INPUT_FP8 = 2    /* gba_workspace_size only: for gemm_bias_act_fp8_ex */
+};
 
 /* gemm_bias_act (or, with GBA_TRANSPOSE_B, gemm_bias_act_nt) with an optional
  * caller-owned device workspace for split-K. When the chosen schedule's tiles
@@ -158,8 +161,8 @@ int gemm_bias_act_ex(const void *A, const void *B, const void *bias, void *C, in
                      int64_t N, int64_t K, int act, int dtype, int flags, void *workspace,
                      size_t workspace_bytes);
 
-/* Workspace bytes gemm_bias_act_ex would use for these arguments (0 if it would
- * not split), written to *bytes. */
+/* Workspace bytes gemm_bias_act_ex (with GBA_INPUT_FP8: gemm_bias_act_fp8_ex)
+ * would use for these arguments (0 if it would not split), written to *bytes. */
 int gba_workspace_size(int64_t M, int64_t N, int64_t K, int act, int dtype, int flags,
                        size_t *bytes);
 
@@ -183,6 +186,16 @@ typedef enum { GBA_FP8_E4M3 = 0, GBA_FP8_E5M2 = 1 } gba_fp8_format;
  * apply. Other rules as gemm_bias_act. */
 int gemm_bias_act_fp8_nt(const void *A, const void *W, const void *bias, void *C, int64_t M,
                          int64_t N, int64_t K, float scale, int act, int fmt, int dtype);
+
+/* gemm_bias_act_fp8_nt with an optional split-K workspace, as gemm_bias_act_ex:
+ * when the 256x256 tiles leave compute units idle and K is deep enough (e.g.
+ * 128 x 4096 x 14336: 16 tiles for 256 CUs), the first pass writes
+ * scale * partial sums of K ranges ([S][M][N] fp32) and the second adds them in
+ * split order, then bias, act and rounding. Size from gba_workspace_size with
+ * GBA_INPUT_FP8; NULL or smaller: the one-kernel path. */
+int gemm_bias_act_fp8_ex(const void *A, const void *W, const void *bias, void *C, int64_t M,
+                         int64_t N, int64_t K, float scale, int act, int fmt, int dtype,
+                         void *workspace, size_t workspace_bytes);
 
 /* Stream for this thread's later calls (a hipStream_t); NULL = default stream. */
 int gba_set_stream(void *hip_stream);

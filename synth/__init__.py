@@ -143,6 +143,10 @@ FP8_WORKLOADS = {
                           a_std=1 / math.sqrt(2), b_std=1 / math.sqrt(2)),
     "c5_fp8": Fp8Workload("c5_fp8", 16384, 14336, 4096, "e4m3", "bf16", "gelu", True, 5,
                           b_std=1 / math.sqrt(4096), bias_std=math.sqrt(0.02)),
+    # mlp_down_m128 with E4M3 inputs (the 8-bit split-K case).
+    "mlp_down_m128_fp8": Fp8Workload("mlp_down_m128_fp8", 128, 4096, 14336, "e4m3", "bf16",
+                                     "none", True, 6, b_std=1 / math.sqrt(14336),
+                                     bias_std=math.sqrt(0.02)),
 }
 
 

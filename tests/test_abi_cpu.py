@@ -131,7 +131,7 @@ def test_ex_and_workspace_argument_errors_precede_device_use(lib):
     assert ex(ws=P16 * 200 + 8, nb=1 << 20) == ERR_ALIGN
     assert ex(ws=P16 * 64 + 256, nb=1 << 20) == ERR_ALIAS   # overlaps C
     size = ctypes.c_size_t(123)
-    assert lib.gba_workspace_size(64, 64, 64, 0, 0, 2, ctypes.byref(size)) == ERR_SHAPE
+    assert lib.gba_workspace_size(64, 64, 64, 0, 0, 4, ctypes.byref(size)) == ERR_SHAPE
     assert lib.gba_workspace_size(-1, 64, 64, 0, 0, 0, ctypes.byref(size)) == ERR_SHAPE
     assert lib.gba_workspace_size(0, 64, 64, 0, 0, 0, ctypes.byref(size)) == OK and size.value == 0
     assert lib.gba_workspace_size(64, 64, 64, 0, 0, 0, None) == ERR_NULL

@@ -163,3 +163,44 @@ def test_float8_tensors_and_argument_errors():
     with pytest.raises(gba.GbaError) as e:   # non-finite scale
         gba.gemm_bias_act_fp8(a, w, None, c, float("nan"), "none")
     assert e.value.status == 2
+
+
+FP8_SPLIT_SHAPES = [(128, 1024, 8192), (200, 520, 4112), (300, 264, 2064)]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("shape", FP8_SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_split_k_exact_integer_bitwise(shape, fmt):
+    import torch
+    M, N, K = shape
+    A, W, bias = int_inputs(M, N, K, fmt, "bf16", seed=M + N + K)
+    nb = gba.workspace_size(M, N, K, "relu", "bf16", fp8=True)
+    assert nb > 0, "this shape is expected to split"
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    want = oracle.encode(oracle.gemm_bias_act_fp8(A, W, bias, 0.5, "relu", fmt, "bf16",
+                                                  nthreads=16), "bf16")
+    c = empty((M, N), "bf16", fill_bits=0x7E00)
+    say("fp8 split exact", shape, fmt, nb)
+    gba.gemm_bias_act_fp8(dev8(A), dev8(W), dev16(bias, "bf16"), c, 0.5, "relu", fmt, workspace=ws)
+    torch.cuda.synchronize()
+    got = to_bits(c)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, "%d mismatches, first %s" % (len(bad), bad[:3].tolist())
+    assert np.array_equal(got, run_fp8(A, W, bias, 0.5, "relu", fmt, "bf16"))
+
+
+@pytest.mark.parametrize("act", ["none", "gelu", "softplus"])
+def test_split_k_random(act):
+    import torch
+    w = synth.Fp8Workload("t", 128, 1024, 8192, "e4m3", "bf16", act, True, 12,
+                          b_std=1 / np.sqrt(8192), bias_std=np.sqrt(0.02))
+    A, W, bias, scale = synth.make_inputs_fp8(w)
+    nb = gba.workspace_size(w.M, w.N, w.K, act, "bf16", fp8=True)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    c = empty((w.M, w.N), "bf16", fill_bits=0x7E00)
+    say("fp8 split random", act)
+    gba.gemm_bias_act_fp8(dev8(A), dev8(W), dev16(bias, "bf16"), c, scale, act, "e4m3",
+                          workspace=ws)
+    torch.cuda.synchronize()
+    check(A, W, bias, scale, act, "e4m3", "bf16", to_bits(c))
+    assert gba.workspace_size(4096, 4096, 4096, "gelu", "f16", fp8=True) == 0

@@ -69,6 +69,8 @@ def _lib():
             "gemm_nt": [p, p, p, i64, i64, i64, ci],
             "gemm_bias_act_fp8_nt": [p, p, p, p, i64, i64, i64, ctypes.c_float, ci, ci, ci],
             "gemm_bias_act_ex": [p, p, p, p, i64, i64, i64, ci, ci, ci, p, ctypes.c_size_t],
+            "gemm_bias_act_fp8_ex": [p, p, p, p, i64, i64, i64, ctypes.c_float, ci, ci, ci, p,
+                                     ctypes.c_size_t],
             "gba_workspace_size": [i64, i64, i64, ci, ci, ci, ctypes.POINTER(ctypes.c_size_t)],
             "bias_act": [p, p, p, i64, i64, ci, ci],
             "gba_set_stream": [p],
@@ -210,11 +212,17 @@ def gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False, workspace=None):
     return c
 
 
-def workspace_size(M: int, N: int, K: int, act="gelu", dtype="f16", transpose_b=False) -> int:
-    """Bytes of split-K workspace gemm_bias_act would use for this shape (0: no split)."""
+INPUT_FP8 = 2
+
+
+def workspace_size(M: int, N: int, K: int, act="gelu", dtype="f16", transpose_b=False,
+                   fp8=False) -> int:
+    """Bytes of split-K workspace gemm_bias_act (gemm_bias_act_fp8 with fp8) would
+    use for this shape (0: no split)."""
     out = ctypes.c_size_t()
+    flags = (TRANSPOSE_B if transpose_b else 0) | (INPUT_FP8 if fp8 else 0)
     st = _lib().gba_workspace_size(M, N, K, _act(act), 0 if dtype in ("f16", "float16") else 1,
-                                   TRANSPOSE_B if transpose_b else 0, ctypes.byref(out))
+                                   flags, ctypes.byref(out))
     if st != 0:
         raise GbaError(st, "gba_workspace_size")
     return int(out.value)
@@ -267,12 +275,14 @@ def _fp8_code(t, fmt) -> int:
     return FP8_FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
 
 
-def gemm_bias_act_fp8(a, w, bias, c, scale=1.0, act="gelu", fmt=None):
+def gemm_bias_act_fp8(a, w, bias, c, scale=1.0, act="gelu", fmt=None, workspace=None):
     """c[M,N] = act(scale * a[M,K] @ w[N,K].T + bias[N]) with 8-bit a and w.
 
     a, w: float8_e4m3fn / float8_e5m2 tensors (or uint8 bit patterns with fmt
     "e4m3" / "e5m2"), w stored [N,K]; bias (or None) and c: float16 or bfloat16.
-    scale: the fp32 dequantization factor of the product. Returns c."""
+    scale: the fp32 dequantization factor of the product. workspace: optional
+    device tensor of workspace_size(..., fp8=True) bytes enabling split-K.
+    Returns c."""
     dev = _check_dev(a, w, bias, c)
     fa, fw = _fp8_code(a, fmt), _fp8_code(w, fmt)
     if fa != fw:
@@ -285,12 +295,18 @@ def gemm_bias_act_fp8(a, w, bias, c, scale=1.0, act="gelu", fmt=None):
     if K2 != K or tuple(c.shape) != (M, N) or (bias is not None and tuple(bias.shape) != (N,)):
         raise ValueError("shape mismatch: a%s w%s c%s" % (tuple(a.shape), tuple(w.shape),
                                                           tuple(c.shape)))
+    if workspace is not None:
+        _check_dev(workspace)
+        ws, nb = _ws_args(workspace)
+        _call("gemm_bias_act_fp8_ex", dev, _ptr(a), _ptr(w), _ptr(bias), _ptr(c), M, N, K,
+              float(scale), _act(act), fa, dt, ws, nb)
+        return c
     _call("gemm_bias_act_fp8_nt", dev, _ptr(a), _ptr(w), _ptr(bias), _ptr(c), M, N, K,
           float(scale), _act(act), fa, dt)
     return c
 
 
-def bind_gemm_bias_act_fp8(a, w, bias, c, scale=1.0, act="gelu", fmt=None):
+def bind_gemm_bias_act_fp8(a, w, bias, c, scale=1.0, act="gelu", fmt=None, workspace=None):
     """bind_gemm_bias_act for the 8-bit-input call (same checks as gemm_bias_act_fp8)."""
     dev = _check_dev(a, w, bias, c)
     fa = _fp8_code(a, fmt)
@@ -308,6 +324,10 @@ def bind_gemm_bias_act_fp8(a, w, bias, c, scale=1.0, act="gelu", fmt=None):
     lib.gba_set_stream(ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
     args = (_ptr(a), _ptr(w), _ptr(bias), _ptr(c), M, N, K, float(scale), _act(act), fa, dt)
     fn = lib.gemm_bias_act_fp8_nt
+    if workspace is not None:
+        _check_dev(workspace)
+        args = args + _ws_args(workspace)
+        fn = lib.gemm_bias_act_fp8_ex
 
     def launch():
         st = fn(*args)

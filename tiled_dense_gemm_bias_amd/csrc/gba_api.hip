@@ -35,6 +35,8 @@ extern const ScheduleEntry i_128x128x64_w2x2_s4_l4_p1_m16;
 extern const ScheduleEntry p_256x256x64_w2x2;
 extern const F8LaunchFn f8_e4m3[2][kNumActs];
 extern const F8LaunchFn f8_e5m2[2][kNumActs];
+extern const F8PartialLaunchFn f8_e4m3_part;
+extern const F8PartialLaunchFn f8_e5m2_part;
 }  // namespace gba
 
 namespace {
@@ -496,6 +498,79 @@ const BiasActFn kBiasAct[2][gba::kNumActs] = {
      launch_bias_act_t<1, 4>, launch_bias_act_t<1, 5>},
 };
 
+// Split factor of the 8-bit kernel (256x256 tiles, 128-deep slices): as
+// split_count, with the 8-bit slice time (~1.8 us per 256x256x128 slice).
+int split_count_fp8(int64_t M, int64_t N, int64_t K, int cus) {
+    if (K <= 0) return 1;
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t nk = (K + 127) / 128;
+    int64_t smax = tiles > 0 ? cus / tiles : 1;
+    smax = std::min<int64_t>(smax, nk / 2);
+    smax = std::min<int64_t>(smax, 16);
+    const double t_slice = 1.8e-6, bw = 4.0e12, t_fixed = 5.0e-6;
+    const double whole = std::max<int64_t>(nk, 2) * t_slice;
+    int best = 1;
+    double best_t = whole;
+    for (int64_t S = 2; S <= smax; ++S) {
+        const double t = ((nk + S - 1) / S) * t_slice + 2.0 * S * (double)M * N * 4.0 / bw + t_fixed;
+        if (t < best_t) {
+            best_t = t;
+            best = (int)S;
+        }
+    }
+    return best_t < 0.85 * whole ? best : 1;
+}
+
+int fp8_common(const void *A, const void *W, const void *bias, void *C, int64_t M, int64_t N,
+               int64_t K, float scale, int act, int fmt, int dtype, void *ws, size_t ws_bytes) {
+    int s = check_enums(act, dtype);
+    if (s) return s;
+    if (fmt != GBA_FP8_E4M3 && fmt != GBA_FP8_E5M2) return GBA_ERR_DTYPE;
+    if (M < 0 || N < 0 || K < 0) return GBA_ERR_SHAPE;
+    if (M > 0x7fffffffLL || N > (1LL << 23) || K > (1LL << 21)) return GBA_ERR_SHAPE;
+    if (!(scale == scale) || scale - scale != 0.0f) return GBA_ERR_SHAPE;   // NaN or inf
+    if (M == 0 || N == 0) return GBA_OK;
+    if (!C) return GBA_ERR_NULL;
+    if (K > 0 && (!A || !W)) return GBA_ERR_NULL;
+    if ((K % 16) || (N % 8)) return GBA_ERR_ALIGN;
+    if (!aligned16(C) || (A && !aligned16(A)) || (W && !aligned16(W)) || (bias && !aligned16(bias)))
+        return GBA_ERR_ALIGN;
+    const size_t cb = (size_t)M * N * 2;
+    if (overlaps(C, cb, A, (size_t)M * K) || overlaps(C, cb, W, (size_t)N * K) ||
+        overlaps(C, cb, bias, (size_t)N * 2))
+        return GBA_ERR_ALIAS;
+    if (ws) {
+        if (!aligned16(ws)) return GBA_ERR_ALIGN;
+        if (overlaps(ws, ws_bytes, A, (size_t)M * K) || overlaps(ws, ws_bytes, W, (size_t)N * K) ||
+            overlaps(ws, ws_bytes, bias, (size_t)N * 2) || overlaps(ws, ws_bytes, C, cb))
+            return GBA_ERR_ALIAS;
+    }
+    const DeviceInfo *d;
+    s = current_device(&d);
+    if (s) return s;
+    if (ws) {
+        const int S = split_count_fp8(M, N, K, d->cus);
+        if (S > 1 && ws_bytes >= (size_t)S * (size_t)M * (size_t)N * 4u) {
+            if (log_enabled())
+                fprintf(stderr, "[gba] fp8 M=%lld N=%lld K=%lld -> split-K %d\n", (long long)M,
+                        (long long)N, (long long)K, S);
+            const gba::F8PartialLaunchFn pf =
+                fmt == GBA_FP8_E4M3 ? gba::f8_e4m3_part : gba::f8_e5m2_part;
+            hipError_t e = pf(A, W, (float *)ws, (int)M, (int)N, (int)K, scale, S, 1, 4, t_stream);
+            if (e != hipSuccess) return hip_fail(e);
+            e = kReduce[dtype][act]((const float *)ws, S, bias, C, (int)M, (int)N, t_stream);
+            return e == hipSuccess ? GBA_OK : hip_fail(e);
+        }
+    }
+    const gba::F8LaunchFn f = (fmt == GBA_FP8_E4M3 ? gba::f8_e4m3 : gba::f8_e5m2)[dtype][act];
+    if (log_enabled())
+        fprintf(stderr, "[gba] fp8 M=%lld N=%lld K=%lld act=%s fmt=%s out=%s scale=%g\n",
+                (long long)M, (long long)N, (long long)K, kActName[act],
+                fmt == GBA_FP8_E4M3 ? "e4m3" : "e5m2", kDtName[dtype], (double)scale);
+    hipError_t e = f(A, W, bias, C, (int)M, (int)N, (int)K, scale, 1, 4, t_stream);
+    return e == hipSuccess ? GBA_OK : hip_fail(e);
+}
+
 }  // namespace
 
 // =================================================================== C ABI ===
@@ -600,7 +675,7 @@ int gba_workspace_size(int64_t M, int64_t N, int64_t K, int act, int dtype, int 
                        size_t *bytes) {
     if (!bytes) return GBA_ERR_NULL;
     *bytes = 0;
-    if (flags & ~GBA_TRANSPOSE_B) return GBA_ERR_SHAPE;
+    if (flags & ~(GBA_TRANSPOSE_B | GBA_INPUT_FP8)) return GBA_ERR_SHAPE;
     int s = check_enums(act, dtype);
     if (s) return s;
     if (M < 0 || N < 0 || K < 0) return GBA_ERR_SHAPE;
@@ -608,6 +683,11 @@ int gba_workspace_size(int64_t M, int64_t N, int64_t K, int act, int dtype, int 
     const DeviceInfo *d;
     s = current_device(&d);
     if (s) return s;
+    if (flags & GBA_INPUT_FP8) {
+        const int S8 = split_count_fp8(M, N, K, d->cus);
+        if (S8 > 1) *bytes = (size_t)S8 * (size_t)M * (size_t)N * 4u;
+        return GBA_OK;
+    }
     const bool tb = (flags & GBA_TRANSPOSE_B) != 0;
     const char *why;
     const gba_schedule sch = choose(*d, M, N, K, act, dtype, tb, &why);
@@ -635,34 +715,17 @@ int bias_act(const void *X, const void *bias, void *Y, int64_t M, int64_t N, int
     return e == hipSuccess ? GBA_OK : hip_fail(e);
 }
 
+
 int gemm_bias_act_fp8_nt(const void *A, const void *W, const void *bias, void *C, int64_t M,
                          int64_t N, int64_t K, float scale, int act, int fmt, int dtype) {
-    int s = check_enums(act, dtype);
-    if (s) return s;
-    if (fmt != GBA_FP8_E4M3 && fmt != GBA_FP8_E5M2) return GBA_ERR_DTYPE;
-    if (M < 0 || N < 0 || K < 0) return GBA_ERR_SHAPE;
-    if (M > 0x7fffffffLL || N > (1LL << 23) || K > (1LL << 21)) return GBA_ERR_SHAPE;
-    if (!(scale == scale) || scale - scale != 0.0f) return GBA_ERR_SHAPE;   // NaN or inf
-    if (M == 0 || N == 0) return GBA_OK;
-    if (!C) return GBA_ERR_NULL;
-    if (K > 0 && (!A || !W)) return GBA_ERR_NULL;
-    if ((K % 16) || (N % 8)) return GBA_ERR_ALIGN;
-    if (!aligned16(C) || (A && !aligned16(A)) || (W && !aligned16(W)) || (bias && !aligned16(bias)))
-        return GBA_ERR_ALIGN;
-    const size_t cb = (size_t)M * N * 2;
-    if (overlaps(C, cb, A, (size_t)M * K) || overlaps(C, cb, W, (size_t)N * K) ||
-        overlaps(C, cb, bias, (size_t)N * 2))
-        return GBA_ERR_ALIAS;
-    const DeviceInfo *d;
-    s = current_device(&d);
-    if (s) return s;
-    const gba::F8LaunchFn f = (fmt == GBA_FP8_E4M3 ? gba::f8_e4m3 : gba::f8_e5m2)[dtype][act];
-    if (log_enabled())
-        fprintf(stderr, "[gba] fp8 M=%lld N=%lld K=%lld act=%s fmt=%s out=%s scale=%g\n",
-                (long long)M, (long long)N, (long long)K, kActName[act],
-                fmt == GBA_FP8_E4M3 ? "e4m3" : "e5m2", kDtName[dtype], (double)scale);
-    hipError_t e = f(A, W, bias, C, (int)M, (int)N, (int)K, scale, 1, 4, t_stream);
-    return e == hipSuccess ? GBA_OK : hip_fail(e);
+    return fp8_common(A, W, bias, C, M, N, K, scale, act, fmt, dtype, nullptr, 0);
+}
+
+int gemm_bias_act_fp8_ex(const void *A, const void *W, const void *bias, void *C, int64_t M,
+                         int64_t N, int64_t K, float scale, int act, int fmt, int dtype,
+                         void *workspace, size_t workspace_bytes) {
+    return fp8_common(A, W, bias, C, M, N, K, scale, act, fmt, dtype, workspace,
+                      workspace ? workspace_bytes : 0);
 }
 
 int gba_epilogue_probe(const float *z, float *y, int64_t n, int act) {

@@ -282,12 +282,19 @@ struct ScheduleEntry {
 namespace gba {
 using F8LaunchFn = hipError_t (*)(const void *, const void *, const void *, void *, int, int, int,
                                   float, int, int, hipStream_t);
+// Split-K first pass: (A, W, part, M, N, K, scale, splits, raster, group_m, stream).
+using F8PartialLaunchFn = hipError_t (*)(const void *, const void *, float *, int, int, int, float,
+                                         int, int, int, hipStream_t);
 }  // namespace gba
 
 #define GBA_F8_INST_(FMT, DT, ACT)                                                             \
     template __global__ void gba::gemm_f8_kernel<FMT, DT, ACT>(                                \
         const uint8_t *__restrict__, const uint8_t *__restrict__, const uint16_t *__restrict__, \
-        uint16_t *__restrict__, int, int, int, float, int, int, int, int);
+        uint16_t *__restrict__, int, int, int, float, int, int, int, int, int, float *__restrict__);
+#define GBA_F8P_INST_(FMT)                                                                     \
+    template __global__ void gba::gemm_f8_kernel<FMT, 0, 0, true>(                             \
+        const uint8_t *__restrict__, const uint8_t *__restrict__, const uint16_t *__restrict__, \
+        uint16_t *__restrict__, int, int, int, float, int, int, int, int, int, float *__restrict__);
 
 #define GBA_F8_INSTS_(FMT)                                                                     \
     GBA_F8_INST_(FMT, 0, 0) GBA_F8_INST_(FMT, 0, 1) GBA_F8_INST_(FMT, 0, 2)                    \
@@ -300,14 +307,17 @@ using F8LaunchFn = hipError_t (*)(const void *, const void *, const void *, void
      gba::launch_gemm_f8<FMT, DT, 2>, gba::launch_gemm_f8<FMT, DT, 3>,                         \
      gba::launch_gemm_f8<FMT, DT, 4>, gba::launch_gemm_f8<FMT, DT, 5>}
 
-// Defines gba::NAME[dtype][act] (host pass) for 8-bit format FMT.
+// Defines gba::NAME[dtype][act] and gba::NAME_part (host pass) for 8-bit format FMT.
 #ifdef __HIP_DEVICE_COMPILE__
-#define GBA_F8_ENTRY(NAME, FMT) GBA_F8_INSTS_(FMT)
+#define GBA_F8_ENTRY(NAME, FMT) GBA_F8_INSTS_(FMT) GBA_F8P_INST_(FMT)
 #else
 #define GBA_F8_ENTRY(NAME, FMT)                                                                \
     GBA_F8_INSTS_(FMT)                                                                         \
+    GBA_F8P_INST_(FMT)                                                                         \
     namespace gba {                                                                            \
     extern const F8LaunchFn NAME[2][kNumActs];                                                 \
     const F8LaunchFn NAME[2][kNumActs] = {GBA_F8_LAUNCHERS_(FMT, 0), GBA_F8_LAUNCHERS_(FMT, 1)}; \
+    extern const F8PartialLaunchFn NAME##_part;                                                \
+    const F8PartialLaunchFn NAME##_part = gba::launch_gemm_f8_partial<FMT>;                    \
     }
 #endif

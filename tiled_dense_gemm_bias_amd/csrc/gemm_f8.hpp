@@ -24,6 +24,10 @@
 //           the global->LDS loads two slices ahead into the stage just freed.
 // The slice stream runs across a workgroup's tiles as in gemm_v5.hpp: the next
 // tile's first two slices load during the current tile's last steps.
+//
+// PARTIAL (split-K first pass): the work units are (tile, split) pairs; unit
+// (t, s) runs K slices [s nk / S, (s+1) nk / S) of tile t and stores scale * its
+// fp32 sums to part[s][M][N]; splitk_reduce_kernel adds them, then bias, act.
 #pragma once
 
 #include "gemm_v5.hpp"
@@ -78,11 +82,12 @@ __device__ __forceinline__ void hazard_gap() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int FMT, int DT, int ACT>
+template <int FMT, int DT, int ACT, bool PARTIAL = false>
 __global__ void __launch_bounds__(256)
 gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
                const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int M, int N, int K,
-               float scale, int tiles_m, int tiles_n, int raster, int group_m) {
+               float scale, int tiles_m, int tiles_n, int raster, int group_m, int splits,
+               float *__restrict__ part) {
     constexpr int BM = 256, BN = 256, BK = 128;   // BK in values = bytes
     constexpr int NT = 256, BD = 16;
     constexpr int WTM = 128, WTN = 128, FM = 8, FN = 8, HM = FM / 2;
@@ -94,21 +99,31 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
     const int wm = wid >> 1, wn = wid & 1;
-    // At least two slices per tile (the stream below assumes it); for K <= 128
-    // the second is all zeros.
-    const int nk = max((K + BK - 1) / BK, 2);
-    const int T = tiles_m * tiles_n;
+    const int nk_all = (K + BK - 1) / BK;
+    const int tiles = tiles_m * tiles_n;
+    const int T = PARTIAL ? tiles * splits : tiles;   // work units
     const int G = gridDim.x;
     const int wid_s = __builtin_amdgcn_readfirstlane(wid);
     const uint32_t smem_lds = (uint32_t)(uintptr_t)(GBA_LDS void *)smem;
     const int slot = raster ? xcd_remap(blockIdx.x, G) : (int)blockIdx.x;
 
+    // A work unit: its tile, split, and K slices [kt0, kt0 + nkl). It streams
+    // nk = max(nkl, 2) slices (the stream below assumes two); the extra one,
+    // for a single-slice unit, is all zeros.
     struct Tile {
-        int m0, n0;
+        int m0, n0, kt0, nkl, nk, split;
     };
     auto tile_of = [&](int r, Tile &t) -> bool {
-        const int idx = r * G + slot;
+        int idx = r * G + slot;
         if (idx >= T) return false;
+        t.split = 0;
+        if constexpr (PARTIAL) {
+            t.split = idx / tiles;
+            idx -= t.split * tiles;
+        }
+        t.kt0 = PARTIAL ? (int)((long long)t.split * nk_all / splits) : 0;
+        t.nkl = PARTIAL ? (int)((long long)(t.split + 1) * nk_all / splits) - t.kt0 : nk_all;
+        t.nk = max(t.nkl, 2);
         int tm, tn;
         if (raster) {
             grouped_tile(idx, tiles_m, tiles_n, group_m, tm, tn);
@@ -137,8 +152,8 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
     auto slice_dma = [&](const Tile &t, bool live, int kt, int stage) {
         SliceDma d;
         d.la = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(stage * STAGE_BYTES + wid_s * 64 * 16));
-        const bool any = live && kt * BK < K;
-        d.k0 = any ? kt * BK : K;
+        const bool any = live && kt < t.nkl;
+        d.k0 = any ? (t.kt0 + kt) * BK : K;
         const uint32_t rows_a = (uint32_t)min(M - t.m0, BM), rows_w = (uint32_t)min(N - t.n0, BN);
         d.ra = make_rsrc(A + (any ? (size_t)t.m0 * K + d.k0 : 0),
                          any ? rows_a * (uint32_t)K - (uint32_t)d.k0 : 0u);
@@ -211,9 +226,9 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
             }
             wait_vmcnt_lgkm0<0>();
             block_barrier();
-            const bool here = kt + 2 < nk;
+            const bool here = kt + 2 < cur_t.nk;
             const SliceDma dn = slice_dma(here ? cur_t : nxt_t, here || nxt_live,
-                                          here ? kt + 2 : kt + 2 - nk, sc);
+                                          here ? kt + 2 : kt + 2 - cur_t.nk, sc);
             // step 1: rows 4..7; the next slice's A fragments 0..3, each W
             // fragment after its last MFMA here, and the loads two slices ahead
 #pragma unroll
@@ -227,12 +242,27 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
             }
         };
         slice(0, std::true_type{});
-        for (int kt = 1; kt < nk; ++kt) slice(kt, std::false_type{});
+        for (int kt = 1; kt < cur_t.nk; ++kt) slice(kt, std::false_type{});
 
         // Epilogue while the next tile's first slices land: z = scale * acc + bias.
         hazard_gap();   // the last MFMAs' results are complete before they are read
         asm volatile("" ::: "memory");
-        {
+        if constexpr (PARTIAL) {
+            // scale * raw sums, 4 adjacent n of one row per lane, masked at the edges
+            float *const Pt = part + (size_t)cur_t.split * M * N + (size_t)cur_t.m0 * N + cur_t.n0;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int cn = wn * WTN + 4 * tg + fn * BD;
+                if (cur_t.n0 + cn >= N) continue;
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    const int rr = mrow + fm * BD;
+                    if (cur_t.m0 + rr >= M) continue;
+                    *reinterpret_cast<f32x4 *>(Pt + (size_t)rr * N + cn) = acc_value(acc[fn][fm]) * scale;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
             char *const Ct = reinterpret_cast<char *>(C + (size_t)cur_t.m0 * N + cur_t.n0);
             int c0 = wn * WTN + 4 * tg, mr = mrow;
             asm volatile("" : "+v"(mr));
@@ -276,7 +306,7 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
 
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
-        stage0 = (stage0 + nk) & 1;
+        stage0 = (stage0 + cur_t.nk) & 1;
         if (!nxt_live) break;
         cur_t = nxt_t;
     }
@@ -300,7 +330,30 @@ hipError_t launch_gemm_f8(const void *A, const void *W, const void *bias, void *
     hipLaunchKernelGGL((gemm_f8_kernel<FMT, DT, ACT>), dim3((unsigned)grid), dim3(256), 0, stream,
                        (const uint8_t *)A, (const uint8_t *)W, (const uint16_t *)bias,
                        (uint16_t *)C, M, N, K, scale, tiles_m, tiles_n, raster,
-                       group_m < 1 ? 1 : group_m);
+                       group_m < 1 ? 1 : group_m, 1, (float *)nullptr);
+    return hipGetLastError();
+}
+
+// Split-K first pass: tiles x splits work units, one workgroup per CU (or per
+// unit when there are fewer), scale * partial sums into part ([splits][M][N]).
+template <int FMT>
+hipError_t launch_gemm_f8_partial(const void *A, const void *W, float *part, int M, int N, int K,
+                                  float scale, int splits, int raster, int group_m,
+                                  hipStream_t stream) {
+    const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+    const long long units = (long long)tiles_m * tiles_n * splits;
+    if (units <= 0) return hipSuccess;
+    if (units > 0x7fffffffLL || splits < 1) return hipErrorInvalidValue;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int grid = (int)(units < cus ? units : cus);
+    hipLaunchKernelGGL((gemm_f8_kernel<FMT, 0, ACT_NONE, true>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, (const uint8_t *)A, (const uint8_t *)W, (const uint16_t *)nullptr,
+                       (uint16_t *)nullptr, M, N, K, scale, tiles_m, tiles_n, raster,
+                       group_m < 1 ? 1 : group_m, splits, part);
     return hipGetLastError();
 }
 
