@@ -482,7 +482,7 @@ hipError_t launch_bias_act_t(const void *X, const void *bias, void *Y, int M, in
     const int gx = (cpr + 255) / 256;
     // Enough workgroups to keep every CU busy several times over; each thread
     // then walks rows with a 4-row unroll.
-    int gy = (M + 3) / 4;
+    int gy = gba::ceil_div(M, 4);
     const int max_y = std::max(1, 4096 / gx);
     if (gy > max_y) gy = max_y;
     hipLaunchKernelGGL((gba::bias_act_kernel<DT, ACT>), dim3(gx, gy), dim3(256), 0, st,

@@ -45,6 +45,39 @@ constexpr int kNumActs = 6;
 
 constexpr int kNumXcd = 8;
 
+// ceil(x / b) for x up to 2^31 - 1 (x + b - 1 would overflow int there).
+__host__ __device__ constexpr int ceil_div(int x, int b) { return (int)(((long long)x + b - 1) / b); }
+
+// Grids of tile workgroups. HIP caps a grid dimension's work-items (workgroups
+// x threads) below 2^32, so more than 2^16 workgroups are launched as a 2-D grid
+// 2^16 wide. The linear id y * gridDim.x + x is the dispatch order (and what
+// xcd_remap assumes); ids past the last tile do nothing.
+constexpr long long kGridX = 1LL << 16;
+inline dim3 tile_grid(long long n) {
+    return n <= kGridX ? dim3((unsigned)n) : dim3((unsigned)kGridX, (unsigned)((n + kGridX - 1) / kGridX));
+}
+__device__ __forceinline__ int linear_block() { return (int)(blockIdx.y * gridDim.x + blockIdx.x); }
+__device__ __forceinline__ int linear_grid() { return (int)(gridDim.x * gridDim.y); }
+
+// Compute units of the current device for the persistent launchers' grids,
+// queried from the runtime once per device (a launch then costs no query).
+inline hipError_t current_cus(int *cus) {
+    static int cached[64];   // 0: not queried yet
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    int c = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+    if (c <= 0) {
+        e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (c <= 0) return hipErrorInvalidDevice;
+        __atomic_store_n(&cached[dev], c, __ATOMIC_RELAXED);
+    }
+    *cus = c;
+    return hipSuccess;
+}
+
 // ---------------------------------------------------------------- scalars --
 
 template <int DT>
@@ -191,8 +224,9 @@ gemm_bias_act_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict_
 
     int tm, tn;
     {
-        int t = blockIdx.x;
-        if (raster) t = xcd_remap(t, gridDim.x);
+        int t = linear_block();
+        if (raster) t = xcd_remap(t, linear_grid());
+        if (t >= tiles_m * tiles_n) return;   // padding of a 2-D grid
         if (raster) {
             grouped_tile(t, tiles_m, tiles_n, group_m, tm, tn);
         } else {
@@ -349,11 +383,11 @@ gemm_bias_act_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict_
 template <int BM, int BN, int BK, int WM, int WN, int DT, int ACT>
 hipError_t launch_gemm(const void *A, const void *B, const void *bias, void *C, int M, int N,
                        int K, int raster, int group_m, hipStream_t stream) {
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int tiles_m = ceil_div(M, BM), tiles_n = ceil_div(N, BN);
     const long long grid = (long long)tiles_m * tiles_n;
     if (grid <= 0) return hipSuccess;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_bias_act_kernel<BM, BN, BK, WM, WN, DT, ACT>), dim3((unsigned)grid),
+    if (grid > 0x7fffffffLL - kGridX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_bias_act_kernel<BM, BN, BK, WM, WN, DT, ACT>), tile_grid(grid),
                        dim3(WM * WN * 64), 0, stream, (const uint16_t *)A, (const uint16_t *)B,
                        (const uint16_t *)bias, (uint16_t *)C, M, N, K, tiles_m, tiles_n, raster,
                        group_m < 1 ? 1 : group_m);
@@ -388,7 +422,8 @@ bias_act_kernel(const uint16_t *X, const uint16_t *__restrict__ bias, uint16_t *
         for (int e = 0; e < 8; ++e) bv[e] = 0.0f;
     }
     constexpr int U = 4;
-    for (int r0 = blockIdx.y * U; r0 < M; r0 += gridDim.y * U) {
+    // 64-bit row index: r0 + gridDim.y * U may pass 2^31 - 1 on the last step.
+    for (long long r0 = (long long)blockIdx.y * U; r0 < M; r0 += (long long)gridDim.y * U) {
         u32x4 x[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -436,7 +471,7 @@ splitk_reduce_kernel(const float *__restrict__ P, int S, const uint16_t *__restr
         for (int e = 0; e < 8; ++e) bv[e] = 0.0f;
     }
     const size_t plane = (size_t)M * N;
-    for (int r = blockIdx.y; r < M; r += gridDim.y) {
+    for (long long r = blockIdx.y; r < M; r += gridDim.y) {   // 64-bit: see bias_act_kernel
         const float *p = P + (size_t)r * N + chunk * 8;
         f32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
         f32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + 4));

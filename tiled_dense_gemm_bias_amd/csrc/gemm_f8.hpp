@@ -269,7 +269,7 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
             uint32_t lane_off = ((uint32_t)mr * (uint32_t)N + (uint32_t)c0) * 2u;
             uint32_t pitch16 = (uint32_t)N * (2u * BD);
             asm volatile("" : "+v"(lane_off), "+v"(c0), "+s"(pitch16));
-            const bool full = cur_t.m0 + BM <= M && cur_t.n0 + BN <= N;
+            const bool full = M - cur_t.m0 >= BM && N - cur_t.n0 >= BN;   // no m0 + BM: overflows near 2^31
             auto store_all = [&](auto masked) {
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
@@ -317,14 +317,13 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
 template <int FMT, int DT, int ACT>
 hipError_t launch_gemm_f8(const void *A, const void *W, const void *bias, void *C, int M, int N,
                           int K, float scale, int raster, int group_m, hipStream_t stream) {
-    const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+    const int tiles_m = ceil_div(M, 256), tiles_n = ceil_div(N, 256);
     const long long tiles = (long long)tiles_m * tiles_n;
     if (tiles <= 0) return hipSuccess;
-    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    // Tile indices r * G + slot run up to tiles + G - 1: keep them in int.
+    if (tiles > 0x7fffffffLL - 0x10000) return hipErrorInvalidValue;
+    int cus = 0;
+    const hipError_t e = current_cus(&cus);
     if (e != hipSuccess) return e;
     const int grid = (int)(tiles < cus ? tiles : cus);
     hipLaunchKernelGGL((gemm_f8_kernel<FMT, DT, ACT>), dim3((unsigned)grid), dim3(256), 0, stream,
@@ -340,14 +339,12 @@ template <int FMT>
 hipError_t launch_gemm_f8_partial(const void *A, const void *W, float *part, int M, int N, int K,
                                   float scale, int splits, int raster, int group_m,
                                   hipStream_t stream) {
-    const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+    const int tiles_m = ceil_div(M, 256), tiles_n = ceil_div(N, 256);
     const long long units = (long long)tiles_m * tiles_n * splits;
     if (units <= 0) return hipSuccess;
-    if (units > 0x7fffffffLL || splits < 1) return hipErrorInvalidValue;
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (units > 0x7fffffffLL - 0x10000 || splits < 1) return hipErrorInvalidValue;
+    int cus = 0;
+    const hipError_t e = current_cus(&cus);
     if (e != hipSuccess) return e;
     const int grid = (int)(units < cus ? units : cus);
     hipLaunchKernelGGL((gemm_f8_kernel<FMT, 0, ACT_NONE, true>), dim3((unsigned)grid), dim3(256), 0,

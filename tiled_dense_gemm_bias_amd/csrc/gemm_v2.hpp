@@ -98,9 +98,10 @@ gemm_v2_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 
     int tm, tn;
     {
-        int t = blockIdx.x;
+        int t = linear_block();
+        if (raster) t = xcd_remap(t, linear_grid());
+        if (t >= tiles_m * tiles_n) return;   // padding of a 2-D grid
         if (raster) {
-            t = xcd_remap(t, gridDim.x);
             grouped_tile(t, tiles_m, tiles_n, group_m, tm, tn);
         } else {
             tm = t / tiles_n;
@@ -282,11 +283,11 @@ gemm_v2_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int DT, int ACT>
 hipError_t launch_gemm_v2(const void *A, const void *B, const void *bias, void *C, int M, int N,
                           int K, int raster, int group_m, hipStream_t stream) {
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int tiles_m = ceil_div(M, BM), tiles_n = ceil_div(N, BN);
     const long long grid = (long long)tiles_m * tiles_n;
     if (grid <= 0) return hipSuccess;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, BK, WM, WN, STAGES, DT, ACT>), dim3((unsigned)grid),
+    if (grid > 0x7fffffffLL - kGridX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_v2_kernel<BM, BN, BK, WM, WN, STAGES, DT, ACT>), tile_grid(grid),
                        dim3(WM * WN * 64), 0, stream, (const uint16_t *)A, (const uint16_t *)B,
                        (const uint16_t *)bias, (uint16_t *)C, M, N, K, tiles_m, tiles_n, raster,
                        group_m < 1 ? 1 : group_m);

@@ -118,8 +118,9 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     static_assert(!PARTIAL || MS == 16, "split-K is written for 16x16x32 MFMAs");
     int tm, tn, split = 0;
     {
-        int t = blockIdx.x;
-        if (raster) t = xcd_remap(t, gridDim.x);
+        int t = linear_block();
+        if (raster) t = xcd_remap(t, linear_grid());
+        if (t >= tiles_m * tiles_n * splits) return;   // padding of a 2-D grid
         if constexpr (PARTIAL) {
             // units of one split are contiguous, so each XCD walks whole tiles' panels
             split = t / (tiles_m * tiles_n);
@@ -365,7 +366,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         return wn * WTN + fn * BD + (MS == 32 ? i * 8 + lhalf * 4 : 4 * (lane >> 4));
     };
     const uint32_t lane_off = ((uint32_t)mrow * (uint32_t)N + (uint32_t)col0(0, 0)) * 2u;
-    const bool full = m0 + BM <= M && n0 + BN <= N;
+    const bool full = M - m0 >= BM && N - n0 >= BN;   // no m0 + BM: overflows near 2^31
     auto store_all = [&](auto masked) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
@@ -405,12 +406,12 @@ template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREA
           int ACT, bool TB = false>
 hipError_t launch_gemm_v3(const void *A, const void *B, const void *bias, void *C, int M, int N,
                           int K, int raster, int group_m, hipStream_t stream) {
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int tiles_m = ceil_div(M, BM), tiles_n = ceil_div(N, BN);
     const long long grid = (long long)tiles_m * tiles_n;
     if (grid <= 0) return hipSuccess;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (grid > 0x7fffffffLL - kGridX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, BK, WM, WN, STAGES, LDW, SPREAD, MS, DT, ACT, TB>),
-                       dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream, (const uint16_t *)A,
+                       tile_grid(grid), dim3(WM * WN * 64), 0, stream, (const uint16_t *)A,
                        (const uint16_t *)B, (const uint16_t *)bias, (uint16_t *)C, M, N, K, tiles_m,
                        tiles_n, raster, group_m < 1 ? 1 : group_m, 1, (float *)nullptr);
     return hipGetLastError();
@@ -421,13 +422,13 @@ hipError_t launch_gemm_v3(const void *A, const void *B, const void *bias, void *
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int DT, bool TB>
 hipError_t launch_gemm_v3_partial(const void *A, const void *B, float *part, int M, int N, int K,
                                   int splits, int raster, int group_m, hipStream_t stream) {
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int tiles_m = ceil_div(M, BM), tiles_n = ceil_div(N, BN);
     const long long grid = (long long)tiles_m * tiles_n * splits;
     if (grid <= 0) return hipSuccess;
-    if (grid > 0x7fffffffLL || splits < 1) return hipErrorInvalidValue;
+    if (grid > 0x7fffffffLL - kGridX || splits < 1) return hipErrorInvalidValue;
     hipLaunchKernelGGL(
         (gemm_v3_kernel<BM, BN, BK, WM, WN, STAGES, LDW, SPREAD, 16, DT, ACT_NONE, TB, true>),
-        dim3((unsigned)grid), dim3(WM * WN * 64), 0, stream, (const uint16_t *)A, (const uint16_t *)B,
+        tile_grid(grid), dim3(WM * WN * 64), 0, stream, (const uint16_t *)A, (const uint16_t *)B,
         (const uint16_t *)nullptr, (uint16_t *)nullptr, M, N, K, tiles_m, tiles_n, raster,
         group_m < 1 ? 1 : group_m, splits, part);
     return hipGetLastError();

@@ -271,7 +271,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             // bias addresses derived from these are hoisted out of the tile loop
             // and held in registers across the main loop.
             asm volatile("" : "+v"(lane_off), "+v"(c0), "+s"(pitch16));
-            const bool full = cur_t.m0 + BM <= M && cur_t.n0 + BN <= N;
+            const bool full = M - cur_t.m0 >= BM && N - cur_t.n0 >= BN;   // no m0 + BM: overflows near 2^31
             auto store_all = [&](auto masked) {
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
@@ -323,15 +323,14 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 template <int BM, int BN, int WM, int WN, int DT, int ACT, bool TB = false>
 hipError_t launch_gemm_v5(const void *A, const void *B, const void *bias, void *C, int M, int N,
                           int K, int raster, int group_m, hipStream_t stream) {
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int tiles_m = ceil_div(M, BM), tiles_n = ceil_div(N, BN);
     const long long tiles = (long long)tiles_m * tiles_n;
     if (tiles <= 0) return hipSuccess;
-    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    // Tile indices r * G + slot run up to tiles + G - 1: keep them in int.
+    if (tiles > 0x7fffffffLL - 0x10000) return hipErrorInvalidValue;
     if (K <= 64) return hipErrorInvalidValue;   // needs two K slices; see the note above
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0;
+    const hipError_t e = current_cus(&cus);
     if (e != hipSuccess) return e;
     const int grid = (int)(tiles < cus ? tiles : cus);
     hipLaunchKernelGGL((gemm_v5_kernel<BM, BN, WM, WN, DT, ACT, TB>), dim3((unsigned)grid),
