@@ -95,6 +95,10 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
     constexpr int A_LD = BM * 8 / NT, LD = 2 * A_LD;   // 16-byte loads per thread and slice
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+    // A tile's bias, staged in LDS with the tile's first slice (as in the 16-bit
+    // persistent kernel): one 1 KiB slot per wave and per tile parity.
+    __shared__ __attribute__((aligned(1024))) char bias_smem[2 * 4 * 1024];
+    static_assert(2 * STAGE_BYTES + 2 * 4 * 1024 <= 160 * 1024, "LDS ring + bias slots too large");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
@@ -170,6 +174,16 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
             buffer_load_lds16(d.rw, o, d.la + A_BYTES + j * NT * 16);
     };
 
+    // Bias of tile t into this wave's slot of parity p: lanes 0..31 load 16 bytes
+    // each (columns past N read zeros), the rest land zeros; counted in vmcnt.
+    const uint32_t bias_lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(GBA_LDS void *)bias_smem + (uint32_t)(wid_s * 1024));
+    auto bias_dma = [&](const Tile &t, int p) {
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias + t.n0, (uint32_t)min(N - t.n0, BN) * 2u);
+        buffer_load_lds16(rb, lane < BN / 8 ? (uint32_t)lane * 16u : kOobOffset,
+                          bias_lds + (uint32_t)(p * 4 * 1024));
+    };
+
     // Fragment bases: lane l of block f reads row 16 f + l%16 of the wave's
     // rows ((row/2) % 4 = (l/2) % 4), 32-byte pair (l/16) ^ ((l/2) % 4).
     const int tg = lane >> 4, tj = lane & 15;
@@ -189,6 +203,7 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
 
     {
         const SliceDma d0 = slice_dma(cur_t, true, 0, 0), d1 = slice_dma(cur_t, true, 1, 1);
+        if (bias) bias_dma(cur_t, 0);   // lands with slice 0 (waited for below)
 #pragma unroll
         for (int i = 0; i < LD; ++i) dma_one(d0, i, (uint32_t)K);
 #pragma unroll
@@ -229,6 +244,8 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
             const bool here = kt + 2 < cur_t.nk;
             const SliceDma dn = slice_dma(here ? cur_t : nxt_t, here || nxt_live,
                                           here ? kt + 2 : kt + 2 - cur_t.nk, sc);
+            // with the next tile's slice 0, its bias into the other parity's slot
+            if (bias && !here && kt + 2 == cur_t.nk && nxt_live) bias_dma(nxt_t, (r + 1) & 1);
             // step 1: rows 4..7; the next slice's A fragments 0..3, each W
             // fragment after its last MFMA here, and the loads two slices ahead
 #pragma unroll
@@ -270,6 +287,7 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
             uint32_t pitch16 = (uint32_t)N * (2u * BD);
             asm volatile("" : "+v"(lane_off), "+v"(c0), "+s"(pitch16));
             const bool full = M - cur_t.m0 >= BM && N - cur_t.n0 >= BN;   // no m0 + BM: overflows near 2^31
+            const char *const bias_mine = bias_smem + ((r & 1) * 4 + wid_s) * 1024;
             auto store_all = [&](auto masked) {
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
@@ -277,7 +295,7 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
                     if (masked && cur_t.n0 + cn >= N) continue;
                     float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
                     if (bias) {
-                        const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + cur_t.n0 + cn);
+                        const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias_mine + cn * 2);
                         b0 = to_f32<DT>(bb.x & 0xffffu);
                         b1 = to_f32<DT>(bb.x >> 16);
                         b2 = to_f32<DT>(bb.y & 0xffffu);

@@ -367,6 +367,17 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     };
     const uint32_t lane_off = ((uint32_t)mrow * (uint32_t)N + (uint32_t)col0(0, 0)) * 2u;
     const bool full = M - m0 >= BM && N - n0 >= BN;   // no m0 + BM: overflows near 2^31
+    // All of this lane's bias values first, in one batch (one load latency, not
+    // one per column group); columns past N read as zero.
+    u32x2 bvals[FN][NI];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int cn = col0(fn, i);
+            bvals[fn][i] = bias && n0 + cn < N ? *reinterpret_cast<const u32x2 *>(bias + n0 + cn)
+                                               : u32x2{0u, 0u};
+        }
     auto store_all = [&](auto masked) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
@@ -376,7 +387,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                 if (masked && n0 + cn >= N) continue;
                 float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
                 if (bias) {
-                    const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + n0 + cn);
+                    const u32x2 bb = bvals[fn][i];
                     b0 = to_f32<DT>(bb.x & 0xffffu);
                     b1 = to_f32<DT>(bb.x >> 16);
                     b2 = to_f32<DT>(bb.y & 0xffffu);

@@ -42,6 +42,13 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // Needs at least two K slices (K > 64): the launcher uses gemm_v3 below that.
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+    // The bias of a tile, staged in LDS with the tile's first slice so that the
+    // epilogue reads it with ds_read instead of waiting on global loads (which
+    // would also wait for the next tile's slices in flight). One 1 KiB slot per
+    // wave (its own copy: no barrier needed) and per tile parity.
+    __shared__ __attribute__((aligned(1024))) char bias_smem[2 * NW * 1024];
+    static_assert(BN * 2 <= 1024 && BN / 8 <= 64, "a tile's bias fits one load per wave");
+    static_assert(2 * STAGE_BYTES + 2 * NW * 1024 <= 160 * 1024, "LDS ring + bias slots too large");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
@@ -109,6 +116,16 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             d.rb = make_rsrc(B + (live ? (size_t)d.k0 * N + t.n0 : 0),
                              live ? (uint32_t)min(K - d.k0, BK) * (uint32_t)N * 2u : 0u);
         return d;
+    };
+    // Bias of tile t into this wave's slot of parity p: lanes 0 .. BN/8-1 load 16
+    // bytes each (columns past N read zeros), the other lanes land zeros. Counted
+    // in vmcnt with the slice loads around it.
+    const uint32_t bias_lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(GBA_LDS void *)bias_smem + (uint32_t)(wid_s * 1024));
+    auto bias_dma = [&](const Tile &t, int p) {
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias + t.n0, (uint32_t)min(N - t.n0, BN) * 2u);
+        buffer_load_lds16(rb, lane < BN / 8 ? (uint32_t)lane * 16u : kOobOffset,
+                          bias_lds + (uint32_t)(p * NW * 1024));
     };
     // `kx`, `nx`: K and N re-read opaquely in each slice, so that the per-load
     // row offsets (multiples of 64 K and 16 N bytes) are recomputed where used
@@ -216,6 +233,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // published, and its first fragments read.
     {
         const SliceDma d0 = slice_dma(cur_t, true, 0, 0), d1 = slice_dma(cur_t, true, 1, 1);
+        if (bias) bias_dma(cur_t, 0);   // lands with slice 0 (waited for below)
 #pragma unroll
         for (int i = 0; i < LD; ++i) dma_one(d0, i, (uint32_t)K, (uint32_t)N);
 #pragma unroll
@@ -253,6 +271,10 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             const bool here = kt + 2 < nk;
             const SliceDma dn = slice_dma(here ? cur_t : nxt_t, here || nxt_live,
                                           here ? kt + 2 : kt + 2 - nk, sc);
+            // With the next tile's slice 0: its bias, into the other parity's slot
+            // (this tile's epilogue still reads its own). Landed by the next
+            // slice's vmcnt(0) wait, long before that tile's epilogue.
+            if (bias && !here && kt + 2 == nk && nxt_live) bias_dma(nxt_t, (r + 1) & 1);
             step(1, true, nxt_base, 0, true, dn, kx, nx);
         }
 
@@ -272,6 +294,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             // and held in registers across the main loop.
             asm volatile("" : "+v"(lane_off), "+v"(c0), "+s"(pitch16));
             const bool full = M - cur_t.m0 >= BM && N - cur_t.n0 >= BN;   // no m0 + BM: overflows near 2^31
+            const char *const bias_mine = bias_smem + ((r & 1) * NW + wid_s) * 1024;
             auto store_all = [&](auto masked) {
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
@@ -279,7 +302,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                     if (masked && cur_t.n0 + cn >= N) continue;
                     float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
                     if (bias) {
-                        const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias + cur_t.n0 + cn);
+                        const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias_mine + cn * 2);
                         b0 = to_f32<DT>(bb.x & 0xffffu);
                         b1 = to_f32<DT>(bb.x >> 16);
                         b2 = to_f32<DT>(bb.y & 0xffffu);
