@@ -244,7 +244,6 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 #pragma unroll
     for (int q = 0; q < NPF; ++q) read_one(0, smem, 0, q);
 
-    const int mrow = wm * WTM + tj;
     int stage0 = 0;   // stage of the current tile's slice 0
     for (int r = 0;; ++r) {
 #pragma unroll
@@ -285,8 +284,12 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         asm volatile("" ::: "memory");
         {
             char *const Ct = reinterpret_cast<char *>(C + (size_t)cur_t.m0 * N + cur_t.n0);
-            int c0 = wn * WTN + 4 * tg, mr = mrow;
-            asm volatile("" : "+v"(mr));
+            // Row and column of this lane, recomputed from the lane id (a volatile
+            // mbcnt, so not merged with the copies from before the K loop) and the
+            // scalar wave id: no vector register is held across the loop for them.
+            int ln;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+            int c0 = (wid_s % WN) * WTN + 4 * (ln >> 4), mr = (wid_s / WN) * WTM + (ln & 15);
             uint32_t lane_off = ((uint32_t)mr * (uint32_t)N + (uint32_t)c0) * 2u;
             uint32_t pitch16 = (uint32_t)N * (2u * BD);   // bytes between row blocks fm
             // Opaque to the optimiser: otherwise the per-store offsets, columns and
