@@ -89,6 +89,9 @@ class Oracle:
         for name in ("oracle_gemm_bias_act", "oracle_gemm_bias_act_nt"):
             getattr(lib, name).argtypes = [p, p, p, p, p, i64, i64, i64, ci, ci, p, i64, ci]
             getattr(lib, name).restype = ci
+        lib.oracle_gemm_bias_act_ex.argtypes = [p, p, p, p, p, i64, i64, i64, ci, ci, ci, ci, p,
+                                                i64, ci]
+        lib.oracle_gemm_bias_act_ex.restype = ci
         lib.oracle_gemm_bias_act_fp8_nt.argtypes = [p, p, p, p, p, i64, i64, i64,
                                                     ctypes.c_double, ci, ci, ci, p, i64, ci]
         lib.oracle_gemm_bias_act_fp8_nt.restype = ci
@@ -103,16 +106,17 @@ class Oracle:
         self.path = path
 
     def gemm_bias_act(self, A, B, bias, act="none", dtype="f16", rows=None, nthreads=0,
-                      with_abs=False, transpose_b=False):
+                      with_abs=False, transpose_b=False, transpose_a=False):
         """fp64 act(A.B + bias) for the given rows (all rows when rows is None).
 
-        A: uint16 bits [M, K]; B: uint16 bits [K, N], or [N, K] with transpose_b
-        (the product is then A.B^T); bias: uint16 bits [N] or None.
+        A: uint16 bits [M, K], or [K, M] with transpose_a (the product is then
+        A^T.B); B: uint16 bits [K, N], or [N, K] with transpose_b (the product
+        is then A.B^T); bias: uint16 bits [N] or None.
         Returns out[len(rows) or M, N] float64, plus sum_k |A_ik B_kj| + |bias_j|
         when with_abs is set.
         """
         A, B = _bits(A), _bits(B)
-        M, K = A.shape
+        M, K = A.shape[::-1] if transpose_a else A.shape
         N, K2 = B.shape if transpose_b else B.shape[::-1]
         if K2 != K:
             raise ValueError("inner dimensions differ: A is %s, B is %s" % (A.shape, B.shape))
@@ -124,9 +128,15 @@ class Oracle:
         nrows = M if r is None else r.shape[0]
         out = np.empty((nrows, N), dtype=np.float64)
         absout = np.empty((nrows, N), dtype=np.float64) if with_abs else None
-        fn = self._lib.oracle_gemm_bias_act_nt if transpose_b else self._lib.oracle_gemm_bias_act
-        rc = fn(_ptr(A), _ptr(B), _ptr(bias), _ptr(out), _ptr(absout), M, N, K, _act(act),
-                _dt(dtype), _ptr(r), 0 if r is None else nrows, int(nthreads))
+        if transpose_a:
+            rc = self._lib.oracle_gemm_bias_act_ex(
+                _ptr(A), _ptr(B), _ptr(bias), _ptr(out), _ptr(absout), M, N, K, _act(act),
+                _dt(dtype), 1, int(bool(transpose_b)), _ptr(r), 0 if r is None else nrows,
+                int(nthreads))
+        else:
+            fn = self._lib.oracle_gemm_bias_act_nt if transpose_b else self._lib.oracle_gemm_bias_act
+            rc = fn(_ptr(A), _ptr(B), _ptr(bias), _ptr(out), _ptr(absout), M, N, K, _act(act),
+                    _dt(dtype), _ptr(r), 0 if r is None else nrows, int(nthreads))
         if rc != 0:
             raise ValueError("oracle_gemm_bias_act rejected its arguments")
         return (out, absout) if with_abs else out

@@ -31,6 +31,9 @@
  *     With it, the second operand is given as an (N,K) row-major array W and
  *     the product is A times its transpose: s[i][j] = sum_k A[i][k] * W[j][k]
  *     (oracle_gemm_bias_act_nt).
+ *   - The same call takes a transpose_A flag: the first operand is then given
+ *     as a (K,M) row-major array At, and A[i][k] = At[k][i]
+ *     (oracle_gemm_bias_act_ex, which takes both flags).
  *
  * The oracle is the mathematical definition written out, in fp64:
  *     s[i][j] = sum_{k<K} A[i][k] * B[k][j]        (each product exact in fp64)
@@ -186,13 +189,13 @@ static double act_apply(int act, double z) {
 /* ---- the fused GEMM ------------------------------------------------------- */
 
 typedef struct {
-    const void *A;         /* operand kind a_kind */
+    const void *A;         /* operand kind a_kind; (M,K), or (K,M) when a_km */
     const uint16_t *bias;  /* dtype */
     const double *Bd;      /* B decoded to fp64, K x N */
     double *out, *absout;
     const int64_t *rows;
-    int64_t nrows, N, K;
-    int act, dtype, a_kind;
+    int64_t nrows, M, N, K;
+    int act, dtype, a_kind, a_km;
     double scale;          /* multiplies the sum before the bias (1 for 16-bit inputs) */
     int64_t r0, r1;        /* this worker's slice of [0, nrows) */
 } gemm_job;
@@ -207,7 +210,7 @@ static void *gemm_worker(void *p) {
         for (int64_t c = 0; c < N; ++c) acc[c] = 0.0;
         if (aacc) for (int64_t c = 0; c < N; ++c) aacc[c] = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            const double a = dec_op(j->a_kind, j->A, i * K + k);
+            const double a = dec_op(j->a_kind, j->A, j->a_km ? k * j->M + i : i * K + k);
             const double *brow = j->Bd + k * N;
             for (int64_t c = 0; c < N; ++c) acc[c] += a * brow[c];
             if (aacc) {
@@ -264,7 +267,7 @@ static int pick_threads(int nthreads, int64_t work_items) {
  * + |bias[c]|, the magnitude that bounds any fp32 summation's rounding error.
  * Returns 0, or -1 on a bad argument.
  */
-static int gemm_impl(const void *A, const void *B, int op_kind, int b_nk, double scale,
+static int gemm_impl(const void *A, int a_km, const void *B, int op_kind, int b_nk, double scale,
                      const uint16_t *bias, double *out, double *absout, int64_t M, int64_t N,
                      int64_t K, int act, int dtype, const int64_t *rows, int64_t nrows,
                      int nthreads) {
@@ -295,8 +298,8 @@ static int gemm_impl(const void *A, const void *B, int op_kind, int b_nk, double
     pthread_t th[256];
     gemm_job jb[256];
     for (int t = 0; t < T; ++t) {
-        gemm_job g = {A, bias, Bd, out, absout, rows, nrows, N, K, act, dtype, op_kind,
-                      scale, nrows * t / T, nrows * (t + 1) / T};
+        gemm_job g = {A, bias, Bd, out, absout, rows, nrows, M, N, K, act, dtype, op_kind,
+                      a_km, scale, nrows * t / T, nrows * (t + 1) / T};
         jb[t] = g;
         pthread_create(&th[t], NULL, gemm_worker, &jb[t]);
     }
@@ -310,7 +313,7 @@ int oracle_gemm_bias_act(const uint16_t *A, const uint16_t *B, const uint16_t *b
                          double *out, double *absout, int64_t M, int64_t N, int64_t K,
                          int act, int dtype, const int64_t *rows, int64_t nrows,
                          int nthreads) {
-    return gemm_impl(A, B, dtype, 0, 1.0, bias, out, absout, M, N, K, act, dtype, rows, nrows,
+    return gemm_impl(A, 0, B, dtype, 0, 1.0, bias, out, absout, M, N, K, act, dtype, rows, nrows,
                      nthreads);
 }
 
@@ -319,8 +322,19 @@ int oracle_gemm_bias_act_nt(const uint16_t *A, const uint16_t *W, const uint16_t
                             double *out, double *absout, int64_t M, int64_t N, int64_t K,
                             int act, int dtype, const int64_t *rows, int64_t nrows,
                             int nthreads) {
-    return gemm_impl(A, W, dtype, 1, 1.0, bias, out, absout, M, N, K, act, dtype, rows, nrows,
+    return gemm_impl(A, 0, W, dtype, 1, 1.0, bias, out, absout, M, N, K, act, dtype, rows, nrows,
                      nthreads);
+}
+
+/* Either operand stored transposed: transpose_a: the first operand is At, stored
+ * (K,M), with A[i][k] = At[k][i]; transpose_b: the second is W, stored (N,K).
+ * out[r][c] = act(sum_k A[i][k]*B[k][c] + bias[c]) with B[k][c] = W[c][k]. */
+int oracle_gemm_bias_act_ex(const uint16_t *A, const uint16_t *B, const uint16_t *bias,
+                            double *out, double *absout, int64_t M, int64_t N, int64_t K,
+                            int act, int dtype, int transpose_a, int transpose_b,
+                            const int64_t *rows, int64_t nrows, int nthreads) {
+    return gemm_impl(A, transpose_a != 0, B, dtype, transpose_b != 0, 1.0, bias, out, absout, M,
+                     N, K, act, dtype, rows, nrows, nthreads);
 }
 
 /* 8-bit inputs, W stored (N,K): out[r][c] = act(scale * sum_k A[i][k]*W[c][k] + bias[c]),
@@ -331,7 +345,7 @@ int oracle_gemm_bias_act_fp8_nt(const uint8_t *A, const uint8_t *W, const uint16
                                 double scale, int act, int fmt, int dtype,
                                 const int64_t *rows, int64_t nrows, int nthreads) {
     if (fmt != 0 && fmt != 1) return -1;
-    return gemm_impl(A, W, fmt == 0 ? OK_E4M3 : OK_E5M2, 1, scale, bias, out, absout, M, N, K,
+    return gemm_impl(A, 0, W, fmt == 0 ? OK_E4M3 : OK_E5M2, 1, scale, bias, out, absout, M, N, K,
                      act, dtype, rows, nrows, nthreads);
 }
 

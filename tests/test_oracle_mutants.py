@@ -48,6 +48,8 @@ MUTANTS = {
     "round_half_up": ("double r = rint(a / q);", "double r = floor(a / q + 0.5);"),
     "abs_sum_signed": ("aacc[c] += aa * fabs(brow[c]);", "aacc[c] += aa * brow[c];"),
     "transpose_b_reads_kn": ("d->b_nk ? j * d->K + k : t", "d->b_nk ? k * d->N + j : t"),
+    "transpose_a_reads_mk": ("j->a_km ? k * j->M + i : i * K + k",
+                             "j->a_km ? i * K + k : i * K + k"),
     "second_operand_row": ("const double *brow = j->Bd + k * N;",
                            "const double *brow = j->Bd + (K - 1 - k) * N;"),
 }

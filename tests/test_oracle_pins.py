@@ -396,6 +396,57 @@ def test_transpose_b_identity_permutation_and_integers(orc):
         np.testing.assert_array_equal(got, np.maximum(want, 0) if act == "relu" else want)
 
 
+@pytest.mark.parametrize("transpose_b", [False, True], ids=["kn", "nk"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 5, 7), (7, 4, 9), (4, 3, 33)])
+def test_transpose_a_equals_exact_rational_sum(orc, dtype, shape, transpose_b):
+    # transpose_A: the first operand is stored (K, M) and enters as its transpose
+    M, N, K = shape
+    At = synth.random_bits((K, M), dtype, 120 + M)
+    B = synth.random_bits((N, K) if transpose_b else (K, N), dtype, 220 + N)
+    bias = synth.random_bits((N,), dtype, 320 + K)
+    Atv, Bv, bv = orc.decode(At, dtype), orc.decode(B, dtype), orc.decode(bias, dtype)
+    exact = _fraction_gemm(Atv.T, Bv.T if transpose_b else Bv, bv)
+    got, S = orc.gemm_bias_act(At, B, bias, "none", dtype, with_abs=True, transpose_a=True,
+                               transpose_b=transpose_b)
+    assert got.shape == (M, N)
+    for i in range(M):
+        for j in range(N):
+            bound = (K + 1) * 2.0 ** -53 * S[i, j]
+            assert abs(Fraction(got[i, j]) - exact[i, j]) <= Fraction(bound), (i, j)
+
+
+def test_transpose_a_identity_permutation_and_integers(orc):
+    K = 40
+    B = synth.random_bits((K, 12), "f16", 15)
+    np.testing.assert_array_equal(orc.gemm_bias_act(f16(np.eye(K)), B, None, transpose_a=True),
+                                  orc.decode(B))
+    # At = P (rows of I permuted, not symmetric): A = P^T, whose row i picks row
+    # inv[i] of B, inv the inverse permutation
+    perm = np.random.default_rng(6).permutation(K)
+    P = f16(np.eye(K)[perm])
+    np.testing.assert_array_equal(orc.gemm_bias_act(P, B, None, transpose_a=True),
+                                  orc.decode(B)[np.argsort(perm)])
+    rng = np.random.default_rng(23)
+    M, N, K = 23, 31, 77   # M != K: a swapped leading dimension cannot hide
+    Ati, Bi, bi = rng.integers(-3, 4, (K, M)), rng.integers(-3, 4, (K, N)), rng.integers(-9, 10, N)
+    Wi = np.ascontiguousarray(Bi.T)
+    for act in ("none", "relu"):
+        want = Ati.T @ Bi + bi
+        want = np.maximum(want, 0) if act == "relu" else want
+        np.testing.assert_array_equal(
+            orc.gemm_bias_act(f16(Ati), f16(Bi), f16(bi), act, transpose_a=True), want)
+        np.testing.assert_array_equal(
+            orc.gemm_bias_act(f16(Ati), f16(Wi), f16(bi), act, transpose_a=True, transpose_b=True),
+            want)
+    # sampled rows of the transposed-A product are the same rows of the full one
+    rows = np.array([22, 0, 7])
+    full = orc.gemm_bias_act(f16(Ati), f16(Bi), f16(bi), "none", transpose_a=True)
+    np.testing.assert_array_equal(
+        orc.gemm_bias_act(f16(Ati), f16(Bi), f16(bi), "none", transpose_a=True, rows=rows),
+        full[rows])
+
+
 def test_identity_and_permutation(orc):
     K, N = 48, 40
     B = synth.random_bits((K, N), "f16", 5)
