@@ -1,7 +1,7 @@
 """Benchmark of the fused GEMM + bias + GELU on one MI355X.
 
     python bench.py [--steps 50] [--warmup 300] [--workload c3_gelu] [--unfused]
-                    [--transpose-b]
+                    [--transpose-b] [--transpose-a]
 
 One step is one gemm_bias_act call over the whole workload (schedule choice,
 global->LDS loads, MFMA main loop, fused epilogue, store), with inputs already
@@ -130,7 +130,8 @@ def time_launches(fn, steps, warmup, stream):
     return wall_ms, avg_ms, per
 
 
-def cpu_baseline(w, A, B, bias, got_bits, target_s=12.0, transpose_b=False, scale=None):
+def cpu_baseline(w, A, B, bias, got_bits, target_s=12.0, transpose_b=False, scale=None,
+                 transpose_a=False):
     """The fp64 oracle on a bounded sample of rows, timed on the host cores
     (8-bit inputs when scale is given)."""
     import oracle
@@ -142,7 +143,8 @@ def cpu_baseline(w, A, B, bias, got_bits, target_s=12.0, transpose_b=False, scal
             return oracle.gemm_bias_act_fp8(A, B, bias, scale, w.act, w.fmt, w.dtype, rows=rows,
                                             nthreads=cores, with_abs=with_abs)
         return oracle.gemm_bias_act(A, B, bias, w.act, w.dtype, rows=rows, nthreads=cores,
-                                    with_abs=with_abs, transpose_b=transpose_b)
+                                    with_abs=with_abs, transpose_b=transpose_b,
+                                    transpose_a=transpose_a)
 
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     rows = synth.sample_rows(w.M, 16, seed=w.seed)
@@ -180,6 +182,9 @@ def main(argv=None) -> int:
                          "than CUs split K")
     ap.add_argument("--transpose-b", action="store_true",
                     help="B stored [N,K] (transpose_B): time gemm_bias_act_nt on the same numbers")
+    ap.add_argument("--transpose-a", action="store_true",
+                    help="A stored [K,M] (transpose_A): time gemm_bias_act_ex with GBA_TRANSPOSE_A "
+                         "on the same numbers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--act", default=None,
                     help="replace the workload's activation (none, relu, sigmoid, gelu, softplus, gelu_tanh)")
@@ -215,9 +220,13 @@ def main(argv=None) -> int:
     else:
         A, B, bias = synth.make_inputs(w)
     tb = a.transpose_b and not fp8
+    ta = a.transpose_a and not fp8
     if tb:
         B = np.ascontiguousarray(B.T)   # the same operand, stored as the [N,K] weight W
-    wl_key = w.name + ("_nt" if tb else "") + ("_" + a.act if a.act else "")
+    if ta:
+        A = np.ascontiguousarray(A.T)   # the same operand, stored as At [K,M]
+    wl_key = (w.name + ("_t" + ("t" if tb else "n") if ta else ("_nt" if tb else ""))
+              + ("_" + a.act if a.act else ""))
     tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
 
     def dev_t(bits):
@@ -249,7 +258,8 @@ def main(argv=None) -> int:
         sched.setdefault("group_m", 4)
         gba.set_schedule(sched)
     elif a.tune and not fp8:
-        best, ms = gba.autotune(a_t, b_t, bias_t, c_t, w.act, all_groups=True, transpose_b=tb)
+        best, ms = gba.autotune(a_t, b_t, bias_t, c_t, w.act, all_groups=True, transpose_b=tb,
+                                transpose_a=ta)
         log("[bench] autotune best %s %.4f ms" % (best, ms))
     if fp8:
         sched = {"kernel": "f8", "fmt": w.fmt, "bm": 256, "bn": 256, "bk": 128, "wm": 2, "wn": 2,
@@ -262,14 +272,17 @@ def main(argv=None) -> int:
         step = gba.bind_gemm_bias_act_fp8(a_t, b_t, bias_t, c_t, scale, w.act, w.fmt,
                                           workspace=ws_t)
     else:
-        sched = gba.get_schedule(w.M, w.N, w.K, w.act, w.dtype, transpose_b=tb)
+        sched = gba.get_schedule(w.M, w.N, w.K, w.act, w.dtype, transpose_b=tb, transpose_a=ta)
         ws_t = None
         if a.workspace:
-            nb = gba.workspace_size(w.M, w.N, w.K, w.act, w.dtype, transpose_b=tb)
+            nb = gba.workspace_size(w.M, w.N, w.K, w.act, w.dtype, transpose_b=tb,
+                                    transpose_a=ta)
             ws_t = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
             sched = dict(sched, splits_workspace_bytes=nb)
-        step = gba.bind_gemm_bias_act(a_t, b_t, bias_t, c_t, w.act, transpose_b=tb, workspace=ws_t)
-    log("[bench] schedule %s%s" % (sched, " (B stored [N,K])" if tb else ""))
+        step = gba.bind_gemm_bias_act(a_t, b_t, bias_t, c_t, w.act, transpose_b=tb, workspace=ws_t,
+                                      transpose_a=ta)
+    log("[bench] schedule %s%s%s" % (sched, " (A stored [K,M])" if ta else "",
+                                     " (B stored [N,K])" if tb else ""))
     wall_ms, kern_avg, per = time_launches(step, a.steps, a.warmup, stream)
     ms_per_step = wall_ms / a.steps
     kern_med = statistics.median(per)
@@ -300,10 +313,11 @@ def main(argv=None) -> int:
         "config": {"workload": ("%s: C = %s(scale * A.W^T + bias), W stored [N,K], M=%d N=%d K=%d, "
                                 "%s in, %s out, fp32 accumulate"
                                 % (wl_key, w.act, w.M, w.N, w.K, w.fmt, w.dtype)) if fp8 else
-                               ("%s: C = %s(A.%s + bias), M=%d N=%d K=%d, %s in/out, fp32 accumulate"
-                                % (wl_key, w.act, "W^T, W stored [N,K]" if tb else "B", w.M, w.N,
-                                   w.K, w.dtype)),
+                               ("%s: C = %s(%s.%s + bias), M=%d N=%d K=%d, %s in/out, fp32 accumulate"
+                                % (wl_key, w.act, "At^T, At stored [K,M]" if ta else "A",
+                                   "W^T, W stored [N,K]" if tb else "B", w.M, w.N, w.K, w.dtype)),
                    "M": w.M, "N": w.N, "K": w.K, "act": w.act, "bias": w.bias,
+                   "a_layout": "KM (transpose_A)" if ta else "MK",
                    "b_layout": "NK (transpose_B)" if (tb or fp8) else "KN",
                    "schedule": sched, "flop_model": "2*M*N*K (epilogue not counted)"},
         "median_ms": round(kern_med, 5),
@@ -317,7 +331,8 @@ def main(argv=None) -> int:
     if a.unfused and not fp8:
         t_t = torch.empty_like(c_t)
         y_t = torch.empty_like(c_t)
-        _, g_ms, _ = time_launches(lambda: gba.gemm(a_t, b_t, t_t, transpose_b=tb), a.steps,
+        _, g_ms, _ = time_launches(lambda: gba.gemm(a_t, b_t, t_t, transpose_b=tb, transpose_a=ta),
+                                   a.steps,
                                    a.warmup, stream)
         _, b_ms, _ = time_launches(lambda: gba.bias_act(t_t, bias_t, y_t, w.act), a.steps,
                                    a.warmup, stream)
@@ -335,7 +350,8 @@ def main(argv=None) -> int:
 
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a row sample")
-        base, parity = cpu_baseline(w, A, B, bias, got_bits, transpose_b=tb, scale=scale)
+        base, parity = cpu_baseline(w, A, B, bias, got_bits, transpose_b=tb, scale=scale,
+                                    transpose_a=ta)
         out["cpu_baseline"] = base
         out["parity_sampled"] = parity
         log("[bench] cpu baseline %.4f TFLOP/s on %d threads; parity %s"

@@ -139,11 +139,22 @@ int gemm_nt(const void *A, const void *W, void *C, int64_t M, int64_t N, int64_t
 /* gemm_bias_act_ex / gba_workspace_size flags. */
 enum {
     GBA_TRANSPOSE_B = 1, /* B is W, stored [N,K], as in gemm_bias_act_nt */
-    GBA_INPUT_FP8 = 2    /* gba_workspace_size only: for gemm_bias_act_fp8_ex */
+    GBA_INPUT_FP8 = 2,   /* gba_workspace_size only: for gemm_bias_act_fp8_ex */
+    GBA_TRANSPOSE_A = 4  /* A is At, stored [K,M]: C = act(At^T.B + bias) */
 };
 
 /* gemm_bias_act (or, with GBA_TRANSPOSE_B, gemm_bias_act_nt) with an optional
- * caller-owned device workspace for split-K. When the chosen schedule's tiles
+ * caller-owned device workspace for split-K, and the first operand in either
+ * layout.
+ * GBA_TRANSPOSE_A: the first operand is At: [K,M] row-major (M-contiguous
+ * rows) and the product is At^T.B (or At^T.W^T with GBA_TRANSPOSE_B): the
+ * transpose_A form of the tile GEMM ("writing-tilelang-kernels", Key API
+ * Patterns, T.gemm(..., transpose_A=True)). M must then be a multiple of 8 as
+ * well (16-byte rows of At; else GBA_ERR_ALIGN) and at most 2^23 (like N; else
+ * GBA_ERR_SHAPE). Kernels 3 and 4 at the built-in tiles have this path (see
+ * gba_list_schedule); a forced schedule without it returns GBA_ERR_SCHEDULE.
+ * The result is bitwise that of the [M,K] path on the same schedule with
+ * A = At^T: both feed the matrix cores the same operands in the same order. When the chosen schedule's tiles
  * leave compute units idle and K is deep enough for the split to pay for its
  * extra traffic (e.g. 256x256x4096: 4 tiles of 128x128 for 256 CUs; not
  * 1024^3, where the fp32 partials' round trip costs more than it saves), K is
@@ -206,15 +217,19 @@ int gba_set_stream(void *hip_stream);
  * are out of range. */
 int gba_set_schedule(const gba_schedule *s);
 
-/* The schedule a gemm_bias_act (gemm_bias_act_nt) call with these arguments
- * would use now. */
+/* The schedule a gemm_bias_act (gemm_bias_act_nt; gemm_bias_act_ex with these
+ * GBA_TRANSPOSE_A / GBA_TRANSPOSE_B flags) call with these arguments would use
+ * now. Unknown flag bits: GBA_ERR_SHAPE. */
 int gba_get_schedule(int64_t M, int64_t N, int64_t K, int act, int dtype, gba_schedule *out);
 int gba_get_schedule_nt(int64_t M, int64_t N, int64_t K, int act, int dtype, gba_schedule *out);
+int gba_get_schedule_ex(int64_t M, int64_t N, int64_t K, int act, int dtype, int flags,
+                        gba_schedule *out);
 
 /* gba_autotune flags. */
 enum {
     GBA_TUNE_ALL_GROUPS = 1,   /* also try every raster group size in {1,2,4,8,16} */
-    GBA_TUNE_TRANSPOSE_B = 2   /* tune gemm_bias_act_nt: B is W, stored [N,K] */
+    GBA_TUNE_TRANSPOSE_B = 2,  /* tune gemm_bias_act_nt: B is W, stored [N,K] */
+    GBA_TUNE_TRANSPOSE_A = 4   /* A is At, stored [K,M] (gemm_bias_act_ex, GBA_TRANSPOSE_A) */
 };
 
 /* Compiled-in kernel instances: count, and the i-th one (raster/group_m are
@@ -224,13 +239,13 @@ int gba_list_schedule(int i, gba_schedule *out);
 
 /* Autotuner ("TileLang: Write, Autotune, and Ship Fused Tensor-Core Kernels from
  * Python", section Autotuning): for every compiled-in instance (with a
- * transpose_B path when GBA_TUNE_TRANSPOSE_B is set) whose LDS ring
+ * path for the operand layouts that GBA_TUNE_TRANSPOSE_A / _B select) whose LDS ring
  * (bm*bk + bk*bn) * 2 * stages fits the 160 KiB LDS of a CU, and each raster
  * variant, run 10 untimed and 50 timed launches on the caller's buffers, keep
  * the median time, and pick the fastest. The winner is stored in the on-disk
  * schedule cache ($GBA_CACHE_DIR, default ~/.cache/gba; disabled by
  * GBA_DISABLE_CACHE=1) under the key (arch, CU count, library version, dtype,
- * act, B layout, M, N, K), and is used by later calls. C holds the winner's
+ * act, operand layouts, M, N, K), and is used by later calls. C holds the winner's
  * result on return. flags: GBA_TUNE_* bits.
  * best / best_ms may be NULL. Synchronous: it waits for its own launches.
  * Returns GBA_ERR_CACHE (with best filled) if the cache file could not be

@@ -131,10 +131,33 @@ def test_ex_and_workspace_argument_errors_precede_device_use(lib):
     assert ex(ws=P16 * 200 + 8, nb=1 << 20) == ERR_ALIGN
     assert ex(ws=P16 * 64 + 256, nb=1 << 20) == ERR_ALIAS   # overlaps C
     size = ctypes.c_size_t(123)
-    assert lib.gba_workspace_size(64, 64, 64, 0, 0, 4, ctypes.byref(size)) == ERR_SHAPE
+    assert lib.gba_workspace_size(64, 64, 64, 0, 0, 8, ctypes.byref(size)) == ERR_SHAPE
     assert lib.gba_workspace_size(-1, 64, 64, 0, 0, 0, ctypes.byref(size)) == ERR_SHAPE
     assert lib.gba_workspace_size(0, 64, 64, 0, 0, 0, ctypes.byref(size)) == OK and size.value == 0
     assert lib.gba_workspace_size(64, 64, 64, 0, 0, 0, None) == ERR_NULL
+
+
+def test_transpose_a_argument_errors_precede_device_use(lib):
+    # A stored [K, M]: M is then a row pitch, so it must be a multiple of 8 (16-byte
+    # rows) and at most 2^23, like N; the other checks are unchanged.
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    ex = lambda M=64, N=64, K=64, flags=4, A=P16, C=P16 * 64: lib.gemm_bias_act_ex(
+        v(A), v(P16), None, v(C), M, N, K, 0, 0, flags, None, 0)
+    assert ex(M=60) == ERR_ALIGN
+    assert ex(M=60, flags=5) == ERR_ALIGN
+    assert ex(M=60, flags=0) != ERR_ALIGN          # [M, K] layout: any M
+    assert ex(M=(1 << 23) + 8, C=P16 * (1 << 20)) == ERR_SHAPE
+    assert ex(K=12) == ERR_ALIGN
+    assert ex(N=60) == ERR_ALIGN
+    assert ex(A=P16 + 2) == ERR_ALIGN
+    assert ex(flags=8) == ERR_SHAPE                # unknown flag bit
+    assert ex(C=P16 + 64) == ERR_ALIAS             # C overlaps At
+    assert ex(M=0) == OK
+    size = ctypes.c_size_t(123)
+    assert lib.gba_workspace_size(0, 64, 64, 0, 0, 4, ctypes.byref(size)) == OK and size.value == 0
+    s = gba.Schedule()
+    assert lib.gba_get_schedule_ex(64, 64, 64, 0, 0, 8, ctypes.byref(s)) == ERR_SHAPE
+    assert lib.gba_get_schedule_ex(64, 64, 64, 6, 0, 4, ctypes.byref(s)) == ERR_ACT
 
 
 def test_bias_act_argument_errors(lib):
@@ -161,5 +184,11 @@ def test_binding_checks_without_gpu():
     a = torch.zeros(4, 8, dtype=torch.float16)
     with pytest.raises(ValueError):
         gba.gemm_bias_act(a, a.t().contiguous(), None, torch.zeros(4, 4, dtype=torch.float16))
+    # transpose_a: a is [K, M], so a [4, 8] operand means M = 8, K = 4
+    assert gba._gemm_shapes(a, torch.zeros(4, 16, dtype=torch.float16), None,
+                            torch.zeros(8, 16, dtype=torch.float16), False, True)[1:] == (8, 16, 4)
+    with pytest.raises(ValueError):
+        gba._gemm_shapes(a, torch.zeros(8, 16, dtype=torch.float16), None,
+                         torch.zeros(8, 16, dtype=torch.float16), False, True)
     with pytest.raises(TypeError):
         gba._dtype_code(torch.zeros(2, dtype=torch.float32))

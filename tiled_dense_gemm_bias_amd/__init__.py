@@ -77,6 +77,7 @@ def _lib():
             "gba_set_schedule": [ctypes.POINTER(Schedule)],
             "gba_get_schedule": [i64, i64, i64, ci, ci, ctypes.POINTER(Schedule)],
             "gba_get_schedule_nt": [i64, i64, i64, ci, ci, ctypes.POINTER(Schedule)],
+            "gba_get_schedule_ex": [i64, i64, i64, ci, ci, ci, ctypes.POINTER(Schedule)],
             "gba_num_schedules": [],
             "gba_list_schedule": [ci, ctypes.POINTER(Schedule)],
             "gba_autotune": [p, p, p, p, i64, i64, i64, ci, ci, ci, ctypes.POINTER(Schedule),
@@ -166,23 +167,29 @@ def _call(fn_name: str, dev, *args):
 
 # ---------------------------------------------------------------- API ----
 
-def _gemm_shapes(a, b, bias, c, transpose_b):
+def _gemm_shapes(a, b, bias, c, transpose_b, transpose_a=False):
     """(dtype code, M, N, K) after the dtype and shape checks of the GEMM calls.
-    b is [K,N], or [N,K] with transpose_b."""
+    a is [M,K], or [K,M] with transpose_a; b is [K,N], or [N,K] with transpose_b."""
     dt = _dtype_code(a)
     for t in (b, bias, c):
         if t is not None and _dtype_code(t) != dt:
             raise TypeError("all operands must share one dtype")
-    M, K = a.shape
+    M, K = tuple(a.shape)[::-1] if transpose_a else tuple(a.shape)
     N, K2 = tuple(b.shape) if transpose_b else tuple(b.shape)[::-1]
     if K2 != K or tuple(c.shape) != (M, N) or (bias is not None and tuple(bias.shape) != (N,)):
-        raise ValueError("shape mismatch: a%s b%s%s bias%s c%s" % (
-            tuple(a.shape), tuple(b.shape), " (transpose_b)" if transpose_b else "",
+        raise ValueError("shape mismatch: a%s%s b%s%s bias%s c%s" % (
+            tuple(a.shape), " (transpose_a)" if transpose_a else "",
+            tuple(b.shape), " (transpose_b)" if transpose_b else "",
             None if bias is None else tuple(bias.shape), tuple(c.shape)))
     return dt, M, N, K
 
 
 TRANSPOSE_B = 1
+TRANSPOSE_A = 4
+
+
+def _layout_flags(transpose_a, transpose_b) -> int:
+    return (TRANSPOSE_A if transpose_a else 0) | (TRANSPOSE_B if transpose_b else 0)
 
 
 def _ws_args(workspace):
@@ -193,19 +200,24 @@ def _ws_args(workspace):
     return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
 
 
-def gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False, workspace=None):
+def gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False, workspace=None,
+                  transpose_a=False):
     """c[M,N] = act(a[M,K] @ b[K,N] + bias[N]); bias may be None. Returns c.
 
     transpose_b: b is stored [N,K] (a linear layer's weight) and c = act(a @ b.T + bias).
+    transpose_a: a is stored [K,M] and c = act(a.T @ b + bias) (gemm_bias_act_ex
+    with GBA_TRANSPOSE_A).
     workspace: optional device tensor of workspace_size(...) bytes that lets
     shapes with fewer tiles than CUs split K (gemm_bias_act_ex)."""
     dev = _check_dev(a, b, bias, c)
-    dt, M, N, K = _gemm_shapes(a, b, bias, c, transpose_b)
-    if workspace is not None:
-        _check_dev(workspace)
-        ws, nb = _ws_args(workspace)
+    dt, M, N, K = _gemm_shapes(a, b, bias, c, transpose_b, transpose_a)
+    if workspace is not None or transpose_a:
+        ws, nb = None, 0
+        if workspace is not None:
+            _check_dev(workspace)
+            ws, nb = _ws_args(workspace)
         _call("gemm_bias_act_ex", dev, _ptr(a), _ptr(b), _ptr(bias), _ptr(c), M, N, K, _act(act),
-              dt, TRANSPOSE_B if transpose_b else 0, ws, nb)
+              dt, _layout_flags(transpose_a, transpose_b), ws, nb)
         return c
     _call("gemm_bias_act_nt" if transpose_b else "gemm_bias_act", dev, _ptr(a), _ptr(b),
           _ptr(bias), _ptr(c), M, N, K, _act(act), dt)
@@ -216,11 +228,11 @@ INPUT_FP8 = 2
 
 
 def workspace_size(M: int, N: int, K: int, act="gelu", dtype="f16", transpose_b=False,
-                   fp8=False) -> int:
+                   fp8=False, transpose_a=False) -> int:
     """Bytes of split-K workspace gemm_bias_act (gemm_bias_act_fp8 with fp8) would
     use for this shape (0: no split)."""
     out = ctypes.c_size_t()
-    flags = (TRANSPOSE_B if transpose_b else 0) | (INPUT_FP8 if fp8 else 0)
+    flags = _layout_flags(transpose_a, transpose_b) | (INPUT_FP8 if fp8 else 0)
     st = _lib().gba_workspace_size(M, N, K, _act(act), 0 if dtype in ("f16", "float16") else 1,
                                    flags, ctypes.byref(out))
     if st != 0:
@@ -228,21 +240,26 @@ def workspace_size(M: int, N: int, K: int, act="gelu", dtype="f16", transpose_b=
     return int(out.value)
 
 
-def bind_gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False, workspace=None):
+def bind_gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False, workspace=None,
+                       transpose_a=False):
     """Check and marshal the arguments once; return a no-argument callable that
-    enqueues c = act(a @ b + bias) (a @ b.T with transpose_b) on the stream
-    current now (one C call per invocation). For tight loops such as benchmarks;
-    the tensors must stay alive and unchanged in shape while the callable is used."""
+    enqueues c = act(a @ b + bias) (a @ b.T with transpose_b, a.T @ b with
+    transpose_a) on the stream current now (one C call per invocation). For tight
+    loops such as benchmarks; the tensors must stay alive and unchanged in shape
+    while the callable is used."""
     dev = _check_dev(a, b, bias, c)
-    dt, M, N, K = _gemm_shapes(a, b, bias, c, transpose_b)
+    dt, M, N, K = _gemm_shapes(a, b, bias, c, transpose_b, transpose_a)
     torch = _torch()
     lib = _lib()
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     args = (_ptr(a), _ptr(b), _ptr(bias), _ptr(c), M, N, K, _act(act), dt)
     name = "gemm_bias_act_nt" if transpose_b else "gemm_bias_act"
-    if workspace is not None:
-        _check_dev(workspace)
-        args = args + ((TRANSPOSE_B if transpose_b else 0,) + _ws_args(workspace))
+    if workspace is not None or transpose_a:
+        ws_args = (None, 0)
+        if workspace is not None:
+            _check_dev(workspace)
+            ws_args = _ws_args(workspace)
+        args = args + ((_layout_flags(transpose_a, transpose_b),) + ws_args)
         name = "gemm_bias_act_ex"
     fn = getattr(lib, name)
     set_stream = lib.gba_set_stream
@@ -337,9 +354,11 @@ def bind_gemm_bias_act_fp8(a, w, bias, c, scale=1.0, act="gelu", fmt=None, works
     return launch
 
 
-def gemm(a, b, c, transpose_b=False):
-    """c[M,N] = a[M,K] @ b[K,N] (a @ b.T for b [N,K] with transpose_b), rounded to
-    the operand dtype. Returns c."""
+def gemm(a, b, c, transpose_b=False, transpose_a=False):
+    """c[M,N] = a[M,K] @ b[K,N] (a @ b.T for b [N,K] with transpose_b; a.T for a
+    [K,M] with transpose_a), rounded to the operand dtype. Returns c."""
+    if transpose_a:
+        return gemm_bias_act(a, b, None, c, "none", transpose_b=transpose_b, transpose_a=True)
     dev = _check_dev(a, b, c)
     dt, M, N, K = _gemm_shapes(a, b, None, c, transpose_b)
     _call("gemm_nt" if transpose_b else "gemm", dev, _ptr(a), _ptr(b), _ptr(c), M, N, K, dt)
@@ -381,10 +400,11 @@ def set_schedule(sched: Optional[dict]) -> None:
         raise GbaError(st, "gba_set_schedule")
 
 
-def get_schedule(M: int, N: int, K: int, act="gelu", dtype="f16", transpose_b=False) -> dict:
+def get_schedule(M: int, N: int, K: int, act="gelu", dtype="f16", transpose_b=False,
+                 transpose_a=False) -> dict:
     s = Schedule()
-    fn = _lib().gba_get_schedule_nt if transpose_b else _lib().gba_get_schedule
-    st = fn(M, N, K, _act(act), 0 if dtype in ("f16", "float16") else 1, ctypes.byref(s))
+    st = _lib().gba_get_schedule_ex(M, N, K, _act(act), 0 if dtype in ("f16", "float16") else 1,
+                                    _layout_flags(transpose_a, transpose_b), ctypes.byref(s))
     if st != 0:
         raise GbaError(st, "gba_get_schedule")
     return s.as_dict()
@@ -400,16 +420,17 @@ def list_schedules() -> list:
     return out
 
 
-TUNE_ALL_GROUPS, TUNE_TRANSPOSE_B = 1, 2
+TUNE_ALL_GROUPS, TUNE_TRANSPOSE_B, TUNE_TRANSPOSE_A = 1, 2, 4
 
 
-def autotune(a, b, bias, c, act="gelu", all_groups: bool = False, transpose_b=False):
+def autotune(a, b, bias, c, act="gelu", all_groups: bool = False, transpose_b=False,
+             transpose_a=False):
     """Time every compiled-in schedule on these buffers; cache and return the best.
 
     Returns (schedule dict, median ms). c holds the winner's result.
     """
     dev = _check_dev(a, b, bias, c)
-    dt, M, N, K = _gemm_shapes(a, b, bias, c, transpose_b)
+    dt, M, N, K = _gemm_shapes(a, b, bias, c, transpose_b, transpose_a)
     best = Schedule()
     ms = ctypes.c_double()
     torch = _torch()
@@ -418,7 +439,8 @@ def autotune(a, b, bias, c, act="gelu", all_groups: bool = False, transpose_b=Fa
         lib.gba_set_stream(ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
         st = lib.gba_autotune(_ptr(a), _ptr(b), _ptr(bias), _ptr(c), M, N, K, _act(act), dt,
                               (TUNE_ALL_GROUPS if all_groups else 0)
-                              | (TUNE_TRANSPOSE_B if transpose_b else 0),
+                              | (TUNE_TRANSPOSE_B if transpose_b else 0)
+                              | (TUNE_TRANSPOSE_A if transpose_a else 0),
                               ctypes.byref(best), ctypes.byref(ms))
     if st not in (0, 10):
         raise GbaError(st, "gba_autotune")

@@ -139,19 +139,25 @@ int check_enums(int act, int dtype) {
 }
 
 // Shared checks of the GEMM entry points. *nothing is set when there is no work.
+// lay: operand layouts, LAY_TB (B stored (N,K)) | LAY_TA (A stored (K,M)): the
+// bits of the public GBA_TRANSPOSE_B / GBA_TRANSPOSE_A flags.
+constexpr int LAY_TB = GBA_TRANSPOSE_B, LAY_TA = GBA_TRANSPOSE_A;
+
 int check_gemm_args(const void *A, const void *B, const void *bias, const void *C, int64_t M,
-                    int64_t N, int64_t K, int act, int dtype, bool *nothing) {
+                    int64_t N, int64_t K, int act, int dtype, bool *nothing, int lay = 0) {
     int s = check_enums(act, dtype);
     if (s) return s;
     if (M < 0 || N < 0 || K < 0) return GBA_ERR_SHAPE;
     // 32-bit buffer offsets inside the kernels: a tile's byte offsets (256 rows of
-    // A, 64 rows of B) stay below 2^31.
-    if (M > 0x7fffffffLL || N > (1LL << 23) || K > (1LL << 21)) return GBA_ERR_SHAPE;
+    // A, 64 rows of B) stay below 2^31. With A stored (K,M), M is a row pitch
+    // like N (64 rows of At per slice).
+    if (M > ((lay & LAY_TA) ? (1LL << 23) : 0x7fffffffLL) || N > (1LL << 23) || K > (1LL << 21))
+        return GBA_ERR_SHAPE;
     *nothing = (M == 0 || N == 0);
     if (*nothing) return GBA_OK;
     if (!C) return GBA_ERR_NULL;
     if (K > 0 && (!A || !B)) return GBA_ERR_NULL;
-    if ((K % 8) || (N % 8)) return GBA_ERR_ALIGN;
+    if ((K % 8) || (N % 8) || ((lay & LAY_TA) && (M % 8))) return GBA_ERR_ALIGN;
     if (!aligned16(C) || (A && !aligned16(A)) || (B && !aligned16(B)) ||
         (bias && !aligned16(bias)))
         return GBA_ERR_ALIGN;
@@ -231,12 +237,14 @@ std::string cache_dir() {
 
 std::string cache_file() { return cache_dir() + "/schedules.json"; }
 
-// tb: B stored (N,K) (transpose_B), "nt" in the key; else "nn".
-std::string cache_key(const DeviceInfo &d, int dtype, int act, bool tb, int64_t M, int64_t N,
+// Layout in the key: "nn", "nt" (B stored (N,K)), "tn" (A stored (K,M)), "tt".
+const char *kLayName[4] = {"nn", "nt", "tn", "tt"};
+std::string cache_key(const DeviceInfo &d, int dtype, int act, int lay, int64_t M, int64_t N,
                       int64_t K) {
     char buf[256];
     snprintf(buf, sizeof buf, "%s|%d|%s|%s|%s|%s|%lld|%lld|%lld", d.arch.c_str(), d.cus,
-             GBA_VERSION_STRING, kDtName[dtype], kActName[act], tb ? "nt" : "nn", (long long)M,
+             GBA_VERSION_STRING, kDtName[dtype], kActName[act],
+             kLayName[((lay & LAY_TA) ? 2 : 0) | ((lay & LAY_TB) ? 1 : 0)], (long long)M,
              (long long)N, (long long)K);
     return buf;
 }
@@ -341,7 +349,7 @@ int cache_save_locked() {
 }
 
 gba_schedule choose(const DeviceInfo &d, int64_t M, int64_t N, int64_t K, int act, int dtype,
-                    bool tb, const char **why) {
+                    int lay, const char **why) {
     if (t_forced) {
         *why = "forced";
         return t_forced_sched;
@@ -349,7 +357,7 @@ gba_schedule choose(const DeviceInfo &d, int64_t M, int64_t N, int64_t K, int ac
     {
         std::lock_guard<std::mutex> lk(g_cache_mu);
         cache_load_locked();
-        auto it = g_cache.find(cache_key(d, dtype, act, tb, M, N, K));
+        auto it = g_cache.find(cache_key(d, dtype, act, lay, M, N, K));
         if (it != g_cache.end()) {
             *why = "cache";
             return it->second.s;
@@ -359,21 +367,29 @@ gba_schedule choose(const DeviceInfo &d, int64_t M, int64_t N, int64_t K, int ac
     return heuristic(M, N, d.cus);
 }
 
-// The instance of schedule s for (dtype, act, B layout), or null.
-gba::GemmLaunchFn launcher(const gba_schedule &s, int dtype, int act, bool tb) {
+// The instance of schedule s for (dtype, act, operand layouts), or null.
+gba::GemmLaunchFn launcher(const gba_schedule &s, int dtype, int act, int lay) {
     const int i = find_entry(s);
     if (i < 0) return nullptr;
+    const bool tb = (lay & LAY_TB) != 0;
+    if (lay & LAY_TA) return kTable[i]->ta[tb ? 1 : 0][dtype][act];
     return tb ? kTable[i]->tb[dtype][act] : kTable[i]->fn[dtype][act];
 }
 
+// Split-K first pass of schedule entry i for (dtype, operand layouts), or null.
+gba::PartialLaunchFn partial_launcher(int i, int dtype, int lay) {
+    const int tb = (lay & LAY_TB) ? 1 : 0;
+    return (lay & LAY_TA) ? kTable[i]->part_ta[dtype][tb] : kTable[i]->part[dtype][tb];
+}
+
 int launch(const gba_schedule &s0, const void *A, const void *B, const void *bias, void *C,
-           int64_t M, int64_t N, int64_t K, int act, int dtype, bool tb) {
+           int64_t M, int64_t N, int64_t K, int act, int dtype, int lay) {
     gba_schedule s = s0;
     // The persistent kernel streams at least two K slices per tile; with one,
     // its non-persistent twin (same tile, kernel 3) does the same work.
     if (s.kernel == 4 && K <= s.bk) s.kernel = 3;
-    const gba::GemmLaunchFn f = launcher(s, dtype, act, tb);
-    if (!f) return GBA_ERR_SCHEDULE;   // unknown, or no transpose_B path in this kernel
+    const gba::GemmLaunchFn f = launcher(s, dtype, act, lay);
+    if (!f) return GBA_ERR_SCHEDULE;   // unknown, or no path for these layouts in this kernel
     hipError_t e = f(A, B, bias, C, (int)M, (int)N, (int)K, s.raster, s.group_m, t_stream);
     return e == hipSuccess ? GBA_OK : hip_fail(e);
 }
@@ -387,11 +403,11 @@ int launch(const gba_schedule &s0, const void *A, const void *B, const void *bia
 // kernel and its launch. Split only if that saves at least 15 %. (At 1024^3 it
 // does not: 19.6 us split against 14.3 us whole; at 256x256x4096 it does.)
 int split_count(const gba_schedule &s0, int64_t M, int64_t N, int64_t K, int cus, int dtype,
-                bool tb) {
+                int lay) {
     gba_schedule s = s0;
     if (s.kernel == 4 && K <= s.bk) s.kernel = 3;
     const int i = find_entry(s);
-    if (i < 0 || !kTable[i]->part[dtype][tb ? 1 : 0] || K <= 0) return 1;
+    if (i < 0 || !partial_launcher(i, dtype, lay) || K <= 0) return 1;
     const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
     const int64_t nk = (K + s.bk - 1) / s.bk;
     int64_t smax = tiles > 0 ? cus / tiles : 1;
@@ -433,9 +449,9 @@ const ReduceFn kReduce[2][gba::kNumActs] = {
 };
 
 int gemm_common(const void *A, const void *B, const void *bias, void *C, int64_t M, int64_t N,
-                int64_t K, int act, int dtype, bool tb, void *ws = nullptr, size_t ws_bytes = 0) {
+                int64_t K, int act, int dtype, int lay, void *ws = nullptr, size_t ws_bytes = 0) {
     bool nothing = false;
-    int s = check_gemm_args(A, B, bias, C, M, N, K, act, dtype, &nothing);
+    int s = check_gemm_args(A, B, bias, C, M, N, K, act, dtype, &nothing, lay);
     if (s || nothing) return s;
     if (ws) {
         if (!aligned16(ws)) return GBA_ERR_ALIGN;
@@ -447,9 +463,9 @@ int gemm_common(const void *A, const void *B, const void *bias, void *C, int64_t
     s = current_device(&d);
     if (s) return s;
     const char *why = "";
-    const gba_schedule sch = choose(*d, M, N, K, act, dtype, tb, &why);
+    const gba_schedule sch = choose(*d, M, N, K, act, dtype, lay, &why);
     if (ws) {
-        const int S = split_count(sch, M, N, K, d->cus, dtype, tb);
+        const int S = split_count(sch, M, N, K, d->cus, dtype, lay);
         if (S > 1 && ws_bytes >= (size_t)S * (size_t)M * (size_t)N * 4u) {
             if (log_enabled())
                 fprintf(stderr, "[gba] M=%lld N=%lld K=%lld act=%s dtype=%s -> split-K %d x k%d %dx%dx%d (%s)\n",
@@ -457,7 +473,7 @@ int gemm_common(const void *A, const void *B, const void *bias, void *C, int64_t
                         sch.kernel, sch.bm, sch.bn, sch.bk, why);
             gba_schedule s3 = sch;
             if (s3.kernel == 4 && K <= s3.bk) s3.kernel = 3;
-            const gba::PartialLaunchFn pf = kTable[find_entry(s3)]->part[dtype][tb ? 1 : 0];
+            const gba::PartialLaunchFn pf = partial_launcher(find_entry(s3), dtype, lay);
             hipError_t e = pf(A, B, (float *)ws, (int)M, (int)N, (int)K, S, s3.raster, s3.group_m,
                               t_stream);
             if (e != hipSuccess) return hip_fail(e);
@@ -467,12 +483,12 @@ int gemm_common(const void *A, const void *B, const void *bias, void *C, int64_t
     }
     if (log_enabled())
         fprintf(stderr,
-                "[gba] M=%lld N=%lld K=%lld act=%s dtype=%s B=%s -> k%d %dx%dx%d w%dx%d s%d r%d g%d "
-                "(%s)\n",
+                "[gba] M=%lld N=%lld K=%lld act=%s dtype=%s A=%s B=%s -> k%d %dx%dx%d w%dx%d s%d r%d "
+                "g%d (%s)\n",
                 (long long)M, (long long)N, (long long)K, kActName[act], kDtName[dtype],
-                tb ? "NK" : "KN", sch.kernel, sch.bm, sch.bn, sch.bk, sch.wm, sch.wn, sch.stages,
+                (lay & LAY_TA) ? "KM" : "MK", (lay & LAY_TB) ? "NK" : "KN", sch.kernel, sch.bm, sch.bn, sch.bk, sch.wm, sch.wn, sch.stages,
                 sch.raster, sch.group_m, why);
-    return launch(sch, A, B, bias, C, M, N, K, act, dtype, tb);
+    return launch(sch, A, B, bias, C, M, N, K, act, dtype, lay);
 }
 
 template <int DT, int ACT>
@@ -623,7 +639,7 @@ int gba_list_schedule(int i, gba_schedule *out) {
     return GBA_OK;
 }
 
-static int get_schedule(int64_t M, int64_t N, int64_t K, int act, int dtype, bool tb,
+static int get_schedule(int64_t M, int64_t N, int64_t K, int act, int dtype, int lay,
                         gba_schedule *out) {
     if (!out) return GBA_ERR_NULL;
     int s = check_enums(act, dtype);
@@ -633,49 +649,56 @@ static int get_schedule(int64_t M, int64_t N, int64_t K, int act, int dtype, boo
     s = current_device(&d);
     if (s) return s;
     const char *why;
-    *out = choose(*d, M, N, K, act, dtype, tb, &why);
+    *out = choose(*d, M, N, K, act, dtype, lay, &why);
     return GBA_OK;
 }
 
 int gba_get_schedule(int64_t M, int64_t N, int64_t K, int act, int dtype, gba_schedule *out) {
-    return get_schedule(M, N, K, act, dtype, false, out);
+    return get_schedule(M, N, K, act, dtype, 0, out);
 }
 
 int gba_get_schedule_nt(int64_t M, int64_t N, int64_t K, int act, int dtype, gba_schedule *out) {
-    return get_schedule(M, N, K, act, dtype, true, out);
+    return get_schedule(M, N, K, act, dtype, LAY_TB, out);
+}
+
+int gba_get_schedule_ex(int64_t M, int64_t N, int64_t K, int act, int dtype, int flags,
+                        gba_schedule *out) {
+    if (flags & ~(GBA_TRANSPOSE_B | GBA_TRANSPOSE_A)) return GBA_ERR_SHAPE;
+    return get_schedule(M, N, K, act, dtype, flags & (GBA_TRANSPOSE_B | GBA_TRANSPOSE_A), out);
 }
 
 int gemm_bias_act(const void *A, const void *B, const void *bias, void *C, int64_t M, int64_t N,
                   int64_t K, int act, int dtype) {
-    return gemm_common(A, B, bias, C, M, N, K, act, dtype, false);
+    return gemm_common(A, B, bias, C, M, N, K, act, dtype, 0);
 }
 
 int gemm(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype) {
-    return gemm_common(A, B, nullptr, C, M, N, K, GBA_ACT_NONE, dtype, false);
+    return gemm_common(A, B, nullptr, C, M, N, K, GBA_ACT_NONE, dtype, 0);
 }
 
 int gemm_bias_act_nt(const void *A, const void *W, const void *bias, void *C, int64_t M,
                      int64_t N, int64_t K, int act, int dtype) {
-    return gemm_common(A, W, bias, C, M, N, K, act, dtype, true);
+    return gemm_common(A, W, bias, C, M, N, K, act, dtype, LAY_TB);
 }
 
 int gemm_nt(const void *A, const void *W, void *C, int64_t M, int64_t N, int64_t K, int dtype) {
-    return gemm_common(A, W, nullptr, C, M, N, K, GBA_ACT_NONE, dtype, true);
+    return gemm_common(A, W, nullptr, C, M, N, K, GBA_ACT_NONE, dtype, LAY_TB);
 }
 
 int gemm_bias_act_ex(const void *A, const void *B, const void *bias, void *C, int64_t M,
                      int64_t N, int64_t K, int act, int dtype, int flags, void *workspace,
                      size_t workspace_bytes) {
-    if (flags & ~GBA_TRANSPOSE_B) return GBA_ERR_SHAPE;
-    return gemm_common(A, B, bias, C, M, N, K, act, dtype, (flags & GBA_TRANSPOSE_B) != 0,
-                       workspace, workspace ? workspace_bytes : 0);
+    if (flags & ~(GBA_TRANSPOSE_B | GBA_TRANSPOSE_A)) return GBA_ERR_SHAPE;
+    return gemm_common(A, B, bias, C, M, N, K, act, dtype,
+                       flags & (GBA_TRANSPOSE_B | GBA_TRANSPOSE_A), workspace,
+                       workspace ? workspace_bytes : 0);
 }
 
 int gba_workspace_size(int64_t M, int64_t N, int64_t K, int act, int dtype, int flags,
                        size_t *bytes) {
     if (!bytes) return GBA_ERR_NULL;
     *bytes = 0;
-    if (flags & ~(GBA_TRANSPOSE_B | GBA_INPUT_FP8)) return GBA_ERR_SHAPE;
+    if (flags & ~(GBA_TRANSPOSE_B | GBA_INPUT_FP8 | GBA_TRANSPOSE_A)) return GBA_ERR_SHAPE;
     int s = check_enums(act, dtype);
     if (s) return s;
     if (M < 0 || N < 0 || K < 0) return GBA_ERR_SHAPE;
@@ -688,10 +711,10 @@ int gba_workspace_size(int64_t M, int64_t N, int64_t K, int act, int dtype, int 
         if (S8 > 1) *bytes = (size_t)S8 * (size_t)M * (size_t)N * 4u;
         return GBA_OK;
     }
-    const bool tb = (flags & GBA_TRANSPOSE_B) != 0;
+    const int lay = flags & (GBA_TRANSPOSE_B | GBA_TRANSPOSE_A);
     const char *why;
-    const gba_schedule sch = choose(*d, M, N, K, act, dtype, tb, &why);
-    const int S = split_count(sch, M, N, K, d->cus, dtype, tb);
+    const gba_schedule sch = choose(*d, M, N, K, act, dtype, lay, &why);
+    const int S = split_count(sch, M, N, K, d->cus, dtype, lay);
     if (S > 1) *bytes = (size_t)S * (size_t)M * (size_t)N * 4u;
     return GBA_OK;
 }
@@ -752,13 +775,14 @@ int gba_epilogue_probe(const float *z, float *y, int64_t n, int act) {
 int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_t M, int64_t N,
                  int64_t K, int act, int dtype, int flags, gba_schedule *best_out,
                  double *best_ms_out) {
+    const int lay = ((flags & GBA_TUNE_TRANSPOSE_B) ? LAY_TB : 0) |
+                    ((flags & GBA_TUNE_TRANSPOSE_A) ? LAY_TA : 0);
     bool nothing = false;
-    int s = check_gemm_args(A, B, bias, C, M, N, K, act, dtype, &nothing);
+    int s = check_gemm_args(A, B, bias, C, M, N, K, act, dtype, &nothing, lay);
     if (s) return s;
     const DeviceInfo *d;
     s = current_device(&d);
     if (s) return s;
-    const bool tb = (flags & GBA_TUNE_TRANSPOSE_B) != 0;
     if (nothing) {
         gba_schedule h = heuristic(M, N, d->cus);
         if (best_out) *best_out = h;
@@ -770,7 +794,7 @@ int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_
     for (int i = 0; i < kNumTable; ++i) {
         gba_schedule c = kTable[i]->sched;
         if (lds_bytes(c) > kLdsBytes) continue;   // the pages' shared-memory filter
-        if (tb && !kTable[i]->tb[0][0]) continue;   // no transpose_B path
+        if (!launcher(c, 0, 0, lay)) continue;   // no path for these layouts
         gba_schedule r0 = c;
         r0.raster = 0;
         cands.push_back(r0);
@@ -795,10 +819,10 @@ int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_
     int status = GBA_OK;
     for (const gba_schedule &c : cands) {
         for (int w = 0; w < 10 && status == GBA_OK; ++w)
-            status = launch(c, A, B, bias, C, M, N, K, act, dtype, tb);
+            status = launch(c, A, B, bias, C, M, N, K, act, dtype, lay);
         for (int r = 0; r < 50 && status == GBA_OK; ++r) {
             hipEventRecord(ev[r], t_stream);
-            status = launch(c, A, B, bias, C, M, N, K, act, dtype, tb);
+            status = launch(c, A, B, bias, C, M, N, K, act, dtype, lay);
         }
         if (status) break;
         hipEventRecord(ev[50], t_stream);
@@ -822,7 +846,7 @@ int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_
     for (auto &e : ev) hipEventDestroy(e);
     if (status) return status;
     // Leave the winner's result in C.
-    status = launch(best, A, B, bias, C, M, N, K, act, dtype, tb);
+    status = launch(best, A, B, bias, C, M, N, K, act, dtype, lay);
     if (status) return status;
     hipError_t he = hipStreamSynchronize(t_stream);
     if (he != hipSuccess) return hip_fail(he);
@@ -830,7 +854,7 @@ int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_
     if (best_ms_out) *best_ms_out = best_ms;
     std::lock_guard<std::mutex> lk(g_cache_mu);
     cache_load_locked();
-    g_cache[cache_key(*d, dtype, act, tb, M, N, K)] = CacheRec{best, best_ms};
+    g_cache[cache_key(*d, dtype, act, lay, M, N, K)] = CacheRec{best, best_ms};
     return cache_save_locked();
 }
 

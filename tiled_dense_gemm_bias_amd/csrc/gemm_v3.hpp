@@ -24,6 +24,12 @@
 // values, the same chunk XOR), is loaded like A, and its MFMA operand is read
 // like A's with ds_read_b128 -- no transposing reads. 16x16x32 MFMAs only.
 //
+// TA (transpose_A): A is given as a (K,M) row-major array At and the product is
+// At^T.B. At's tile then has B's shape and layout (BK k rows of BM M-contiguous
+// values, B's chunk XOR), is loaded like B (M edge masked per 16-byte chunk, K
+// edge by the descriptor range), and its MFMA operand is gathered like B's by
+// two transposing reads of four k rows each. 16x16x32 MFMAs only.
+//
 // PARTIAL (split-K, first pass): the grid holds `splits` work units per tile;
 // unit s covers K slices [s nk / splits, (s+1) nk / splits) and writes its raw
 // fp32 sums to part[s][M][N] instead of running the epilogue. The second pass
@@ -75,7 +81,7 @@ __device__ __forceinline__ int bswz(int r) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int MS, int DT,
-          int ACT, bool TB = false, bool PARTIAL = false>
+          int ACT, bool TB = false, bool PARTIAL = false, bool TA = false>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int M, int N, int K,
@@ -85,13 +91,15 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     constexpr int NTL = LDW * 64;         // loader threads
     constexpr int CHA = BK / 8;
     constexpr int CHB = BN / 8;
+    constexpr int CHT = BM / 8;           // chunks per k row of At's tile (TA)
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int BD = MS;                // MFMA output block: BD x BD
     constexpr int KS = MS == 32 ? 16 : 32;  // K depth of one MFMA
     constexpr int NI = MS == 32 ? 4 : 1;  // 4-column groups per lane and block
     constexpr int FM = WTM / BD, FN = WTN / BD;
     constexpr int NMF = FM * FN;          // MFMAs per step
-    constexpr int NPF = FM + (TB ? 1 : 2) * FN;   // fragment reads per step
+    constexpr int NFA = (TA ? 2 : 1) * FM;        // A fragment reads per step
+    constexpr int NPF = NFA + (TB ? 1 : 2) * FN;  // fragment reads per step
     constexpr int KK = BK / KS;           // steps per slice
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
     constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
@@ -105,6 +113,8 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     static_assert(WTM % BD == 0 && WTN % BD == 0, "wave tile must be whole MFMA blocks");
     static_assert(TB || BN >= 128, "B swizzle needs at least 16 chunks per row");
     static_assert(!TB || MS == 16, "transpose_B is written for 16x16x32 MFMAs");
+    static_assert(!TA || (MS == 16 && BM >= 128), "transpose_A: 16x16x32 MFMAs, at least 16 chunks per k row");
+    static_assert(!TA || (BK * CHT) % NTL == 0, "At slices split evenly");
     static_assert(LDW >= 1 && LDW <= NW && NW % LDW == 0, "loader waves");
     static_assert((BM * CHA) % NTL == 0 && (B_LD * NTL == (TB ? BN * CHA : BK * CHB)),
                   "slices split evenly");
@@ -150,16 +160,26 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // Loader lanes' byte offsets within a slice (row r, logical chunk c), fixed
     // for the whole K loop; the slice's K offset goes into the descriptor base.
     // K-contiguous tiles (A, and W when TB) also keep each load's first k.
-    constexpr int NKC = TB ? LD : A_LD;
+    // With TA, At's loads are row-major like B's: k row r, chunk c, masked at
+    // the M edge (no per-load k: the descriptor range ends at K).
     uint32_t off[LD];
-    int a_k[NKC];
+    int a_k[LD];
 #pragma unroll
-    for (int i = 0; i < NKC; ++i) {
-        const int s = (i < A_LD ? i : i - A_LD) * NTL + tid;
-        const int r = s / CHA, p = s % CHA;
-        const int c = aswz<MS, CHA>(r, p);
-        a_k[i] = c * 8;
-        off[i] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)c * 16u;
+    for (int i = 0; i < LD; ++i) {
+        a_k[i] = 0;
+        if (TA && i < A_LD) {
+            const int s = i * NTL + tid;
+            const int r = s / CHT, p = s % CHT;
+            const int c = p ^ bswz<CHT>(r);
+            off[i] = m0 + c * 8 < M ? (uint32_t)r * (uint32_t)M * 2u + (uint32_t)c * 16u
+                                    : kOobOffset;
+        } else if (i < A_LD || TB) {
+            const int s = (i < A_LD ? i : i - A_LD) * NTL + tid;
+            const int r = s / CHA, p = s % CHA;
+            const int c = aswz<MS, CHA>(r, p);
+            a_k[i] = c * 8;
+            off[i] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)c * 16u;
+        }
     }
     if constexpr (!TB) {
 #pragma unroll
@@ -185,9 +205,14 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         d.lb = d.la + A_BYTES;
         d.k0 = (kt0 + kt) * BK;
         const bool live = PARTIAL ? kt < nk : d.k0 < K;
-        const uint32_t bytes_a =
-            live ? (uint32_t)rows_a * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u;
-        d.ra = make_rsrc(A + (size_t)m0 * K + (live ? d.k0 : 0), bytes_a);
+        if constexpr (TA) {
+            const uint32_t bytes_a = live ? (uint32_t)min(K - d.k0, BK) * (uint32_t)M * 2u : 0u;
+            d.ra = make_rsrc(A + (size_t)(live ? d.k0 : 0) * M + m0, bytes_a);
+        } else {
+            const uint32_t bytes_a =
+                live ? (uint32_t)rows_a * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u;
+            d.ra = make_rsrc(A + (size_t)m0 * K + (live ? d.k0 : 0), bytes_a);
+        }
         if constexpr (TB) {
             const uint32_t bytes_b =
                 live ? (uint32_t)rows_b * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u;
@@ -200,7 +225,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     };
     auto dma_one = [&](const SliceDma &d, int i) {
         if (i < A_LD) {
-            const uint32_t o = d.k0 + a_k[i] < K ? off[i] : kOobOffset;
+            const uint32_t o = TA || d.k0 + a_k[i] < K ? off[i] : kOobOffset;
             buffer_load_lds16(d.ra, o, d.la + i * NTL * 16);
         } else if constexpr (TB) {
             const uint32_t o = d.k0 + a_k[i] < K ? off[i] : kOobOffset;
@@ -229,6 +254,13 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         const int c = (n >> 3) ^ bswz<CHB>(k);
         return A_BYTES + k * (BN * 2) + c * 16 + (n & 4) * 2;
     };
+    // TA: A operand of block fm gathered from At's tile like B^T's from B's.
+    auto t_addr = [&](int fm, int kk, int h) -> int {
+        const int k = kk * 32 + 8 * tg + 4 * h + (tj >> 2);
+        const int m = wm * WTM + fm * 16 + 4 * (tj & 3);
+        const int c = (m >> 3) ^ bswz<CHT>(k);
+        return k * (BM * 2) + c * 16 + (m & 4) * 2;
+    };
     // TB: W^T operand of block fn read like A's (row n of W's tile, K chunk).
     auto w_addr = [&](int fn, int kk) -> int {
         const int r = wn * WTN + fn * BD + lrow_b;
@@ -245,15 +277,26 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             for (int e = 0; e < Acc<MS>::n; ++e) acc[a][b][e] = 0.0f;
 
     u32x4 fa[2][FM];
+    i16x4 fal[2][FM], fah[2][FM];
     i16x4 fbl[2][FN], fbh[2][FN];
     u32x4 fw[2][FN];
     auto read_one = [&](int buf, const char *base, int kk, int r) {
-        if (r < FM) {
-            fa[buf][r] = *reinterpret_cast<const u32x4 *>(base + a_addr(r, kk));
+        if (r < NFA) {
+            if constexpr (TA) {
+                const int fm = r >> 1, h = r & 1;
+                const i16x4 v =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((GBA_LDS i16x4 *)(base + t_addr(fm, kk, h)));
+                if (h)
+                    fah[buf][fm] = v;
+                else
+                    fal[buf][fm] = v;
+            } else {
+                fa[buf][r] = *reinterpret_cast<const u32x4 *>(base + a_addr(r, kk));
+            }
         } else if constexpr (TB) {
-            fw[buf][r - FM] = *reinterpret_cast<const u32x4 *>(base + w_addr(r - FM, kk));
+            fw[buf][r - NFA] = *reinterpret_cast<const u32x4 *>(base + w_addr(r - NFA, kk));
         } else {
-            const int fn = (r - FM) >> 1, h = (r - FM) & 1;
+            const int fn = (r - NFA) >> 1, h = (r - NFA) & 1;
             const i16x4 v =
                 __builtin_amdgcn_ds_read_tr16_b64_v4i16((GBA_LDS i16x4 *)(base + b_addr(fn, kk, h)));
             if (h)
@@ -278,10 +321,16 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             else
                 bop = __builtin_bit_cast(u32x4, __builtin_shufflevector(fbl[cur][fn], fbh[cur][fn],
                                                                         0, 1, 2, 3, 4, 5, 6, 7));
-            if constexpr (MS == 32)
-                acc[fn][fm] = mfma32x32x16<DT>(bop, fa[cur][fm], acc[fn][fm]);
+            u32x4 aop;
+            if constexpr (TA)
+                aop = __builtin_bit_cast(u32x4, __builtin_shufflevector(fal[cur][fm], fah[cur][fm],
+                                                                        0, 1, 2, 3, 4, 5, 6, 7));
             else
-                acc[fn][fm] = mfma16x16x32<DT>(bop, fa[cur][fm], acc[fn][fm]);
+                aop = fa[cur][fm];
+            if constexpr (MS == 32)
+                acc[fn][fm] = mfma32x32x16<DT>(bop, aop, acc[fn][fm]);
+            else
+                acc[fn][fm] = mfma16x16x32<DT>(bop, aop, acc[fn][fm]);
             if (q < NPF) read_one(cur ^ 1, pf_base, pf_kk, q);
             if (dma && q % every == 0 && q / every < nd) dma_one(d, d0 + q / every);
             __builtin_amdgcn_sched_barrier(0);
@@ -414,14 +463,14 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int MS, int DT,
-          int ACT, bool TB = false>
+          int ACT, bool TB = false, bool TA = false>
 hipError_t launch_gemm_v3(const void *A, const void *B, const void *bias, void *C, int M, int N,
                           int K, int raster, int group_m, hipStream_t stream) {
     const int tiles_m = ceil_div(M, BM), tiles_n = ceil_div(N, BN);
     const long long grid = (long long)tiles_m * tiles_n;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL - kGridX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, BK, WM, WN, STAGES, LDW, SPREAD, MS, DT, ACT, TB>),
+    hipLaunchKernelGGL((gemm_v3_kernel<BM, BN, BK, WM, WN, STAGES, LDW, SPREAD, MS, DT, ACT, TB, false, TA>),
                        tile_grid(grid), dim3(WM * WN * 64), 0, stream, (const uint16_t *)A,
                        (const uint16_t *)B, (const uint16_t *)bias, (uint16_t *)C, M, N, K, tiles_m,
                        tiles_n, raster, group_m < 1 ? 1 : group_m, 1, (float *)nullptr);
@@ -430,7 +479,8 @@ hipError_t launch_gemm_v3(const void *A, const void *B, const void *bias, void *
 
 // Split-K first pass: `splits` units per tile write fp32 partials to part
 // ([splits][M][N]); the epilogue runs in splitk_reduce_kernel.
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int DT, bool TB>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int DT, bool TB,
+          bool TA = false>
 hipError_t launch_gemm_v3_partial(const void *A, const void *B, float *part, int M, int N, int K,
                                   int splits, int raster, int group_m, hipStream_t stream) {
     const int tiles_m = ceil_div(M, BM), tiles_n = ceil_div(N, BN);
@@ -438,7 +488,7 @@ hipError_t launch_gemm_v3_partial(const void *A, const void *B, float *part, int
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL - kGridX || splits < 1) return hipErrorInvalidValue;
     hipLaunchKernelGGL(
-        (gemm_v3_kernel<BM, BN, BK, WM, WN, STAGES, LDW, SPREAD, 16, DT, ACT_NONE, TB, true>),
+        (gemm_v3_kernel<BM, BN, BK, WM, WN, STAGES, LDW, SPREAD, 16, DT, ACT_NONE, TB, true, TA>),
         tile_grid(grid), dim3(WM * WN * 64), 0, stream, (const uint16_t *)A, (const uint16_t *)B,
         (const uint16_t *)nullptr, (uint16_t *)nullptr, M, N, K, tiles_m, tiles_n, raster,
         group_m < 1 ? 1 : group_m, splits, part);

@@ -10,14 +10,15 @@
 // (bias, activation, rounding, stores) runs, and the next main loop starts
 // without the pipeline fill of a fresh workgroup. Tiles, LDS layouts,
 // fragments, MFMA order and epilogue are gemm_v3's (results are bit-identical).
-// TB (transpose_B, B given as an (N,K) array W) is gemm_v3's TB layout.
+// TB (transpose_B, B given as an (N,K) array W) is gemm_v3's TB layout, and TA
+// (transpose_A, A given as a (K,M) array At) gemm_v3's TA layout.
 #pragma once
 
 #include "gemm_v3.hpp"
 
 namespace gba {
 
-template <int BM, int BN, int WM, int WN, int DT, int ACT, bool TB = false>
+template <int BM, int BN, int WM, int WN, int DT, int ACT, bool TB = false, bool TA = false>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                const uint16_t *__restrict__ bias, uint16_t *__restrict__ C, int M, int N, int K,
@@ -27,7 +28,8 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     constexpr int CHA = BK / 8, CHB = BN / 8;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / BD, FN = WTN / BD;
-    constexpr int NMF = FM * FN, NPF = FM + (TB ? 1 : 2) * FN;
+    constexpr int NFA = (TA ? 2 : 1) * FM;
+    constexpr int NMF = FM * FN, NPF = NFA + (TB ? 1 : 2) * FN;
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
     constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     constexpr int A_LD = BM * CHA / NT, B_LD = (TB ? BN * CHA : BK * CHB) / NT, LD = A_LD + B_LD;
@@ -35,6 +37,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     static_assert(KK == 2, "two MFMA steps per slice");
     static_assert(WTM % BD == 0 && WTN % BD == 0, "wave tile must be whole MFMA blocks");
     static_assert(BN >= 128, "B swizzle needs at least 16 chunks per row");
+    static_assert(!TA || BM == BN, "At's tile is loaded with B's per-thread mapping");
     static_assert((BM * CHA) % NT == 0 && B_LD * NT == (TB ? BN * CHA : BK * CHB),
                   "slices split evenly");
     static_assert(2 * STAGE_BYTES <= 160 * 1024, "LDS ring too large");
@@ -93,12 +96,14 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const uint32_t a_base = (uint32_t)(tid >> 3) * (uint32_t)K * 2u + (uint32_t)c_a * 16u;
     const int c_b0 = (tid & 31) ^ bswz<CHB>(tid >> 5);
     const uint32_t b_row = (uint32_t)(tid >> 5) * (uint32_t)N * 2u;
+    // TA: At's tile (64 k rows of BM = BN values) is loaded like B's.
+    const uint32_t t_row = (uint32_t)(tid >> 5) * (uint32_t)M * 2u;
     // Loads of slice kt of tile t (live) into stage `stage`; a dead slice reads
     // nothing (every lane out of range) but keeps the wait counts uniform.
     struct SliceDma {
         __amdgpu_buffer_rsrc_t ra, rb;
         uint32_t la, lb;
-        int k0, n0;
+        int k0, n0, m0;
     };
     auto slice_dma = [&](const Tile &t, bool live, int kt, int stage) {
         SliceDma d;
@@ -106,8 +111,13 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         d.lb = d.la + A_BYTES;
         d.k0 = live ? kt * BK : K;
         d.n0 = live ? t.n0 : N;
-        d.ra = make_rsrc(A + (live ? (size_t)t.m0 * K + d.k0 : 0),
-                         live ? (uint32_t)t.rows * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u);
+        d.m0 = live ? t.m0 : M;
+        if constexpr (TA)
+            d.ra = make_rsrc(A + (live ? (size_t)d.k0 * M + t.m0 : 0),
+                             live ? (uint32_t)min(K - d.k0, BK) * (uint32_t)M * 2u : 0u);
+        else
+            d.ra = make_rsrc(A + (live ? (size_t)t.m0 * K + d.k0 : 0),
+                             live ? (uint32_t)t.rows * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u);
         if constexpr (TB)
             d.rb = make_rsrc(B + (live ? (size_t)t.n0 * K + d.k0 : 0),
                              live ? (uint32_t)min(N - t.n0, BN) * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u
@@ -130,10 +140,18 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // `kx`, `nx`: K and N re-read opaquely in each slice, so that the per-load
     // row offsets (multiples of 64 K and 16 N bytes) are recomputed where used
     // rather than held in scalar registers for the whole loop.
-    auto dma_one = [&](const SliceDma &d, int i, uint32_t kx, uint32_t nx) {
+    auto dma_one = [&](const SliceDma &d, int i, uint32_t kx, uint32_t nx, uint32_t mx) {
         if (i < A_LD) {
-            const uint32_t o = d.k0 + c_a * 8 < K ? a_base + (uint32_t)(i * 64) * kx : kOobOffset;
-            buffer_load_lds16(d.ra, o, d.la + i * NT * 16);
+            if constexpr (TA) {
+                const int c = c_b0 ^ (8 * (i & 3));
+                const uint32_t o = d.m0 + c * 8 < M
+                                       ? t_row + (uint32_t)(i * 16) * mx + (uint32_t)c * 16u
+                                       : kOobOffset;
+                buffer_load_lds16(d.ra, o, d.la + i * NT * 16);
+            } else {
+                const uint32_t o = d.k0 + c_a * 8 < K ? a_base + (uint32_t)(i * 64) * kx : kOobOffset;
+                buffer_load_lds16(d.ra, o, d.la + i * NT * 16);
+            }
         } else if constexpr (TB) {
             const int j = i - A_LD;
             const uint32_t o = d.k0 + c_a * 8 < K ? a_base + (uint32_t)(j * 64) * kx : kOobOffset;
@@ -180,6 +198,20 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         }
     }
     auto a_addr = [&](int fm, int kk) -> uint32_t { return fa_base[kk] + fm * BD * (BK * 2); };
+    // TA: A block fm, step kk, half h gathered from At's tile like B^T's from
+    // B's. Lane l asks for k row 32 kk + 8 (l/16) + 4 h + (l%16)/4 and m =
+    // wm*WTM + 16 fm + 4 (l%4); 16 fm rows flip only chunk bits 1..3 (byte
+    // address bits 5..7) of the fm = 0 address, so one base serves every block.
+    uint32_t ft_base;
+    {
+        const int k = 8 * tg + (tj >> 2);
+        const int m = wm * WTM + 4 * (tj & 3);
+        const int c = (m >> 3) ^ bswz<CHB>(k);
+        ft_base = (uint32_t)(k * (BM * 2) + c * 16 + (m & 4) * 2);
+    }
+    auto t_addr = [&](int fm, int kk, int h) -> uint32_t {
+        return (ft_base ^ (uint32_t)(fm << 5)) + (32 * kk + 4 * h) * (BM * 2);
+    };
     auto b_addr = [&](int fn, int kk, int h) -> uint32_t {
         if constexpr (TB)
             return fb_base[kk] + fn * BD * (BK * 2);
@@ -189,15 +221,26 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 
     f32x4 acc[FN][FM];
     u32x4 fa[2][FM];
+    i16x4 fal[2][FM], fah[2][FM];
     i16x4 fbl[2][FN], fbh[2][FN];
     u32x4 fw[2][FN];
     auto read_one = [&](int buf, const char *base, int kk, int r) {
-        if (r < FM) {
-            fa[buf][r] = *reinterpret_cast<const u32x4 *>(base + a_addr(r, kk));
+        if (r < NFA) {
+            if constexpr (TA) {
+                const int fm = r >> 1, h = r & 1;
+                const i16x4 v =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((GBA_LDS i16x4 *)(base + t_addr(fm, kk, h)));
+                if (h)
+                    fah[buf][fm] = v;
+                else
+                    fal[buf][fm] = v;
+            } else {
+                fa[buf][r] = *reinterpret_cast<const u32x4 *>(base + a_addr(r, kk));
+            }
         } else if constexpr (TB) {
-            fw[buf][r - FM] = *reinterpret_cast<const u32x4 *>(base + b_addr(r - FM, kk, 0));
+            fw[buf][r - NFA] = *reinterpret_cast<const u32x4 *>(base + b_addr(r - NFA, kk, 0));
         } else {
-            const int fn = (r - FM) >> 1, h = (r - FM) & 1;
+            const int fn = (r - NFA) >> 1, h = (r - NFA) & 1;
             const i16x4 v =
                 __builtin_amdgcn_ds_read_tr16_b64_v4i16((GBA_LDS i16x4 *)(base + b_addr(fn, kk, h)));
             if (h)
@@ -209,7 +252,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // One MFMA step on buffer `cur`; `reads`: the next step's fragments (from
     // `pf_base` step pf_kk); `dma`: all LD loads of slice d, one per EVERY MFMAs.
     auto step = [&](int cur, bool reads, const char *pf_base, int pf_kk, bool dma,
-                    const SliceDma &d, uint32_t kx, uint32_t nx) {
+                    const SliceDma &d, uint32_t kx, uint32_t nx, uint32_t mx) {
 #pragma unroll
         for (int q = 0; q < NMF; ++q) {
             const int fn = q / FM, fm = q % FM;
@@ -219,9 +262,15 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             else
                 bop = __builtin_bit_cast(u32x4, __builtin_shufflevector(fbl[cur][fn], fbh[cur][fn],
                                                                         0, 1, 2, 3, 4, 5, 6, 7));
-            acc[fn][fm] = mfma16x16x32<DT>(bop, fa[cur][fm], acc[fn][fm]);
+            u32x4 aop;
+            if constexpr (TA)
+                aop = __builtin_bit_cast(u32x4, __builtin_shufflevector(fal[cur][fm], fah[cur][fm],
+                                                                        0, 1, 2, 3, 4, 5, 6, 7));
+            else
+                aop = fa[cur][fm];
+            acc[fn][fm] = mfma16x16x32<DT>(bop, aop, acc[fn][fm]);
             if (reads && q < NPF) read_one(cur ^ 1, pf_base, pf_kk, q);
-            if (dma && q % EVERY == 0) dma_one(d, q / EVERY, kx, nx);
+            if (dma && q % EVERY == 0) dma_one(d, q / EVERY, kx, nx, mx);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -235,9 +284,9 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         const SliceDma d0 = slice_dma(cur_t, true, 0, 0), d1 = slice_dma(cur_t, true, 1, 1);
         if (bias) bias_dma(cur_t, 0);   // lands with slice 0 (waited for below)
 #pragma unroll
-        for (int i = 0; i < LD; ++i) dma_one(d0, i, (uint32_t)K, (uint32_t)N);
+        for (int i = 0; i < LD; ++i) dma_one(d0, i, (uint32_t)K, (uint32_t)N, (uint32_t)M);
 #pragma unroll
-        for (int i = 0; i < LD; ++i) dma_one(d1, i, (uint32_t)K, (uint32_t)N);
+        for (int i = 0; i < LD; ++i) dma_one(d1, i, (uint32_t)K, (uint32_t)N, (uint32_t)M);
     }
     wait_vmcnt<LD>();
     block_barrier();
@@ -262,9 +311,9 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             const int sc = (stage0 + kt) & 1;
             const char *cur_base = smem + sc * STAGE_BYTES;
             const char *nxt_base = smem + (sc ^ 1) * STAGE_BYTES;
-            uint32_t kx = (uint32_t)K, nx = (uint32_t)N;
-            asm volatile("" : "+s"(kx), "+s"(nx));
-            step(0, true, cur_base, 1, false, SliceDma{}, kx, nx);
+            uint32_t kx = (uint32_t)K, nx = (uint32_t)N, mx = (uint32_t)M;
+            asm volatile("" : "+s"(kx), "+s"(nx), "+s"(mx));
+            step(0, true, cur_base, 1, false, SliceDma{}, kx, nx, mx);
             wait_vmcnt_lgkm0<0>();
             block_barrier();
             const bool here = kt + 2 < nk;
@@ -274,7 +323,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             // (this tile's epilogue still reads its own). Landed by the next
             // slice's vmcnt(0) wait, long before that tile's epilogue.
             if (bias && !here && kt + 2 == nk && nxt_live) bias_dma(nxt_t, (r + 1) & 1);
-            step(1, true, nxt_base, 0, true, dn, kx, nx);
+            step(1, true, nxt_base, 0, true, dn, kx, nx, mx);
         }
 
         // Epilogue of this tile while the next tile's first slices land. The
@@ -346,7 +395,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 // Grid: one workgroup per CU (two 64 KiB stages fill the LDS), or fewer when
 // there are fewer tiles. K must exceed 64 (at least two K slices per tile): the
 // library sends K <= 64 to gemm_v3 with the same tile.
-template <int BM, int BN, int WM, int WN, int DT, int ACT, bool TB = false>
+template <int BM, int BN, int WM, int WN, int DT, int ACT, bool TB = false, bool TA = false>
 hipError_t launch_gemm_v5(const void *A, const void *B, const void *bias, void *C, int M, int N,
                           int K, int raster, int group_m, hipStream_t stream) {
     const int tiles_m = ceil_div(M, BM), tiles_n = ceil_div(N, BN);
@@ -359,7 +408,7 @@ hipError_t launch_gemm_v5(const void *A, const void *B, const void *bias, void *
     const hipError_t e = current_cus(&cus);
     if (e != hipSuccess) return e;
     const int grid = (int)(tiles < cus ? tiles : cus);
-    hipLaunchKernelGGL((gemm_v5_kernel<BM, BN, WM, WN, DT, ACT, TB>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((gemm_v5_kernel<BM, BN, WM, WN, DT, ACT, TB, TA>), dim3((unsigned)grid),
                        dim3(WM * WN * 64), 0, stream, (const uint16_t *)A, (const uint16_t *)B,
                        (const uint16_t *)bias, (uint16_t *)C, M, N, K, tiles_m, tiles_n, raster,
                        group_m < 1 ? 1 : group_m);
