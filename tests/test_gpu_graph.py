@@ -1,4 +1,5 @@
-"""The transpose_B, 8-bit and split-K entry points captured into one HIP graph.
+"""The transpose_B, transpose_A, 8-bit and split-K entry points captured into
+HIP graphs.
 
 None of them allocates, copies, fills or synchronises, so a caller can capture
 them. Replays, with eager work and device synchronisation between them and the
@@ -75,6 +76,57 @@ def test_new_entry_points_replay_like_eager():
             o.fill_(0.0)
         ws.fill_(255)   # the workspace carries nothing between calls
         say("graph replay", r)
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, ref in zip(outs, refs[i]):
+            assert torch.equal(o.view(torch.int16), ref.view(torch.int16)), r
+
+
+def test_transpose_a_replays_like_eager():
+    import torch
+    # transpose_A with B [K,N] (f16, 520 x 776 x 328) and with W [N,K] plus split-K
+    # (bf16, 256 x 384 x 4096)
+    At1 = [synth.random_bits((328, 520), "f16", s) for s in (11, 12)]
+    B1 = synth.random_bits((328, 776), "f16", 13)
+    b1 = synth.random_bits((776,), "f16", 14)
+    At2 = [synth.random_bits((4096, 256), "bf16", s) for s in (15, 16)]
+    W2 = synth.random_bits((384, 4096), "bf16", 17, scale=1 / 64)
+    b2 = synth.random_bits((384,), "bf16", 18)
+    nb = gba.workspace_size(256, 384, 4096, "gelu", "bf16", transpose_b=True, transpose_a=True)
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    a1 = [to_dev(x, "f16") for x in At1]
+    a2 = [to_dev(x, "bf16") for x in At2]
+    bm1, bb1 = to_dev(B1, "f16"), to_dev(b1, "f16")
+    w2, bb2 = to_dev(W2, "bf16"), to_dev(b2, "bf16")
+
+    def run_all(x1, x2, c1, c2):
+        gba.gemm_bias_act(x1, bm1, bb1, c1, "sigmoid", transpose_a=True)
+        gba.gemm_bias_act(x2, w2, bb2, c2, "gelu", transpose_a=True, transpose_b=True,
+                          workspace=ws)
+
+    refs = []
+    for i in range(2):
+        outs = (empty((520, 776), "f16"), empty((256, 384), "bf16"))
+        run_all(a1[i], a2[i], *outs)
+        refs.append(outs)
+    torch.cuda.synchronize()
+
+    src = (a1[0].clone(), a2[0].clone())
+    outs = (empty((520, 776), "f16"), empty((256, 384), "bf16"))
+    graph = torch.cuda.CUDAGraph()
+    say("graph capture: transpose_A, transpose_A + transpose_B + split-K")
+    with torch.cuda.graph(graph):
+        run_all(*src, *outs)
+    torch.cuda.synchronize()
+    for r in range(4):
+        i = r % 2
+        src[0].copy_(a1[i])
+        src[1].copy_(a2[i])
+        for o in outs:
+            o.fill_(0.0)
+        ws.fill_(255)
+        say("graph replay transpose_A", r)
         graph.replay()
         torch.cuda.synchronize()
         for o, ref in zip(outs, refs[i]):

@@ -1,8 +1,8 @@
 """Entry points at the sizes the header gives as limits, through the C ABI.
 
 K = 2^21 (every compiled-in schedule, both B layouts, split-K, 8-bit inputs),
-N = 2^23 (2^30 for bias_act) and M = 2^31 - 1 (the largest tile offsets; the
-last tile is ragged). Inputs are small integers, so every sum is exact in fp32
+N = 2^23 (2^30 for bias_act), M = 2^31 - 1 (the largest tile offsets; the
+last tile is ragged) and, with A stored [K, M], M = 2^23. Inputs are small integers, so every sum is exact in fp32
 and the results must equal the fp64 oracle's bitwise (relu, or no activation).
 
 At M = 2^31 - 1 and at N = 2^30 the inputs repeat with period P along the large
@@ -324,3 +324,44 @@ def test_max_n_bias_act(_free):
         assert torch.equal(yi[:, c0:c1], yi[:, c0 - L:c1 - L]), "columns %d..%d" % (c0, c1)
     g = flat.view(torch.int16)[M * N:]
     assert bool((g == int(np.uint16(SENT).view(np.int16))).all()), "write past the end of Y"
+
+
+def test_max_m_transpose_a_every_schedule_both_layouts(_free):
+    # A stored [K, M]: M is then a row pitch, limited to 2^23 like N. At's columns
+    # repeat with period P, so C's rows do; K = 72 is a 64-deep slice and a tail,
+    # N = 24 a ragged column tile.
+    import torch
+    M, N, K = NMAX, 24, 72
+    rng = np.random.default_rng(35)
+    T = enc(rng.integers(-1, 2, (K, P), dtype=np.int8), "bf16")   # At's first P columns
+    W = enc(rng.integers(-1, 2, (N, K), dtype=np.int8), "bf16")
+    bias = enc(rng.integers(-8, 9, N, dtype=np.int8), "bf16")
+    want = oracle.encode(oracle.gemm_bias_act(T, W, bias, "relu", "bf16", transpose_a=True,
+                                              transpose_b=True), "bf16")
+    say("max M transpose_A: building At", K, M)
+    td = to_dev(T, "bf16")
+    at = td.repeat(1, -(-M // P))[:, :M].contiguous()
+    del td
+    w, bb = to_dev(W, "bf16"), to_dev(bias, "bf16")
+    b = to_dev(np.ascontiguousarray(W.T), "bf16")
+    flat, c = guarded(M, N, "bf16")
+    ran = 0
+    for s in [None] + gba.list_schedules():
+        for tb in (False, True):
+            refill(flat)
+            say("max M transpose_A", "heuristic" if s is None else sched_id(s),
+                "NK" if tb else "KN")
+            gba.set_schedule(s)
+            try:
+                gba.gemm_bias_act(at, w if tb else b, bb, c, "relu", transpose_b=tb,
+                                  transpose_a=True)
+            except gba.GbaError as e:
+                if s is not None and e.status == 9:   # no transpose_A path in this kernel
+                    continue
+                raise
+            finally:
+                gba.set_schedule(None)
+            torch.cuda.synchronize()
+            check_row_periodic(flat, c, want)
+            ran += 1
+    assert ran >= 12
