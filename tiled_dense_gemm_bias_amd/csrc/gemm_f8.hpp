@@ -98,7 +98,11 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
     // A tile's bias, staged in LDS with the tile's first slice (as in the 16-bit
     // persistent kernel): one 1 KiB slot per wave and per tile parity.
     __shared__ __attribute__((aligned(1024))) char bias_smem[2 * 4 * 1024];
-    static_assert(2 * STAGE_BYTES + 2 * 4 * 1024 <= 160 * 1024, "LDS ring + bias slots too large");
+    // Epilogue staging: two buffers of 16 rows x 64 columns of C per wave.
+    constexpr int STG_BYTES = 16 * 64 * 2;
+    __shared__ __attribute__((aligned(1024))) char stage_smem[PARTIAL ? 16 : 4 * 2 * STG_BYTES];
+    static_assert(2 * STAGE_BYTES + 2 * 4 * 1024 + 4 * 2 * STG_BYTES <= 160 * 1024,
+                  "LDS ring + bias slots + staging too large");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
@@ -280,38 +284,77 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
-            char *const Ct = reinterpret_cast<char *>(C + (size_t)cur_t.m0 * N + cur_t.n0);
-            int c0 = wn * WTN + 4 * tg, mr = mrow;
-            asm volatile("" : "+v"(mr));
-            uint32_t lane_off = ((uint32_t)mr * (uint32_t)N + (uint32_t)c0) * 2u;
-            uint32_t pitch16 = (uint32_t)N * (2u * BD);
-            asm volatile("" : "+v"(lane_off), "+v"(c0), "+s"(pitch16));
-            const bool full = M - cur_t.m0 >= BM && N - cur_t.n0 >= BN;   // no m0 + BM: overflows near 2^31
-            const char *const bias_mine = bias_smem + ((r & 1) * 4 + wid_s) * 1024;
+            // As in the 16-bit persistent kernel: the wave's 128 x 128 block leaves
+            // through two alternating 16 x 64 staging buffers of its own in LDS,
+            // so that each 16-byte store instruction writes 8 whole 128-byte row
+            // segments; the bias is converted to fp32 once per tile (upper half of
+            // the wave's slot) and read into registers once per column half.
+            int ln;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+            const int wn_s = wid_s & 1, wm_s = wid_s >> 1;
+            char *const bias_mine = bias_smem + ((r & 1) * 4 + wid_s) * 1024;
+            if (bias) {
+                const uint32_t bb =
+                    *reinterpret_cast<const uint32_t *>(bias_mine + wn_s * (WTN * 2) + 4 * ln);
+                *reinterpret_cast<f32x2 *>(bias_mine + 512 + 8 * ln) =
+                    f32x2{to_f32<DT>(bb & 0xffffu), to_f32<DT>(bb >> 16)};
+            }
+            char *const stg = stage_smem + wid_s * 2 * STG_BYTES;
+            const int wr = ln & 15, wg = ln >> 4;   // write side: row, 4-column group
+            const int rr = ln >> 3, rc = ln & 7;    // read side: row (of 8), 16-byte chunk
+            char *const Cw = reinterpret_cast<char *>(C + (size_t)cur_t.m0 * N + cur_t.n0) +
+                             ((size_t)wm_s * WTM * N + (size_t)wn_s * WTN) * 2;
+            uint32_t st_off = (uint32_t)rr * (uint32_t)N * 2u + (uint32_t)rc * 16u;
+            uint32_t pitch8 = (uint32_t)N * 16u;   // bytes between read rows rr and rr + 8
+            asm volatile("" : "+v"(st_off), "+s"(pitch8));
+            const int rows_left = M - cur_t.m0 - wm_s * WTM, cols_left = N - cur_t.n0 - wn_s * WTN;
+            const bool full = rows_left >= WTM && cols_left >= WTN;   // no m0 + BM: overflows near 2^31
+            constexpr int NG = 2 * FM;
             auto store_all = [&](auto masked) {
+                f32x4 bq[4];
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
-                    const int cn = c0 + fn * BD;
-                    if (masked && cur_t.n0 + cn >= N) continue;
-                    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
-                    if (bias) {
-                        const u32x2 bb = *reinterpret_cast<const u32x2 *>(bias_mine + cn * 2);
-                        b0 = to_f32<DT>(bb.x & 0xffffu);
-                        b1 = to_f32<DT>(bb.x >> 16);
-                        b2 = to_f32<DT>(bb.y & 0xffffu);
-                        b3 = to_f32<DT>(bb.y >> 16);
+                for (int g = 0; g <= NG; ++g) {
+                    u32x4 v[2];
+                    if (g > 0) {
+                        const char *const sb = stg + ((g - 1) & 1) * STG_BYTES;
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            v[j] = *reinterpret_cast<const u32x4 *>(sb + (8 * j + rr) * 128 +
+                                                                    ((rc ^ (rr & 7)) * 16));
                     }
+                    if (g < NG) {
+                        const int fh = g / FM, fm = g % FM;
+                        char *const sb = stg + (g & 1) * STG_BYTES;
+                        if (g % FM == 0) {
 #pragma unroll
-                    for (int fm = 0; fm < FM; ++fm) {
-                        if (masked && cur_t.m0 + mr + fm * BD >= M) continue;
-                        const f32x4 a = acc_value(acc[fn][fm]);
-                        u32x2 o;
-                        o.x = pack2<DT>(act_fn<ACT>(fmaf(a[0], scale, b0)),
-                                        act_fn<ACT>(fmaf(a[1], scale, b1)));
-                        o.y = pack2<DT>(act_fn<ACT>(fmaf(a[2], scale, b2)),
-                                        act_fn<ACT>(fmaf(a[3], scale, b3)));
-                        const uint32_t offs = lane_off + (uint32_t)fm * pitch16 + (uint32_t)(fn * BD) * 2u;
-                        *reinterpret_cast<u32x2 *>(Ct + offs) = o;
+                            for (int f = 0; f < 4; ++f)
+                                bq[f] = bias ? *reinterpret_cast<const f32x4 *>(
+                                                   bias_mine + 512 + (16 * (4 * fh + f) + 4 * wg) * 4)
+                                             : f32x4{0.f, 0.f, 0.f, 0.f};
+                        }
+#pragma unroll
+                        for (int f = 0; f < 4; ++f) {
+                            const f32x4 a = acc_value(acc[4 * fh + f][fm]);
+                            u32x2 o;
+                            o.x = pack2<DT>(act_fn<ACT>(fmaf(a[0], scale, bq[f][0])),
+                                            act_fn<ACT>(fmaf(a[1], scale, bq[f][1])));
+                            o.y = pack2<DT>(act_fn<ACT>(fmaf(a[2], scale, bq[f][2])),
+                                            act_fn<ACT>(fmaf(a[3], scale, bq[f][3])));
+                            const int chunk = 2 * f + (wg >> 1);
+                            *reinterpret_cast<u32x2 *>(sb + wr * 128 + ((chunk ^ (wr & 7)) * 16) +
+                                                       (wg & 1) * 8) = o;
+                        }
+                    }
+                    if (g > 0) {
+                        const int fh = (g - 1) / FM, fm = (g - 1) % FM;
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            if (masked && (fm * BD + 8 * j + rr >= rows_left || fh * 64 + rc * 8 >= cols_left))
+                                continue;
+                            const uint32_t offs = st_off + (uint32_t)(2 * fm + j) * pitch8 +
+                                                  (uint32_t)(fh * 128);
+                            *reinterpret_cast<u32x4 *>(Cw + offs) = v[j];
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
