@@ -124,6 +124,13 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     static_assert(LD_STEP <= NMF, "at most one load per MFMA");
 
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+    // Epilogue staging (16x16x32 MFMAs): two buffers of 16 rows x 64 columns of C
+    // per wave, as in the persistent kernel.
+    constexpr bool STAGED = MS == 16 && !PARTIAL;
+    constexpr int STG_BYTES = 16 * 64 * 2;
+    __shared__ __attribute__((aligned(1024))) char stage_smem[STAGED ? NW * 2 * STG_BYTES : 16];
+    static_assert(!STAGED || (WTN % 64 == 0 && STAGES * STAGE_BYTES + NW * 2 * STG_BYTES <= 160 * 1024),
+                  "staged epilogue: 64-column halves, LDS ring + staging within 160 KiB");
 
     static_assert(!PARTIAL || MS == 16, "split-K is written for 16x16x32 MFMAs");
     int tm, tn, split = 0;
@@ -405,7 +412,88 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         return;
     }
 
-    // Epilogue: + bias[n], activation, round once, 8-byte stores. Addresses are a
+    if constexpr (STAGED) {
+        // + bias[n], activation, round once; each group of four 16x16 blocks (one
+        // row block fm, one 64-column half fh) goes through the wave's staging
+        // buffers and leaves as 16-byte stores of whole 128-byte row segments (8
+        // rows per store instruction). Two buffers alternate so the LDS round trip
+        // of group g - 1 overlaps the arithmetic of group g. Lane l holds row l % 16
+        // and columns 16 fn + 4 (l / 16) .. +3 of the MFMA blocks.
+        const int wid_u = __builtin_amdgcn_readfirstlane(wid);
+        char *const stg = stage_smem + wid_u * 2 * STG_BYTES;
+        const int wr = lane & 15, wg = lane >> 4;   // write side: row, 4-column group
+        const int rr = lane >> 3, rc = lane & 7;    // read side: row (of 8), 16-byte chunk
+        char *const Cw = reinterpret_cast<char *>(C + (size_t)m0 * N + n0) +
+                         ((size_t)wm * WTM * N + (size_t)wn * WTN) * 2;
+        const uint32_t st_off = (uint32_t)rr * (uint32_t)N * 2u + (uint32_t)rc * 16u;
+        const uint32_t pitch8 = (uint32_t)N * 16u;   // bytes between read rows rr and rr + 8
+        const int rows_left = M - m0 - wm * WTM, cols_left = N - n0 - wn * WTN;
+        const bool full = rows_left >= WTM && cols_left >= WTN;   // no m0 + BM: overflows near 2^31
+        // bias of the lane's columns, columns past N as zero
+        u32x2 bvals[FN];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int cn = wn * WTN + fn * BD + 4 * wg;
+            bvals[fn] = bias && n0 + cn < N ? *reinterpret_cast<const u32x2 *>(bias + n0 + cn)
+                                            : u32x2{0u, 0u};
+        }
+        constexpr int NH = WTN / 64, NG = NH * FM;
+        auto store_all = [&](auto masked) {
+            float bq[4][4];
+#pragma unroll
+            for (int g = 0; g <= NG; ++g) {
+                u32x4 v[2];
+                if (g > 0) {
+                    const char *const sb = stg + ((g - 1) & 1) * STG_BYTES;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        v[j] = *reinterpret_cast<const u32x4 *>(sb + (8 * j + rr) * 128 +
+                                                                ((rc ^ (rr & 7)) * 16));
+                }
+                if (g < NG) {
+                    const int fh = g / FM, fm = g % FM;
+                    char *const sb = stg + (g & 1) * STG_BYTES;
+                    if (g % FM == 0) {
+#pragma unroll
+                        for (int f = 0; f < 4; ++f) {
+                            const u32x2 bb = bvals[4 * fh + f];
+                            bq[f][0] = to_f32<DT>(bb.x & 0xffffu);
+                            bq[f][1] = to_f32<DT>(bb.x >> 16);
+                            bq[f][2] = to_f32<DT>(bb.y & 0xffffu);
+                            bq[f][3] = to_f32<DT>(bb.y >> 16);
+                        }
+                    }
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) {
+                        const AccT &a = acc[4 * fh + f][fm];
+                        u32x2 o;
+                        o.x = pack2<DT>(act_fn<ACT>(a[0] + bq[f][0]), act_fn<ACT>(a[1] + bq[f][1]));
+                        o.y = pack2<DT>(act_fn<ACT>(a[2] + bq[f][2]), act_fn<ACT>(a[3] + bq[f][3]));
+                        const int chunk = 2 * f + (wg >> 1);
+                        *reinterpret_cast<u32x2 *>(sb + wr * 128 + ((chunk ^ (wr & 7)) * 16) +
+                                                   (wg & 1) * 8) = o;
+                    }
+                }
+                if (g > 0) {
+                    const int fh = (g - 1) / FM, fm = (g - 1) % FM;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        if (masked && (fm * BD + 8 * j + rr >= rows_left || fh * 64 + rc * 8 >= cols_left))
+                            continue;
+                        const uint32_t offs = st_off + (uint32_t)(2 * fm + j) * pitch8 + (uint32_t)(fh * 128);
+                        *reinterpret_cast<u32x4 *>(Cw + offs) = v[j];
+                    }
+                }
+            }
+        };
+        if (full)
+            store_all(std::false_type{});
+        else
+            store_all(std::true_type{});
+        return;
+    }
+
+    // Epilogue (32x32x16 MFMAs): + bias[n], activation, round once, 8-byte stores. Addresses are a
     // 32-bit byte offset from the tile's corner (row pitch N*2, at most 2^32 for
     // N <= 2^23); rows and columns are masked only in edge tiles. Lane l holds
     // row (l % BD) of block fm and, per 4-column group i, columns c0(i) .. +3.
