@@ -1,7 +1,8 @@
 // Interleaved direct-to-LDS GEMM kernel for gfx950.
 //
-// Same tiles, LDS layouts and epilogue as gemm_v2.hpp; the difference is the
-// order in which a wave issues its instructions. Moving a slice from HBM/L2 into
+// Same tiles and LDS layouts as gemm_v2.hpp; the difference is the order in
+// which a wave issues its instructions (and, with 16x16x32 MFMAs, an epilogue
+// that stores whole row segments through LDS; see the epilogue). Moving a slice from HBM/L2 into
 // LDS takes the CU's address path about as long as half of the slice's MFMA
 // work, and a wave that issues all its direct-to-LDS loads back to back stalls
 // in issue for that whole time. Here every MFMA step is written out
