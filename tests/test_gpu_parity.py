@@ -254,19 +254,41 @@ def test_degenerate_shapes():
     check_random(A, B, None, "none", dt, run_gpu(A, B, None, "none", dt))
 
 
-def test_writes_stay_inside_C():
+@pytest.mark.parametrize("shape", [(133, 200, 96), (300, 264, 136)], ids=lambda s: "x".join(map(str, s)))
+def test_writes_stay_inside_C(shape):
+    # every schedule (the staged epilogues of kernels 3 and 4 mask rows and 16-byte
+    # column chunks per wave block) and the 8-bit kernel: a guard band on both
+    # sides of C keeps its fill
     import torch
-    M, N, K = 133, 200, 96
+    M, N, K = shape
     A = synth.random_bits((M, K), "f16", 1)
     B = synth.random_bits((K, N), "f16", 2)
     guard = 4096
-    buf = torch.full((M * N + 2 * guard,), 7.0, dtype=torch.float16, device="cuda")
+    buf = torch.empty((M * N + 2 * guard,), dtype=torch.float16, device="cuda")
     c = buf[guard:guard + M * N].view(M, N)
-    say("guard band")
-    gba.gemm_bias_act(to_dev(A, "f16"), to_dev(B, "f16"), None, c, "none")
+    for s in [None] + gba.list_schedules():
+        buf.fill_(7.0)
+        say("guard band", shape, "heuristic" if s is None else s)
+        gba.set_schedule(s)
+        try:
+            gba.gemm_bias_act(to_dev(A, "f16"), to_dev(B, "f16"), None, c, "none")
+        finally:
+            gba.set_schedule(None)
+        torch.cuda.synchronize()
+        assert bool((buf[:guard] == 7.0).all()) and bool((buf[guard + M * N:] == 7.0).all()), s
+        check_random(A, B, None, "none", "f16", to_bits(c))
+    # 8-bit inputs (K a multiple of 16)
+    K8 = K // 16 * 16
+    A8 = synth.f32_to_fp8_bits(np.random.default_rng(3).integers(-2, 3, (M, K8)).astype(np.float32), "e4m3")
+    W8 = synth.f32_to_fp8_bits(np.random.default_rng(4).integers(-2, 3, (N, K8)).astype(np.float32), "e4m3")
+    buf.fill_(7.0)
+    say("guard band fp8", shape)
+    gba.gemm_bias_act_fp8(torch.from_numpy(A8).cuda(), torch.from_numpy(W8).cuda(), None, c, 1.0,
+                          "none", "e4m3")
     torch.cuda.synchronize()
     assert bool((buf[:guard] == 7.0).all()) and bool((buf[guard + M * N:] == 7.0).all())
-    check_random(A, B, None, "none", "f16", to_bits(c))
+    want = oracle.encode(oracle.gemm_bias_act_fp8(A8, W8, None, 1.0, "none", "e4m3", "f16"), "f16")
+    assert np.array_equal(to_bits(c), want)
 
 
 def test_run_to_run_bitwise_determinism():
