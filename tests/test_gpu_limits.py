@@ -1,6 +1,7 @@
 """Entry points at the sizes the header gives as limits, through the C ABI.
 
-K = 2^21 (every compiled-in schedule, both B layouts, split-K, 8-bit inputs),
+K = 2^21 (every compiled-in schedule, both B layouts, A stored [K, M] too,
+split-K, 8-bit inputs),
 N = 2^23 (2^30 for bias_act), M = 2^31 - 1 (the largest tile offsets; the
 last tile is ragged) and, with A stored [K, M], M = 2^23. Inputs are small integers, so every sum is exact in fp32
 and the results must equal the fp64 oracle's bitwise (relu, or no activation).
@@ -138,6 +139,47 @@ def test_max_k_split(kmax, dtype, transpose_b):
                       workspace=ws)
     got = to_bits(c)
     assert np.array_equal(got, want), first_mismatch(got, want)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_max_k_transpose_a_every_schedule_and_split(kmax, dtype):
+    # A stored [K, M] at K = 2^21, the largest slice count. M must be a multiple
+    # of 8 in that layout, so A gets three more rows, copies of rows 0..2, and C's
+    # rows 37..39 must equal rows 0..2.
+    import torch
+    a, b, w, bias, want37 = kmax_case(kmax, dtype)
+    want = np.concatenate([want37, want37[:3]])
+    M, N = want.shape
+    at = torch.cat([a, a[:3]]).t().contiguous()
+    ran = 0
+    for s in gba.list_schedules():
+        for tb in (False, True):
+            c = empty((M, N), dtype, fill_bits=SENT)
+            say("max K transpose_A", dtype, sched_id(s), "NK" if tb else "KN")
+            gba.set_schedule(s)
+            try:
+                gba.gemm_bias_act(at, w if tb else b, bias, c, "relu", transpose_b=tb,
+                                  transpose_a=True)
+            except gba.GbaError as e:
+                if e.status == 9:   # no transpose_A path in this kernel
+                    continue
+                raise
+            finally:
+                gba.set_schedule(None)
+            got = to_bits(c)
+            assert np.array_equal(got, want), (sched_id(s), tb, first_mismatch(got, want))
+            ran += 1
+    assert ran >= 10
+    for tb in (False, True):
+        nb = gba.workspace_size(M, N, KMAX, "relu", dtype, transpose_b=tb, transpose_a=True)
+        assert nb > 0, "40 x 136 x 2^21 is expected to split"
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        c = empty((M, N), dtype, fill_bits=SENT)
+        say("max K transpose_A split", dtype, tb, nb)
+        gba.gemm_bias_act(at, w if tb else b, bias, c, "relu", transpose_b=tb,
+                          transpose_a=True, workspace=ws)
+        got = to_bits(c)
+        assert np.array_equal(got, want), (tb, first_mismatch(got, want))
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
