@@ -167,7 +167,9 @@ static double act_apply(int act, double z) {
         if (z >= 0.0) return 1.0 / (1.0 + exp(-z));
         else { double e = exp(z); return e / (1.0 + e); }
     case OR_GELU:
-        /* z * Phi(z); Phi(z) = 0.5 * (1 + erf(z/sqrt2)) = 0.5 * erfc(-z/sqrt2) */
+        /* z * Phi(z); Phi(z) = 0.5 * (1 + erf(z/sqrt2)) = 0.5 * erfc(-z/sqrt2).
+         * At z = -inf the product is -inf * 0: the value there is the limit, 0. */
+        if (isinf(z) && z < 0.0) return 0.0;
         return 0.5 * z * erfc(-z / sqrt(2.0));
     case OR_SOFTPLUS:
         /* log(1 + e^z), written so that neither branch overflows or cancels:
@@ -175,7 +177,8 @@ static double act_apply(int act, double z) {
         return z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z));
     case OR_GELU_TANH: {
         /* 0.5 z (1 + tanh(y)); for y < 0, 1 + tanh(y) = 2 e^(2y) / (1 + e^(2y))
-         * (no cancellation). */
+         * (no cancellation). At z = -inf: the limit, 0. */
+        if (isinf(z) && z < 0.0) return 0.0;
         const double y = sqrt(2.0 / 3.14159265358979323846) * (z + 0.044715 * z * z * z);
         if (y >= 0.0) return 0.5 * z * (1.0 + tanh(y));
         const double e = exp(2.0 * y);

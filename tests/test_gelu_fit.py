@@ -67,8 +67,9 @@ def test_kernel_constants_are_the_tested_ones():
     start = src.index("ACT == ACT_GELU")
     body = src[start:src.index("} else", start)]
     consts = [float(v) for v in re.findall(r"(-?\d+\.\d+(?:e-?\d+)?)f", body)]
-    # the eight Horner coefficients, then the 0 of max(z, 0)
-    assert consts[:8] == gelu_fit.KERNEL_Q and consts[8:] == [0.0], consts
+    # the eight Horner coefficients, then the clamp of the multiplier (3e38, for
+    # z = +-inf) and the 0 of max(z, 0)
+    assert consts[:8] == gelu_fit.KERNEL_Q and consts[8:] == [3.0e38, 0.0], consts
 
 
 def test_fit_reproduces_kernel_constants():

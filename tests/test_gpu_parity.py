@@ -452,6 +452,29 @@ def test_epilogue_device_functions_on_dense_grid(act):
         assert np.all(err <= bound), float((err / bound).max())
 
 
+@pytest.mark.parametrize("act", ["none", "relu", "sigmoid", "gelu", "softplus", "gelu_tanh"])
+def test_epilogue_non_finite(act):
+    """An fp32 accumulator can overflow (bf16 operands reach 3.4e38): each
+    activation gives its limit at +-inf (no inf * 0 NaN) and NaN for NaN, as the
+    oracle does."""
+    import torch
+    z = np.array([np.inf, -np.inf, np.nan, 3.0e38, -3.0e38, 1e20, -1e20], dtype=np.float32)
+    zt = torch.from_numpy(z).cuda()
+    yt = torch.empty_like(zt)
+    say("epilogue non-finite", act)
+    gba.epilogue_probe(zt, yt, act)
+    torch.cuda.synchronize()
+    y = yt.cpu().numpy().astype(np.float64)
+    ref = oracle.act(z.astype(np.float64), act)
+    if act == "relu":
+        assert y[2] == 0.0 and ref[2] == 0.0   # max(NaN, 0): IEEE maxNum on both sides
+    else:
+        assert np.isnan(y[2]) and np.isnan(ref[2])
+    fin = [0, 1, 3, 4, 5, 6]
+    assert np.array_equal(np.isinf(y[fin]), np.isinf(ref[fin])), (y, ref)
+    assert np.allclose(y[fin], ref[fin], rtol=1e-5, atol=0.0), (y, ref)
+
+
 # ------------------------------------------------------------ tuner ----
 
 def test_autotune_writes_cache_and_is_used(tmp_path, monkeypatch):

@@ -180,6 +180,35 @@ def test_gelu_closed_forms(orc):
     np.testing.assert_array_equal(g[big], x[big])   # Phi(10) = 1 - 7.6e-24
 
 
+def test_activations_at_non_finite_inputs(orc):
+    """At +-inf each activation takes its limit (mpmath's limit of the formula
+    at +-1e6 stands for it: every limit is reached there to double precision),
+    and a NaN input gives NaN (ReLU: 0, max(NaN, 0) read as IEEE maxNum, the
+    hardware max). GELU(-inf) and tanh-GELU(-inf) are 0, not the
+    -inf * 0 = NaN that the formulas give when evaluated at the infinity."""
+    lim = {"none": (math.inf, -math.inf), "relu": (math.inf, 0.0), "sigmoid": (1.0, 0.0),
+           "gelu": (math.inf, 0.0), "softplus": (math.inf, 0.0), "gelu_tanh": (math.inf, 0.0)}
+    big = mpmath.mpf(10) ** 6
+    mp = {"sigmoid": lambda v: 1 / (1 + mpmath.exp(-v)), "gelu": lambda v: v * mpmath.ncdf(v),
+          "softplus": lambda v: mpmath.log(1 + mpmath.exp(v)),
+          "gelu_tanh": lambda v: v / 2 * (1 + mpmath.tanh(mpmath.sqrt(2 / mpmath.pi)
+                                                        * (v + mpmath.mpf("0.044715") * v ** 3)))}
+    for act, (hi, lo) in lim.items():
+        got = orc.act([math.inf, -math.inf, math.nan], act)
+        assert got[0] == hi and got[1] == lo, (act, got)
+        if act == "relu":
+            assert got[2] == 0.0   # max(z, 0) as IEEE maxNum: the number wins over NaN
+        else:
+            assert math.isnan(got[2]), act
+        if act in mp:
+            # the finite side of each limit, from the formula itself
+            assert abs(float(mp[act](-big)) - lo) < 1e-300, act
+            if math.isfinite(hi):
+                assert abs(float(mp[act](big)) - hi) < 1e-15, act
+            else:
+                assert float(mp[act](big)) > 1e5, act
+
+
 def test_gelu_dense_grid_against_mpmath(orc):
     x = np.concatenate([np.linspace(-40, 40, 4001), np.geomspace(1e-300, 1e3, 500)])
     x = np.concatenate([x, -x])

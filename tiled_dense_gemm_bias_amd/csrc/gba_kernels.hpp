@@ -119,6 +119,9 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 //           z / (1 + e^(-2y)) (1 + tanh(y) = 2 / (1 + e^(-2y))): one exp2 and one
 //           reciprocal. For z << 0, e^(-2y) overflows to +inf and the result is
 //           -0 (the true value is below 1e-30 in magnitude there).
+//  Non-finite z (an fp32 accumulator can overflow with bf16 operands): every
+//  activation gives its limit at z = +-inf (GELU and GELU_TANH: +inf and 0,
+//  the latter instead of inf * 0) and NaN for NaN.
 template <int ACT>
 __device__ __forceinline__ float act_fn(float z) {
     if constexpr (ACT == ACT_RELU) {
@@ -135,7 +138,10 @@ __device__ __forceinline__ float act_fn(float z) {
         q = fmaf(az, q, -0.4584644138813019f);
         q = fmaf(az, q, -1.1512510776519775f);
         q = fmaf(az, q, -0.9999952912330627f);
-        return fmaf(-az, __builtin_amdgcn_exp2f(q), fmaxf(z, 0.0f));
+        // The multiplier is clamped below +inf so that z = +-inf gives
+        // max(z, 0) - 3e38 * 0 (the limits +inf and 0) rather than inf * 0; a NaN z
+        // still reaches the result through q.
+        return fmaf(-fminf(az, 3.0e38f), __builtin_amdgcn_exp2f(q), fmaxf(z, 0.0f));
     } else if constexpr (ACT == ACT_SOFTPLUS) {
         const float t = __builtin_amdgcn_exp2f(-fabsf(z) * 1.4426950408889634f);
         const float u = 1.0f + t;
@@ -146,7 +152,9 @@ __device__ __forceinline__ float act_fn(float z) {
     } else if constexpr (ACT == ACT_GELU_TANH) {
         // -2 y log2(e) = -z (c1 + c3 z^2), c1 = 2 sqrt(2/pi) log2(e), c3 = 0.044715 c1
         const float a = -z * fmaf(z * z, 0.10294324159622192f, 2.302208185195923f);
-        return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a));
+        // z clamped above -inf: at z = -inf the reciprocal is 0 and the result the
+        // limit 0 rather than -inf * 0 (a NaN z still propagates through a).
+        return fmaxf(z, -3.0e38f) * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a));
     } else {
         return z;
     }
