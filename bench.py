@@ -45,6 +45,143 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def host_cpu() -> dict:
+    """Model name and usable core count of the host this process runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"model": model, "cores": cores, "nproc": os.cpu_count()}
+
+
+def _smi_handle(dev_index: int):
+    """amdsmi handle of torch device dev_index (matched by PCI bus), or None."""
+    import amdsmi
+    import torch
+    amdsmi.amdsmi_init()
+    handles = amdsmi.amdsmi_get_processor_handles()
+    props = torch.cuda.get_device_properties(dev_index)
+    bus = getattr(props, "pci_bus_id", None)
+    for h in handles:
+        bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)   # "dddd:bb:dd.f"
+        if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+            return h
+    return handles[0] if len(handles) == 1 else None
+
+
+def gpu_stack(dev_index: int) -> dict:
+    """Software stack and device identity, best effort (a field that cannot be
+    read is None, with the reason under "errors")."""
+    import torch
+    out = {"torch": torch.__version__, "hip_runtime": getattr(torch.version, "hip", None),
+           "rocm": None, "driver": None, "gpu": None, "cus": None, "arch": None,
+           "max_sclk_mhz": None, "errors": {}}
+    try:
+        props = torch.cuda.get_device_properties(dev_index)
+        out["gpu"] = props.name
+        out["cus"] = props.multi_processor_count
+        out["arch"] = getattr(props, "gcnArchName", None)
+    except Exception as e:   # noqa: BLE001 - report, do not fail the bench
+        out["errors"]["device"] = repr(e)
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            out["rocm"] = f.read().strip()
+    except OSError as e:
+        out["errors"]["rocm"] = repr(e)
+    try:
+        import amdsmi
+        h = _smi_handle(dev_index)
+        if h is not None:
+            d = amdsmi.amdsmi_get_gpu_driver_info(h)
+            out["driver"] = "%s %s" % (d.get("driver_name"), d.get("driver_version"))
+            c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            out["max_sclk_mhz"] = c.get("max_clk")
+    except Exception as e:   # noqa: BLE001
+        out["errors"]["amdsmi"] = repr(e)
+    if not out["errors"]:
+        del out["errors"]
+    return out
+
+
+class SclkSampler:
+    """Polls the GPU's graphics clock (amdsmi gpu_metrics: the mean of the
+    per-XCD current_gfxclks, and the firmware's average_gfxclk_frequency) from a
+    background thread, so that the clock during the timed region can be
+    reported beside the spec denominator. Best effort: None if amdsmi fails."""
+
+    def __init__(self, dev_index: int):
+        import threading
+        self.samples = []   # (perf_counter, current MHz, average MHz)
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            self._amdsmi = amdsmi
+            self._h = _smi_handle(dev_index)
+            if self._h is None:
+                self.error = "no amdsmi handle for the device"
+        except Exception as e:   # noqa: BLE001
+            self.error = repr(e)
+        if self.error is None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+        cur = m.get("current_gfxclks")
+        if isinstance(cur, list):
+            cur = [c for c in cur if isinstance(c, (int, float)) and 0 < c < 10000]
+            cur = sum(cur) / len(cur) if cur else None
+        else:
+            cur = m.get("current_gfxclk")
+            cur = cur if isinstance(cur, (int, float)) else None
+        avg = m.get("average_gfxclk_frequency")
+        return cur, (avg if isinstance(avg, (int, float)) else None)
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                cur, avg = self._read()
+            except Exception as e:   # noqa: BLE001
+                self.error = repr(e)
+                return
+            self.samples.append((time.perf_counter(), cur, avg))
+            self._stop.wait(0.0005)
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join(timeout=2.0)
+
+    def summary(self, t0: float, t1: float) -> dict:
+        """Samples taken inside [t0, t1]; if none, the last one before t0 and the
+        first one after t1."""
+        if self.error is not None and not self.samples:
+            return {"source": "amdsmi gpu_metrics", "error": self.error}
+        inside = [s for s in self.samples if t0 <= s[0] <= t1]
+        basis = "inside the timed region"
+        if not inside:
+            before = [s for s in self.samples if s[0] < t0][-1:]
+            after = [s for s in self.samples if s[0] > t1][:1]
+            inside = before + after
+            basis = "nearest samples before and after the timed region"
+        cur = [s[1] for s in inside if s[1] is not None]
+        avg = [s[2] for s in inside if s[2] is not None]
+        return {"source": "amdsmi gpu_metrics (current_gfxclks mean; average_gfxclk_frequency)",
+                "basis": basis, "samples": len(inside),
+                "current_mhz_mean": round(sum(cur) / len(cur), 1) if cur else None,
+                "current_mhz_min": min(cur) if cur else None,
+                "current_mhz_max": max(cur) if cur else None,
+                "average_mhz_mean": round(sum(avg) / len(avg), 1) if avg else None}
+
+
 # Sources each kernel family is compiled from (the schedule table and host code
 # are left out: they do not change what a launch of the kernel does).
 KERNEL_HEADERS = {0: ["gba_kernels.hpp"],
@@ -94,10 +231,11 @@ def measured_traffic(workload: str, sched: dict):
     return rec.get("bytes_per_launch")
 
 
-def time_launches(fn, steps, warmup, stream):
+def time_launches(fn, steps, warmup, stream, window=None):
     """W untimed calls, then K timed ones between two device synchronisations.
 
-    Returns (wall_ms, avg_ms, per):
+    Returns (wall_ms, avg_ms, per); window, if given, receives the host-clock
+    bounds of the timed region as window["t0"], window["t1"]:
       wall_ms  host clock over the K timed calls (sync before and after);
       avg_ms   average launch duration: two HIP events on the launch stream
                bracket the K launches, divided by K (each launch's kernel plus
@@ -118,7 +256,10 @@ def time_launches(fn, steps, warmup, stream):
         fn()
     e1.record(stream)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3
+    if window is not None:
+        window["t0"], window["t1"] = t0, t1
     avg_ms = e0.elapsed_time(e1) / steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     for i in range(steps):
@@ -168,6 +309,27 @@ def cpu_baseline(w, A, B, bias, got_bits, target_s=12.0, transpose_b=False, scal
     parity = {k: rep[k] for k in ("ok", "strict_ok", "rel_frobenius", "max_abs", "max_ulp")}
     parity["rows"] = len(rows)
     return base, parity
+
+
+def cpu_single_thread() -> dict:
+    """The oracle on one host thread over the two small workloads, whole (256^3
+    with and without bias+GELU, 1024^3 plain): median of 5 runs at 256^3, one
+    run at 1024^3."""
+    import oracle
+    import synth
+    res = {}
+    for name, reps in (("c1_plain", 5), ("c1_gelu", 5), ("c2_plain", 1)):
+        w = synth.WORKLOADS[name]
+        A, B, bias = synth.make_inputs(w)
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.gemm_bias_act(A, B, bias, w.act, w.dtype, nthreads=1)
+            ts.append(time.perf_counter() - t0)
+        t = statistics.median(ts)
+        res[name] = {"seconds": round(t, 4), "GFLOP/s": round(w.flops / t / 1e9, 3),
+                     "runs": reps, "threads": 1}
+    return res
 
 
 def main(argv=None) -> int:
@@ -283,18 +445,27 @@ def main(argv=None) -> int:
                                       transpose_a=ta)
     log("[bench] schedule %s%s%s" % (sched, " (A stored [K,M])" if ta else "",
                                      " (B stored [N,K])" if tb else ""))
-    wall_ms, kern_avg, per = time_launches(step, a.steps, a.warmup, stream)
+    sampler = SclkSampler(dev.index)
+    window = {}
+    try:
+        wall_ms, kern_avg, per = time_launches(step, a.steps, a.warmup, stream, window)
+    finally:
+        sampler.stop()
+    sclk = sampler.summary(window.get("t0", 0.0), window.get("t1", 0.0))
     ms_per_step = wall_ms / a.steps
     kern_med = statistics.median(per)
     flops = float(w.flops)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_avg * 1e-3) / 1e12
+    tflops_med = flops / (kern_med * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[w.fmt if fp8 else w.dtype]
     in_bytes = 1 if fp8 else 2
     alg_bytes = (w.M * w.K + w.K * w.N) * in_bytes + (w.M * w.N + (w.N if w.bias else 0)) * 2
-    log("[bench] %d steps: %.4f ms/step wall, kernel avg %.4f ms, median %.4f ms -> %.1f TFLOP/s"
-        " (%.1f%% of peak)" % (a.steps, ms_per_step, kern_avg, kern_med, achieved,
-                               100 * achieved / peak))
+    log("[bench] %d steps after %d warmups: wall %.4f ms/step -> %.1f TFLOP/s (value); "
+        "event-bracketed kernel avg %.4f ms -> %.1f TFLOP/s (%.1f%% of peak, roofline); "
+        "per-launch-event median %.4f ms -> %.1f TFLOP/s; sclk %s"
+        % (a.steps, a.warmup, ms_per_step, value, kern_avg, achieved, 100 * achieved / peak,
+           kern_med, tflops_med, sclk.get("current_mhz_mean")))
     got_bits = c_t.view(torch.int16).cpu().numpy().view(np.uint16)
 
     out = {
@@ -322,6 +493,21 @@ def main(argv=None) -> int:
                    "schedule": sched, "flop_model": "2*M*N*K (epilogue not counted)"},
         "median_ms": round(kern_med, 5),
         "pct_of_peak": round(100 * achieved / peak, 2),
+        "timing": {
+            "value": "2*M*N*K / (host wall clock over the K timed steps / K); ms_per_step",
+            "kernel_avg_ms": round(kern_avg, 5),
+            "kernel_avg": "two HIP events on the launch stream bracket the K timed launches, "
+                          "divided by K; gives roofline.achieved and pct_of_peak",
+            "tflops_kernel_avg": round(achieved, 2),
+            "median_ms": round(kern_med, 5),
+            "median": "separate untimed pass of K launches with one HIP event before each; "
+                      "every interval includes one event record (~3 us at this size)",
+            "tflops_median": round(tflops_med, 2),
+        },
+        "sclk_mhz": sclk,
+        "spec_sclk_mhz": 2400,
+        "stack": gpu_stack(dev.index),
+        "host": host_cpu(),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(wl_key, sched),
@@ -354,6 +540,8 @@ def main(argv=None) -> int:
                                     transpose_a=ta)
         out["cpu_baseline"] = base
         out["parity_sampled"] = parity
+        if not fp8:
+            out["cpu_baseline"]["single_thread"] = cpu_single_thread()
         log("[bench] cpu baseline %.4f TFLOP/s on %d threads; parity %s"
             % (base["value"], base["cores"], parity))
     print(json.dumps(out), flush=True)

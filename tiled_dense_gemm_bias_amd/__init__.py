@@ -82,6 +82,14 @@ def _lib():
             "gba_list_schedule": [ci, ctypes.POINTER(Schedule)],
             "gba_autotune": [p, p, p, p, i64, i64, i64, ci, ci, ci, ctypes.POINTER(Schedule),
                              ctypes.POINTER(ctypes.c_double)],
+            "gba_autotune_num_trials": [],
+            "gba_autotune_trial": [ci, ctypes.POINTER(Schedule), ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ci)],
+            "gba_build_id": [],
+            "gba_cache_lookup": [ctypes.c_char_p, ci, i64, i64, i64, ci, ci, ci,
+                                 ctypes.POINTER(Schedule), ctypes.POINTER(ctypes.c_double)],
+            "gba_cache_store": [ctypes.c_char_p, ci, i64, i64, i64, ci, ci, ci,
+                                ctypes.POINTER(Schedule), ctypes.c_double],
             "gba_epilogue_probe": [p, p, i64, ci],
             "gba_status_string": [ci],
             "gba_last_hip_error": [],
@@ -93,6 +101,7 @@ def _lib():
             fn.restype = ci
         lib.gba_status_string.restype = ctypes.c_char_p
         lib.gba_version.restype = ctypes.c_char_p
+        lib.gba_build_id.restype = ctypes.c_char_p
         _LIB = lib
     return _LIB
 
@@ -263,9 +272,12 @@ def bind_gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False, workspace=N
         name = "gemm_bias_act_ex"
     fn = getattr(lib, name)
     set_stream = lib.gba_set_stream
-    set_stream(stream)
 
     def launch():
+        # The library's stream is per thread and shared by every entry point:
+        # set it on each call, so that launches stay on the bound stream
+        # whatever other calls, or another thread, did in between.
+        set_stream(stream)
         st = fn(*args)
         if st != 0:
             raise GbaError(st, name)
@@ -338,7 +350,8 @@ def bind_gemm_bias_act_fp8(a, w, bias, c, scale=1.0, act="gelu", fmt=None, works
     if torch.cuda.current_device() != dev.index:
         raise ValueError("bind on the tensors' device (torch.cuda.set_device first)")
     lib = _lib()
-    lib.gba_set_stream(ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    set_stream = lib.gba_set_stream
     args = (_ptr(a), _ptr(w), _ptr(bias), _ptr(c), M, N, K, float(scale), _act(act), fa, dt)
     fn = lib.gemm_bias_act_fp8_nt
     if workspace is not None:
@@ -347,6 +360,7 @@ def bind_gemm_bias_act_fp8(a, w, bias, c, scale=1.0, act="gelu", fmt=None, works
         fn = lib.gemm_bias_act_fp8_ex
 
     def launch():
+        set_stream(stream)   # per call, as in bind_gemm_bias_act
         st = fn(*args)
         if st != 0:
             raise GbaError(st, "gemm_bias_act_fp8_nt")
@@ -442,6 +456,81 @@ def autotune(a, b, bias, c, act="gelu", all_groups: bool = False, transpose_b=Fa
                               | (TUNE_TRANSPOSE_B if transpose_b else 0)
                               | (TUNE_TRANSPOSE_A if transpose_a else 0),
                               ctypes.byref(best), ctypes.byref(ms))
-    if st not in (0, 10):
+    if st not in (0, 10, 11):
         raise GbaError(st, "gba_autotune")
     return best.as_dict(), ms.value
+
+
+def autotune_status(a, b, bias, c, act="gelu", all_groups: bool = False, transpose_b=False,
+                    transpose_a=False):
+    """autotune, returning (status, schedule dict, median ms, trials): status 0
+    (done, cached), 10 (cache not writable) or 11 (stopped at GBA_TUNE_BUDGET;
+    progress kept in the tuning journal, call again to resume); trials as
+    autotune_trials()."""
+    dev = _check_dev(a, b, bias, c)
+    dt, M, N, K = _gemm_shapes(a, b, bias, c, transpose_b, transpose_a)
+    best = Schedule()
+    ms = ctypes.c_double()
+    torch = _torch()
+    with torch.cuda.device(dev):
+        lib = _lib()
+        lib.gba_set_stream(ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+        st = lib.gba_autotune(_ptr(a), _ptr(b), _ptr(bias), _ptr(c), M, N, K, _act(act), dt,
+                              (TUNE_ALL_GROUPS if all_groups else 0)
+                              | (TUNE_TRANSPOSE_B if transpose_b else 0)
+                              | (TUNE_TRANSPOSE_A if transpose_a else 0),
+                              ctypes.byref(best), ctypes.byref(ms))
+    if st not in (0, 10, 11):
+        raise GbaError(st, "gba_autotune")
+    return st, best.as_dict(), ms.value, autotune_trials()
+
+
+def autotune_trials() -> list:
+    """Per-candidate results of this thread's last autotune: dicts of the
+    schedule plus "ms" (median) and "resumed" (taken from the tuning journal)."""
+    lib = _lib()
+    out = []
+    for i in range(lib.gba_autotune_num_trials()):
+        s, ms, res = Schedule(), ctypes.c_double(), ctypes.c_int()
+        st = lib.gba_autotune_trial(i, ctypes.byref(s), ctypes.byref(ms), ctypes.byref(res))
+        if st != 0:
+            raise GbaError(st, "gba_autotune_trial")
+        out.append(dict(s.as_dict(), ms=ms.value, resumed=bool(res.value)))
+    return out
+
+
+def build_id() -> str:
+    """Hash of the sources this library was compiled from (gba_build_id)."""
+    return _lib().gba_build_id().decode()
+
+
+def _cache_args(arch, cus, M, N, K, act, dtype, transpose_b, transpose_a):
+    return (arch.encode() if isinstance(arch, str) else arch, int(cus), int(M), int(N), int(K),
+            _act(act), {"f16": 0, "bf16": 1}[dtype] if isinstance(dtype, str) else int(dtype),
+            _layout_flags(transpose_a, transpose_b))
+
+
+def cache_lookup(arch, cus, M, N, K, act="gelu", dtype="f16", transpose_b=False,
+                 transpose_a=False):
+    """The cached schedule (dict with "ms") for these arguments, or None (no
+    entry, or the cache is disabled). Needs no device."""
+    s, ms = Schedule(), ctypes.c_double()
+    st = _lib().gba_cache_lookup(*_cache_args(arch, cus, M, N, K, act, dtype, transpose_b,
+                                              transpose_a), ctypes.byref(s), ctypes.byref(ms))
+    if st == 9:
+        return None
+    if st != 0:
+        raise GbaError(st, "gba_cache_lookup")
+    return dict(s.as_dict(), ms=ms.value)
+
+
+def cache_store(arch, cus, M, N, K, sched: dict, ms: float, act="gelu", dtype="f16",
+                transpose_b=False, transpose_a=False) -> int:
+    """Merge one entry into the schedule cache; returns the status (0, or 10 if
+    the cache could not be written). Needs no device."""
+    s = Schedule.from_dict(sched)
+    st = _lib().gba_cache_store(*_cache_args(arch, cus, M, N, K, act, dtype, transpose_b,
+                                             transpose_a), ctypes.byref(s), float(ms))
+    if st not in (0, 10):
+        raise GbaError(st, "gba_cache_store")
+    return st
