@@ -67,7 +67,9 @@ typedef enum {
     GBA_ERR_DEVICE = 7,   /* no HIP device, or not gfx950 */
     GBA_ERR_HIP = 8,      /* a HIP runtime call failed; see gba_last_hip_error() */
     GBA_ERR_SCHEDULE = 9, /* schedule not among the compiled-in ones */
-    GBA_ERR_CACHE = 10    /* schedule cache could not be written (tuning still done) */
+    GBA_ERR_CACHE = 10,   /* schedule cache could not be written (tuning still done) */
+    GBA_TUNE_INCOMPLETE = 11 /* gba_autotune stopped at its candidate budget (GBA_TUNE_BUDGET);
+                                its progress is kept, a later call resumes */
 } gba_status;
 
 /* A GEMM schedule: one compiled-in kernel instance plus its launch mapping.
@@ -238,21 +240,67 @@ int gba_num_schedules(void);
 int gba_list_schedule(int i, gba_schedule *out);
 
 /* Autotuner ("TileLang: Write, Autotune, and Ship Fused Tensor-Core Kernels from
- * Python", section Autotuning): for every compiled-in instance (with a
- * path for the operand layouts that GBA_TUNE_TRANSPOSE_A / _B select) whose LDS ring
- * (bm*bk + bk*bn) * 2 * stages fits the 160 KiB LDS of a CU, and each raster
- * variant, run 10 untimed and 50 timed launches on the caller's buffers, keep
- * the median time, and pick the fastest. The winner is stored in the on-disk
- * schedule cache ($GBA_CACHE_DIR, default ~/.cache/gba; disabled by
- * GBA_DISABLE_CACHE=1) under the key (arch, CU count, library version, dtype,
- * act, operand layouts, M, N, K), and is used by later calls. C holds the winner's
- * result on return. flags: GBA_TUNE_* bits.
+ * Python", section Autotuning: how it works and how much it costs): for every
+ * compiled-in instance (with a path for the operand layouts that
+ * GBA_TUNE_TRANSPOSE_A / _B select) whose LDS ring (bm*bk + bk*bn) * 2 * stages
+ * fits the 160 KiB LDS of a CU, and each raster variant, run 10 untimed and 50
+ * timed launches on the caller's buffers, keep the median time, and pick the
+ * fastest. C holds the winner's result on return. flags: GBA_TUNE_* bits.
  * best / best_ms may be NULL. Synchronous: it waits for its own launches.
- * Returns GBA_ERR_CACHE (with best filled) if the cache file could not be
- * written. */
+ *
+ * Persistence (the page's on-disk cache, kept across runs and CI; disabled as
+ * a whole by GBA_DISABLE_CACHE=1):
+ *   - The winner is stored in $GBA_CACHE_DIR/schedules.json (default
+ *     ~/.cache/gba) under the key (arch, CU count, gba_build_id(), dtype, act,
+ *     operand layouts, M, N, K), and used by later calls in any process.
+ *     Entries of other builds stay in the file and are never used by this one.
+ *   - Writers merge into the file under an exclusive lock and replace it by
+ *     rename: concurrent processes lose no entries and readers never see a
+ *     partial file. A process re-reads the file when GBA_CACHE_DIR changes.
+ *   - Each timed candidate is appended to $GBA_CACHE_DIR/tuning.json as it
+ *     finishes. A call with the same key first takes the candidates already
+ *     there (an interrupted run's) instead of timing them again; the journal
+ *     entries of a key are removed when its tuning completes.
+ *   - GBA_TUNE_BUDGET=n (environment) limits a call to timing n new
+ *     candidates: if some remain, it returns GBA_TUNE_INCOMPLETE with the best
+ *     so far in best / best_ms and in C, writes nothing to schedules.json, and
+ *     the next call resumes.
+ * Returns GBA_ERR_CACHE (with best filled and C written) if the cache or the
+ * journal could not be written. */
 int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_t M,
                  int64_t N, int64_t K, int act, int dtype, int flags, gba_schedule *best,
                  double *best_ms);
+
+/* Per-candidate results of this thread's last gba_autotune call (the page's
+ * tuning cost accounting): their number, and the i-th candidate's schedule,
+ * median ms, and whether it came from the tuning journal (1) rather than being
+ * timed by that call (0). Any pointer may be NULL; i out of range:
+ * GBA_ERR_SHAPE. */
+int gba_autotune_num_trials(void);
+int gba_autotune_trial(int i, gba_schedule *sched, double *ms, int *resumed);
+
+/* Identifies the kernels compiled into this library (a hash of its sources);
+ * part of every schedule-cache key. */
+const char *gba_build_id(void);
+
+/* Read or seed the schedule cache without a device (e.g. to ship schedules
+ * tuned elsewhere, or to inspect them): the entry gba_autotune would write for
+ * a gemm_bias_act_ex call with these sizes, act, dtype and GBA_TRANSPOSE_A /
+ * GBA_TRANSPOSE_B flags on a device of this arch (gcnArchName, e.g.
+ * "gfx950:sramecc+:xnack-") and CU count, for this build.
+ * gba_cache_lookup: GBA_OK with *sched (and *ms, the tuned median; either may
+ * be NULL) if the cache holds such an entry; GBA_ERR_SCHEDULE if it does not or
+ * the cache is disabled. gba_cache_store: merges the entry into the file as
+ * gba_autotune does (GBA_ERR_SCHEDULE if sched is not compiled in,
+ * GBA_ERR_CACHE if the file cannot be written, GBA_OK and nothing written if
+ * the cache is disabled). Both: NULL arch: GBA_ERR_NULL; an arch string with
+ * '"', '|' or a newline, or longer than 64: GBA_ERR_DEVICE; cus <= 0,
+ * negative sizes, unknown flags, or (store) a negative or non-finite ms:
+ * GBA_ERR_SHAPE; bad act / dtype as gemm_bias_act. */
+int gba_cache_lookup(const char *arch, int cus, int64_t M, int64_t N, int64_t K, int act,
+                     int dtype, int flags, gba_schedule *sched, double *ms);
+int gba_cache_store(const char *arch, int cus, int64_t M, int64_t N, int64_t K, int act,
+                    int dtype, int flags, const gba_schedule *sched, double ms);
 
 /* Device-side epilogue probe: y[i] = act(z[i]) in fp32, computed by the same
  * device function the GEMM epilogue uses. z, y: device float arrays of n. */

@@ -12,6 +12,7 @@ from __future__ import annotations
 import argparse
 import concurrent.futures as cf
 import glob
+import hashlib
 import os
 import shutil
 import subprocess
@@ -34,9 +35,25 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, isa: bool) -> str:
+def build_id() -> str:
+    """Hash of everything the kernels are compiled from (sources, the public
+    header, the flags): part of every schedule-cache key, so that a schedule
+    tuned on other kernels is never reused."""
+    h = hashlib.sha256()
+    for fn in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp"))
+                     + [os.path.join(INCLUDE, "gba.h")]):
+        h.update(os.path.basename(fn).encode())
+        with open(fn, "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
+def _compile(src: str, isa: bool, bid: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
     cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    if os.path.basename(src) == "gba_api.hip":
+        cmd.append('-DGBA_BUILD_ID="%s"' % bid)
     if isa:
         isadir = os.path.join(BUILD, "isa")
         os.makedirs(isadir, exist_ok=True)
@@ -55,8 +72,9 @@ def build(isa: bool = False, jobs: int = 0) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
+    bid = build_id()
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, isa), srcs))
+        objs = list(ex.map(lambda s: _compile(s, isa, bid), srcs))
     tmp = LIB + ".tmp%d" % os.getpid()
     res = subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs,
                          capture_output=True, text=True)

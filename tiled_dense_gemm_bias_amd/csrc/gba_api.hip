@@ -2,13 +2,16 @@
 // argument checks, device check, schedule choice (forced, on-disk cache, or
 // heuristic), kernel launch, the autotuner and its schedule cache.
 #include <errno.h>
+#include <fcntl.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+#include <sys/file.h>
 #include <sys/stat.h>
 #include <unistd.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <unordered_map>
@@ -18,7 +21,7 @@
 #include "gba_kernels.hpp"
 #include "gba_registry.hpp"
 
-#define GBA_VERSION_STRING "0.2.0"
+#define GBA_VERSION_STRING "0.3.0"
 
 namespace gba {
 extern const ScheduleEntry s_256x256x64_w2x2;
@@ -64,6 +67,14 @@ thread_local hipStream_t t_stream = nullptr;
 thread_local bool t_forced = false;
 thread_local gba_schedule t_forced_sched;
 thread_local int t_last_hip = 0;
+
+// Per-candidate results of this thread's last gba_autotune call.
+struct Trial {
+    gba_schedule s;
+    double ms;
+    int resumed;   // 1: taken from the tuning journal, not timed by that call
+};
+thread_local std::vector<Trial> t_trials;
 
 bool log_enabled() {
     static int v = -1;
@@ -210,6 +221,25 @@ gba_schedule heuristic(int64_t M, int64_t N, int cus) {
 }
 
 // ------------------------------------------------------------ disk cache ----
+//
+// The schedule cache of the autotuner ("TileLang: Write, Autotune, and Ship
+// Fused Tensor-Core Kernels from Python", Autotuning: how it works and how much
+// it costs: re-runs hit an on-disk cache, which can be kept across CI runs and
+// switched off by an environment variable). One JSON object per line in
+// $GBA_CACHE_DIR/schedules.json, keyed by (arch, CU count, build id, dtype,
+// act, operand layouts, M, N, K). The build id is a hash of the library's
+// sources, so a schedule timed on other kernels is never used (its entry stays
+// in the file for the build that wrote it). Every write re-reads the file under
+// an exclusive flock on schedules.json.lock and merges into it, so concurrent
+// writers lose nothing; the merged file replaces the old one by rename, so a
+// reader never sees half of it. The in-memory copy is tied to the file's path:
+// a changed GBA_CACHE_DIR is re-read. Tuning progress (each timed candidate)
+// goes to tuning.json in the same directory with the same rules, so that an
+// interrupted or budget-limited tuning run resumes where it stopped.
+
+#ifndef GBA_BUILD_ID
+#define GBA_BUILD_ID "unhashed"
+#endif
 
 const char *kDtName[2] = {"f16", "bf16"};
 const char *kActName[gba::kNumActs] = {"none", "relu", "sigmoid", "gelu", "softplus", "gelu_tanh"};
@@ -218,10 +248,12 @@ struct CacheRec {
     gba_schedule s;
     double ms;
 };
+using CacheMap = std::unordered_map<std::string, CacheRec>;
 
-std::mutex g_cache_mu;
+std::mutex g_cache_mu;          // guards the three below
 bool g_cache_loaded = false;
-std::unordered_map<std::string, CacheRec> g_cache;
+std::string g_cache_path;       // file the in-memory copy was read from
+CacheMap g_cache;
 
 bool cache_disabled() {
     const char *e = getenv("GBA_DISABLE_CACHE");
@@ -236,17 +268,22 @@ std::string cache_dir() {
 }
 
 std::string cache_file() { return cache_dir() + "/schedules.json"; }
+std::string journal_file() { return cache_dir() + "/tuning.json"; }
 
 // Layout in the key: "nn", "nt" (B stored (N,K)), "tn" (A stored (K,M)), "tt".
 const char *kLayName[4] = {"nn", "nt", "tn", "tt"};
-std::string cache_key(const DeviceInfo &d, int dtype, int act, int lay, int64_t M, int64_t N,
+std::string cache_key(const char *arch, int cus, int dtype, int act, int lay, int64_t M, int64_t N,
                       int64_t K) {
-    char buf[256];
-    snprintf(buf, sizeof buf, "%s|%d|%s|%s|%s|%s|%lld|%lld|%lld", d.arch.c_str(), d.cus,
-             GBA_VERSION_STRING, kDtName[dtype], kActName[act],
+    char buf[320];
+    snprintf(buf, sizeof buf, "%s|%d|%s|%s|%s|%s|%lld|%lld|%lld", arch, cus, GBA_BUILD_ID,
+             kDtName[dtype], kActName[act],
              kLayName[((lay & LAY_TA) ? 2 : 0) | ((lay & LAY_TB) ? 1 : 0)], (long long)M,
              (long long)N, (long long)K);
     return buf;
+}
+std::string cache_key(const DeviceInfo &d, int dtype, int act, int lay, int64_t M, int64_t N,
+                      int64_t K) {
+    return cache_key(d.arch.c_str(), d.cus, dtype, act, lay, M, N, K);
 }
 
 bool json_int(const char *line, const char *name, int *out) {
@@ -262,13 +299,13 @@ bool json_int(const char *line, const char *name, int *out) {
     return true;
 }
 
-// One entry per line: {"key": "...", "bm": 256, ..., "ms": 0.08}. Lines that do
-// not parse, or a file of another format version, are ignored.
-void cache_load_locked() {
-    if (g_cache_loaded) return;
-    g_cache_loaded = true;
-    if (cache_disabled()) return;
-    FILE *f = fopen(cache_file().c_str(), "r");
+// One record per line: {"key": "...", "bm": 256, ..., "ms": 0.08}. A file
+// without the format header, and lines that do not parse or name no
+// compiled-in schedule, are skipped. Several records may share a key (the
+// tuning journal); `add` sees each in file order.
+template <class F>
+void read_records(const std::string &path, F add) {
+    FILE *f = fopen(path.c_str(), "r");
     if (!f) return;
     char line[1024];
     bool header_ok = false;
@@ -282,10 +319,6 @@ void cache_load_locked() {
         const char *ke = strchr(k, '"');
         if (!ke) continue;
         CacheRec r;
-        r.s.stages = 2;
-        r.s.kernel = 0;
-        r.s.loaders = 0;
-        r.s.spread = 0;
         if (!json_int(line, "bm", &r.s.bm) || !json_int(line, "bn", &r.s.bn) ||
             !json_int(line, "bk", &r.s.bk) || !json_int(line, "wm", &r.s.wm) ||
             !json_int(line, "wn", &r.s.wn) || !json_int(line, "stages", &r.s.stages) ||
@@ -296,7 +329,7 @@ void cache_load_locked() {
         const char *m = strstr(line, "\"ms\":");
         r.ms = m ? atof(m + 5) : 0.0;
         if (!sched_valid(r.s)) continue;
-        g_cache[std::string(k, ke)] = r;
+        add(std::string(k, ke), r);
     }
     fclose(f);
 }
@@ -309,43 +342,147 @@ int mkdir_p(const std::string &path) {
             if (mkdir(cur.c_str(), 0755) != 0 && errno != EEXIST) return -1;
         }
     }
-    return 0;
+    struct stat st;
+    return stat(path.c_str(), &st) == 0 && S_ISDIR(st.st_mode) ? 0 : -1;
 }
 
-// Rewrites the whole file through a temporary and a rename, so a reader never
-// sees a half-written cache.
-int cache_save_locked() {
-    if (cache_disabled()) return GBA_OK;
-    const std::string dir = cache_dir();
-    if (mkdir_p(dir) != 0) return GBA_ERR_CACHE;
-    const std::string fn = cache_file();
-    char tmpn[64];
-    snprintf(tmpn, sizeof tmpn, ".tmp.%d", (int)getpid());
-    const std::string tmp = fn + tmpn;
+// Writes records (key, rec) to `path` through a temporary file and a rename.
+int write_records(const std::string &path, const std::vector<std::pair<std::string, CacheRec>> &recs) {
+    static std::atomic<unsigned> serial{0};
+    char tmpn[96];
+    snprintf(tmpn, sizeof tmpn, ".tmp.%d.%u", (int)getpid(), serial.fetch_add(1));
+    const std::string tmp = path + tmpn;
     FILE *f = fopen(tmp.c_str(), "w");
     if (!f) return GBA_ERR_CACHE;
     fprintf(f, "{\"format\": \"gba-schedule-cache\", \"version\": 1, \"entries\": [\n");
-    std::vector<std::string> keys;
-    for (auto &kv : g_cache) keys.push_back(kv.first);
-    std::sort(keys.begin(), keys.end());
-    for (size_t i = 0; i < keys.size(); ++i) {
-        const CacheRec &r = g_cache[keys[i]];
+    for (size_t i = 0; i < recs.size(); ++i) {
+        const gba_schedule &s = recs[i].second.s;
         fprintf(f,
                 "{\"key\": \"%s\", \"bm\": %d, \"bn\": %d, \"bk\": %d, \"wm\": %d, \"wn\": %d, "
                 "\"stages\": %d, \"raster\": %d, \"group_m\": %d, \"kernel\": %d, "
                 "\"loaders\": %d, \"spread\": %d, \"ms\": %.6f}%s\n",
-                keys[i].c_str(), r.s.bm, r.s.bn, r.s.bk, r.s.wm, r.s.wn, r.s.stages, r.s.raster,
-                r.s.group_m, r.s.kernel, r.s.loaders, r.s.spread, r.ms,
-                i + 1 < keys.size() ? "," : "");
+                recs[i].first.c_str(), s.bm, s.bn, s.bk, s.wm, s.wn, s.stages, s.raster, s.group_m,
+                s.kernel, s.loaders, s.spread, recs[i].second.ms, i + 1 < recs.size() ? "," : "");
     }
     fprintf(f, "]}\n");
-    const bool ok = fflush(f) == 0;
-    fclose(f);
-    if (!ok || rename(tmp.c_str(), fn.c_str()) != 0) {
+    bool ok = fflush(f) == 0;
+    ok = fsync(fileno(f)) == 0 && ok;
+    ok = fclose(f) == 0 && ok;
+    if (!ok || rename(tmp.c_str(), path.c_str()) != 0) {
         unlink(tmp.c_str());
         return GBA_ERR_CACHE;
     }
     return GBA_OK;
+}
+
+// Exclusive advisory lock on <dir>/schedules.json.lock for a read-merge-write
+// of the cache or the journal; -1 if the directory cannot be made or locked.
+int lock_cache_dir() {
+    const std::string dir = cache_dir();
+    if (mkdir_p(dir) != 0) return -1;
+    const int fd = open((dir + "/schedules.json.lock").c_str(), O_RDWR | O_CREAT | O_CLOEXEC, 0644);
+    if (fd < 0) return -1;
+    while (flock(fd, LOCK_EX) != 0) {
+        if (errno != EINTR) {
+            close(fd);
+            return -1;
+        }
+    }
+    return fd;
+}
+void unlock_cache_dir(int fd) {
+    flock(fd, LOCK_UN);
+    close(fd);
+}
+
+// Brings the in-memory copy up to date with the current cache file (read once
+// per path). Caller holds g_cache_mu.
+void cache_sync_locked() {
+    const std::string path = cache_file();
+    if (g_cache_loaded && path == g_cache_path) return;
+    g_cache.clear();
+    g_cache_path = path;
+    g_cache_loaded = true;
+    read_records(path, [](const std::string &k, const CacheRec &r) { g_cache[k] = r; });
+}
+
+// The cached schedule for `key`, if the cache is on and holds one.
+bool cache_get(const std::string &key, CacheRec *out) {
+    if (cache_disabled()) return false;
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    cache_sync_locked();
+    auto it = g_cache.find(key);
+    if (it == g_cache.end()) return false;
+    *out = it->second;
+    return true;
+}
+
+// Merges (key, rec) into the cache file and the in-memory copy. GBA_OK when
+// the cache is disabled (nothing written), GBA_ERR_CACHE if it cannot be
+// written.
+int cache_put(const std::string &key, const CacheRec &rec) {
+    if (cache_disabled()) return GBA_OK;
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    const int fd = lock_cache_dir();
+    if (fd < 0) return GBA_ERR_CACHE;
+    const std::string path = cache_file();
+    CacheMap merged;
+    read_records(path, [&](const std::string &k, const CacheRec &r) { merged[k] = r; });
+    merged[key] = rec;
+    std::vector<std::pair<std::string, CacheRec>> recs(merged.begin(), merged.end());
+    std::sort(recs.begin(), recs.end(),
+              [](const std::pair<std::string, CacheRec> &a, const std::pair<std::string, CacheRec> &b) {
+                  return a.first < b.first;
+              });
+    const int st = write_records(path, recs);
+    unlock_cache_dir(fd);
+    g_cache = std::move(merged);
+    g_cache_path = path;
+    g_cache_loaded = true;
+    return st;
+}
+
+bool same_sched(const gba_schedule &a, const gba_schedule &b) {
+    return a.bm == b.bm && a.bn == b.bn && a.bk == b.bk && a.wm == b.wm && a.wn == b.wn &&
+           a.stages == b.stages && a.raster == b.raster && a.group_m == b.group_m &&
+           a.kernel == b.kernel && a.loaders == b.loaders && a.spread == b.spread;
+}
+
+// Tuning journal: the candidates already timed for `key`.
+std::vector<CacheRec> journal_get(const std::string &key) {
+    std::vector<CacheRec> out;
+    if (cache_disabled()) return out;
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    const int fd = lock_cache_dir();
+    if (fd < 0) return out;
+    read_records(journal_file(), [&](const std::string &k, const CacheRec &r) {
+        if (k == key) out.push_back(r);
+    });
+    unlock_cache_dir(fd);
+    return out;
+}
+
+// Replaces the journal's records for `key` by `recs` (none: the key's tuning is
+// finished), keeping every other key's.
+int journal_set(const std::string &key, const std::vector<CacheRec> &recs) {
+    if (cache_disabled()) return GBA_OK;
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    const int fd = lock_cache_dir();
+    if (fd < 0) return GBA_ERR_CACHE;
+    const std::string path = journal_file();
+    std::vector<std::pair<std::string, CacheRec>> all;
+    read_records(path, [&](const std::string &k, const CacheRec &r) {
+        if (k != key) all.emplace_back(k, r);
+    });
+    for (const CacheRec &r : recs) all.emplace_back(key, r);
+    int st = GBA_OK;
+    if (all.empty()) {
+        if (unlink(path.c_str()) != 0 && errno != ENOENT) st = GBA_ERR_CACHE;
+    } else {
+        st = write_records(path, all);
+    }
+    unlock_cache_dir(fd);
+    return st;
 }
 
 gba_schedule choose(const DeviceInfo &d, int64_t M, int64_t N, int64_t K, int act, int dtype,
@@ -354,14 +491,10 @@ gba_schedule choose(const DeviceInfo &d, int64_t M, int64_t N, int64_t K, int ac
         *why = "forced";
         return t_forced_sched;
     }
-    {
-        std::lock_guard<std::mutex> lk(g_cache_mu);
-        cache_load_locked();
-        auto it = g_cache.find(cache_key(d, dtype, act, lay, M, N, K));
-        if (it != g_cache.end()) {
-            *why = "cache";
-            return it->second.s;
-        }
+    CacheRec rec;
+    if (cache_get(cache_key(d, dtype, act, lay, M, N, K), &rec)) {
+        *why = "cache";
+        return rec.s;
     }
     *why = "heuristic";
     return heuristic(M, N, d.cus);
@@ -608,6 +741,7 @@ const char *gba_status_string(int s) {
     case GBA_ERR_HIP: return "HIP runtime error";
     case GBA_ERR_SCHEDULE: return "unknown schedule";
     case GBA_ERR_CACHE: return "schedule cache not writable";
+    case GBA_TUNE_INCOMPLETE: return "tuning stopped at its candidate budget; call again to resume";
     default: return "unknown status";
     }
 }
@@ -775,6 +909,7 @@ int gba_epilogue_probe(const float *z, float *y, int64_t n, int act) {
 int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_t M, int64_t N,
                  int64_t K, int act, int dtype, int flags, gba_schedule *best_out,
                  double *best_ms_out) {
+    t_trials.clear();
     const int lay = ((flags & GBA_TUNE_TRANSPOSE_B) ? LAY_TB : 0) |
                     ((flags & GBA_TUNE_TRANSPOSE_A) ? LAY_TA : 0);
     bool nothing = false;
@@ -809,15 +944,34 @@ int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_
             cands.push_back(c);
         }
     }
+    // Candidates timed by an earlier, interrupted or budget-limited run with the
+    // same key are taken from the journal, not timed again.
+    const std::string key = cache_key(*d, dtype, act, lay, M, N, K);
+    std::vector<CacheRec> done = journal_get(key);
+    long budget = -1;   // GBA_TUNE_BUDGET: at most this many candidates timed by this call
+    if (const char *e = getenv("GBA_TUNE_BUDGET")) {
+        if (*e) budget = strtol(e, nullptr, 10);
+    }
     hipEvent_t ev[51];
     for (auto &e : ev) {
         hipError_t he = hipEventCreate(&e);
         if (he != hipSuccess) return hip_fail(he);
     }
-    double best_ms = 1e30;
-    gba_schedule best = cands[0];
-    int status = GBA_OK;
+    int status = GBA_OK, journal_status = GBA_OK;
+    bool incomplete = false;
+    long timed = 0;
     for (const gba_schedule &c : cands) {
+        const CacheRec *prev = nullptr;
+        for (const CacheRec &r : done)
+            if (same_sched(r.s, c)) prev = &r;
+        if (prev) {
+            t_trials.push_back(Trial{c, prev->ms, 1});
+            continue;
+        }
+        if (budget >= 0 && timed >= budget) {
+            incomplete = true;
+            continue;
+        }
         for (int w = 0; w < 10 && status == GBA_OK; ++w)
             status = launch(c, A, B, bias, C, M, N, K, act, dtype, lay);
         for (int r = 0; r < 50 && status == GBA_OK; ++r) {
@@ -838,24 +992,73 @@ int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_
         if (log_enabled())
             fprintf(stderr, "[gba] tune k%d %dx%dx%d w%dx%d s%d r%d g%d: %.4f ms\n", c.kernel,
                     c.bm, c.bn, c.bk, c.wm, c.wn, c.stages, c.raster, c.group_m, med);
-        if (med < best_ms) {
-            best_ms = med;
-            best = c;
-        }
+        t_trials.push_back(Trial{c, med, 0});
+        done.push_back(CacheRec{c, med});
+        ++timed;
+        const int js = journal_set(key, done);   // progress survives an interruption
+        if (js) journal_status = js;
     }
     for (auto &e : ev) hipEventDestroy(e);
     if (status) return status;
-    // Leave the winner's result in C.
-    status = launch(best, A, B, bias, C, M, N, K, act, dtype, lay);
+    if (t_trials.empty()) return GBA_TUNE_INCOMPLETE;   // a budget of 0 with nothing journaled
+    const Trial *best = &t_trials[0];
+    for (const Trial &t : t_trials)
+        if (t.ms < best->ms) best = &t;
+    // Leave the best result so far in C.
+    status = launch(best->s, A, B, bias, C, M, N, K, act, dtype, lay);
     if (status) return status;
     hipError_t he = hipStreamSynchronize(t_stream);
     if (he != hipSuccess) return hip_fail(he);
-    if (best_out) *best_out = best;
-    if (best_ms_out) *best_ms_out = best_ms;
-    std::lock_guard<std::mutex> lk(g_cache_mu);
-    cache_load_locked();
-    g_cache[cache_key(*d, dtype, act, lay, M, N, K)] = CacheRec{best, best_ms};
-    return cache_save_locked();
+    if (best_out) *best_out = best->s;
+    if (best_ms_out) *best_ms_out = best->ms;
+    if (incomplete) return journal_status ? journal_status : GBA_TUNE_INCOMPLETE;
+    status = cache_put(key, CacheRec{best->s, best->ms});
+    const int js = journal_set(key, {});
+    if (status) return status;
+    return js ? js : journal_status;
+}
+
+int gba_autotune_num_trials(void) { return (int)t_trials.size(); }
+
+int gba_autotune_trial(int i, gba_schedule *sched, double *ms, int *resumed) {
+    if (i < 0 || i >= (int)t_trials.size()) return GBA_ERR_SHAPE;
+    if (sched) *sched = t_trials[i].s;
+    if (ms) *ms = t_trials[i].ms;
+    if (resumed) *resumed = t_trials[i].resumed;
+    return GBA_OK;
+}
+
+const char *gba_build_id(void) { return GBA_BUILD_ID; }
+
+static int cache_args(const char *arch, int cus, int64_t M, int64_t N, int64_t K, int act,
+                      int dtype, int flags) {
+    if (!arch) return GBA_ERR_NULL;
+    if (strlen(arch) > 64 || strchr(arch, '"') || strchr(arch, '|') || strchr(arch, '\n'))
+        return GBA_ERR_DEVICE;
+    if (cus <= 0 || M < 0 || N < 0 || K < 0) return GBA_ERR_SHAPE;
+    if (flags & ~(GBA_TRANSPOSE_B | GBA_TRANSPOSE_A)) return GBA_ERR_SHAPE;
+    return check_enums(act, dtype);
+}
+
+int gba_cache_lookup(const char *arch, int cus, int64_t M, int64_t N, int64_t K, int act,
+                     int dtype, int flags, gba_schedule *out, double *ms) {
+    int s = cache_args(arch, cus, M, N, K, act, dtype, flags);
+    if (s) return s;
+    CacheRec r;
+    if (!cache_get(cache_key(arch, cus, dtype, act, flags, M, N, K), &r)) return GBA_ERR_SCHEDULE;
+    if (out) *out = r.s;
+    if (ms) *ms = r.ms;
+    return GBA_OK;
+}
+
+int gba_cache_store(const char *arch, int cus, int64_t M, int64_t N, int64_t K, int act,
+                    int dtype, int flags, const gba_schedule *sched, double ms) {
+    int s = cache_args(arch, cus, M, N, K, act, dtype, flags);
+    if (s) return s;
+    if (!sched) return GBA_ERR_NULL;
+    if (!sched_valid(*sched)) return GBA_ERR_SCHEDULE;
+    if (!(ms >= 0.0) || ms > 1e12) return GBA_ERR_SHAPE;
+    return cache_put(cache_key(arch, cus, dtype, act, flags, M, N, K), CacheRec{*sched, ms});
 }
 
 }  // extern "C"
