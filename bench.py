@@ -301,7 +301,7 @@ def cpu_baseline(w, A, B, bias, got_bits, target_s=12.0, transpose_b=False, scal
     flops = 2.0 * len(rows) * w.N * w.K
     rep = compare.check(oracle.decode(got_bits[rows], w.dtype), R, K=w.K, dtype=w.dtype,
                         act=oracle.ACTS[w.act], S=S,
-                        sum_rel=None if scale is None else compare.FP8_SUM_REL)
+                        sum_rel=None if scale is None else compare.fp8_sum_rel(w.K))
     base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": "%d of %d output rows of %dx%dx%d %s %s (fp64 triple loop, %.1f s)"
                       % (len(rows), w.M, w.M, w.N, w.K,

@@ -638,6 +638,54 @@ def test_checker_flags_planted_errors():
     assert not compare.check(nan, R, K=64, dtype="f16")["ok"]
 
 
+def _f32_add_rz(a, b):
+    """a + b rounded toward zero to float32 (a, b float32 whose exact sum fits
+    a float64: true for the exponent ranges used here)."""
+    s = float(a) + float(b)
+    r = np.float32(s)
+    if abs(float(r)) > abs(s):
+        r = np.nextafter(r, np.float32(0.0))
+    return np.float32(r)
+
+
+def test_fp8_gate_bounds_fp32_summation_in_any_order():
+    """compare.fp8_sum_rel models the 8-bit kernel's accumulation as fp32 sums
+    of exact products, each addition faithfully rounded: any order within each
+    128-term instruction, then in order across instructions. Brute force: sum
+    exact E4M3 products of random data that way in float32, with adversarial
+    inner orders (largest first, smallest first, sorted by sign, random) and
+    both round-to-nearest and truncation, and check that the error per unit of
+    sum |x| stays within the bound."""
+    rng = np.random.default_rng(3)
+    f32 = np.float32
+    for K in (128, 512, 4096):
+        worst = 0.0
+        for trial in range(8):
+            # E4M3 values (4-bit significands): products have <= 8 significant bits
+            a = np.ldexp(rng.integers(8, 16, K) * rng.choice([-1, 1], K), rng.integers(-9, 1, K))
+            w = np.ldexp(rng.integers(8, 16, K) * rng.choice([-1, 1], K), rng.integers(-9, 1, K))
+            if trial >= 4:        # one sign throughout: the partial sums grow to S
+                a, w = np.abs(a), np.abs(w)
+            x = (a * w).astype(np.float64)
+            assert np.array_equal(x.astype(f32).astype(np.float64), x)   # exact in fp32
+            exact = math.fsum(x.tolist())
+            for add in ((lambda p, v: f32(p + v)), _f32_add_rz):
+                acc = f32(0.0)
+                for i0 in range(0, K, 128):
+                    blk = x[i0:i0 + 128]
+                    order = [np.argsort(-np.abs(blk)), np.argsort(np.abs(blk)),
+                             np.argsort(blk), rng.permutation(blk.size)][trial % 4]
+                    part = f32(0.0)
+                    for v in blk[order]:
+                        part = add(part, f32(v))
+                    acc = add(acc, part)
+                worst = max(worst, abs(float(acc) - exact) / np.abs(x).sum())
+        assert worst <= compare.fp8_sum_rel(K), (K, worst, compare.fp8_sum_rel(K))
+    # and the coefficient grows with the number of instructions in the chain
+    assert compare.fp8_sum_rel(4096) == (127 + 31 + 2) * 2.0 ** -23
+    assert compare.fp8_sum_rel(128) < compare.fp8_sum_rel(4096) < compare.fp8_sum_rel(14336)
+
+
 # ---------------------------------------------------------- generators --
 
 def test_generators_are_deterministic_and_shaped():
