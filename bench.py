@@ -185,11 +185,9 @@ class SclkSampler:
 # Sources each kernel family is compiled from (the schedule table and host code
 # are left out: they do not change what a launch of the kernel does).
 KERNEL_HEADERS = {0: ["gba_kernels.hpp"],
-                  1: ["gba_kernels.hpp", "gemm_v2.hpp"],
-                  2: ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp"],
-                  3: ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp"],
-                  4: ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp", "gemm_v5.hpp"],
-                  "f8": ["gba_kernels.hpp", "gemm_v2.hpp", "gemm_v3.hpp", "gemm_v5.hpp",
+                  3: ["gba_kernels.hpp", "gba_dma.hpp", "gemm_v3.hpp"],
+                  4: ["gba_kernels.hpp", "gba_dma.hpp", "gemm_v3.hpp", "gemm_v5.hpp"],
+                  "f8": ["gba_kernels.hpp", "gba_dma.hpp", "gemm_v3.hpp", "gemm_v5.hpp",
                          "gemm_f8.hpp"]}
 
 
@@ -199,12 +197,9 @@ def instance_file(s: dict) -> str:
         return "f8_256x256x128_w2x2_persistent_%s.hip" % s["fmt"]
     if s["kernel"] == 4:
         return "v5_%dx%dx%d_w%dx%d_persistent.hip" % (s["bm"], s["bn"], s["bk"], s["wm"], s["wn"])
-    if s["kernel"] in (2, 3):
-        return "v3_%dx%dx%d_w%dx%d_s%d_l%d_p%d_m%d.hip" % (
-            s["bm"], s["bn"], s["bk"], s["wm"], s["wn"], s["stages"], s["loaders"], s["spread"],
-            32 if s["kernel"] == 2 else 16)
-    if s["kernel"] == 1:
-        return "v2_%dx%dx%d_w%dx%d_s%d.hip" % (s["bm"], s["bn"], s["bk"], s["wm"], s["wn"], s["stages"])
+    if s["kernel"] == 3:
+        return "v3_%dx%dx%d_w%dx%d_s%d_l%d_p%d_m16.hip" % (
+            s["bm"], s["bn"], s["bk"], s["wm"], s["wn"], s["stages"], s["loaders"], s["spread"])
     return "inst_%dx%dx%d_w%dx%d.hip" % (s["bm"], s["bn"], s["bk"], s["wm"], s["wn"])
 
 

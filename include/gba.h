@@ -80,18 +80,21 @@ typedef enum {
  * groups of group_m tile rows so that neighbouring workgroups share A and B
  * panels in that XCD's L2 ("use_swizzle ... L2 cache locality",
  * "writing-tilelang-kernels", Key API Patterns). kernel selects the main-loop
- * design: 0 = tiles staged through registers into LDS (B transposed on the
- * way), 1 = direct global->LDS loads into a `stages`-deep ring with transposing
- * LDS reads for B, 2 = the same with every instruction of an MFMA step placed
- * by hand: global->LDS loads (issued by the first `loaders` waves, spread over
- * `spread` steps) and the next step's LDS reads between the MFMAs, using
- * 32x32x16 MFMAs; 3 = kernel 2 with 16x16x32 MFMAs (the default: same work, less
- * power, so higher sustained clocks); 4 = kernel 3 run persistently: one
- * workgroup per CU walks tiles w, w + G, ... (G = min(tiles, CUs)) as one stream
- * of K slices, so the next tile's first slices load during the current tile's
- * last steps and epilogue (the built-in choice for 256x256 tiles; with K <= bk
- * it runs as kernel 3). loaders and spread are 0 for kernels
- * 0, 1. */
+ * design; the compiled-in ones are:
+ *   0 = tiles staged through registers into LDS (B transposed on the way), at
+ *       the pages' 128x128x32 starting tile;
+ *   3 = direct global->LDS loads into a `stages`-deep ring, every instruction
+ *       of an MFMA step placed by hand (global->LDS loads issued by the first
+ *       `loaders` waves, spread over `spread` steps; the next step's LDS reads
+ *       between the 16x16x32 MFMAs), one tile per workgroup;
+ *   4 = kernel 3's loop run persistently: one workgroup per CU walks tiles w,
+ *       w + G, ... (G = min(tiles, CUs)) as one stream of K slices, so the next
+ *       tile's first slices load during the current tile's last steps and
+ *       epilogue (the built-in choice for 256x256 tiles). With K <= bk it hands
+ *       the call to the 128x128 four-stage kernel 3, which feeds every output
+ *       element the same MFMAs in the same order.
+ * (Ids 1 and 2, earlier designs that never won, are no longer compiled in.)
+ * loaders and spread are 0 for kernel 0. */
 typedef struct {
     int32_t bm, bn, bk;
     int32_t wm, wn;

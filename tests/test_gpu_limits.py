@@ -169,7 +169,8 @@ def test_max_k_transpose_a_every_schedule_and_split(kmax, dtype):
             got = to_bits(c)
             assert np.array_equal(got, want), (sched_id(s), tb, first_mismatch(got, want))
             ran += 1
-    assert ran >= 10
+    # kernel 4 and kernel 3 at 256x128, 128x256 and 128x128 s4, both B layouts
+    assert ran >= 8
     for tb in (False, True):
         nb = gba.workspace_size(M, N, KMAX, "relu", dtype, transpose_b=tb, transpose_a=True)
         assert nb > 0, "40 x 136 x 2^21 is expected to split"
@@ -406,4 +407,5 @@ def test_max_m_transpose_a_every_schedule_both_layouts(_free):
             torch.cuda.synchronize()
             check_row_periodic(flat, c, want)
             ran += 1
-    assert ran >= 12
+    # the heuristic, kernel 4 and kernel 3 at 256x128, 128x256, 128x128 s4; both B layouts
+    assert ran >= 10

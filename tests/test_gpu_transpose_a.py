@@ -109,7 +109,7 @@ def test_exact_integer_bitwise_every_schedule(shape, dtype, transpose_b):
     want = oracle.encode(oracle.gemm_bias_act(At, B, bias, "none", dtype, transpose_a=True,
                                               transpose_b=transpose_b), dtype)
     scheds = ta_schedules()
-    assert len(scheds) >= 5
+    assert len(scheds) >= 4   # kernel 4; kernel 3 at 256x128, 128x256, 128x128 s4
     for s in scheds:
         for raster in (0, 1):
             say("tn exact", shape, dtype, transpose_b, sched_id(s), "raster", raster)

@@ -24,7 +24,7 @@ ACTS = {"none": 0, "relu": 1, "sigmoid": 2, "gelu": 3, "softplus": 4, "gelu_tanh
 STATUS = {
     0: "GBA_OK", 1: "GBA_ERR_NULL", 2: "GBA_ERR_SHAPE", 3: "GBA_ERR_DTYPE", 4: "GBA_ERR_ACT",
     5: "GBA_ERR_ALIGN", 6: "GBA_ERR_ALIAS", 7: "GBA_ERR_DEVICE", 8: "GBA_ERR_HIP",
-    9: "GBA_ERR_SCHEDULE", 10: "GBA_ERR_CACHE",
+    9: "GBA_ERR_SCHEDULE", 10: "GBA_ERR_CACHE", 11: "GBA_TUNE_INCOMPLETE",
 }
 SCHED_FIELDS = ("bm", "bn", "bk", "wm", "wn", "stages", "raster", "group_m", "kernel", "loaders",
                 "spread")

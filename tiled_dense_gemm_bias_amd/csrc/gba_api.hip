@@ -24,13 +24,7 @@
 #define GBA_VERSION_STRING "0.3.0"
 
 namespace gba {
-extern const ScheduleEntry s_256x256x64_w2x2;
 extern const ScheduleEntry s_128x128x32_w2x2;
-extern const ScheduleEntry d_256x256x64_w2x2_s2;
-extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p1_m32;
-extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p2_m32;
-extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p1_m16;
-extern const ScheduleEntry i_256x256x64_w2x2_s2_l4_p2_m16;
 extern const ScheduleEntry i_256x128x64_w2x2_s3_l4_p1_m16;
 extern const ScheduleEntry i_128x256x64_w2x2_s3_l4_p1_m16;
 extern const ScheduleEntry i_128x128x64_w2x2_s3_l4_p1_m16;
@@ -47,18 +41,14 @@ namespace {
 using gba::ScheduleEntry;
 
 const ScheduleEntry *const kTable[] = {
-    // interleaved direct-to-LDS kernels with 16x16x32 MFMAs (the default family)
-    &gba::i_256x256x64_w2x2_s2_l4_p1_m16, &gba::i_256x256x64_w2x2_s2_l4_p2_m16,
+    // persistent kernel: one workgroup per CU walks its 256x256 tiles as one
+    // stream of K slices (the built-in choice when the tiles fill the CUs)
+    &gba::p_256x256x64_w2x2,
+    // interleaved direct-to-LDS kernels with 16x16x32 MFMAs, one tile per workgroup
     &gba::i_256x128x64_w2x2_s3_l4_p1_m16, &gba::i_128x256x64_w2x2_s3_l4_p1_m16,
     &gba::i_128x128x64_w2x2_s3_l4_p1_m16, &gba::i_128x128x64_w2x2_s4_l4_p1_m16,
-    // persistent version of the first: one workgroup per CU walks its tiles
-    &gba::p_256x256x64_w2x2,
-    // the same with 32x32x16 MFMAs
-    &gba::i_256x256x64_w2x2_s2_l4_p1_m32, &gba::i_256x256x64_w2x2_s2_l4_p2_m32,
-    // direct-to-LDS kernel with compiler-scheduled steps
-    &gba::d_256x256x64_w2x2_s2,
-    // register-staged kernels, incl. the 128x128x32 starting tile
-    &gba::s_256x256x64_w2x2, &gba::s_128x128x32_w2x2,
+    // register-staged kernel at the pages' 128x128x32 starting tile
+    &gba::s_128x128x32_w2x2,
 };
 constexpr int kNumTable = sizeof(kTable) / sizeof(kTable[0]);
 constexpr long long kLdsBytes = 160 * 1024;
@@ -515,12 +505,22 @@ gba::PartialLaunchFn partial_launcher(int i, int dtype, int lay) {
     return (lay & LAY_TA) ? kTable[i]->part_ta[dtype][tb] : kTable[i]->part[dtype][tb];
 }
 
+// The persistent kernel streams at least two K slices per tile. With one (K <=
+// 64) it hands the call to the 128x128 four-stage kernel 3: per output element
+// the same MFMAs in the same order (two 32-deep steps), so the same bits.
+gba_schedule effective(const gba_schedule &s0, int64_t K) {
+    if (s0.kernel == 4 && K <= s0.bk) {
+        gba_schedule s = gba::i_128x128x64_w2x2_s4_l4_p1_m16.sched;
+        s.raster = s0.raster;
+        s.group_m = s0.group_m;
+        return s;
+    }
+    return s0;
+}
+
 int launch(const gba_schedule &s0, const void *A, const void *B, const void *bias, void *C,
            int64_t M, int64_t N, int64_t K, int act, int dtype, int lay) {
-    gba_schedule s = s0;
-    // The persistent kernel streams at least two K slices per tile; with one,
-    // its non-persistent twin (same tile, kernel 3) does the same work.
-    if (s.kernel == 4 && K <= s.bk) s.kernel = 3;
+    const gba_schedule s = effective(s0, K);
     const gba::GemmLaunchFn f = launcher(s, dtype, act, lay);
     if (!f) return GBA_ERR_SCHEDULE;   // unknown, or no path for these layouts in this kernel
     hipError_t e = f(A, B, bias, C, (int)M, (int)N, (int)K, s.raster, s.group_m, t_stream);
@@ -537,8 +537,7 @@ int launch(const gba_schedule &s0, const void *A, const void *B, const void *bia
 // does not: 19.6 us split against 14.3 us whole; at 256x256x4096 it does.)
 int split_count(const gba_schedule &s0, int64_t M, int64_t N, int64_t K, int cus, int dtype,
                 int lay) {
-    gba_schedule s = s0;
-    if (s.kernel == 4 && K <= s.bk) s.kernel = 3;
+    const gba_schedule s = effective(s0, K);
     const int i = find_entry(s);
     if (i < 0 || !partial_launcher(i, dtype, lay) || K <= 0) return 1;
     const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
@@ -604,8 +603,7 @@ int gemm_common(const void *A, const void *B, const void *bias, void *C, int64_t
                 fprintf(stderr, "[gba] M=%lld N=%lld K=%lld act=%s dtype=%s -> split-K %d x k%d %dx%dx%d (%s)\n",
                         (long long)M, (long long)N, (long long)K, kActName[act], kDtName[dtype], S,
                         sch.kernel, sch.bm, sch.bn, sch.bk, why);
-            gba_schedule s3 = sch;
-            if (s3.kernel == 4 && K <= s3.bk) s3.kernel = 3;
+            const gba_schedule s3 = effective(sch, K);
             const gba::PartialLaunchFn pf = partial_launcher(find_entry(s3), dtype, lay);
             hipError_t e = pf(A, B, (float *)ws, (int)M, (int)N, (int)K, S, s3.raster, s3.group_m,
                               t_stream);

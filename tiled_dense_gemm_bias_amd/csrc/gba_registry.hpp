@@ -6,7 +6,7 @@
 
 #include "gba.h"
 #include "gba_kernels.hpp"
-#include "gemm_v2.hpp"
+#include "gba_dma.hpp"
 #include "gemm_v3.hpp"
 #include "gemm_v5.hpp"
 #include "gemm_f8.hpp"
@@ -67,46 +67,6 @@ struct ScheduleEntry {
     const ScheduleEntry NAME = {{BM, BN, BK, WM, WN, 2, 1, GROUP_M, 0, 0, 0},                     \
                                 {GBA_LAUNCHERS_(BM, BN, BK, WM, WN, 0),                     \
                                  GBA_LAUNCHERS_(BM, BN, BK, WM, WN, 1)}};                   \
-    }
-#endif
-
-// ---- direct-to-LDS kernel (gemm_v2.hpp) ----
-#define GBA_V2_INST_(BM, BN, BK, WM, WN, S, DT, ACT)                                          \
-    template __global__ void gba::gemm_v2_kernel<BM, BN, BK, WM, WN, S, DT, ACT>(             \
-        const uint16_t *__restrict__, const uint16_t *__restrict__, const uint16_t *__restrict__, \
-        uint16_t *__restrict__, int, int, int, int, int, int, int);
-
-#define GBA_V2_INSTS_(BM, BN, BK, WM, WN, S)                                                   \
-    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 0)                                                  \
-    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 1)                                                  \
-    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 2)                                                  \
-    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 3)                                                  \
-    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 4) \
-    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 0, 5) \
-    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 0)                                                  \
-    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 1)                                                  \
-    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 2)                                                  \
-    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 3)    \
-    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 4) \
-    GBA_V2_INST_(BM, BN, BK, WM, WN, S, 1, 5)
-
-#define GBA_V2_LAUNCHERS_(BM, BN, BK, WM, WN, S, DT)                                           \
-    {gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 0>,                                        \
-     gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 1>,                                        \
-     gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 2>,                                        \
-     gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 3>, \
-     gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 4>, gba::launch_gemm_v2<BM, BN, BK, WM, WN, S, DT, 5>}
-
-#ifdef __HIP_DEVICE_COMPILE__
-#define GBA_V2_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, S, GROUP_M) GBA_V2_INSTS_(BM, BN, BK, WM, WN, S)
-#else
-#define GBA_V2_SCHEDULE_ENTRY(NAME, BM, BN, BK, WM, WN, S, GROUP_M)                          \
-    GBA_V2_INSTS_(BM, BN, BK, WM, WN, S)                                                     \
-    namespace gba {                                                                          \
-    extern const ScheduleEntry NAME;                                                         \
-    const ScheduleEntry NAME = {{BM, BN, BK, WM, WN, S, 1, GROUP_M, 1, 0, 0},                      \
-                                {GBA_V2_LAUNCHERS_(BM, BN, BK, WM, WN, S, 0),                \
-                                 GBA_V2_LAUNCHERS_(BM, BN, BK, WM, WN, S, 1)}};              \
     }
 #endif
 

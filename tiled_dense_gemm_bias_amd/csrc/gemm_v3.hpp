@@ -1,8 +1,13 @@
 // Interleaved direct-to-LDS GEMM kernel for gfx950.
 //
-// Same tiles and LDS layouts as gemm_v2.hpp; the difference is the order in
-// which a wave issues its instructions (and, with 16x16x32 MFMAs, an epilogue
-// that stores whole row segments through LDS; see the epilogue). Moving a slice from HBM/L2 into
+// Each workgroup owns one BM x BN tile of C and walks K in BK-deep slices
+// through a STAGES-deep LDS ring filled by direct-to-LDS loads (gba_dma.hpp).
+// A stays K-contiguous in LDS ([BM][BK], 16-byte chunks XOR-swizzled by row) and
+// is read with ds_read_b128; B stays N-contiguous ([BK][BN], chunks swizzled by
+// k row) and the MFMA's K-contiguous B^T operand is gathered with
+// ds_read_b64_tr_b16. The epilogue stores whole row segments through LDS (see
+// there). What matters most is the order in which a wave issues its
+// instructions. Moving a slice from HBM/L2 into
 // LDS takes the CU's address path about as long as half of the slice's MFMA
 // work, and a wave that issues all its direct-to-LDS loads back to back stalls
 // in issue for that whole time. Here every MFMA step is written out
@@ -37,14 +42,13 @@
 // (splitk_reduce_kernel) adds the partials in s order, then bias, act, rounding.
 #pragma once
 
-#include "gemm_v2.hpp"
+#include "gba_dma.hpp"
 
 #include <type_traits>
 
 namespace gba {
 
 template <int MS> struct Acc;
-template <> struct Acc<32> { typedef f32x16 type; static constexpr int n = 16; };
 template <> struct Acc<16> { typedef f32x4 type; static constexpr int n = 4; };
 
 // v_mfma_f32_16x16x32_{f16,bf16}: lane l holds row/column l % 16 and K chunk
@@ -95,8 +99,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     constexpr int CHT = BM / 8;           // chunks per k row of At's tile (TA)
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int BD = MS;                // MFMA output block: BD x BD
-    constexpr int KS = MS == 32 ? 16 : 32;  // K depth of one MFMA
-    constexpr int NI = MS == 32 ? 4 : 1;  // 4-column groups per lane and block
+    constexpr int KS = 32;                // K depth of one MFMA
     constexpr int FM = WTM / BD, FN = WTN / BD;
     constexpr int NMF = FM * FN;          // MFMAs per step
     constexpr int NFA = (TA ? 2 : 1) * FM;        // A fragment reads per step
@@ -108,7 +111,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     constexpr int B_LD = TB ? BN * CHA / NTL : BK * CHB / NTL;
     constexpr int LD = A_LD + B_LD;       // loads per loader thread per slice
     constexpr int LD_STEP = (LD + SPREAD - 1) / SPREAD;
-    static_assert(MS == 32 || MS == 16, "MFMA 32x32x16 or 16x16x32");
+    static_assert(MS == 16, "16x16x32 MFMAs");
     static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
     static_assert(KK % 2 == 0, "fragment buffers alternate within a slice");
     static_assert(WTM % BD == 0 && WTN % BD == 0, "wave tile must be whole MFMA blocks");
@@ -255,10 +258,8 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         return r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * kk + lchunk) * 16;
     };
     auto b_addr = [&](int fn, int kk, int h) -> int {
-        const int k = MS == 32 ? kk * 16 + 8 * (tg >> 1) + 4 * h + (tj >> 2)
-                               : kk * 32 + 8 * tg + 4 * h + (tj >> 2);
-        const int n = MS == 32 ? wn * WTN + fn * 32 + 16 * (tg & 1) + 4 * (tj & 3)
-                               : wn * WTN + fn * 16 + 4 * (tj & 3);
+        const int k = kk * 32 + 8 * tg + 4 * h + (tj >> 2);
+        const int n = wn * WTN + fn * 16 + 4 * (tj & 3);
         const int c = (n >> 3) ^ bswz<CHB>(k);
         return A_BYTES + k * (BN * 2) + c * 16 + (n & 4) * 2;
     };
@@ -335,10 +336,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                                                                         0, 1, 2, 3, 4, 5, 6, 7));
             else
                 aop = fa[cur][fm];
-            if constexpr (MS == 32)
-                acc[fn][fm] = mfma32x32x16<DT>(bop, aop, acc[fn][fm]);
-            else
-                acc[fn][fm] = mfma16x16x32<DT>(bop, aop, acc[fn][fm]);
+            acc[fn][fm] = mfma16x16x32<DT>(bop, aop, acc[fn][fm]);
             if (q < NPF) read_one(cur ^ 1, pf_base, pf_kk, q);
             if (dma && q % every == 0 && q / every < nd) dma_one(d, d0 + q / every);
             __builtin_amdgcn_sched_barrier(0);
@@ -413,7 +411,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         return;
     }
 
-    if constexpr (STAGED) {
+    {
         // + bias[n], activation, round once; each group of four 16x16 blocks (one
         // row block fm, one 64-column half fh) goes through the wave's staging
         // buffers and leaves as 16-byte stores of whole 128-byte row segments (8
@@ -493,62 +491,6 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             store_all(std::true_type{});
         return;
     }
-
-    // Epilogue (32x32x16 MFMAs): + bias[n], activation, round once, 8-byte stores. Addresses are a
-    // 32-bit byte offset from the tile's corner (row pitch N*2, at most 2^32 for
-    // N <= 2^23); rows and columns are masked only in edge tiles. Lane l holds
-    // row (l % BD) of block fm and, per 4-column group i, columns c0(i) .. +3.
-    char *const Ct = reinterpret_cast<char *>(C + (size_t)m0 * N + n0);
-    const int mrow = wm * WTM + lrow_b;
-    auto col0 = [&](int fn, int i) {
-        return wn * WTN + fn * BD + (MS == 32 ? i * 8 + lhalf * 4 : 4 * (lane >> 4));
-    };
-    const uint32_t lane_off = ((uint32_t)mrow * (uint32_t)N + (uint32_t)col0(0, 0)) * 2u;
-    const bool full = M - m0 >= BM && N - n0 >= BN;   // no m0 + BM: overflows near 2^31
-    // All of this lane's bias values first, in one batch (one load latency, not
-    // one per column group); columns past N read as zero.
-    u32x2 bvals[FN][NI];
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int cn = col0(fn, i);
-            bvals[fn][i] = bias && n0 + cn < N ? *reinterpret_cast<const u32x2 *>(bias + n0 + cn)
-                                               : u32x2{0u, 0u};
-        }
-    auto store_all = [&](auto masked) {
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const int cn = col0(fn, i);
-                if (masked && n0 + cn >= N) continue;
-                float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
-                if (bias) {
-                    const u32x2 bb = bvals[fn][i];
-                    b0 = to_f32<DT>(bb.x & 0xffffu);
-                    b1 = to_f32<DT>(bb.x >> 16);
-                    b2 = to_f32<DT>(bb.y & 0xffffu);
-                    b3 = to_f32<DT>(bb.y >> 16);
-                }
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm) {
-                    if (masked && m0 + mrow + fm * BD >= M) continue;
-                    const AccT &a = acc[fn][fm];
-                    u32x2 o;
-                    o.x = pack2<DT>(act_fn<ACT>(a[4 * i + 0] + b0), act_fn<ACT>(a[4 * i + 1] + b1));
-                    o.y = pack2<DT>(act_fn<ACT>(a[4 * i + 2] + b2), act_fn<ACT>(a[4 * i + 3] + b3));
-                    const uint32_t off = lane_off + (uint32_t)(fm * BD) * (uint32_t)N * 2u +
-                                         (uint32_t)(cn - col0(0, 0)) * 2u;
-                    *reinterpret_cast<u32x2 *>(Ct + off) = o;
-                }
-            }
-        }
-    };
-    if (full)
-        store_all(std::false_type{});
-    else
-        store_all(std::true_type{});
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int MS, int DT,

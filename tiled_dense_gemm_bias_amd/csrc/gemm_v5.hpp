@@ -1,22 +1,74 @@
-// Persistent variant of the interleaved 16x16x32 GEMM kernel (gemm_v3.hpp).
+// Persistent GEMM kernel (kernel 4): the interleaved 16x16x32 main loop of
+// gemm_v3.hpp, run by one workgroup per CU over all of its tiles.
 //
 // One workgroup per CU walks its tiles (t = w, w + G, w + 2G, ... in raster
-// order, G = grid size) as one stream of 64-deep K slices through the same
-// two-stage LDS ring. The loads of stream position p + 2 are issued in the
-// last MFMA step of position p, exactly as in gemm_v3, except that positions
-// past a tile's last slice are the next tile's first slices. So when a tile's
-// main loop ends, the next tile's slice 0 is already in LDS (published by the
-// last barrier) and its slice 1 is in flight; both land while the epilogue
-// (bias, activation, rounding, stores) runs, and the next main loop starts
-// without the pipeline fill of a fresh workgroup. Tiles, LDS layouts,
-// fragments, MFMA order and epilogue are gemm_v3's (results are bit-identical).
-// TB (transpose_B, B given as an (N,K) array W) is gemm_v3's TB layout, and TA
-// (transpose_A, A given as a (K,M) array At) gemm_v3's TA layout.
+// order, G = grid size) as one stream of 64-deep K slices through a two-stage
+// LDS ring. The loads of stream position p + 2 are issued in the last MFMA step
+// of position p; positions past a tile's last slice are the next tile's first
+// slices. So when a tile's main loop ends, the next tile's slice 0 is already in
+// LDS (published by the last barrier) and its slice 1 is in flight; both land
+// while the epilogue (bias, activation, rounding, stores) runs, and the next
+// main loop starts without the pipeline fill of a fresh workgroup.
+//
+// The main loop is written so that a wave issues almost nothing but MFMAs, LDS
+// reads and direct-to-LDS loads (vector ALU work between MFMAs that also carry
+// memory instructions costs the matrix core issue time; address arithmetic is
+// kept out of the stream):
+//  * LDS ring layout [A stage 0 | A stage 1 | B stage 0 | B stage 1] (32 KiB
+//    each). Every fragment read is a per-thread base register, which names the
+//    stage being read, plus a compile-time offset (the ds_read offset field).
+//    Once per slice each base moves to the other stage (one add, issued among
+//    MFMAs that carry no memory instructions).
+//  * Each thread's load offsets (one per load of a slice) are held in
+//    registers for the whole stream; a slice's K position moves the buffer
+//    descriptor's base, not the offsets. They are re-masked (out-of-range
+//    offset) only where the load stream enters a tile (N or M edge) or the
+//    last, partial K slice (chunks past K), a few times per tile.
+//  * The LDS destination of each load is one scalar add into M0 from a scalar
+//    stage base.
+//
+// Tiles, LDS swizzles, fragments, MFMA order and epilogue are gemm_v3's, so
+// results are bit-identical to it. TB (transpose_B, B given as an (N,K) array
+// W) and TA (transpose_A, A given as a (K,M) array At) are gemm_v3's layouts.
 #pragma once
 
 #include "gemm_v3.hpp"
 
+#include <type_traits>
+#include <utility>
+
 namespace gba {
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, unrolled at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_seq(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// This lane's index in its wave, read afresh (volatile: not merged with earlier
+// reads, so no register has to hold it across the loops).
+__device__ __forceinline__ int lane_now() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
+// buffer_load_dwordx4 ... lds into LDS byte address lds_base + IMM (+ 16 per lane).
+template <uint32_t IMM>
+__device__ __forceinline__ void buffer_load_lds16_at(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset,
+                                                     uint32_t lds_base) {
+    asm volatile(
+        "s_add_u32 m0, %2, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
+        : "v"(voffset), "s"(rsrc), "s"(lds_base), "n"(IMM)
+        : "memory", "m0", "scc");
+}
 
 template <int BM, int BN, int WM, int WN, int DT, int ACT, bool TB = false, bool TA = false>
 __global__ void __launch_bounds__(WM * WN * 64)
@@ -31,7 +83,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     constexpr int NFA = (TA ? 2 : 1) * FM;
     constexpr int NMF = FM * FN, NPF = NFA + (TB ? 1 : 2) * FN;
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;
-    constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    constexpr uint32_t B_REGION = 2 * A_BYTES;   // B's stages follow A's
     constexpr int A_LD = BM * CHA / NT, B_LD = (TB ? BN * CHA : BK * CHB) / NT, LD = A_LD + B_LD;
     constexpr int EVERY = NMF / LD;
     static_assert(KK == 2, "two MFMA steps per slice");
@@ -40,11 +92,13 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     static_assert(!TA || BM == BN, "At's tile is loaded with B's per-thread mapping");
     static_assert((BM * CHA) % NT == 0 && B_LD * NT == (TB ? BN * CHA : BK * CHB),
                   "slices split evenly");
-    static_assert(2 * STAGE_BYTES <= 160 * 1024, "LDS ring too large");
+    static_assert(A_BYTES == 32768 && B_BYTES == 32768,
+                  "fragment offsets (stage + block) must fit the 16-bit ds_read offset");
     static_assert(2 * LD < 64 && NMF % LD == 0 && NPF <= NMF, "step layout");
-    // Needs at least two K slices (K > 64): the launcher uses gemm_v3 below that.
+    static_assert(A_LD == 8 && B_LD == 8, "one register of load offsets per load");
+    // Needs at least two K slices (K > 64): the library sends K <= 64 elsewhere.
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * (A_BYTES + B_BYTES)];
     // The bias of a tile, staged in LDS with the tile's first slice so that the
     // epilogue reads it with ds_read instead of waiting on global loads (which
     // would also wait for the next tile's slices in flight). One 1 KiB slot per
@@ -56,13 +110,16 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     constexpr int STG_BYTES = 16 * 64 * 2;
     __shared__ __attribute__((aligned(1024))) char stage_smem[NW * 2 * STG_BYTES];
     static_assert(WTN == 128 && BD == 16, "the epilogue stages 16 x 64 halves of 128-column wave blocks");
-    static_assert(2 * STAGE_BYTES + 2 * NW * 1024 + NW * 2 * STG_BYTES <= 160 * 1024,
+    static_assert(2 * (A_BYTES + B_BYTES) + 2 * NW * 1024 + NW * 2 * STG_BYTES <= 160 * 1024,
                   "LDS ring + bias slots + staging too large");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
     const int wm = wid / WN, wn = wid % WN;
     const int nk = (K + BK - 1) / BK;
+    // Index of every tile's partial last slice (K % 64 != 0), or -1 (kept as an
+    // int: a uniform bool can end up materialised in a vector register).
+    const int tail_k = (K % BK) != 0 ? nk - 1 : -1;
     const int T = tiles_m * tiles_n;
     const int G = gridDim.x;
     const int wid_s = __builtin_amdgcn_readfirstlane(wid);
@@ -90,48 +147,88 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         return true;
     };
 
-    // Loader offsets within a slice (independent of the tile). Load i of a
-    // thread fills LDS chunk s = i*NT + tid of the A (B) part. For A that is row
-    // 32i + tid/8, logical chunk c_a = (tid%8) ^ (row%8), the same for every i;
-    // for B, k row 8i + tid/32 and logical chunk c_b(i) = c_b(0) ^ 8(i%4)
-    // (the B swizzle's row/8 term). So a handful of registers describe them all.
+    // ---- loads ----
+    // A-like tiles (A [M,K]; W [N,K] with TB): load i of a thread fills LDS chunk
+    // i*NT + tid of the stage: row 32i + tid/8, logical chunk c_a = (tid%8) ^
+    // (row%8), the same for every i. B-like tiles (B [K,N]; At [K,M] with TA):
+    // k row 8j + tid/32, logical chunk c_b(j) = c_b0 ^ 8(j%4) (the B swizzle's
+    // row/8 term). The offsets below are relative to the slice's corner, which
+    // the buffer descriptor carries.
     static_assert(NT == 256 && CHA == 8 && CHB == 32, "loader mapping written for 256 threads, BK 64, BN 256");
-    // TB: W's tile is loaded like A's (BN = 256 rows of 64 k), with the same
-    // per-thread base.
-    const int c_a = (tid & 7) ^ ((tid >> 3) & 7);
-    const uint32_t a_base = (uint32_t)(tid >> 3) * (uint32_t)K * 2u + (uint32_t)c_a * 16u;
-    const int c_b0 = (tid & 31) ^ bswz<CHB>(tid >> 5);
-    const uint32_t b_row = (uint32_t)(tid >> 5) * (uint32_t)N * 2u;
-    // TA: At's tile (64 k rows of BM = BN values) is loaded like B's.
-    const uint32_t t_row = (uint32_t)(tid >> 5) * (uint32_t)M * 2u;
-    // Loads of slice kt of tile t (live) into stage `stage`; a dead slice reads
-    // nothing (every lane out of range) but keeps the wait counts uniform.
+    // av: A-like offsets (rows 32i); chunks past K of the last slice masked when
+    // `tail`. bv: B [K,N] offsets (k rows 8j) of a tile at column n0, chunks
+    // past N masked. tv: At [K,M] offsets of a tile at row m0, chunks past M
+    // masked. The row and column masks of the descriptor's range cover the
+    // other edges (rows of A/W past M/N, k rows past K).
+    // The thread index is rebuilt in each call (lane_now), so that the offsets
+    // are formed where they are set rather than hoisted out of the loops and
+    // held, with the index, across them (which would spill).
+    uint32_t av[8], bv[8], tv[8];
+    auto set_av = [&](bool tail) __attribute__((always_inline)) {
+        const int t = wid_s * 64 + lane_now();
+        const int ca = (t & 7) ^ ((t >> 3) & 7);
+        const bool ok = !tail || (nk - 1) * BK + ca * 8 < K;
+        const uint32_t base = (uint32_t)(t >> 3) * (uint32_t)K * 2u + (uint32_t)ca * 16u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) av[i] = ok ? base + (uint32_t)(i * 64) * (uint32_t)K : kOobOffset;
+    };
+    auto set_bv = [&](int n0) __attribute__((always_inline)) {
+        const int t = wid_s * 64 + lane_now();
+        const int cb0 = (t & 31) ^ bswz<CHB>(t >> 5);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = cb0 ^ (8 * (j & 3));
+            bv[j] = n0 + c * 8 < N ? (uint32_t)((t >> 5) + 8 * j) * (uint32_t)N * 2u + (uint32_t)c * 16u
+                                   : kOobOffset;
+        }
+    };
+    auto set_tv = [&](int m0) __attribute__((always_inline)) {
+        const int t = wid_s * 64 + lane_now();
+        const int cb0 = (t & 31) ^ bswz<CHB>(t >> 5);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = cb0 ^ (8 * (j & 3));
+            tv[j] = m0 + c * 8 < M ? (uint32_t)((t >> 5) + 8 * j) * (uint32_t)M * 2u + (uint32_t)c * 16u
+                                   : kOobOffset;
+        }
+    };
+    // Descriptors of stream position (tile t, slice kt); a dead position (past the
+    // last tile) has empty ranges: every lane reads zeros and no memory, which
+    // keeps the wait counts uniform.
     struct SliceDma {
         __amdgpu_buffer_rsrc_t ra, rb;
-        uint32_t la, lb;
-        int k0, n0, m0;
     };
-    auto slice_dma = [&](const Tile &t, bool live, int kt, int stage) {
+    auto slice_dma = [&](const Tile &t, bool live, int kt) {
         SliceDma d;
-        d.la = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(stage * STAGE_BYTES + wid_s * 64 * 16));
-        d.lb = d.la + A_BYTES;
-        d.k0 = live ? kt * BK : K;
-        d.n0 = live ? t.n0 : N;
-        d.m0 = live ? t.m0 : M;
+        const int k0 = kt * BK;
         if constexpr (TA)
-            d.ra = make_rsrc(A + (live ? (size_t)d.k0 * M + t.m0 : 0),
-                             live ? (uint32_t)min(K - d.k0, BK) * (uint32_t)M * 2u : 0u);
+            d.ra = make_rsrc(A + (live ? (size_t)k0 * M + t.m0 : 0),
+                             live ? (uint32_t)min(K - k0, BK) * (uint32_t)M * 2u : 0u);
         else
-            d.ra = make_rsrc(A + (live ? (size_t)t.m0 * K + d.k0 : 0),
-                             live ? (uint32_t)t.rows * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u);
+            d.ra = make_rsrc(A + (live ? (size_t)t.m0 * K + k0 : 0),
+                             live ? (uint32_t)t.rows * (uint32_t)K * 2u - (uint32_t)k0 * 2u : 0u);
         if constexpr (TB)
-            d.rb = make_rsrc(B + (live ? (size_t)t.n0 * K + d.k0 : 0),
-                             live ? (uint32_t)min(N - t.n0, BN) * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u
+            d.rb = make_rsrc(B + (live ? (size_t)t.n0 * K + k0 : 0),
+                             live ? (uint32_t)min(N - t.n0, BN) * (uint32_t)K * 2u - (uint32_t)k0 * 2u
                                   : 0u);
         else
-            d.rb = make_rsrc(B + (live ? (size_t)d.k0 * N + t.n0 : 0),
-                             live ? (uint32_t)min(K - d.k0, BK) * (uint32_t)N * 2u : 0u);
+            d.rb = make_rsrc(B + (live ? (size_t)k0 * N + t.n0 : 0),
+                             live ? (uint32_t)min(K - k0, BK) * (uint32_t)N * 2u : 0u);
         return d;
+    };
+    // This wave's LDS load base in stage 0; load i of a slice lands at + region
+    // + stage * 32 KiB + i * NT * 16 (the stage term comes with `lds_stage`).
+    const uint32_t ld_wave = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(wid_s * 64 * 16));
+    auto dma_one = [&](uint32_t lds_stage, const SliceDma &d, auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        if constexpr (i < A_LD) {
+            constexpr uint32_t off = (uint32_t)(i * NT * 16);
+            buffer_load_lds16_at<off>(d.ra, TA ? tv[i] : av[i], lds_stage);
+        } else {
+            constexpr int j = i - A_LD;
+            constexpr uint32_t off = B_REGION + (uint32_t)(j * NT * 16);
+            buffer_load_lds16_at<off>(d.rb, TB ? av[j] : bv[j], lds_stage);
+        }
     };
     // Bias of tile t into this wave's slot of parity p: lanes 0 .. BN/8-1 load 16
     // bytes each (columns past N read zeros), the other lanes land zeros. Counted
@@ -140,52 +237,26 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         (uint32_t)(uintptr_t)(GBA_LDS void *)bias_smem + (uint32_t)(wid_s * 1024));
     auto bias_dma = [&](const Tile &t, int p) {
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias + t.n0, (uint32_t)min(N - t.n0, BN) * 2u);
-        buffer_load_lds16(rb, lane < BN / 8 ? (uint32_t)lane * 16u : kOobOffset,
+        const int l = lane_now();   // formed here, not held across the loops
+        buffer_load_lds16(rb, l < BN / 8 ? (uint32_t)l * 16u : kOobOffset,
                           bias_lds + (uint32_t)(p * NW * 1024));
     };
-    // `kx`, `nx`: K and N re-read opaquely in each slice, so that the per-load
-    // row offsets (multiples of 64 K and 16 N bytes) are recomputed where used
-    // rather than held in scalar registers for the whole loop.
-    auto dma_one = [&](const SliceDma &d, int i, uint32_t kx, uint32_t nx, uint32_t mx) {
-        if (i < A_LD) {
-            if constexpr (TA) {
-                const int c = c_b0 ^ (8 * (i & 3));
-                const uint32_t o = d.m0 + c * 8 < M
-                                       ? t_row + (uint32_t)(i * 16) * mx + (uint32_t)c * 16u
-                                       : kOobOffset;
-                buffer_load_lds16(d.ra, o, d.la + i * NT * 16);
-            } else {
-                const uint32_t o = d.k0 + c_a * 8 < K ? a_base + (uint32_t)(i * 64) * kx : kOobOffset;
-                buffer_load_lds16(d.ra, o, d.la + i * NT * 16);
-            }
-        } else if constexpr (TB) {
-            const int j = i - A_LD;
-            const uint32_t o = d.k0 + c_a * 8 < K ? a_base + (uint32_t)(j * 64) * kx : kOobOffset;
-            buffer_load_lds16(d.rb, o, d.lb + j * NT * 16);
-        } else {
-            const int j = i - A_LD;
-            const int c = c_b0 ^ (8 * (j & 3));
-            const uint32_t o = d.n0 + c * 8 < N
-                                   ? b_row + (uint32_t)(j * 16) * nx + (uint32_t)c * 16u
-                                   : kOobOffset;
-            buffer_load_lds16(d.rb, o, d.lb + j * NT * 16);
-        }
-    };
 
-    // Fragments (as gemm_v3 with 16x16x32 MFMAs). A block fm, step kk: lane l
-    // reads row wm*WTM + 16 fm + l%16, logical chunk 4 kk + l/16, stored at
-    // chunk ^ (row % 8); row % 8 = l % 8, so the address is a per-kk lane base
-    // plus 16 fm rows (the ds_read offset field). B^T block fn, step kk, half
-    // h: k row 32 kk + 8 (l/16) + 4 h + (l%16)/4 and columns n = wn*WTN + 16 fn
-    // + 4 (l%4); its swizzle term depends only on the lane, and 16 fn columns
-    // only flip chunk bits 1..3, so the address is a per-fn lane base plus the
-    // k-row offset of kk and h.
+    // ---- fragments ----
+    // (As gemm_v3 with 16x16x32 MFMAs.) A block fm, step kk: lane l reads row
+    // wm*WTM + 16 fm + l%16, logical chunk 4 kk + l/16, stored at chunk ^ (row %
+    // 8); row % 8 = l % 8, so the address is a per-kk lane base plus 16 fm rows.
+    // B^T block fn, step kk, half h: k row 32 kk + 8 (l/16) + 4 h + (l%16)/4 and
+    // columns n = wn*WTN + 16 fn + 4 (l%4); its swizzle term depends only on the
+    // lane, so the address is a per-fn lane base plus the k-row offset of kk and
+    // h. All bases are LDS addresses in the stage being read (stage 0 at the
+    // start); the block and k-row terms are compile-time offsets.
     const int tg = lane >> 4, tj = lane & 15;
     uint32_t fa_base[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
         const int r = wm * WTM + tj;
-        fa_base[kk] = (uint32_t)(r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * kk + tg) * 16);
+        fa_base[kk] = smem_lds + (uint32_t)(r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * kk + tg) * 16);
     }
     // TB: W^T block fn, step kk: lane l reads row wn*WTN + 16 fn + l%16 of W's
     // tile like A's (a per-kk lane base plus 16 fn rows).
@@ -195,73 +266,86 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     for (int f = 0; f < NFB; ++f) {
         if constexpr (TB) {
             const int r = wn * WTN + tj;
-            fb_base[f] = (uint32_t)(A_BYTES + r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * f + tg) * 16);
+            fb_base[f] = smem_lds + B_REGION + (uint32_t)(r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * f + tg) * 16);
         } else {
             const int k = 8 * tg + (tj >> 2);
             const int n = wn * WTN + f * 16 + 4 * (tj & 3);
             const int c = (n >> 3) ^ bswz<CHB>(k);
-            fb_base[f] = (uint32_t)(A_BYTES + k * (BN * 2) + c * 16 + (n & 4) * 2);
+            fb_base[f] = smem_lds + B_REGION + (uint32_t)(k * (BN * 2) + c * 16 + (n & 4) * 2);
         }
     }
-    auto a_addr = [&](int fm, int kk) -> uint32_t { return fa_base[kk] + fm * BD * (BK * 2); };
     // TA: A block fm, step kk, half h gathered from At's tile like B^T's from
     // B's. Lane l asks for k row 32 kk + 8 (l/16) + 4 h + (l%16)/4 and m =
     // wm*WTM + 16 fm + 4 (l%4); 16 fm rows flip only chunk bits 1..3 (byte
-    // address bits 5..7) of the fm = 0 address, so one base serves every block.
-    uint32_t ft_base;
-    {
+    // address bits 5..7) of the fm = 0 address: one base per block fm.
+    uint32_t ft_base[TA ? FM : 1];
+    if constexpr (TA) {
         const int k = 8 * tg + (tj >> 2);
         const int m = wm * WTM + 4 * (tj & 3);
         const int c = (m >> 3) ^ bswz<CHB>(k);
-        ft_base = (uint32_t)(k * (BM * 2) + c * 16 + (m & 4) * 2);
+        const uint32_t b0 = (uint32_t)(k * (BM * 2) + c * 16 + (m & 4) * 2);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) ft_base[fm] = smem_lds + (b0 ^ (uint32_t)(fm << 5));
     }
-    auto t_addr = [&](int fm, int kk, int h) -> uint32_t {
-        return (ft_base ^ (uint32_t)(fm << 5)) + (32 * kk + 4 * h) * (BM * 2);
-    };
-    auto b_addr = [&](int fn, int kk, int h) -> uint32_t {
-        if constexpr (TB)
-            return fb_base[kk] + fn * BD * (BK * 2);
-        else
-            return fb_base[fn] + (32 * kk + 4 * h) * (BN * 2);
-    };
 
     f32x4 acc[FN][FM];
     u32x4 fa[2][FM];
     i16x4 fal[2][FM], fah[2][FM];
     i16x4 fbl[2][FN], fbh[2][FN];
     u32x4 fw[2][FN];
-    auto read_one = [&](int buf, const char *base, int kk, int r) {
+    // Fragment r of step kk of the slice in the bases' stage into buffer buf.
+    auto read_one = [&](int buf, int kk, int r) __attribute__((always_inline)) {
         if (r < NFA) {
             if constexpr (TA) {
                 const int fm = r >> 1, h = r & 1;
-                const i16x4 v =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((GBA_LDS i16x4 *)(base + t_addr(fm, kk, h)));
+                const uint32_t o = (uint32_t)((32 * kk + 4 * h) * (BM * 2));
+                const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GBA_LDS i16x4 *)(ft_base[fm] + o));
                 if (h)
                     fah[buf][fm] = v;
                 else
                     fal[buf][fm] = v;
             } else {
-                fa[buf][r] = *reinterpret_cast<const u32x4 *>(base + a_addr(r, kk));
+                const uint32_t o = (uint32_t)(r * BD * (BK * 2));
+                fa[buf][r] = *(GBA_LDS const u32x4 *)(fa_base[kk] + o);
             }
         } else if constexpr (TB) {
-            fw[buf][r - NFA] = *reinterpret_cast<const u32x4 *>(base + b_addr(r - NFA, kk, 0));
+            const int fn = r - NFA;
+            const uint32_t o = (uint32_t)(fn * BD * (BK * 2));
+            fw[buf][fn] = *(GBA_LDS const u32x4 *)(fb_base[kk] + o);
         } else {
             const int fn = (r - NFA) >> 1, h = (r - NFA) & 1;
-            const i16x4 v =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((GBA_LDS i16x4 *)(base + b_addr(fn, kk, h)));
+            const uint32_t o = (uint32_t)((32 * kk + 4 * h) * (BN * 2));
+            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GBA_LDS i16x4 *)(fb_base[fn] + o));
             if (h)
                 fbh[buf][fn] = v;
             else
                 fbl[buf][fn] = v;
         }
     };
-    // One MFMA step on buffer `cur`; `reads`: the next step's fragments (from
-    // `pf_base` step pf_kk); `dma`: all LD loads of slice d, one per EVERY MFMAs.
-    auto step = [&](int cur, bool reads, const char *pf_base, int pf_kk, bool dma,
-                    const SliceDma &d, uint32_t kx, uint32_t nx, uint32_t mx) {
-#pragma unroll
-        for (int q = 0; q < NMF; ++q) {
-            const int fn = q / FM, fm = q % FM;
+    // Moves base b (A bases, then B's, then At's) to the other stage.
+    constexpr int NBA = TA ? FM : KK, NBB = NFB, NBASE = NBA + NBB;
+    static_assert(NPF + NBASE <= NMF, "base moves after the step's reads");
+    auto move_base = [&](int b, int delta) __attribute__((always_inline)) {
+        if (b < NBA) {
+            if constexpr (TA)
+                ft_base[b] += (uint32_t)delta;
+            else
+                fa_base[b] += (uint32_t)delta;
+        } else {
+            fb_base[b - NBA] += (uint32_t)delta;
+        }
+    };
+    // One MFMA step on buffer `cur`: with READS, reads the next step's fragments
+    // (step pf_kk of the slice in the bases' stage); with MOVE, then moves every base to the
+    // other stage (by `delta`); with DMA, issues the LD loads of slice d into the
+    // stage at `lds_stage`, one per EVERY MFMAs.
+    auto step = [&](int cur, auto reads_c, int pf_kk, auto move_c, int delta, auto dma_c,
+                    uint32_t lds_stage, const SliceDma &d) __attribute__((always_inline)) {
+        constexpr bool READS = decltype(reads_c)::value;
+        constexpr bool MOVE = decltype(move_c)::value, DMA = decltype(dma_c)::value;
+        static_for<NMF>([&](auto q_c) __attribute__((always_inline)) {
+            constexpr int q = decltype(q_c)::value;
+            constexpr int fn = q / FM, fm = q % FM;
             u32x4 bop;
             if constexpr (TB)
                 bop = fw[cur][fn];
@@ -275,31 +359,46 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             else
                 aop = fa[cur][fm];
             acc[fn][fm] = mfma16x16x32<DT>(bop, aop, acc[fn][fm]);
-            if (reads && q < NPF) read_one(cur ^ 1, pf_base, pf_kk, q);
-            if (dma && q % EVERY == 0) dma_one(d, q / EVERY, kx, nx, mx);
+            if constexpr (READS && q < NPF) read_one(cur ^ 1, pf_kk, q);
+            if constexpr (MOVE && q >= NPF && q < NPF + NBASE) move_base(q - NPF, delta);
+            if constexpr (DMA && q % EVERY == 0)
+                dma_one(lds_stage, d, std::integral_constant<int, q / EVERY>{});
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     };
 
     Tile cur_t;
     if (!tile_of(0, cur_t)) return;   // more workgroups than tiles: nothing to do
 
+    // av is always masked for the slice the last load went to (tail_k or not),
+    // so a slice re-masks it only when the slice it loads differs in that.
+    // Offsets for a tile whose slice k was loaded last.
+    auto set_offsets = [&](const Tile &t, int k) __attribute__((always_inline)) {
+        set_av(k == tail_k);
+        if constexpr (!TB) set_bv(t.n0);
+        if constexpr (TA) set_tv(t.m0);
+    };
+
     // Prologue: slices 0 and 1 of the first tile; slice 0 waited for and
     // published, and its first fragments read.
     {
-        const SliceDma d0 = slice_dma(cur_t, true, 0, 0), d1 = slice_dma(cur_t, true, 1, 1);
+        set_offsets(cur_t, 0);
         if (bias) bias_dma(cur_t, 0);   // lands with slice 0 (waited for below)
-#pragma unroll
-        for (int i = 0; i < LD; ++i) dma_one(d0, i, (uint32_t)K, (uint32_t)N, (uint32_t)M);
-#pragma unroll
-        for (int i = 0; i < LD; ++i) dma_one(d1, i, (uint32_t)K, (uint32_t)N, (uint32_t)M);
+        const SliceDma d0 = slice_dma(cur_t, true, 0);
+        static_for<LD>([&](auto i_c) { dma_one(ld_wave, d0, i_c); });
+        if (tail_k == 1) set_av(true);
+        const SliceDma d1 = slice_dma(cur_t, true, 1);
+        static_for<LD>([&](auto i_c) { dma_one(ld_wave + (uint32_t)A_BYTES, d1, i_c); });
     }
     wait_vmcnt<LD>();
     block_barrier();
 #pragma unroll
-    for (int q = 0; q < NPF; ++q) read_one(0, smem, 0, q);
+    for (int q = 0; q < NPF; ++q) read_one(0, 0, q);
 
-    int stage0 = 0;   // stage of the current tile's slice 0
+    // Stream state: the stage of the slice being computed (its LDS load base),
+    // and the add that moves a fragment base from that stage to the other.
+    uint32_t lds_cur = ld_wave;
+    int delta = A_BYTES;
     for (int r = 0;; ++r) {
 #pragma unroll
         for (int a = 0; a < FN; ++a)
@@ -308,29 +407,42 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         Tile nxt_t;
         const bool nxt_live = tile_of(r + 1, nxt_t);
         if (!nxt_live) nxt_t = cur_t;
+        // Offsets for this tile's loads from slice 2 on, as after loading slice 1
+        // (recomputed here so that they are dead across the previous epilogue).
+        if (r > 0) set_offsets(cur_t, 1);
 
-        // Slice kt: step 0 reads its kk=1 fragments; the barrier publishes stream
-        // position kt+1 (the next tile's slice 0 after the last slice) and frees
-        // kt's stage; step 1 loads position kt+2 into it and reads position
-        // kt+1's kk=0 fragments.
-        for (int kt = 0; kt < nk; ++kt) {
-            const int sc = (stage0 + kt) & 1;
-            const char *cur_base = smem + sc * STAGE_BYTES;
-            const char *nxt_base = smem + (sc ^ 1) * STAGE_BYTES;
-            uint32_t kx = (uint32_t)K, nx = (uint32_t)N, mx = (uint32_t)M;
-            asm volatile("" : "+s"(kx), "+s"(nx), "+s"(mx));
-            step(0, true, cur_base, 1, false, SliceDma{}, kx, nx, mx);
+        // Slice kt: step 0 reads its kk=1 fragments, then moves the bases to the
+        // other stage; the barrier publishes stream position kt+1 (the next tile's
+        // slice 0 after the last slice) and frees this slice's stage; step 1 loads
+        // position kt+2 into it and reads position kt+1's kk=0 fragments, except
+        // in a tile's last slice: the next tile's first fragments are read after
+        // the epilogue, which then has their registers.
+        auto slice = [&](int kt, auto reads_c) __attribute__((always_inline)) {
+            step(0, std::true_type{}, 1, std::true_type{}, delta, std::false_type{}, 0u, SliceDma{});
             wait_vmcnt_lgkm0<0>();
             block_barrier();
             const bool here = kt + 2 < nk;
-            const SliceDma dn = slice_dma(here ? cur_t : nxt_t, here || nxt_live,
-                                          here ? kt + 2 : kt + 2 - nk, sc);
+            const int k2 = here ? kt + 2 : kt + 2 - nk;
+            // Load offsets for position kt+2: its tile's edges, and whether it is
+            // the partial last slice (uniform branches, a few times per tile).
+            if (!here && k2 == 0 && nxt_live) {
+                if constexpr (!TB) set_bv(nxt_t.n0);
+                if constexpr (TA) set_tv(nxt_t.m0);
+            }
+            const int k1 = kt + 1 < nk ? kt + 1 : kt + 1 - nk;   // the slice loaded last
+            if ((k2 == tail_k) != (k1 == tail_k)) set_av(k2 == tail_k);
+            const SliceDma dn = slice_dma(here ? cur_t : nxt_t, here || nxt_live, k2);
             // With the next tile's slice 0: its bias, into the other parity's slot
             // (this tile's epilogue still reads its own). Landed by the next
             // slice's vmcnt(0) wait, long before that tile's epilogue.
-            if (bias && !here && kt + 2 == nk && nxt_live) bias_dma(nxt_t, (r + 1) & 1);
-            step(1, true, nxt_base, 0, true, dn, kx, nx, mx);
-        }
+            if (bias && !here && k2 == 0 && nxt_live) bias_dma(nxt_t, (r + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            step(1, reads_c, 0, std::false_type{}, 0, std::true_type{}, lds_cur, dn);
+            lds_cur += (uint32_t)delta;   // the next slice's stage
+            delta = -delta;
+        };
+        for (int kt = 0; kt + 1 < nk; ++kt) slice(kt, std::true_type{});
+        slice(nk - 1, std::false_type{});
 
         // Epilogue of this tile while the next tile's first slices land. The
         // scheduling fences keep the next tile's fragment reads and the epilogue
@@ -368,7 +480,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             // bits: 127 rows of at most 2^24 bytes); opaque to the optimiser, so
             // the per-store offsets are not hoisted and held across the K loop.
             uint32_t st_off = (uint32_t)rr * (uint32_t)N * 2u + (uint32_t)rc * 16u;
-            uint32_t pitch8 = (uint32_t)N * 16u;   // bytes between read rows rr and rr + 8
+            uint32_t pitch8 = __builtin_amdgcn_readfirstlane((uint32_t)N * 16u);   // bytes between read rows rr and rr + 8
             asm volatile("" : "+v"(st_off), "+s"(pitch8));
             // Rows and columns left in this wave's block (edge tiles; no m0 + BM:
             // it overflows near 2^31).
@@ -439,9 +551,12 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
-        stage0 = (stage0 + nk) & 1;
         if (!nxt_live) break;
         cur_t = nxt_t;
+        // The next tile's slice 0 was published by the last barrier; its first
+        // fragments (the bases already name its stage).
+#pragma unroll
+        for (int q = 0; q < NPF; ++q) read_one(0, 0, q);
     }
     // No direct-to-LDS write may outlive the workgroup's LDS.
     wait_vmcnt<0>();
@@ -449,7 +564,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 
 // Grid: one workgroup per CU (two 64 KiB stages fill the LDS), or fewer when
 // there are fewer tiles. K must exceed 64 (at least two K slices per tile): the
-// library sends K <= 64 to gemm_v3 with the same tile.
+// library sends K <= 64 to kernel 3.
 template <int BM, int BN, int WM, int WN, int DT, int ACT, bool TB = false, bool TA = false>
 hipError_t launch_gemm_v5(const void *A, const void *B, const void *bias, void *C, int M, int N,
                           int K, int raster, int group_m, hipStream_t stream) {
