@@ -68,8 +68,10 @@ typedef enum {
     GBA_ERR_HIP = 8,      /* a HIP runtime call failed; see gba_last_hip_error() */
     GBA_ERR_SCHEDULE = 9, /* schedule not among the compiled-in ones */
     GBA_ERR_CACHE = 10,   /* schedule cache could not be written (tuning still done) */
-    GBA_TUNE_INCOMPLETE = 11 /* gba_autotune stopped at its candidate budget (GBA_TUNE_BUDGET);
-                                its progress is kept, a later call resumes */
+    GBA_TUNE_INCOMPLETE = 11, /* gba_autotune stopped at its candidate budget (GBA_TUNE_BUDGET);
+                                 its progress is kept, a later call resumes */
+    GBA_ERR_SCRATCH = 12  /* gemm_bias_act_noalloc: the split-K partials would exceed its
+                             static scratch (gba_noalloc_scratch_bytes) */
 } gba_status;
 
 /* A GEMM schedule: one compiled-in kernel instance plus its launch mapping.
@@ -176,6 +178,25 @@ enum {
 int gemm_bias_act_ex(const void *A, const void *B, const void *bias, void *C, int64_t M,
                      int64_t N, int64_t K, int act, int dtype, int flags, void *workspace,
                      size_t workspace_bytes);
+
+/* gemm_bias_act_ex for callers that cannot allocate device memory: code
+ * recorded under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. It takes no workspace; when the call splits K (the same
+ * choice as gemm_bias_act_ex with a large enough workspace, and the same
+ * result, bitwise), the fp32 partials go to a static device array of the
+ * library, gba_noalloc_scratch_bytes() = 16 MiB, one per GPU, held until the
+ * process ends. It calls no allocating routine: the array's address is taken
+ * (hipGetSymbolAddress) on the first call on each device. Splits whose
+ * partials (S * M * N * 4 bytes) would exceed the array return GBA_ERR_SCRATCH
+ * before any launch; with 128 x 128 tiles and at most CUs / tiles splits that
+ * bound is never reached on a 256-CU device. The array needs no clearing: the
+ * first pass writes every partial it reads back. All calls on one GPU share
+ * the array, so calls that overlap on that GPU (different streams, or
+ * different host threads without ordering) race; order them on one stream.
+ * Arguments, flags and errors otherwise as gemm_bias_act_ex. */
+int gemm_bias_act_noalloc(const void *A, const void *B, const void *bias, void *C, int64_t M,
+                          int64_t N, int64_t K, int act, int dtype, int flags);
+size_t gba_noalloc_scratch_bytes(void);
 
 /* Workspace bytes gemm_bias_act_ex (with GBA_INPUT_FP8: gemm_bias_act_fp8_ex)
  * would use for these arguments (0 if it would not split), written to *bytes. */

@@ -1,0 +1,84 @@
+"""gemm_bias_act_noalloc: the split-K path with the library's static scratch in
+place of a caller's workspace, for callers that cannot allocate. Called through
+the C ABI; its output must equal gemm_bias_act_ex's with a workspace bitwise
+(same kernels, same split), on two calls in a row, the second smaller, and
+agree with the oracle."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import tiled_dense_gemm_bias_amd as gba
+from oracle import compare
+from tests.gpu_util import empty, say, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+ACT = {"none": 0, "relu": 1, "sigmoid": 2, "gelu": 3, "softplus": 4, "gelu_tanh": 5}
+
+
+def _run_pair(M, N, K, dtype, act, tb, seed):
+    import torch
+    A = synth.random_bits((M, K), dtype, seed)
+    B = synth.random_bits((N, K) if tb else (K, N), dtype, seed + 1, scale=1 / 64)
+    bias = synth.random_bits((N,), dtype, seed + 2)
+    a, b, bb = to_dev(A, dtype), to_dev(B, dtype), to_dev(bias, dtype)
+    dt = 0 if dtype == "f16" else 1
+    flags = 1 if tb else 0
+    nb = gba.workspace_size(M, N, K, act, dtype, transpose_b=tb)
+    assert 0 < nb <= gba.lib().gba_noalloc_scratch_bytes(), nb   # the case splits K
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ref = empty((M, N), dtype, fill_bits=0x7E00)
+    got = empty((M, N), dtype, fill_bits=0x7C01)
+    lib = gba.lib()
+    lib.gba_set_stream(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    say("noalloc", M, N, K, dtype, act, "NK" if tb else "KN")
+    st = lib.gemm_bias_act_ex(a.data_ptr(), b.data_ptr(), bb.data_ptr(), ref.data_ptr(), M, N, K,
+                              ACT[act], dt, flags, ws.data_ptr(), nb)
+    assert st == 0, st
+    st = lib.gemm_bias_act_noalloc(a.data_ptr(), b.data_ptr(), bb.data_ptr(), got.data_ptr(), M, N,
+                                   K, ACT[act], dt, flags)
+    assert st == 0, gba.lib().gba_status_string(st)
+    torch.cuda.synchronize()
+    g, r = to_bits(got), to_bits(ref)
+    assert np.array_equal(g, r)
+    R, S = oracle.gemm_bias_act(A, B, bias, act, dtype, with_abs=True, transpose_b=tb)
+    rep = compare.check(oracle.decode(g, dtype), R, K=K, dtype=dtype, act=oracle.ACTS[act], S=S)
+    assert rep["ok"] and rep["strict_ok"], rep
+    return g
+
+
+def test_noalloc_equals_workspace_path_twice_second_smaller():
+    first = _run_pair(256, 384, 16384, "f16", "softplus", False, 11)
+    second = _run_pair(128, 256, 4096, "bf16", "gelu", True, 21)
+    assert first.shape != second.shape
+
+
+def test_noalloc_without_split_and_errors():
+    import torch
+    M, N, K = 512, 512, 256   # 256 tiles of 256^2 would not split; 16 of 128^2: no split at K=256
+    A = synth.random_bits((M, K), "f16", 31)
+    B = synth.random_bits((K, N), "f16", 32)
+    a, b = to_dev(A, "f16"), to_dev(B, "f16")
+    c = empty((M, N), "f16")
+    ref = empty((M, N), "f16")
+    say("noalloc no split")
+    gba.gemm_bias_act_noalloc(a, b, None, c, "relu")
+    gba.gemm_bias_act(a, b, None, ref, "relu")
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(c), to_bits(ref))
+    lib = gba.lib()
+    assert lib.gemm_bias_act_noalloc(a.data_ptr(), b.data_ptr(), None, c.data_ptr(), M, N, K, 1, 0,
+                                     64) == 2   # unknown flag bit
+    assert lib.gemm_bias_act_noalloc(a.data_ptr(), b.data_ptr(), None, c.data_ptr(), M, N, 12, 1, 0,
+                                     0) == 5   # K % 8

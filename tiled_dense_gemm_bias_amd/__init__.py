@@ -24,7 +24,7 @@ ACTS = {"none": 0, "relu": 1, "sigmoid": 2, "gelu": 3, "softplus": 4, "gelu_tanh
 STATUS = {
     0: "GBA_OK", 1: "GBA_ERR_NULL", 2: "GBA_ERR_SHAPE", 3: "GBA_ERR_DTYPE", 4: "GBA_ERR_ACT",
     5: "GBA_ERR_ALIGN", 6: "GBA_ERR_ALIAS", 7: "GBA_ERR_DEVICE", 8: "GBA_ERR_HIP",
-    9: "GBA_ERR_SCHEDULE", 10: "GBA_ERR_CACHE", 11: "GBA_TUNE_INCOMPLETE",
+    9: "GBA_ERR_SCHEDULE", 10: "GBA_ERR_CACHE", 11: "GBA_TUNE_INCOMPLETE", 12: "GBA_ERR_SCRATCH",
 }
 SCHED_FIELDS = ("bm", "bn", "bk", "wm", "wn", "stages", "raster", "group_m", "kernel", "loaders",
                 "spread")
@@ -82,6 +82,8 @@ def _lib():
             "gba_list_schedule": [ci, ctypes.POINTER(Schedule)],
             "gba_autotune": [p, p, p, p, i64, i64, i64, ci, ci, ci, ctypes.POINTER(Schedule),
                              ctypes.POINTER(ctypes.c_double)],
+            "gemm_bias_act_noalloc": [p, p, p, p, i64, i64, i64, ci, ci, ci],
+            "gba_noalloc_scratch_bytes": [],
             "gba_autotune_num_trials": [],
             "gba_autotune_trial": [ci, ctypes.POINTER(Schedule), ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ci)],
@@ -102,6 +104,7 @@ def _lib():
         lib.gba_status_string.restype = ctypes.c_char_p
         lib.gba_version.restype = ctypes.c_char_p
         lib.gba_build_id.restype = ctypes.c_char_p
+        lib.gba_noalloc_scratch_bytes.restype = ctypes.c_size_t
         _LIB = lib
     return _LIB
 
@@ -234,6 +237,16 @@ def gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False, workspace=None,
 
 
 INPUT_FP8 = 2
+
+
+def gemm_bias_act_noalloc(a, b, bias, c, act="gelu", transpose_b=False, transpose_a=False):
+    """gemm_bias_act with a split-K workspace from the library's static scratch
+    (no allocation; for graph capture and serving loops). Returns c."""
+    dev = _check_dev(a, b, bias, c)
+    dt, M, N, K = _gemm_shapes(a, b, bias, c, transpose_b, transpose_a)
+    _call("gemm_bias_act_noalloc", dev, _ptr(a), _ptr(b), _ptr(bias), _ptr(c), M, N, K, _act(act),
+          dt, _layout_flags(transpose_a, transpose_b))
+    return c
 
 
 def workspace_size(M: int, N: int, K: int, act="gelu", dtype="f16", transpose_b=False,

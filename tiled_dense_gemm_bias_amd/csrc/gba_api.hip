@@ -718,6 +718,42 @@ int fp8_common(const void *A, const void *W, const void *bias, void *C, int64_t 
     return e == hipSuccess ? GBA_OK : hip_fail(e);
 }
 
+// ------------------------------------------------- static scratch ----
+//
+// Device memory for callers that cannot allocate (gemm_bias_act_noalloc): the
+// split-K partial sums live in this file-scope array instead of a caller's
+// workspace. Every GPU the library runs on holds its own copy until the process
+// ends. Host code never uses the array's name as an address: the device address
+// is taken once per device with hipGetSymbolAddress (with that device current)
+// and kept in g_scratch[].
+//
+// Size: the split needs S * M * N * 4 bytes with S <= CUs / tiles of 128 x 128,
+// so at most CUs * 128 * 128 * 4 bytes = 16 MiB on a 256-CU MI355X.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch[64];   // device address of `scratch` per device (null: not taken yet)
+
+int scratch_of_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        t_last_hip = (int)e;
+        return GBA_ERR_DEVICE;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return GBA_OK;
+}
+
 }  // namespace
 
 // =================================================================== C ABI ===
@@ -740,6 +776,7 @@ const char *gba_status_string(int s) {
     case GBA_ERR_SCHEDULE: return "unknown schedule";
     case GBA_ERR_CACHE: return "schedule cache not writable";
     case GBA_TUNE_INCOMPLETE: return "tuning stopped at its candidate budget; call again to resume";
+    case GBA_ERR_SCRATCH: return "split-K partials larger than the static scratch of gemm_bias_act_noalloc";
     default: return "unknown status";
     }
 }
@@ -825,6 +862,29 @@ int gemm_bias_act_ex(const void *A, const void *B, const void *bias, void *C, in
                        flags & (GBA_TRANSPOSE_B | GBA_TRANSPOSE_A), workspace,
                        workspace ? workspace_bytes : 0);
 }
+
+int gemm_bias_act_noalloc(const void *A, const void *B, const void *bias, void *C, int64_t M,
+                          int64_t N, int64_t K, int act, int dtype, int flags) {
+    if (flags & ~(GBA_TRANSPOSE_B | GBA_TRANSPOSE_A)) return GBA_ERR_SHAPE;
+    const int lay = flags & (GBA_TRANSPOSE_B | GBA_TRANSPOSE_A);
+    bool nothing = false;
+    int s = check_gemm_args(A, B, bias, C, M, N, K, act, dtype, &nothing, lay);
+    if (s || nothing) return s;
+    const DeviceInfo *d;
+    s = current_device(&d);
+    if (s) return s;
+    void *ws = nullptr;
+    s = scratch_of_current_device(&ws);
+    if (s) return s;
+    // The split this call would make, and whether its partials fit the scratch.
+    const char *why;
+    const gba_schedule sch = choose(*d, M, N, K, act, dtype, lay, &why);
+    const int S = split_count(sch, M, N, K, d->cus, dtype, lay);
+    if (S > 1 && (size_t)S * (size_t)M * (size_t)N * 4u > kScratchBytes) return GBA_ERR_SCRATCH;
+    return gemm_common(A, B, bias, C, M, N, K, act, dtype, lay, ws, kScratchBytes);
+}
+
+size_t gba_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int gba_workspace_size(int64_t M, int64_t N, int64_t K, int act, int dtype, int flags,
                        size_t *bytes) {
