@@ -109,77 +109,34 @@ def gpu_stack(dev_index: int) -> dict:
     return out
 
 
-class SclkSampler:
-    """Polls the GPU's graphics clock (amdsmi gpu_metrics: the mean of the
-    per-XCD current_gfxclks, and the firmware's average_gfxclk_frequency) from a
-    background thread, so that the clock during the timed region can be
-    reported beside the spec denominator. Best effort: None if amdsmi fails."""
+class ClockProbe:
+    """The core clock the power manager has set at a point of the stream, read
+    on the device by the library's clock probe (one wave per workgroup, 4
+    workgroups per CU, each dividing elapsed s_memtime core cycles by elapsed
+    constant-rate wall-clock ticks over spin_us), enqueued on the launch stream
+    right behind the launches it describes. The probe itself is a light load:
+    under the GEMM's full matrix-core load the chip's current limiting runs the
+    clock lower than the set point this reads."""
 
-    def __init__(self, dev_index: int):
-        import threading
-        self.samples = []   # (perf_counter, current MHz, average MHz)
-        self.error = None
-        self._stop = threading.Event()
-        self._thread = None
-        try:
-            import amdsmi
-            self._amdsmi = amdsmi
-            self._h = _smi_handle(dev_index)
-            if self._h is None:
-                self.error = "no amdsmi handle for the device"
-        except Exception as e:   # noqa: BLE001
-            self.error = repr(e)
-        if self.error is None:
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
+    def __init__(self, dev, n_wg=1024, spin_us=10):
+        import torch
+        self.n_wg, self.spin_us = n_wg, spin_us
+        self.buf = [torch.zeros(2 * n_wg, dtype=torch.int64, device=dev) for _ in range(2)]
+        self.khz = None
 
-    def _read(self):
-        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
-        cur = m.get("current_gfxclks")
-        if isinstance(cur, list):
-            cur = [c for c in cur if isinstance(c, (int, float)) and 0 < c < 10000]
-            cur = sum(cur) / len(cur) if cur else None
-        else:
-            cur = m.get("current_gfxclk")
-            cur = cur if isinstance(cur, (int, float)) else None
-        avg = m.get("average_gfxclk_frequency")
-        return cur, (avg if isinstance(avg, (int, float)) else None)
+    def enqueue(self, slot: int):
+        import tiled_dense_gemm_bias_amd as gba
+        self.khz = gba.clock_probe(self.buf[slot], self.n_wg, self.spin_us)
 
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                cur, avg = self._read()
-            except Exception as e:   # noqa: BLE001
-                self.error = repr(e)
-                return
-            self.samples.append((time.perf_counter(), cur, avg))
-            self._stop.wait(0.0005)
-
-    def stop(self):
-        self._stop.set()
-        if self._thread is not None:
-            self._thread.join(timeout=2.0)
-
-    def summary(self, t0: float, t1: float) -> dict:
-        """Samples taken inside [t0, t1]; if none, the last one before t0 and the
-        first one after t1."""
-        if self.error is not None and not self.samples:
-            return {"source": "amdsmi gpu_metrics", "error": self.error}
-        inside = [s for s in self.samples if t0 <= s[0] <= t1]
-        basis = "inside the timed region"
-        if not inside:
-            before = [s for s in self.samples if s[0] < t0][-1:]
-            after = [s for s in self.samples if s[0] > t1][:1]
-            inside = before + after
-            basis = "nearest samples before and after the timed region"
-        cur = [s[1] for s in inside if s[1] is not None]
-        avg = [s[2] for s in inside if s[2] is not None]
-        return {"source": "amdsmi gpu_metrics (current_gfxclks mean; average_gfxclk_frequency)",
-                "basis": basis, "samples": len(inside),
-                "current_mhz_mean": round(sum(cur) / len(cur), 1) if cur else None,
-                "current_mhz_min": min(cur) if cur else None,
-                "current_mhz_max": max(cur) if cur else None,
-                "average_mhz_mean": round(sum(avg) / len(avg), 1) if avg else None}
+    def read(self, slot: int) -> dict:
+        """Per-workgroup MHz after the stream has finished: median, min, max."""
+        v = self.buf[slot].cpu().numpy().reshape(-1, 2).astype(np.float64)
+        ok = v[:, 1] > 0
+        if not ok.any() or not self.khz:
+            return {"median": None}
+        mhz = v[ok, 0] / v[ok, 1] * self.khz / 1000.0
+        return {"median": round(float(np.median(mhz)), 1), "min": round(float(mhz.min()), 1),
+                "max": round(float(mhz.max()), 1)}
 
 
 # Sources each kernel family is compiled from (the schedule table and host code
@@ -226,11 +183,10 @@ def measured_traffic(workload: str, sched: dict):
     return rec.get("bytes_per_launch")
 
 
-def time_launches(fn, steps, warmup, stream, window=None):
+def time_launches(fn, steps, warmup, stream, clock=None):
     """W untimed calls, then K timed ones between two device synchronisations.
 
-    Returns (wall_ms, avg_ms, per); window, if given, receives the host-clock
-    bounds of the timed region as window["t0"], window["t1"]:
+    Returns (wall_ms, avg_ms, per):
       wall_ms  host clock over the K timed calls (sync before and after);
       avg_ms   average launch duration: two HIP events on the launch stream
                bracket the K launches, divided by K (each launch's kernel plus
@@ -239,10 +195,15 @@ def time_launches(fn, steps, warmup, stream, window=None):
                with an event before each (for the median). An event record
                between launches costs ~3 us on this device, so those intervals
                run a little longer; they are not part of the timed region.
+    clock, a ClockProbe, if given, is enqueued right behind the warmup calls
+    (slot 0: the clock the timed region starts at) and right behind the second
+    pass (slot 1: the clock at its end); neither probe is inside a timed interval.
     """
     import torch
     for _ in range(warmup):
         fn()
+    if clock is not None:
+        clock.enqueue(0)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -253,14 +214,14 @@ def time_launches(fn, steps, warmup, stream, window=None):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1e3
-    if window is not None:
-        window["t0"], window["t1"] = t0, t1
     avg_ms = e0.elapsed_time(e1) / steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     for i in range(steps):
         ev[i].record(stream)
         fn()
     ev[steps].record(stream)
+    if clock is not None:
+        clock.enqueue(1)
     torch.cuda.synchronize()
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     return wall_ms, avg_ms, per
@@ -440,13 +401,16 @@ def main(argv=None) -> int:
                                       transpose_a=ta)
     log("[bench] schedule %s%s%s" % (sched, " (A stored [K,M])" if ta else "",
                                      " (B stored [N,K])" if tb else ""))
-    sampler = SclkSampler(dev.index)
-    window = {}
-    try:
-        wall_ms, kern_avg, per = time_launches(step, a.steps, a.warmup, stream, window)
-    finally:
-        sampler.stop()
-    sclk = sampler.summary(window.get("t0", 0.0), window.get("t1", 0.0))
+    clock = ClockProbe(dev)
+    wall_ms, kern_avg, per = time_launches(step, a.steps, a.warmup, stream, clock)
+    sclk = {"at_start": clock.read(0), "at_end": clock.read(1),
+            "source": "device clock probe (s_memtime / s_memrealtime per workgroup, %d "
+                      "workgroups over %d us) enqueued behind the warmups and behind the "
+                      "per-launch-event pass" % (clock.n_wg, clock.spin_us),
+            "meaning": "the clock the power manager has set at those two moments, read under "
+                       "the probe's light load; under the GEMM's full matrix-core load the "
+                       "chip runs below it (GRBM_GUI_ACTIVE cycles per dispatch in the "
+                       "committed counter profile)"}
     ms_per_step = wall_ms / a.steps
     kern_med = statistics.median(per)
     flops = float(w.flops)
@@ -460,7 +424,7 @@ def main(argv=None) -> int:
         "event-bracketed kernel avg %.4f ms -> %.1f TFLOP/s (%.1f%% of peak, roofline); "
         "per-launch-event median %.4f ms -> %.1f TFLOP/s; sclk %s"
         % (a.steps, a.warmup, ms_per_step, value, kern_avg, achieved, 100 * achieved / peak,
-           kern_med, tflops_med, sclk.get("current_mhz_mean")))
+           kern_med, tflops_med, sclk["at_end"]["median"]))
     got_bits = c_t.view(torch.int16).cpu().numpy().view(np.uint16)
 
     out = {

@@ -330,6 +330,18 @@ int gba_cache_store(const char *arch, int cus, int64_t M, int64_t N, int64_t K, 
  * device function the GEMM epilogue uses. z, y: device float arrays of n. */
 int gba_epilogue_probe(const float *z, float *y, int64_t n, int act);
 
+/* Shader-clock probe, for reporting the clock a measurement ran at: n_wg
+ * workgroups of one wave each spin for spin_us microseconds of the device's
+ * constant-rate wall clock; workgroup i writes out[2i] = elapsed core clock
+ * cycles (s_memtime) and out[2i+1] = elapsed wall-clock ticks (s_memrealtime).
+ * The core clock in MHz is out[2i] / out[2i+1] * (*wall_khz) / 1000. Enqueued on
+ * the library's stream (gba_set_stream) right after the work to be described, it
+ * reads the clock that work ended at. out: device array of 2 * n_wg uint64,
+ * owned by the caller; *wall_khz (host): the wall clock's rate. Errors: NULL
+ * pointers: GBA_ERR_NULL; n_wg outside 1..65536 or spin_us outside 1..100000:
+ * GBA_ERR_SHAPE. */
+int gba_clock_probe(uint64_t *out, int n_wg, int spin_us, int *wall_khz);
+
 const char *gba_status_string(int status);
 int gba_last_hip_error(void);
 const char *gba_version(void);

@@ -102,7 +102,8 @@ def kernels(tmp_path_factory):
 
 def _kind(name):
     for k in ("gemm_v5_kernel", "gemm_v3_kernel", "gemm_f8_kernel", "gemm_bias_act_kernel",
-              "bias_act_kernel", "splitk_reduce_kernel", "epilogue_probe_kernel"):
+              "bias_act_kernel", "splitk_reduce_kernel", "epilogue_probe_kernel",
+              "clock_probe_kernel"):
         if k in name:
             return k
     return None

@@ -93,6 +93,7 @@ def _lib():
             "gba_cache_store": [ctypes.c_char_p, ci, i64, i64, i64, ci, ci, ci,
                                 ctypes.POINTER(Schedule), ctypes.c_double],
             "gba_epilogue_probe": [p, p, i64, ci],
+            "gba_clock_probe": [p, ci, ci, p],
             "gba_status_string": [ci],
             "gba_last_hip_error": [],
             "gba_version": [],
@@ -413,6 +414,20 @@ def epilogue_probe(z, y, act="gelu"):
         raise ValueError("epilogue_probe takes two float32 tensors of one size")
     _call("gba_epilogue_probe", dev, _ptr(z), _ptr(y), z.numel(), _act(act))
     return y
+
+
+def clock_probe(out, n_wg: int = 1024, spin_us: int = 20) -> int:
+    """Enqueue the shader-clock probe on the current stream: out (a device
+    int64 tensor of 2 * n_wg) receives per workgroup (core clock cycles,
+    wall-clock ticks); returns the wall clock's rate in kHz. Core MHz =
+    cycles / ticks * kHz / 1000, once the stream has finished."""
+    torch = _torch()
+    dev = _check_dev(out)
+    if out.dtype != torch.int64 or out.numel() != 2 * n_wg or not out.is_contiguous():
+        raise ValueError("clock_probe takes a contiguous int64 tensor of 2 * n_wg")
+    khz = ctypes.c_int(0)
+    _call("gba_clock_probe", dev, _ptr(out), n_wg, spin_us, ctypes.byref(khz))
+    return khz.value
 
 
 def set_schedule(sched: Optional[dict]) -> None:

@@ -964,6 +964,44 @@ int gba_epilogue_probe(const float *z, float *y, int64_t n, int act) {
     return e == hipSuccess ? GBA_OK : hip_fail(e);
 }
 
+namespace {
+// Shader clock of the CU a workgroup runs on: s_memtime counts core clock
+// cycles, s_memrealtime a constant-rate wall clock. One wave spins until
+// `ticks` wall-clock ticks have passed (or a fixed iteration cap, so every wave
+// ends) and writes both elapsed counts for the host to divide.
+__global__ void __launch_bounds__(64) clock_probe_kernel(unsigned long long *out, unsigned long long ticks) {
+    const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+    const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+    unsigned long long r1 = r0;
+    for (int it = 0; it < (1 << 20) && r1 - r0 < ticks; ++it) r1 = __builtin_amdgcn_s_memrealtime();
+    const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+    r1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+        out[2 * blockIdx.x] = c1 - c0;
+        out[2 * blockIdx.x + 1] = r1 - r0;
+    }
+}
+}  // namespace
+
+int gba_clock_probe(uint64_t *out, int n_wg, int spin_us, int *wall_khz) {
+    if (!out || !wall_khz) return GBA_ERR_NULL;
+    if (n_wg < 1 || n_wg > 65536 || spin_us < 1 || spin_us > 100000) return GBA_ERR_SHAPE;
+    const DeviceInfo *d;
+    int s = current_device(&d);
+    if (s) return s;
+    int dev = 0, khz = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (khz <= 0) return GBA_ERR_DEVICE;
+    *wall_khz = khz;
+    const unsigned long long ticks = (unsigned long long)khz * (unsigned long long)spin_us / 1000ull;
+    hipLaunchKernelGGL(clock_probe_kernel, dim3((unsigned)n_wg), dim3(64), 0, t_stream,
+                       reinterpret_cast<unsigned long long *>(out), ticks);
+    e = hipGetLastError();
+    return e == hipSuccess ? GBA_OK : hip_fail(e);
+}
+
 int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_t M, int64_t N,
                  int64_t K, int act, int dtype, int flags, gba_schedule *best_out,
                  double *best_ms_out) {
