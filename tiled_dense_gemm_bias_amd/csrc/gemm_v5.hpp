@@ -325,22 +325,30 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // Moves base b (A bases, then B's, then At's) to the other stage.
     constexpr int NBA = TA ? FM : KK, NBB = NFB, NBASE = NBA + NBB;
     static_assert(NPF + NBASE <= NMF, "base moves after the step's reads");
+    // (An asm statement: a plain add is sunk by the compiler to the first use,
+    // past the barrier, where it delays the next step's first MFMA.)
+    auto add_to = [](uint32_t &x, int delta) __attribute__((always_inline)) {
+        asm volatile("v_add_u32 %0, %1, %0" : "+v"(x) : "s"(delta));
+    };
     auto move_base = [&](int b, int delta) __attribute__((always_inline)) {
         if (b < NBA) {
             if constexpr (TA)
-                ft_base[b] += (uint32_t)delta;
+                add_to(ft_base[b], delta);
             else
-                fa_base[b] += (uint32_t)delta;
+                add_to(fa_base[b], delta);
         } else {
-            fb_base[b - NBA] += (uint32_t)delta;
+            add_to(fb_base[b - NBA], delta);
         }
     };
     // One MFMA step on buffer `cur`: with READS, reads the next step's fragments
     // (step pf_kk of the slice in the bases' stage); with MOVE, then moves every base to the
     // other stage (by `delta`); with DMA, issues the LD loads of slice d into the
     // stage at `lds_stage`, one per EVERY MFMAs.
+    // PAYLOAD (if given) runs after MFMA PQ, in the stream's shadow.
+    constexpr int PQ = NPF + NBASE + 2;
+    static_assert(PQ < NMF, "payload slot inside the step");
     auto step = [&](int cur, auto reads_c, int pf_kk, auto move_c, int delta, auto dma_c,
-                    uint32_t lds_stage, const SliceDma &d) __attribute__((always_inline)) {
+                    uint32_t lds_stage, const SliceDma &d, auto &&payload) __attribute__((always_inline)) {
         constexpr bool READS = decltype(reads_c)::value;
         constexpr bool MOVE = decltype(move_c)::value, DMA = decltype(dma_c)::value;
         static_for<NMF>([&](auto q_c) __attribute__((always_inline)) {
@@ -363,9 +371,11 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             if constexpr (MOVE && q >= NPF && q < NPF + NBASE) move_base(q - NPF, delta);
             if constexpr (DMA && q % EVERY == 0)
                 dma_one(lds_stage, d, std::integral_constant<int, q / EVERY>{});
+            if constexpr (q == PQ) payload();
             __builtin_amdgcn_sched_barrier(0);
         });
     };
+    auto no_payload = []() __attribute__((always_inline)) {};
 
     Tile cur_t;
     if (!tile_of(0, cur_t)) return;   // more workgroups than tiles: nothing to do
@@ -411,33 +421,44 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         // (recomputed here so that they are dead across the previous epilogue).
         if (r > 0) set_offsets(cur_t, 1);
 
-        // Slice kt: step 0 reads its kk=1 fragments, then moves the bases to the
-        // other stage; the barrier publishes stream position kt+1 (the next tile's
-        // slice 0 after the last slice) and frees this slice's stage; step 1 loads
-        // position kt+2 into it and reads position kt+1's kk=0 fragments, except
-        // in a tile's last slice: the next tile's first fragments are read after
-        // the epilogue, which then has their registers.
+        // Slice kt: step 0 reads its kk=1 fragments, moves the bases to the other
+        // stage and, in its shadow, prepares the loads of stream position kt+2
+        // (offsets at a tile edge or K tail, descriptors); the barrier publishes
+        // position kt+1 (the next tile's slice 0 after the last slice) and frees
+        // this slice's stage; step 1 loads position kt+2 into it and reads position
+        // kt+1's kk=0 fragments, except in a tile's last slice: the next tile's
+        // first fragments are read after the epilogue, which then has their
+        // registers. Nothing but the wait and the barrier sits between the steps.
         auto slice = [&](int kt, auto reads_c) __attribute__((always_inline)) {
-            step(0, std::true_type{}, 1, std::true_type{}, delta, std::false_type{}, 0u, SliceDma{});
-            wait_vmcnt_lgkm0<0>();
-            block_barrier();
             const bool here = kt + 2 < nk;
             const int k2 = here ? kt + 2 : kt + 2 - nk;
-            // Load offsets for position kt+2: its tile's edges, and whether it is
-            // the partial last slice (uniform branches, a few times per tile).
-            if (!here && k2 == 0 && nxt_live) {
-                if constexpr (!TB) set_bv(nxt_t.n0);
-                if constexpr (TA) set_tv(nxt_t.m0);
-            }
             const int k1 = kt + 1 < nk ? kt + 1 : kt + 1 - nk;   // the slice loaded last
-            if ((k2 == tail_k) != (k1 == tail_k)) set_av(k2 == tail_k);
-            const SliceDma dn = slice_dma(here ? cur_t : nxt_t, here || nxt_live, k2);
+            SliceDma dn;
+            bool bias_next = false;
+            auto prep = [&]() __attribute__((always_inline)) {
+                // The position's tile edges, and whether it is the partial last
+                // slice (uniform branches, taken a few times per tile). The loads
+                // that used the old offsets were issued a step earlier.
+                if (!here && k2 == 0 && nxt_live) {
+                    if constexpr (!TB) set_bv(nxt_t.n0);
+                    if constexpr (TA) set_tv(nxt_t.m0);
+                }
+                if ((k2 == tail_k) != (k1 == tail_k)) set_av(k2 == tail_k);
+                dn = slice_dma(here ? cur_t : nxt_t, here || nxt_live, k2);
+                bias_next = bias && !here && k2 == 0 && nxt_live;
+                // Formed here, in the MFMA shadow, not at their first use after the
+                // barrier.
+                asm volatile("" : "+s"(dn.ra), "+s"(dn.rb));
+            };
+            step(0, std::true_type{}, 1, std::true_type{}, delta, std::false_type{}, 0u, SliceDma{}, prep);
+            wait_vmcnt_lgkm0<0>();
+            block_barrier();
             // With the next tile's slice 0: its bias, into the other parity's slot
             // (this tile's epilogue still reads its own). Landed by the next
             // slice's vmcnt(0) wait, long before that tile's epilogue.
-            if (bias && !here && k2 == 0 && nxt_live) bias_dma(nxt_t, (r + 1) & 1);
+            if (__builtin_expect(bias_next, 0)) bias_dma(nxt_t, (r + 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
-            step(1, reads_c, 0, std::false_type{}, 0, std::true_type{}, lds_cur, dn);
+            step(1, reads_c, 0, std::false_type{}, 0, std::true_type{}, lds_cur, dn, no_payload);
             lds_cur += (uint32_t)delta;   // the next slice's stage
             delta = -delta;
         };
