@@ -198,22 +198,54 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     struct SliceDma {
         __amdgpu_buffer_rsrc_t ra, rb;
     };
-    auto slice_dma = [&](const Tile &t, bool live, int kt) {
-        SliceDma d;
+    // A position's slice corners and byte ranges, from which its descriptors are
+    // made. From one slice to the next of a tile (other than into the partial
+    // last slice) they change by constants: the A-like corner moves 64 elements
+    // along K (its range shrinks by 128 bytes), the B-like corner 64 rows (its
+    // range is one slice); so only the first slice of a tile, the last one and
+    // dead positions are formed from scratch.
+    struct DmaPos {
+        const uint16_t *pa, *pb;
+        uint32_t na, nb;
+    };
+    auto pos_full = [&](const Tile &t, bool live, int kt) __attribute__((always_inline)) {
         const int k0 = kt * BK;
-        if constexpr (TA)
-            d.ra = make_rsrc(A + (live ? (size_t)k0 * M + t.m0 : 0),
-                             live ? (uint32_t)min(K - k0, BK) * (uint32_t)M * 2u : 0u);
-        else
-            d.ra = make_rsrc(A + (live ? (size_t)t.m0 * K + k0 : 0),
-                             live ? (uint32_t)t.rows * (uint32_t)K * 2u - (uint32_t)k0 * 2u : 0u);
-        if constexpr (TB)
-            d.rb = make_rsrc(B + (live ? (size_t)t.n0 * K + k0 : 0),
-                             live ? (uint32_t)min(N - t.n0, BN) * (uint32_t)K * 2u - (uint32_t)k0 * 2u
-                                  : 0u);
-        else
-            d.rb = make_rsrc(B + (live ? (size_t)k0 * N + t.n0 : 0),
-                             live ? (uint32_t)min(K - k0, BK) * (uint32_t)N * 2u : 0u);
+        const uint32_t kin = (uint32_t)min(K - k0, BK);
+        DmaPos p;
+        if constexpr (TA) {
+            p.pa = A + (live ? (size_t)k0 * M + t.m0 : 0);
+            p.na = live ? kin * (uint32_t)M * 2u : 0u;
+        } else {
+            p.pa = A + (live ? (size_t)t.m0 * K + k0 : 0);
+            p.na = live ? (uint32_t)t.rows * (uint32_t)K * 2u - (uint32_t)k0 * 2u : 0u;
+        }
+        if constexpr (TB) {
+            p.pb = B + (live ? (size_t)t.n0 * K + k0 : 0);
+            p.nb = live ? (uint32_t)min(N - t.n0, BN) * (uint32_t)K * 2u - (uint32_t)k0 * 2u : 0u;
+        } else {
+            p.pb = B + (live ? (size_t)k0 * N + t.n0 : 0);
+            p.nb = live ? kin * (uint32_t)N * 2u : 0u;
+        }
+        return p;
+    };
+    auto pos_next = [&](DmaPos &p) __attribute__((always_inline)) {
+        if constexpr (TA) {
+            p.pa += (size_t)BK * M;
+        } else {
+            p.pa += BK;
+            p.na -= 2u * BK;
+        }
+        if constexpr (TB) {
+            p.pb += BK;
+            p.nb -= 2u * BK;
+        } else {
+            p.pb += (size_t)BK * N;
+        }
+    };
+    auto make_dma = [](const DmaPos &p) __attribute__((always_inline)) {
+        SliceDma d;
+        d.ra = make_rsrc(p.pa, p.na);
+        d.rb = make_rsrc(p.pb, p.nb);
         return d;
     };
     // This wave's LDS load base in stage 0; load i of a slice lands at + region
@@ -344,9 +376,11 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // (step pf_kk of the slice in the bases' stage); with MOVE, then moves every base to the
     // other stage (by `delta`); with DMA, issues the LD loads of slice d into the
     // stage at `lds_stage`, one per EVERY MFMAs.
-    // PAYLOAD (if given) runs after MFMA PQ, in the stream's shadow.
+    // payload(q) runs after MFMA q: per-slice scalar work placed in pieces
+    // into the MFMA stream's shadow (a wave issues only a few instructions
+    // between two MFMAs without delaying the second).
     constexpr int PQ = NPF + NBASE + 2;
-    static_assert(PQ < NMF, "payload slot inside the step");
+    static_assert(PQ + 6 < NMF, "payload slots inside the step");
     auto step = [&](int cur, auto reads_c, int pf_kk, auto move_c, int delta, auto dma_c,
                     uint32_t lds_stage, const SliceDma &d, auto &&payload) __attribute__((always_inline)) {
         constexpr bool READS = decltype(reads_c)::value;
@@ -371,11 +405,11 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             if constexpr (MOVE && q >= NPF && q < NPF + NBASE) move_base(q - NPF, delta);
             if constexpr (DMA && q % EVERY == 0)
                 dma_one(lds_stage, d, std::integral_constant<int, q / EVERY>{});
-            if constexpr (q == PQ) payload();
+            payload(q_c);
             __builtin_amdgcn_sched_barrier(0);
         });
     };
-    auto no_payload = []() __attribute__((always_inline)) {};
+    auto no_payload = [](auto) __attribute__((always_inline)) {};
 
     Tile cur_t;
     if (!tile_of(0, cur_t)) return;   // more workgroups than tiles: nothing to do
@@ -390,14 +424,16 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     };
 
     // Prologue: slices 0 and 1 of the first tile; slice 0 waited for and
-    // published, and its first fragments read.
+    // published, and its first fragments read. pos: the position loaded last.
+    DmaPos pos;
     {
         set_offsets(cur_t, 0);
         if (bias) bias_dma(cur_t, 0);   // lands with slice 0 (waited for below)
-        const SliceDma d0 = slice_dma(cur_t, true, 0);
+        const SliceDma d0 = make_dma(pos_full(cur_t, true, 0));
         static_for<LD>([&](auto i_c) { dma_one(ld_wave, d0, i_c); });
         if (tail_k == 1) set_av(true);
-        const SliceDma d1 = slice_dma(cur_t, true, 1);
+        pos = pos_full(cur_t, true, 1);
+        const SliceDma d1 = make_dma(pos);
         static_for<LD>([&](auto i_c) { dma_one(ld_wave + (uint32_t)A_BYTES, d1, i_c); });
     }
     wait_vmcnt<LD>();
@@ -435,20 +471,35 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             const int k1 = kt + 1 < nk ? kt + 1 : kt + 1 - nk;   // the slice loaded last
             SliceDma dn;
             bool bias_next = false;
-            auto prep = [&]() __attribute__((always_inline)) {
-                // The position's tile edges, and whether it is the partial last
-                // slice (uniform branches, taken a few times per tile). The loads
-                // that used the old offsets were issued a step earlier.
-                if (!here && k2 == 0 && nxt_live) {
-                    if constexpr (!TB) set_bv(nxt_t.n0);
-                    if constexpr (TA) set_tv(nxt_t.m0);
+            auto prep = [&](auto q_c) __attribute__((always_inline)) {
+                constexpr int q = decltype(q_c)::value;
+                if constexpr (q == PQ) {
+                    // The position's tile edges (uniform branch, taken once per
+                    // tile). The loads that used the old offsets were issued a
+                    // step earlier.
+                    if (__builtin_expect((!here) & (k2 == 0) & nxt_live, 0)) {
+                        if constexpr (!TB) set_bv(nxt_t.n0);
+                        if constexpr (TA) set_tv(nxt_t.m0);
+                    }
+                } else if constexpr (q == PQ + 2) {
+                    // Whether it is the partial last slice.
+                    if (__builtin_expect((k2 == tail_k) != (k1 == tail_k), 0)) set_av(k2 == tail_k);
+                } else if constexpr (q == PQ + 4) {
+                    // The first or partial last slice of a tile, or a dead
+                    // position: from scratch (a few times per tile); otherwise
+                    // one step on.
+                    if (__builtin_expect((k2 == 0) | (k2 == tail_k) | !(here | nxt_live), 0))
+                        pos = pos_full(here ? cur_t : nxt_t, here | nxt_live, k2);
+                    else
+                        pos_next(pos);
+                    asm volatile("" : "+s"(pos.pa), "+s"(pos.pb), "+s"(pos.na), "+s"(pos.nb));
+                } else if constexpr (q == PQ + 6) {
+                    dn = make_dma(pos);
+                    bias_next = (bias != nullptr) & (!here) & (k2 == 0) & nxt_live;
+                    // Formed here, in the MFMA shadow, not at their first use
+                    // after the barrier.
+                    asm volatile("" : "+s"(dn.ra), "+s"(dn.rb));
                 }
-                if ((k2 == tail_k) != (k1 == tail_k)) set_av(k2 == tail_k);
-                dn = slice_dma(here ? cur_t : nxt_t, here || nxt_live, k2);
-                bias_next = bias && !here && k2 == 0 && nxt_live;
-                // Formed here, in the MFMA shadow, not at their first use after the
-                // barrier.
-                asm volatile("" : "+s"(dn.ra), "+s"(dn.rb));
             };
             step(0, std::true_type{}, 1, std::true_type{}, delta, std::false_type{}, 0u, SliceDma{}, prep);
             wait_vmcnt_lgkm0<0>();
