@@ -66,7 +66,7 @@ def _code_objects(tmp):
 @pytest.fixture(scope="module")
 def kernels(tmp_path_factory):
     tmp = str(tmp_path_factory.mktemp("co"))
-    meta, insts = {}, defaultdict(set)
+    meta, insts, seq = {}, defaultdict(set), defaultdict(list)
     for path in _code_objects(tmp):
         notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", path],
                                capture_output=True, text=True, check=True).stdout
@@ -96,8 +96,9 @@ def kernels(tmp_path_factory):
             t = line.strip().split()
             if t and re.match(r"^[a-z_][a-z0-9_]*$", t[0]):
                 insts[sym].add(t[0] + (" lds" if t[0].startswith("buffer_load") and "lds" in t else ""))
+                seq[sym].append(t[0])
     assert meta
-    return meta, insts
+    return meta, insts, seq
 
 
 def _kind(name):
@@ -116,7 +117,7 @@ def _targs(name):
 
 
 def test_every_kernel_is_known(kernels):
-    meta, _ = kernels
+    meta, _, _ = kernels
     unknown = [n for n in meta if _kind(n) is None]
     assert not unknown, unknown
     kinds = {_kind(n) for n in meta}
@@ -125,7 +126,7 @@ def test_every_kernel_is_known(kernels):
 
 
 def test_no_scratch_and_resources_fit(kernels):
-    meta, _ = kernels
+    meta, _, _ = kernels
     bad = []
     for name, m in meta.items():
         if m.get("private_segment_fixed_size", 0) != 0 or m.get("vgpr_spill_count", 0) != 0:
@@ -136,7 +137,7 @@ def test_no_scratch_and_resources_fit(kernels):
 
 
 def test_gemm_kernels_use_the_matrix_cores(kernels):
-    meta, insts = kernels
+    meta, insts, _ = kernels
     for name in meta:
         kind = _kind(name)
         ins = insts[name]
@@ -153,7 +154,7 @@ def test_gemm_kernels_use_the_matrix_cores(kernels):
 
 
 def test_direct_to_lds_kernels_instruction_mix(kernels):
-    meta, insts = kernels
+    meta, insts, _ = kernels
     seen = 0
     for name in meta:
         kind = _kind(name)
@@ -173,3 +174,24 @@ def test_direct_to_lds_kernels_instruction_mix(kernels):
         assert not any(i.startswith("scratch_") for i in ins), name
         seen += 1
     assert seen >= 100
+
+
+def test_persistent_main_loop_keeps_accumulators_in_place(kernels):
+    """In the persistent kernel's first 128 MFMAs (one 64-deep slice of the
+    main loop: 2 steps of 8x8 16x16x32 MFMAs per wave) no accumulator is copied
+    or rewritten (v_accvgpr_mov / v_accvgpr_write) and nothing touches scratch:
+    a register allocation that shuffles accumulators there costs the matrix core
+    every slice even when the kernel has no scratch at all."""
+    meta, _, seq = kernels
+    seen = 0
+    for name in meta:
+        if _kind(name) != "gemm_v5_kernel":
+            continue
+        ops = seq[name]
+        mf = [i for i, op in enumerate(ops) if op.startswith("v_mfma")]
+        assert len(mf) >= 128, name
+        loop = ops[mf[0]:mf[127]]
+        bad = [op for op in loop if op.startswith(("v_accvgpr_mov", "v_accvgpr_write", "scratch_"))]
+        assert not bad, (name, sorted(set(bad)))
+        seen += 1
+    assert seen >= 40

@@ -114,8 +114,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                   "LDS ring + bias slots + staging too large");
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wid = tid >> 6;
-    const int wm = wid / WN, wn = wid % WN;
+    const int wid = tid >> 6;
     const int nk = (K + BK - 1) / BK;
     // Index of every tile's partial last slice (K % 64 != 0), or -1 (kept as an
     // int: a uniform bool can end up materialised in a vector register).
@@ -283,42 +282,51 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // lane, so the address is a per-fn lane base plus the k-row offset of kk and
     // h. All bases are LDS addresses in the stage being read (stage 0 at the
     // start); the block and k-row terms are compile-time offsets.
-    const int tg = lane >> 4, tj = lane & 15;
-    uint32_t fa_base[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-        const int r = wm * WTM + tj;
-        fa_base[kk] = smem_lds + (uint32_t)(r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * kk + tg) * 16);
-    }
-    // TB: W^T block fn, step kk: lane l reads row wn*WTN + 16 fn + l%16 of W's
-    // tile like A's (a per-kk lane base plus 16 fn rows).
+    // The bases are formed by set_bases for the stage at byte offset `st` from
+    // stage 0: at the start, and again after each epilogue (from the lane id
+    // read afresh), so that they are not held across the epilogue.
     constexpr int NFB = TB ? KK : FN;
+    uint32_t fa_base[KK];
     uint32_t fb_base[NFB];
-#pragma unroll
-    for (int f = 0; f < NFB; ++f) {
-        if constexpr (TB) {
-            const int r = wn * WTN + tj;
-            fb_base[f] = smem_lds + B_REGION + (uint32_t)(r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * f + tg) * 16);
-        } else {
-            const int k = 8 * tg + (tj >> 2);
-            const int n = wn * WTN + f * 16 + 4 * (tj & 3);
-            const int c = (n >> 3) ^ bswz<CHB>(k);
-            fb_base[f] = smem_lds + B_REGION + (uint32_t)(k * (BN * 2) + c * 16 + (n & 4) * 2);
-        }
-    }
-    // TA: A block fm, step kk, half h gathered from At's tile like B^T's from
-    // B's. Lane l asks for k row 32 kk + 8 (l/16) + 4 h + (l%16)/4 and m =
-    // wm*WTM + 16 fm + 4 (l%4); 16 fm rows flip only chunk bits 1..3 (byte
-    // address bits 5..7) of the fm = 0 address: one base per block fm.
     uint32_t ft_base[TA ? FM : 1];
-    if constexpr (TA) {
-        const int k = 8 * tg + (tj >> 2);
-        const int m = wm * WTM + 4 * (tj & 3);
-        const int c = (m >> 3) ^ bswz<CHB>(k);
-        const uint32_t b0 = (uint32_t)(k * (BM * 2) + c * 16 + (m & 4) * 2);
+    auto set_bases = [&](uint32_t st) __attribute__((always_inline)) {
+        const int l = lane_now();
+        const int tg = l >> 4, tj = l & 15;
+        const int wm_s = wid_s / WN, wn_s = wid_s % WN;
+        const uint32_t s0 = smem_lds + st;
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) ft_base[fm] = smem_lds + (b0 ^ (uint32_t)(fm << 5));
-    }
+        for (int kk = 0; kk < KK; ++kk) {
+            const int r = wm_s * WTM + tj;
+            fa_base[kk] = s0 + (uint32_t)(r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * kk + tg) * 16);
+        }
+        // TB: W^T block fn, step kk: lane l reads row wn*WTN + 16 fn + l%16 of
+        // W's tile like A's (a per-kk lane base plus 16 fn rows).
+#pragma unroll
+        for (int f = 0; f < NFB; ++f) {
+            if constexpr (TB) {
+                const int r = wn_s * WTN + tj;
+                fb_base[f] = s0 + B_REGION + (uint32_t)(r * (BK * 2) + aswz<MS, CHA>(r, (KS / 8) * f + tg) * 16);
+            } else {
+                const int k = 8 * tg + (tj >> 2);
+                const int n = wn_s * WTN + f * 16 + 4 * (tj & 3);
+                const int c = (n >> 3) ^ bswz<CHB>(k);
+                fb_base[f] = s0 + B_REGION + (uint32_t)(k * (BN * 2) + c * 16 + (n & 4) * 2);
+            }
+        }
+        // TA: A block fm, step kk, half h gathered from At's tile like B^T's
+        // from B's. Lane l asks for k row 32 kk + 8 (l/16) + 4 h + (l%16)/4 and
+        // m = wm*WTM + 16 fm + 4 (l%4); 16 fm rows flip only chunk bits 1..3
+        // (byte address bits 5..7) of the fm = 0 address: one base per block fm.
+        if constexpr (TA) {
+            const int k = 8 * tg + (tj >> 2);
+            const int m = wm_s * WTM + 4 * (tj & 3);
+            const int c = (m >> 3) ^ bswz<CHB>(k);
+            const uint32_t b0 = (uint32_t)(k * (BM * 2) + c * 16 + (m & 4) * 2);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) ft_base[fm] = s0 + (b0 ^ (uint32_t)(fm << 5));
+        }
+    };
+    set_bases(0u);
 
     f32x4 acc[FN][FM];
     u32x4 fa[2][FM];
@@ -513,8 +521,18 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             lds_cur += (uint32_t)delta;   // the next slice's stage
             delta = -delta;
         };
-        for (int kt = 0; kt + 1 < nk; ++kt) slice(kt, std::true_type{});
-        slice(nk - 1, std::false_type{});
+        // The last slice also reads the next position's first fragments (they
+        // are read again after the epilogue, which needs their registers): so it
+        // runs the loop's own code, not a copy that starts cold in the
+        // instruction cache (about 1000 cycles a tile). With W [N,K] and A
+        // [M,K] that leaves the register allocator shuffling accumulators in
+        // the loop; there the last slice keeps its own copy.
+        if constexpr (TB && !TA) {
+            for (int kt = 0; kt + 1 < nk; ++kt) slice(kt, std::true_type{});
+            slice(nk - 1, std::false_type{});
+        } else {
+            for (int kt = 0; kt < nk; ++kt) slice(kt, std::true_type{});
+        }
 
         // Epilogue of this tile while the next tile's first slices land. The
         // scheduling fences keep the next tile's fragment reads and the epilogue
@@ -625,8 +643,9 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         asm volatile("" ::: "memory");
         if (!nxt_live) break;
         cur_t = nxt_t;
-        // The next tile's slice 0 was published by the last barrier; its first
-        // fragments (the bases already name its stage).
+        // The next tile's slice 0 was published by the last barrier, in the
+        // stage lds_cur names; its first fragments.
+        set_bases(lds_cur - ld_wave);
 #pragma unroll
         for (int q = 0; q < NPF; ++q) read_one(0, 0, q);
     }
