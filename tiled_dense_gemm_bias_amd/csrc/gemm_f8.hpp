@@ -157,25 +157,55 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
     // Slice kt of tile t into stage `stage`; slices past K (or of no tile) read
     // nothing: every lane is out of range and lands zeros, which keeps the wait
     // counts uniform.
-    auto slice_dma = [&](const Tile &t, bool live, int kt, int stage) {
+    // (Selects, not conditional code: in the main loop this is formed in the
+    // MFMA stream, where a taken branch stalls the wave.)
+    // In the main loop the pieces are formed one per MFMA gap (dma_part), each
+    // pinned where it is formed, with selects rather than conditional code: a
+    // burst of scalar work or a taken branch between two MFMAs stalls the wave.
+    auto dma_part = [&](SliceDma &d, int part, const Tile &t, bool live, int kt, int stage)
+        __attribute__((always_inline)) {
+        const bool any = live & (kt < t.nkl);
+        const int k0 = (t.kt0 + kt) * BK;
+        if (part == 0) {
+            d.la = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(stage * STAGE_BYTES + wid_s * 64 * 16));
+            d.k0 = any ? k0 : K;
+            asm volatile("" : "+s"(d.la), "+s"(d.k0));
+        } else if (part == 1) {
+            const uint32_t rows_a = (uint32_t)min(M - t.m0, BM);
+            const size_t oa = (size_t)t.m0 * K + k0;
+            d.ra = make_rsrc(A + (any ? oa : 0), any ? rows_a * (uint32_t)K - (uint32_t)k0 : 0u);
+            asm volatile("" : "+s"(d.ra));
+        } else {
+            const uint32_t rows_w = (uint32_t)min(N - t.n0, BN);
+            const size_t ow = (size_t)t.n0 * K + k0;
+            d.rw = make_rsrc(W + (any ? ow : 0), any ? rows_w * (uint32_t)K - (uint32_t)k0 : 0u);
+            asm volatile("" : "+s"(d.rw));
+        }
+    };
+    auto slice_dma = [&](const Tile &t, bool live, int kt, int stage) __attribute__((always_inline)) {
         SliceDma d;
-        d.la = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(stage * STAGE_BYTES + wid_s * 64 * 16));
-        const bool any = live && kt < t.nkl;
-        d.k0 = any ? (t.kt0 + kt) * BK : K;
-        const uint32_t rows_a = (uint32_t)min(M - t.m0, BM), rows_w = (uint32_t)min(N - t.n0, BN);
-        d.ra = make_rsrc(A + (any ? (size_t)t.m0 * K + d.k0 : 0),
-                         any ? rows_a * (uint32_t)K - (uint32_t)d.k0 : 0u);
-        d.rw = make_rsrc(W + (any ? (size_t)t.n0 * K + d.k0 : 0),
-                         any ? rows_w * (uint32_t)K - (uint32_t)d.k0 : 0u);
+        dma_part(d, 0, t, live, kt, stage);
+        dma_part(d, 1, t, live, kt, stage);
+        dma_part(d, 2, t, live, kt, stage);
         return d;
     };
-    auto dma_one = [&](const SliceDma &d, int i, uint32_t kx) {
+    // Load j of a thread reads row 32 j + tid/8 of its tile's slice: offset lo[j]
+    // from the slice corner, held for the whole stream; eo[j] is the offset the
+    // next slice's loads use, lo[j] or (chunks past K) out of range, formed in
+    // step 0's shadow so that no address arithmetic sits between step 1's loads.
+    uint32_t lo[A_LD], eo[A_LD];
+#pragma unroll
+    for (int j = 0; j < A_LD; ++j) lo[j] = ld_base + (uint32_t)(j * 32) * (uint32_t)K;
+    auto dma_one = [&](const SliceDma &d, int i) __attribute__((always_inline)) {
         const int j = i & (A_LD - 1);
-        const uint32_t o = d.k0 + c_a * 16 < K ? ld_base + (uint32_t)(j * 32) * kx : kOobOffset;
         if (i < A_LD)
-            buffer_load_lds16(d.ra, o, d.la + j * NT * 16);
+            buffer_load_lds16(d.ra, eo[j], d.la + j * NT * 16);
         else
-            buffer_load_lds16(d.rw, o, d.la + A_BYTES + j * NT * 16);
+            buffer_load_lds16(d.rw, eo[j], d.la + A_BYTES + j * NT * 16);
+    };
+    auto set_eo = [&](int k0, int j) __attribute__((always_inline)) {
+        eo[j] = k0 + c_a * 16 < K ? lo[j] : kOobOffset;
+        asm volatile("" : "+v"(eo[j]));
     };
 
     // Bias of tile t into this wave's slot of parity p: lanes 0..31 load 16 bytes
@@ -209,9 +239,13 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
         const SliceDma d0 = slice_dma(cur_t, true, 0, 0), d1 = slice_dma(cur_t, true, 1, 1);
         if (bias) bias_dma(cur_t, 0);   // lands with slice 0 (waited for below)
 #pragma unroll
-        for (int i = 0; i < LD; ++i) dma_one(d0, i, (uint32_t)K);
+        for (int j = 0; j < A_LD; ++j) set_eo(d0.k0, j);
 #pragma unroll
-        for (int i = 0; i < LD; ++i) dma_one(d1, i, (uint32_t)K);
+        for (int i = 0; i < LD; ++i) dma_one(d0, i);
+#pragma unroll
+        for (int j = 0; j < A_LD; ++j) set_eo(d1.k0, j);
+#pragma unroll
+        for (int i = 0; i < LD; ++i) dma_one(d1, i);
     }
     wait_vmcnt<LD>();
     block_barrier();
@@ -233,30 +267,36 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
             const int sc = (stage0 + kt) & 1;
             const char *cur_base = smem + sc * STAGE_BYTES;
             const char *nxt_base = smem + (sc ^ 1) * STAGE_BYTES;
-            uint32_t kx = (uint32_t)K;
-            asm volatile("" : "+s"(kx));
-            // step 0: rows 0..3; this slice's A fragments 4..7 are read meanwhile
+            // step 0: rows 0..3; this slice's A fragments 4..7 are read meanwhile,
+            // and (in the MFMA stream's shadow, not after the barrier where they
+            // would delay step 1's first MFMA) the descriptors of the loads two
+            // slices ahead
+            const bool here = kt + 2 < cur_t.nk;
+            SliceDma dn;
+            bool bias_next = false;
 #pragma unroll
             for (int q = 0; q < FN * HM; ++q) {
                 const int fn = q / HM, fm = q % HM;
                 mfma16x16x128_f8<FMT, F>(acc[fn][fm], fw[fn], fa[0][fm]);
                 if (q % 8 == 0) fa[1][q / 8] = read_frag(cur_base, ra_row, HM + q / 8);
+                if (q >= 12 && q <= 16 && q % 2 == 0)
+                    dma_part(dn, (q - 12) / 2, here ? cur_t : nxt_t, here | nxt_live,
+                             here ? kt + 2 : kt + 2 - cur_t.nk, sc);
+                // with the next tile's slice 0, its bias into the other parity's slot
+                if (q == 17) bias_next = (bias != nullptr) & (!here) & (kt + 2 == cur_t.nk) & nxt_live;
+                if (q >= 18 && q < 18 + A_LD) set_eo(dn.k0, q - 18);
                 __builtin_amdgcn_sched_barrier(0);
             }
             wait_vmcnt_lgkm0<0>();
             block_barrier();
-            const bool here = kt + 2 < cur_t.nk;
-            const SliceDma dn = slice_dma(here ? cur_t : nxt_t, here || nxt_live,
-                                          here ? kt + 2 : kt + 2 - cur_t.nk, sc);
-            // with the next tile's slice 0, its bias into the other parity's slot
-            if (bias && !here && kt + 2 == cur_t.nk && nxt_live) bias_dma(nxt_t, (r + 1) & 1);
+            if (__builtin_expect(bias_next, 0)) bias_dma(nxt_t, (r + 1) & 1);
             // step 1: rows 4..7; the next slice's A fragments 0..3, each W
             // fragment after its last MFMA here, and the loads two slices ahead
 #pragma unroll
             for (int q = 0; q < FN * HM; ++q) {
                 const int fn = q / HM, fm = q % HM;
                 mfma16x16x128_f8<FMT, F>(acc[fn][HM + fm], fw[fn], fa[1][fm]);
-                if (q % 2 == 0) dma_one(dn, q / 2, kx);
+                if (q % 2 == 0) dma_one(dn, q / 2);
                 if (fm == HM - 1) fw[fn] = read_frag(nxt_base, rw_row, fn);
                 if (q % 8 == 1) fa[0][q / 8] = read_frag(nxt_base, ra_row, q / 8);
                 __builtin_amdgcn_sched_barrier(0);
