@@ -15,10 +15,12 @@
 // slice's share of global->LDS loads, then the next MFMA, ... so the matrix core
 // keeps running while the loads drain.
 //
-//  * The loads of slice t+STAGES are spread over SPREAD MFMA steps: the one
-//    right after the barrier that frees their stage, and the first SPREAD-1
-//    steps of the next slice. All of them are issued before the next barrier,
-//    so every wait is "all but the (STAGES-2) newest slices".
+//  * The loads of slice t+STAGES are issued in the MFMA step right after the
+//    barrier that frees their stage (SPREAD = 1), before the next barrier, so
+//    every wait is "all but the (STAGES-2) newest slices". Their descriptors
+//    and K-masked offsets are formed in the step before the barrier, a few
+//    instructions per MFMA gap: a burst of scalar or address work between two
+//    MFMAs, or a taken branch, delays the second.
 //  * Only the first LDW waves issue global->LDS loads; with LDW < waves, the
 //    other waves on the same SIMDs keep issuing MFMAs while the loaders wait
 //    on the address path.
@@ -124,7 +126,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                   "slices split evenly");
     static_assert(STAGES >= 2 && STAGES * STAGE_BYTES <= 160 * 1024, "LDS ring too large");
     static_assert(STAGES * LD < 64, "vmcnt range");
-    static_assert(SPREAD >= 1 && SPREAD <= KK, "loads must be issued before the next barrier");
+    static_assert(SPREAD == 1, "a slice's loads are issued in the step after the barrier");
     static_assert(LD_STEP <= NMF, "at most one load per MFMA");
 
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
@@ -204,46 +206,70 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     }
 
     // Descriptors and LDS targets of one slice (slices at or past nk read nothing).
+    // In the main loop they are formed in pieces (dma_part), one per MFMA gap of
+    // the step before the barrier, each pinned where it is formed and written
+    // with selects: a burst of scalar work, or a taken branch, between two MFMAs
+    // delays the second.
     struct SliceDma {
         __amdgpu_buffer_rsrc_t ra, rb;
         uint32_t la, lb;
         int k0;
     };
-    auto slice_dma = [&](int kt) {
+    auto dma_part = [&](SliceDma &d, int part, int kt) __attribute__((always_inline)) {
+        const int k0 = (kt0 + kt) * BK;
+        const bool live = PARTIAL ? kt < nk : k0 < K;
+        if (part == 0) {
+            const int stage = kt % STAGES;
+            d.la = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(stage * STAGE_BYTES + wid_s * 64 * 16));
+            d.lb = d.la + A_BYTES;
+            d.k0 = k0;
+            asm volatile("" : "+s"(d.la), "+s"(d.lb), "+s"(d.k0));
+        } else if (part == 1) {
+            if constexpr (TA) {
+                const uint32_t bytes_a = live ? (uint32_t)min(K - k0, BK) * (uint32_t)M * 2u : 0u;
+                d.ra = make_rsrc(A + (size_t)(live ? k0 : 0) * M + m0, bytes_a);
+            } else {
+                const uint32_t bytes_a =
+                    live ? (uint32_t)rows_a * (uint32_t)K * 2u - (uint32_t)k0 * 2u : 0u;
+                d.ra = make_rsrc(A + (size_t)m0 * K + (live ? k0 : 0), bytes_a);
+            }
+            asm volatile("" : "+s"(d.ra));
+        } else {
+            if constexpr (TB) {
+                const uint32_t bytes_b =
+                    live ? (uint32_t)rows_b * (uint32_t)K * 2u - (uint32_t)k0 * 2u : 0u;
+                d.rb = make_rsrc(B + (size_t)n0 * K + (live ? k0 : 0), bytes_b);
+            } else {
+                const uint32_t bytes_b = live ? (uint32_t)min(K - k0, BK) * (uint32_t)N * 2u : 0u;
+                d.rb = make_rsrc(B + (size_t)(live ? k0 : 0) * N + n0, bytes_b);
+            }
+            asm volatile("" : "+s"(d.rb));
+        }
+    };
+    auto slice_dma = [&](int kt) __attribute__((always_inline)) {
         SliceDma d;
-        const int stage = kt % STAGES;
-        d.la = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(stage * STAGE_BYTES + wid_s * 64 * 16));
-        d.lb = d.la + A_BYTES;
-        d.k0 = (kt0 + kt) * BK;
-        const bool live = PARTIAL ? kt < nk : d.k0 < K;
-        if constexpr (TA) {
-            const uint32_t bytes_a = live ? (uint32_t)min(K - d.k0, BK) * (uint32_t)M * 2u : 0u;
-            d.ra = make_rsrc(A + (size_t)(live ? d.k0 : 0) * M + m0, bytes_a);
-        } else {
-            const uint32_t bytes_a =
-                live ? (uint32_t)rows_a * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u;
-            d.ra = make_rsrc(A + (size_t)m0 * K + (live ? d.k0 : 0), bytes_a);
-        }
-        if constexpr (TB) {
-            const uint32_t bytes_b =
-                live ? (uint32_t)rows_b * (uint32_t)K * 2u - (uint32_t)d.k0 * 2u : 0u;
-            d.rb = make_rsrc(B + (size_t)n0 * K + (live ? d.k0 : 0), bytes_b);
-        } else {
-            const uint32_t bytes_b = live ? (uint32_t)min(K - d.k0, BK) * (uint32_t)N * 2u : 0u;
-            d.rb = make_rsrc(B + (size_t)(live ? d.k0 : 0) * N + n0, bytes_b);
-        }
+        dma_part(d, 0, kt);
+        dma_part(d, 1, kt);
+        dma_part(d, 2, kt);
         return d;
     };
-    auto dma_one = [&](const SliceDma &d, int i) {
-        if (i < A_LD) {
-            const uint32_t o = TA || d.k0 + a_k[i] < K ? off[i] : kOobOffset;
-            buffer_load_lds16(d.ra, o, d.la + i * NTL * 16);
-        } else if constexpr (TB) {
-            const uint32_t o = d.k0 + a_k[i] < K ? off[i] : kOobOffset;
-            buffer_load_lds16(d.rb, o, d.lb + (i - A_LD) * NTL * 16);
-        } else {
-            buffer_load_lds16(d.rb, off[i], d.lb + (i - A_LD) * NTL * 16);
+    // K-contiguous loads (A, and W with TB) of the slice being loaded take eo[i]:
+    // off[i], or out of range for chunks past K; formed with the descriptors, so
+    // that no address arithmetic sits between the loads.
+    uint32_t eo[LD];
+    auto masked = [](int i) { return i < A_LD ? !TA : TB; };
+    auto set_eo = [&](const SliceDma &d, int i) __attribute__((always_inline)) {
+        if (masked(i)) {
+            eo[i] = d.k0 + a_k[i] < K ? off[i] : kOobOffset;
+            asm volatile("" : "+v"(eo[i]));
         }
+    };
+    auto dma_one = [&](const SliceDma &d, int i) __attribute__((always_inline)) {
+        const uint32_t o = masked(i) ? eo[i] : off[i];
+        if (i < A_LD)
+            buffer_load_lds16(d.ra, o, d.la + i * NTL * 16);
+        else
+            buffer_load_lds16(d.rb, o, d.lb + (i - A_LD) * NTL * 16);
     };
 
     // Fragment reads for MFMA step kk of a stage.
@@ -319,7 +345,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // reads (into cur^1, from `pf_base` step pf_kk) and, when `dma` is set, `nd`
     // loads of slice `d` starting at load index `d0` woven in between.
     auto step = [&](int cur, const char *pf_base, int pf_kk, bool dma, const SliceDma &d, int d0,
-                    int nd) {
+                    int nd, auto &&payload) {
         constexpr int every = NMF / (LD_STEP > 0 ? LD_STEP : 1);
 #pragma unroll
         for (int q = 0; q < NMF; ++q) {
@@ -339,53 +365,64 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             acc[fn][fm] = mfma16x16x32<DT>(bop, aop, acc[fn][fm]);
             if (q < NPF) read_one(cur ^ 1, pf_base, pf_kk, q);
             if (dma && q % every == 0 && q / every < nd) dma_one(d, d0 + q / every);
+            payload(q);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int r = NMF; r < NPF; ++r) read_one(cur ^ 1, pf_base, pf_kk, r);
     };
 
-    // Prologue: slices 0 .. STAGES-2 requested in full and the first LD_STEP
-    // loads of slice STAGES-1 (the rest follow in slice 0's first steps, as in
-    // the steady state); slice 0 waited for.
+    // Prologue: slices 0 .. STAGES-1 requested; slice 0 waited for.
+    auto no_payload = [](int) {};
     if (loader) {
 #pragma unroll
         for (int s = 0; s < STAGES; ++s) {
             const SliceDma d = slice_dma(s);
 #pragma unroll
-            for (int i = 0; i < (s + 1 < STAGES ? LD : LD_STEP); ++i) dma_one(d, i);
+            for (int i = 0; i < LD; ++i) set_eo(d, i);
+#pragma unroll
+            for (int i = 0; i < LD; ++i) dma_one(d, i);
         }
     }
-    wait_vmcnt<(STAGES - 2) * LD + LD_STEP>();
+    wait_vmcnt<(STAGES - 1) * LD>();
     block_barrier();
 #pragma unroll
     for (int r = 0; r < NPF; ++r) read_one(0, smem, 0, r);
 
+    // The step before the barrier forms the descriptors and offsets of slice
+    // kt+STAGES in its shadow, from MFMA PQ on (after its fragment reads where
+    // the step has room): three descriptor pieces, then the NMASK offsets that
+    // carry the K mask (the k-th is load MI(k)).
+    constexpr int NMASK = (TA ? 0 : A_LD) + (TB ? B_LD : 0);
+    constexpr int PQ = NPF < NMF - 3 - NMASK ? NPF : NMF - 3 - NMASK;
+    static_assert(PQ >= 0, "payload slots inside the step");
+    auto MI = [](int k) { return TA ? A_LD + k : k; };
     for (int kt = 0; kt < nk; ++kt) {
         const char *cur_base = smem + (kt % STAGES) * STAGE_BYTES;
         const char *nxt_base = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
-        const SliceDma dprev = slice_dma(kt - 1 + STAGES);   // its loads LD_STEP.. go here
+        SliceDma dnew;
+        auto prep = [&](int q) __attribute__((always_inline)) {
+            if (q >= PQ && q < PQ + 3) dma_part(dnew, q - PQ, kt + STAGES);
+            if (q >= PQ + 3 && q < PQ + 3 + NMASK) set_eo(dnew, MI(q - PQ - 3));
+        };
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             const int cur = kk & 1;
             if (kk + 1 < KK) {
-                const int first = (kk + 1) * LD_STEP;
-                const int nd = kk + 1 < SPREAD ? min(LD_STEP, LD - first) : 0;
-                if (loader)
-                    step(cur, cur_base, kk + 1, nd > 0, dprev, first, nd);
+                if (kk + 2 == KK)
+                    step(cur, cur_base, kk + 1, false, dnew, 0, 0, prep);
                 else
-                    step(cur, cur_base, kk + 1, false, dprev, first, 0);
+                    step(cur, cur_base, kk + 1, false, dnew, 0, 0, no_payload);
             } else {
                 // Publish slice kt+1 (own loads landed, own reads of slice kt
                 // returned; then the same for all waves) and recycle slice kt's
                 // stage for slice kt+STAGES.
                 wait_vmcnt_lgkm0<(STAGES - 2) * LD>();
                 block_barrier();
-                const SliceDma dnew = slice_dma(kt + STAGES);
                 if (loader)
-                    step(cur, nxt_base, 0, true, dnew, 0, min(LD_STEP, LD));
+                    step(cur, nxt_base, 0, true, dnew, 0, LD, no_payload);
                 else
-                    step(cur, nxt_base, 0, false, dnew, 0, 0);
+                    step(cur, nxt_base, 0, false, dnew, 0, 0, no_payload);
             }
         }
     }
