@@ -130,6 +130,33 @@ def test_persistent_kernel_random_gelu_and_short_k():
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_direct_to_lds_schedules_agree_bitwise_on_random_inputs(dtype):
+    """Kernels 3 and 4 feed every output element the same 16x16x32 MFMAs in the
+    same K order (64-deep slices of two 32-deep steps) and the same epilogue,
+    whatever the tile, ring depth or persistence: on random inputs (inexact
+    sums) every such schedule must give the same bits. Ragged M and N, a K tail
+    (1000 = 15 x 64 + 40), and for the persistent kernel 17 x 17 = 289 tiles of
+    256 x 256, so that some workgroups run two."""
+    M, N, K = 4100, 4200, 1000
+    A = synth.random_bits((M, K), dtype, 41)
+    B = synth.random_bits((K, N), dtype, 42, scale=1 / 16)
+    bias = synth.random_bits((N,), dtype, 43)
+    scheds = [s for s in schedules() if s["kernel"] in (3, 4)]
+    assert len(scheds) >= 5
+    ref = None
+    for s in scheds:
+        for raster in (0, 1):
+            say("agree", dtype, sched_id(s), "raster", raster)
+            got = run_gpu(A, B, bias, "gelu", dtype, sched=dict(s, raster=raster))
+            if ref is None:
+                ref = got
+                check_random(A, B, bias, "gelu", dtype, got, rows=synth.sample_rows(M, 64, seed=4))
+            else:
+                bad = np.argwhere(got != ref)
+                assert bad.size == 0, (sched_id(s), raster, len(bad), bad[:3].tolist())
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_exact_relu_epilogue_bitwise(dtype):
     A, B, bias = int_inputs(200, 136, 520, dtype, seed=9)
     want = oracle.encode(oracle.gemm_bias_act(A, B, bias, "relu", dtype), dtype)
