@@ -57,7 +57,9 @@ def test_schedule_table(lib):
     for s in scheds:
         # the pages' shared-memory filter, against the 160 KiB LDS of a CU
         assert (s["bm"] * s["bk"] + s["bk"] * s["bn"]) * 2 * s["stages"] <= 160 * 1024
-        assert s["bm"] % (32 * s["wm"]) == 0 and s["bn"] % (32 * s["wn"]) == 0
+        # whole MFMA blocks per wave: 16x16 (kernels 3, 4), else 32x32
+        blk = 16 if s["kernel"] in (3, 4) else 32
+        assert s["bm"] % (blk * s["wm"]) == 0 and s["bn"] % (blk * s["wn"]) == 0
     assert any((s["bm"], s["bn"], s["bk"]) == (128, 128, 32) for s in scheds)
     assert lib.gba_list_schedule(len(scheds), ctypes.byref(gba.Schedule())) == ERR_SCHEDULE
 

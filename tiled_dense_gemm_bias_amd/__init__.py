@@ -169,11 +169,20 @@ def _act(act) -> int:
 
 
 def _call(fn_name: str, dev, *args):
+    """Run entry point fn_name on dev's current stream. The library launches on
+    the calling thread's current device, so it is switched only when the
+    tensors live elsewhere (the switch and torch's stream object cost a few
+    microseconds, as much as a small GEMM)."""
     torch = _torch()
-    with torch.cuda.device(dev):
-        lib = _lib()
-        lib.gba_set_stream(ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    lib = _lib()
+    C = torch._C
+    if dev.index == C._cuda_getDevice():
+        lib.gba_set_stream(C._cuda_getCurrentRawStream(dev.index))
         st = getattr(lib, fn_name)(*args)
+    else:
+        with torch.cuda.device(dev):
+            lib.gba_set_stream(C._cuda_getCurrentRawStream(dev.index))
+            st = getattr(lib, fn_name)(*args)
     if st != 0:
         raise GbaError(st, fn_name)
 

@@ -29,6 +29,7 @@ extern const ScheduleEntry i_256x128x64_w2x2_s3_l4_p1_m16;
 extern const ScheduleEntry i_128x256x64_w2x2_s3_l4_p1_m16;
 extern const ScheduleEntry i_128x128x64_w2x2_s3_l4_p1_m16;
 extern const ScheduleEntry i_128x128x64_w2x2_s4_l4_p1_m16;
+extern const ScheduleEntry i_64x64x64_w4x1_s4_l4_p1_m16;
 extern const ScheduleEntry p_256x256x64_w2x2;
 extern const F8LaunchFn f8_e4m3[2][kNumActs];
 extern const F8LaunchFn f8_e5m2[2][kNumActs];
@@ -47,6 +48,7 @@ const ScheduleEntry *const kTable[] = {
     // interleaved direct-to-LDS kernels with 16x16x32 MFMAs, one tile per workgroup
     &gba::i_256x128x64_w2x2_s3_l4_p1_m16, &gba::i_128x256x64_w2x2_s3_l4_p1_m16,
     &gba::i_128x128x64_w2x2_s3_l4_p1_m16, &gba::i_128x128x64_w2x2_s4_l4_p1_m16,
+    &gba::i_64x64x64_w4x1_s4_l4_p1_m16,
     // register-staged kernel at the pages' 128x128x32 starting tile
     &gba::s_128x128x32_w2x2,
 };
@@ -197,7 +199,7 @@ long long lds_bytes(const gba_schedule &s) {
 // the largest tile that still gives every CU about one tile; at 256x256 the
 // persistent kernel (same tile and loop as kernel 3, measured 1-2% faster with
 // one tile per CU and 4-6% faster with several).
-gba_schedule heuristic(int64_t M, int64_t N, int cus) {
+gba_schedule heuristic(int64_t M, int64_t N, int cus, int lay) {
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     const int64_t want = (int64_t)cus * 9 / 10;
     const ScheduleEntry *e;
@@ -205,8 +207,13 @@ gba_schedule heuristic(int64_t M, int64_t N, int cus) {
         e = &gba::p_256x256x64_w2x2;   // persistent: streams several tiles per CU
     else if (tiles(256, 128) >= want)
         e = M >= N ? &gba::i_256x128x64_w2x2_s3_l4_p1_m16 : &gba::i_128x256x64_w2x2_s3_l4_p1_m16;
-    else
+    else if (2 * tiles(128, 128) > cus || (lay & LAY_TA))   // 64x64 has no (K,M) A path
         e = &gba::i_128x128x64_w2x2_s4_l4_p1_m16;   // 4 stages: 10-20 % faster than 3 here
+    else
+        // 128x128 tiles would leave half the CUs or more idle: 4x the tiles
+        // (1024^3 5-21 % faster, 1024x2048x1024 10 %, K = 4096..8192 40-50 %;
+        // at 144 and 256 tiles of 128x128 the larger tile is 24-26 % faster)
+        e = &gba::i_64x64x64_w4x1_s4_l4_p1_m16;
     return e->sched;
 }
 
@@ -487,7 +494,7 @@ gba_schedule choose(const DeviceInfo &d, int64_t M, int64_t N, int64_t K, int ac
         return rec.s;
     }
     *why = "heuristic";
-    return heuristic(M, N, d.cus);
+    return heuristic(M, N, d.cus, lay);
 }
 
 // The instance of schedule s for (dtype, act, operand layouts), or null.
@@ -1015,7 +1022,7 @@ int gba_autotune(const void *A, const void *B, const void *bias, void *C, int64_
     s = current_device(&d);
     if (s) return s;
     if (nothing) {
-        gba_schedule h = heuristic(M, N, d->cus);
+        gba_schedule h = heuristic(M, N, d->cus, lay);
         if (best_out) *best_out = h;
         if (best_ms_out) *best_ms_out = 0.0;
         return GBA_OK;

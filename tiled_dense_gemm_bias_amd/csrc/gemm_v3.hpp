@@ -81,10 +81,16 @@ __device__ __forceinline__ int aswz(int r, int c) {
 
 // XOR (in 16-byte chunks) of k row r of a B stage. The transposing reads of one
 // instruction touch k rows r0 + {0..3} + 8 {0..3} at one 32-byte column pair;
-// the even XOR moves each of those rows to its own pair slot.
+// the even XOR moves each of those rows to its own pair slot. A 128-byte row
+// (8 chunks, 64 columns) has only 4 pair slots: rows r and r + 2 share a bank
+// half and take different slots by bit 1 of r, rows r and r + 8 by bit 3, so
+// each half-wave's 8 rows (r0 + {0..3} + 8 {0, 1}) fall on distinct banks.
 template <int CHB>
 __device__ __forceinline__ int bswz(int r) {
-    return (2 * (r & 3) + 8 * ((r >> 3) & 3)) & (CHB - 1);
+    if constexpr (CHB == 8)
+        return 4 * ((r >> 1) & 1) + 2 * ((r >> 3) & 1);
+    else
+        return (2 * (r & 3) + 8 * ((r >> 3) & 3)) & (CHB - 1);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LDW, int SPREAD, int MS, int DT,
@@ -117,7 +123,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
     static_assert(KK % 2 == 0, "fragment buffers alternate within a slice");
     static_assert(WTM % BD == 0 && WTN % BD == 0, "wave tile must be whole MFMA blocks");
-    static_assert(TB || BN >= 128, "B swizzle needs at least 16 chunks per row");
+    static_assert(TB || BN >= 64, "B swizzle needs at least 8 chunks per row");
     static_assert(!TB || MS == 16, "transpose_B is written for 16x16x32 MFMAs");
     static_assert(!TA || (MS == 16 && BM >= 128), "transpose_A: 16x16x32 MFMAs, at least 16 chunks per k row");
     static_assert(!TA || (BK * CHT) % NTL == 0, "At slices split evenly");
@@ -394,16 +400,24 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // the step has room): three descriptor pieces, then the NMASK offsets that
     // carry the K mask (the k-th is load MI(k)).
     constexpr int NMASK = (TA ? 0 : A_LD) + (TB ? B_LD : 0);
-    constexpr int PQ = NPF < NMF - 3 - NMASK ? NPF : NMF - 3 - NMASK;
-    static_assert(PQ >= 0, "payload slots inside the step");
+    constexpr int NITEM = 3 + NMASK;
+    constexpr int PQ = NPF < NMF - NITEM ? NPF : (NMF - NITEM > 0 ? NMF - NITEM : 0);
+    // Gap of payload item i (in a step shorter than the payload, several share one).
+    auto item_q = [](int i) { return PQ + NITEM <= NMF ? PQ + i : i * NMF / NITEM; };
     auto MI = [](int k) { return TA ? A_LD + k : k; };
     for (int kt = 0; kt < nk; ++kt) {
         const char *cur_base = smem + (kt % STAGES) * STAGE_BYTES;
         const char *nxt_base = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
         SliceDma dnew;
         auto prep = [&](int q) __attribute__((always_inline)) {
-            if (q >= PQ && q < PQ + 3) dma_part(dnew, q - PQ, kt + STAGES);
-            if (q >= PQ + 3 && q < PQ + 3 + NMASK) set_eo(dnew, MI(q - PQ - 3));
+#pragma unroll
+            for (int i = 0; i < NITEM; ++i) {
+                if (item_q(i) != q) continue;
+                if (i < 3)
+                    dma_part(dnew, i, kt + STAGES);
+                else
+                    set_eo(dnew, MI(i - 3));
+            }
         };
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
