@@ -326,8 +326,8 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
         } else {
             // As in the 16-bit persistent kernel: the wave's 128 x 128 block leaves
             // through two alternating 16 x 64 staging buffers of its own in LDS,
-            // so that each 16-byte store instruction writes 8 whole 128-byte row
-            // segments; the bias is converted to fp32 once per tile (upper half of
+            // so that each 16-byte (non-temporal) store instruction writes 8 whole
+            // 128-byte row segments; the bias is converted to fp32 once per tile (upper half of
             // the wave's slot) and read into registers once per column half.
             int ln;
             asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
@@ -393,7 +393,7 @@ gemm_f8_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ W,
                                 continue;
                             const uint32_t offs = st_off + (uint32_t)(2 * fm + j) * pitch8 +
                                                   (uint32_t)(fh * 128);
-                            *reinterpret_cast<u32x4 *>(Cw + offs) = v[j];
+                            __builtin_nontemporal_store(v[j], reinterpret_cast<u32x4 *>(Cw + offs));
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);

@@ -466,7 +466,8 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         // + bias[n], activation, round once; each group of four 16x16 blocks (one
         // row block fm, one 64-column half fh) goes through the wave's staging
         // buffers and leaves as 16-byte stores of whole 128-byte row segments (8
-        // rows per store instruction). Two buffers alternate so the LDS round trip
+        // rows per store instruction, non-temporal as in the persistent kernel).
+        // Two buffers alternate so the LDS round trip
         // of group g - 1 overlaps the arithmetic of group g. Lane l holds row l % 16
         // and columns 16 fn + 4 (l / 16) .. +3 of the MFMA blocks.
         const int wid_u = __builtin_amdgcn_readfirstlane(wid);
@@ -531,7 +532,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                         if (masked && (fm * BD + 8 * j + rr >= rows_left || fh * 64 + rc * 8 >= cols_left))
                             continue;
                         const uint32_t offs = st_off + (uint32_t)(2 * fm + j) * pitch8 + (uint32_t)(fh * 128);
-                        *reinterpret_cast<u32x4 *>(Cw + offs) = v[j];
+                        __builtin_nontemporal_store(v[j], reinterpret_cast<u32x4 *>(Cw + offs));
                     }
                 }
             }
