@@ -216,12 +216,15 @@ def test_split_k_bitwise_and_equal_to_one_kernel(shape, transpose_b):
     got = run(At, B, bias, "relu", "bf16", transpose_b=transpose_b, ws=ws)
     assert np.array_equal(got, want)
     assert np.array_equal(got, run(At, B, bias, "relu", "bf16", transpose_b=transpose_b))
-    # random inputs: the split's summation order is the [M, K] split's order
+    # random inputs: the split's summation order is the [M, K] split's order at
+    # the same schedule (the [M, K] layout's own choice may be another tile, as
+    # the 64x64 one has no [K, M] form)
     At = synth.random_bits((K, M), "bf16", 7)
     Bb = synth.random_bits((N, K) if transpose_b else (K, N), "bf16", 8, scale=0.05)
     got = run(At, Bb, bias, "gelu", "bf16", transpose_b=transpose_b, ws=ws)
     A = np.ascontiguousarray(At.T)
-    assert np.array_equal(got, run(A, Bb, bias, "gelu", "bf16", transpose_a=False,
+    s = gba.get_schedule(M, N, K, "gelu", "bf16", transpose_b=transpose_b, transpose_a=True)
+    assert np.array_equal(got, run(A, Bb, bias, "gelu", "bf16", sched=s, transpose_a=False,
                                    transpose_b=transpose_b, ws=ws))
     R, S = oracle.gemm_bias_act(At, Bb, bias, "gelu", "bf16", with_abs=True, transpose_a=True,
                                 transpose_b=transpose_b, nthreads=16)

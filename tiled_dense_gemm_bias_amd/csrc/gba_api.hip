@@ -537,23 +537,26 @@ int launch(const gba_schedule &s0, const void *A, const void *B, const void *bia
 // Split-K factor for schedule s: > 1 only for schedules with a split-K first
 // pass, when their tiles leave CUs idle and the split pays for itself. Units
 // (tiles x splits) stay within the CU count, each split keeps at least two K
-// slices, at most 16 splits. Cost model (measured on MI355X with the 128x128
-// schedule): a K slice takes ~0.65 us per tile; the split adds the fp32
-// partials' round trip, 2 S M N 4 bytes at ~4 TB/s, and ~5 us for the second
-// kernel and its launch. Split only if that saves at least 15 %. (At 1024^3 it
-// does not: 19.6 us split against 14.3 us whole; at 256x256x4096 it does.)
+// slices, at most 16 splits. Cost model (measured on MI355X): a K slice takes
+// ~0.65 us per 128x128 tile and ~0.28 us per 64x64 tile (latency-bound); the
+// split adds the fp32 partials' round trip, 2 S M N 4 bytes at ~4 TB/s, and
+// ~5 us for the second kernel and its launch. Split only if that saves at least
+// 15 %. (At 1024^3 it does not: 19.6 us split against 14.3 us whole; at
+// 256x256x4096 it does.) *t_pred: the model's time for the returned factor.
 int split_count(const gba_schedule &s0, int64_t M, int64_t N, int64_t K, int cus, int dtype,
-                int lay) {
+                int lay, double *t_pred = nullptr) {
     const gba_schedule s = effective(s0, K);
     const int i = find_entry(s);
+    const int64_t nk = K > 0 ? (K + s.bk - 1) / s.bk : 0;
+    const double t_slice = (int64_t)s.bm * s.bn <= 64 * 64 ? 0.28e-6 : 0.65e-6;
+    const double bw = 4.0e12, t_fixed = 5.0e-6;
+    const double whole = nk * t_slice;
+    if (t_pred) *t_pred = whole;
     if (i < 0 || !partial_launcher(i, dtype, lay) || K <= 0) return 1;
     const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
-    const int64_t nk = (K + s.bk - 1) / s.bk;
     int64_t smax = tiles > 0 ? cus / tiles : 1;
     smax = std::min<int64_t>(smax, nk / 2);
     smax = std::min<int64_t>(smax, 16);
-    const double t_slice = 0.65e-6, bw = 4.0e12, t_fixed = 5.0e-6;
-    const double whole = nk * t_slice;
     int best = 1;
     double best_t = whole;
     for (int64_t S = 2; S <= smax; ++S) {
@@ -563,7 +566,34 @@ int split_count(const gba_schedule &s0, int64_t M, int64_t N, int64_t K, int cus
             best = (int)S;
         }
     }
-    return best_t < 0.85 * whole ? best : 1;
+    if (best_t < 0.85 * whole) {
+        if (t_pred) *t_pred = best_t;
+        return best;
+    }
+    return 1;
+}
+
+// Schedule and split factor of a call that may split K. The chosen schedule
+// with split_count's factor; but when the built-in choice is the 64x64 tile
+// (few tiles), the 128x128 tile split instead if the model predicts that
+// faster: its fewer tiles leave room for more splits (128x4096x14336: 64x64
+// whole 61 us, 64x64 in 2 splits 45 us, 128x128 in 8 splits 32 us).
+int split_plan(const DeviceInfo &d, int64_t M, int64_t N, int64_t K, int act, int dtype, int lay,
+               gba_schedule *sch, const char **why) {
+    *sch = choose(d, M, N, K, act, dtype, lay, why);
+    double t = 0.0;
+    int S = split_count(*sch, M, N, K, d.cus, dtype, lay, &t);
+    const gba_schedule &small = gba::i_64x64x64_w4x1_s4_l4_p1_m16.sched;
+    if (strcmp(*why, "heuristic") == 0 && sch->bm == small.bm && sch->bn == small.bn) {
+        const gba_schedule alt = gba::i_128x128x64_w2x2_s4_l4_p1_m16.sched;
+        double t2 = 0.0;
+        const int S2 = split_count(alt, M, N, K, d.cus, dtype, lay, &t2);
+        if (S2 > 1 && t2 < t) {
+            *sch = alt;
+            S = S2;
+        }
+    }
+    return S;
 }
 
 template <int DT, int ACT>
@@ -602,15 +632,15 @@ int gemm_common(const void *A, const void *B, const void *bias, void *C, int64_t
     s = current_device(&d);
     if (s) return s;
     const char *why = "";
-    const gba_schedule sch = choose(*d, M, N, K, act, dtype, lay, &why);
     if (ws) {
-        const int S = split_count(sch, M, N, K, d->cus, dtype, lay);
+        gba_schedule ss;
+        const int S = split_plan(*d, M, N, K, act, dtype, lay, &ss, &why);
         if (S > 1 && ws_bytes >= (size_t)S * (size_t)M * (size_t)N * 4u) {
             if (log_enabled())
                 fprintf(stderr, "[gba] M=%lld N=%lld K=%lld act=%s dtype=%s -> split-K %d x k%d %dx%dx%d (%s)\n",
                         (long long)M, (long long)N, (long long)K, kActName[act], kDtName[dtype], S,
-                        sch.kernel, sch.bm, sch.bn, sch.bk, why);
-            const gba_schedule s3 = effective(sch, K);
+                        ss.kernel, ss.bm, ss.bn, ss.bk, why);
+            const gba_schedule s3 = effective(ss, K);
             const gba::PartialLaunchFn pf = partial_launcher(find_entry(s3), dtype, lay);
             hipError_t e = pf(A, B, (float *)ws, (int)M, (int)N, (int)K, S, s3.raster, s3.group_m,
                               t_stream);
@@ -619,6 +649,7 @@ int gemm_common(const void *A, const void *B, const void *bias, void *C, int64_t
             return e == hipSuccess ? GBA_OK : hip_fail(e);
         }
     }
+    const gba_schedule sch = choose(*d, M, N, K, act, dtype, lay, &why);
     if (log_enabled())
         fprintf(stderr,
                 "[gba] M=%lld N=%lld K=%lld act=%s dtype=%s A=%s B=%s -> k%d %dx%dx%d w%dx%d s%d r%d "
@@ -885,8 +916,8 @@ int gemm_bias_act_noalloc(const void *A, const void *B, const void *bias, void *
     if (s) return s;
     // The split this call would make, and whether its partials fit the scratch.
     const char *why;
-    const gba_schedule sch = choose(*d, M, N, K, act, dtype, lay, &why);
-    const int S = split_count(sch, M, N, K, d->cus, dtype, lay);
+    gba_schedule sch;
+    const int S = split_plan(*d, M, N, K, act, dtype, lay, &sch, &why);
     if (S > 1 && (size_t)S * (size_t)M * (size_t)N * 4u > kScratchBytes) return GBA_ERR_SCRATCH;
     return gemm_common(A, B, bias, C, M, N, K, act, dtype, lay, ws, kScratchBytes);
 }
@@ -912,8 +943,8 @@ int gba_workspace_size(int64_t M, int64_t N, int64_t K, int act, int dtype, int 
     }
     const int lay = flags & (GBA_TRANSPOSE_B | GBA_TRANSPOSE_A);
     const char *why;
-    const gba_schedule sch = choose(*d, M, N, K, act, dtype, lay, &why);
-    const int S = split_count(sch, M, N, K, d->cus, dtype, lay);
+    gba_schedule sch;
+    const int S = split_plan(*d, M, N, K, act, dtype, lay, &sch, &why);
     if (S > 1) *bytes = (size_t)S * (size_t)M * (size_t)N * 4u;
     return GBA_OK;
 }
