@@ -396,7 +396,9 @@ def main(argv=None) -> int:
             nb = gba.workspace_size(w.M, w.N, w.K, w.act, w.dtype, transpose_b=tb,
                                     transpose_a=ta)
             ws_t = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
-            sched = dict(sched, splits_workspace_bytes=nb)
+            plan, splits = gba.split_plan(w.M, w.N, w.K, w.act, w.dtype, transpose_b=tb,
+                                          transpose_a=ta)
+            sched = dict(plan, splits=splits, splits_workspace_bytes=nb)
         step = gba.bind_gemm_bias_act(a_t, b_t, bias_t, c_t, w.act, transpose_b=tb, workspace=ws_t,
                                       transpose_a=ta)
     log("[bench] schedule %s%s%s" % (sched, " (A stored [K,M])" if ta else "",

@@ -163,7 +163,7 @@ enum {
  * The result is bitwise that of the [M,K] path on the same schedule with
  * A = At^T: both feed the matrix cores the same operands in the same order. When the chosen schedule's tiles
  * leave compute units idle and K is deep enough for the split to pay for its
- * extra traffic (e.g. 256x256x4096: 4 tiles of 128x128 for 256 CUs; not
+ * extra traffic (e.g. 256x256x4096: 16 tiles of 64x64 for 256 CUs; not
  * 1024^3, where the fp32 partials' round trip costs more than it saves), K is
  * split S ways: a first kernel writes the S fp32 partial sums
  * [S][M][N] into the workspace, and a second adds them in split order and
@@ -188,8 +188,9 @@ int gemm_bias_act_ex(const void *A, const void *B, const void *bias, void *C, in
  * process ends. It calls no allocating routine: the array's address is taken
  * (hipGetSymbolAddress) on the first call on each device. Splits whose
  * partials (S * M * N * 4 bytes) would exceed the array return GBA_ERR_SCRATCH
- * before any launch; with 128 x 128 tiles and at most CUs / tiles splits that
- * bound is never reached on a 256-CU device. The array needs no clearing: the
+ * before any launch; with 64 x 64 or 128 x 128 tiles and at most CUs / tiles
+ * splits the partials take at most CUs * 128 * 128 * 4 bytes, so that bound is
+ * never reached on a 256-CU device. The array needs no clearing: the
  * first pass writes every partial it reads back. All calls on one GPU share
  * the array, so calls that overlap on that GPU (different streams, or
  * different host threads without ordering) race; order them on one stream.
@@ -197,6 +198,17 @@ int gemm_bias_act_ex(const void *A, const void *B, const void *bias, void *C, in
 int gemm_bias_act_noalloc(const void *A, const void *B, const void *bias, void *C, int64_t M,
                           int64_t N, int64_t K, int act, int dtype, int flags);
 size_t gba_noalloc_scratch_bytes(void);
+
+/* The plan of a gemm_bias_act_ex call with these arguments, these
+ * GBA_TRANSPOSE_A / GBA_TRANSPOSE_B flags and a workspace of at least
+ * gba_workspace_size bytes: *splits K ranges computed with the tile schedule
+ * *sched (*splits = 1: one kernel, *sched as gba_get_schedule_ex). The split's
+ * schedule can differ from the one-kernel choice: where the built-in choice is
+ * the 64x64 tile, the 128x128 tile's split is taken when the cost model
+ * predicts it faster. Launches nothing. Errors as gba_get_schedule_ex, and
+ * GBA_ERR_NULL for a NULL output. */
+int gba_split_plan(int64_t M, int64_t N, int64_t K, int act, int dtype, int flags,
+                   gba_schedule *sched, int *splits);
 
 /* Workspace bytes gemm_bias_act_ex (with GBA_INPUT_FP8: gemm_bias_act_fp8_ex)
  * would use for these arguments (0 if it would not split), written to *bytes. */

@@ -137,6 +137,12 @@ def test_ex_and_workspace_argument_errors_precede_device_use(lib):
     assert lib.gba_workspace_size(-1, 64, 64, 0, 0, 0, ctypes.byref(size)) == ERR_SHAPE
     assert lib.gba_workspace_size(0, 64, 64, 0, 0, 0, ctypes.byref(size)) == OK and size.value == 0
     assert lib.gba_workspace_size(64, 64, 64, 0, 0, 0, None) == ERR_NULL
+    sch, splits = gba.Schedule(), ctypes.c_int(7)
+    assert lib.gba_split_plan(64, 64, 64, 0, 0, 0, None, ctypes.byref(splits)) == ERR_NULL
+    assert lib.gba_split_plan(64, 64, 64, 0, 0, 0, ctypes.byref(sch), None) == ERR_NULL
+    assert lib.gba_split_plan(64, 64, 64, 0, 0, 2, ctypes.byref(sch), ctypes.byref(splits)) == ERR_SHAPE
+    assert lib.gba_split_plan(64, -1, 64, 0, 0, 0, ctypes.byref(sch), ctypes.byref(splits)) == ERR_SHAPE
+    assert lib.gba_split_plan(64, 64, 64, 6, 0, 0, ctypes.byref(sch), ctypes.byref(splits)) == ERR_ACT
 
 
 def test_transpose_a_argument_errors_precede_device_use(lib):

@@ -127,6 +127,22 @@ def test_small_workspace_falls_back_and_large_shapes_do_not_split():
     assert gba.workspace_size(0, 1024, 1024, "gelu", "f16") == 0
 
 
+@pytest.mark.parametrize("shape,tile,split", [
+    ((128, 4096, 14336), 128, True),    # 64x64 whole 60 us, 128x128 in 8 splits 31 us
+    ((256, 256, 4096), 64, True),       # 64x64 split beats 128x128 split
+    ((520, 776, 3000), 64, False),      # 64x64 whole beats either split
+    ((4096, 4096, 4096), 256, False)])
+def test_split_plan_agrees_with_workspace_size(shape, tile, split):
+    M, N, K = shape
+    s, S = gba.split_plan(M, N, K, "gelu", "bf16")
+    nb = gba.workspace_size(M, N, K, "gelu", "bf16")
+    assert (S > 1) == split and s["bm"] == tile
+    assert nb == (S * M * N * 4 if S > 1 else 0)
+    if S == 1:
+        assert s == gba.get_schedule(M, N, K, "gelu", "bf16")
+    say("split plan", shape, s["bm"], S)
+
+
 def test_workspace_argument_errors():
     import torch
     a = torch.zeros(64, 64, dtype=torch.float16, device="cuda")

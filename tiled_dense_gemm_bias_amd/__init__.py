@@ -72,6 +72,8 @@ def _lib():
             "gemm_bias_act_fp8_ex": [p, p, p, p, i64, i64, i64, ctypes.c_float, ci, ci, ci, p,
                                      ctypes.c_size_t],
             "gba_workspace_size": [i64, i64, i64, ci, ci, ci, ctypes.POINTER(ctypes.c_size_t)],
+            "gba_split_plan": [i64, i64, i64, ci, ci, ci, ctypes.POINTER(Schedule),
+                               ctypes.POINTER(ci)],
             "bias_act": [p, p, p, i64, i64, ci, ci],
             "gba_set_stream": [p],
             "gba_set_schedule": [ctypes.POINTER(Schedule)],
@@ -270,6 +272,21 @@ def workspace_size(M: int, N: int, K: int, act="gelu", dtype="f16", transpose_b=
     if st != 0:
         raise GbaError(st, "gba_workspace_size")
     return int(out.value)
+
+
+def split_plan(M: int, N: int, K: int, act="gelu", dtype="f16", transpose_b=False,
+               transpose_a=False):
+    """(schedule dict, splits) of a gemm_bias_act call with a workspace of
+    workspace_size(...) bytes: K split `splits` ways on that schedule's tiles
+    (splits 1: one kernel, the get_schedule choice)."""
+    sched = Schedule()
+    splits = ctypes.c_int()
+    st = _lib().gba_split_plan(M, N, K, _act(act), 0 if dtype in ("f16", "float16") else 1,
+                               _layout_flags(transpose_a, transpose_b), ctypes.byref(sched),
+                               ctypes.byref(splits))
+    if st != 0:
+        raise GbaError(st, "gba_split_plan")
+    return sched.as_dict(), int(splits.value)
 
 
 def bind_gemm_bias_act(a, b, bias, c, act="gelu", transpose_b=False, workspace=None,

@@ -874,6 +874,29 @@ int gba_get_schedule_ex(int64_t M, int64_t N, int64_t K, int act, int dtype, int
     return get_schedule(M, N, K, act, dtype, flags & (GBA_TRANSPOSE_B | GBA_TRANSPOSE_A), out);
 }
 
+int gba_split_plan(int64_t M, int64_t N, int64_t K, int act, int dtype, int flags,
+                   gba_schedule *sched, int *splits) {
+    if (!sched || !splits) return GBA_ERR_NULL;
+    if (flags & ~(GBA_TRANSPOSE_B | GBA_TRANSPOSE_A)) return GBA_ERR_SHAPE;
+    int s = check_enums(act, dtype);
+    if (s) return s;
+    if (M < 0 || N < 0 || K < 0) return GBA_ERR_SHAPE;
+    const DeviceInfo *d;
+    s = current_device(&d);
+    if (s) return s;
+    const char *why;
+    int S = 1;
+    gba_schedule sch;
+    if (M > 0 && N > 0) S = split_plan(*d, M, N, K, act, dtype, flags, &sch, &why);
+    if (S <= 1) {
+        S = 1;
+        sch = choose(*d, M, N, K, act, dtype, flags, &why);
+    }
+    *sched = sch;
+    *splits = S;
+    return GBA_OK;
+}
+
 int gemm_bias_act(const void *A, const void *B, const void *bias, void *C, int64_t M, int64_t N,
                   int64_t K, int act, int dtype) {
     return gemm_common(A, B, bias, C, M, N, K, act, dtype, 0);
