@@ -6,8 +6,9 @@ them deep enough in K to split), activation, dtype, operand layouts
 in 3 of 10 cases a forced schedule from the compiled-in table (skipped when
 that kernel has no path for the layouts). Bar: the oracle's tolerance and the
 strict accumulation gate on 48 sampled rows (always rows 0 and M-1), and a
-NaN sentinel in C that every element must overwrite. The case list is fixed
-by the seed, so a failure names a reproducible case.
+NaN sentinel in C that every element must overwrite. The 8-bit entry point
+gets its own cases (format, output dtype, activation, bias, workspace). The
+case lists are fixed by their seeds, so a failure names a reproducible case.
 """
 import numpy as np
 import pytest
@@ -85,4 +86,49 @@ def test_random_case(c):
                                 transpose_b=tb, transpose_a=ta, nthreads=16)
     rep = compare.check(oracle.decode(got[rows], dtype), R, K=K, dtype=dtype,
                         act=oracle.ACTS[act], S=S)
+    assert rep["ok"] and rep["strict_ok"], rep
+
+
+N_CASES_FP8 = 40
+
+
+def _cases_fp8():
+    rng = np.random.default_rng(2025)
+    out = []
+    for i in range(N_CASES_FP8):
+        M = int(rng.integers(1, 1500))
+        N = int(rng.integers(1, 190)) * 8
+        K = int(rng.integers(1, 400)) * 16
+        if rng.random() < 0.3:
+            K = int(rng.integers(400, 1000)) * 16
+        out.append(dict(i=i, M=M, N=N, K=K, fmt="e4m3" if rng.random() < 0.5 else "e5m2",
+                        dtype="f16" if rng.random() < 0.5 else "bf16",
+                        act=ACTS[int(rng.integers(0, 6))], bias=bool(rng.random() < 0.8),
+                        ws=bool(rng.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("c", _cases_fp8(), ids=lambda c: "fp8case%d" % c["i"])
+def test_random_case_fp8(c):
+    """8-bit inputs (per-tensor scaled onto the format's range), W stored [N,K]:
+    the oracle's tolerance and the 8-bit strict gate on 48 sampled rows."""
+    import torch
+    M, N, K, fmt, dtype, act = c["M"], c["N"], c["K"], c["fmt"], c["dtype"], c["act"]
+    w = synth.Fp8Workload("r%d" % c["i"], M, N, K, fmt, dtype, act, c["bias"], 5000 + c["i"])
+    A, W, bias, scale = synth.make_inputs_fp8(w)
+    out = empty((M, N), dtype, fill_bits=0x7E00)
+    ws = None
+    if c["ws"]:
+        nb = gba.workspace_size(M, N, K, act, dtype, fp8=True)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda") if nb else None
+    say("random fp8 case", c)
+    gba.gemm_bias_act_fp8(torch.from_numpy(A).cuda(), torch.from_numpy(W).cuda(),
+                          to_dev(bias, dtype), out, scale, act, fmt, workspace=ws)
+    torch.cuda.synchronize()
+    got = to_bits(out)
+    rows = synth.sample_rows(M, 48, c["i"])
+    R, S = oracle.gemm_bias_act_fp8(A, W, bias, scale, act, fmt, dtype, rows=rows,
+                                    with_abs=True, nthreads=16)
+    rep = compare.check(oracle.decode(got[rows], dtype), R, K=K, dtype=dtype,
+                        act=oracle.ACTS[act], S=S, sum_rel=compare.fp8_sum_rel(K))
     assert rep["ok"] and rep["strict_ok"], rep
