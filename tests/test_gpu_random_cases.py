@@ -5,8 +5,9 @@ them deep enough in K to split), activation, dtype, operand layouts
 (transpose_A / transpose_B), bias or none, a split-K workspace or none, and
 in 3 of 10 cases a forced schedule from the compiled-in table (skipped when
 that kernel has no path for the layouts). Bar: the oracle's tolerance and the
-strict accumulation gate on 48 sampled rows (always rows 0 and M-1), and a
-NaN sentinel in C that every element must overwrite. The 8-bit entry point
+strict accumulation gate on 48 sampled rows (always rows 0 and M-1), a NaN
+sentinel in C that every element must overwrite, and a guard region past C
+that must keep it. The 8-bit entry point
 gets its own cases (format, output dtype, activation, bias, workspace). The
 case lists are fixed by their seeds, so a failure names a reproducible case.
 """
@@ -45,6 +46,20 @@ def _cases():
     return out
 
 
+GUARD = 8192   # elements past C that must keep their fill
+
+
+def guarded(M, N, dtype):
+    """A NaN-filled flat buffer and its leading (M, N) view."""
+    flat = empty((M * N + GUARD,), dtype, fill_bits=0x7E00)
+    return flat, flat[: M * N].view(M, N)
+
+
+def check_guard(flat, M, N):
+    g = to_bits(flat[M * N:])
+    assert bool((g == 0x7E00).all()), "write past the end of C"
+
+
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     torch = pytest.importorskip("torch")
@@ -63,7 +78,7 @@ def test_random_case(c):
     A = synth.random_bits((K, M) if ta else (M, K), dtype, 1000 + c["i"])
     B = synth.random_bits((N, K) if tb else (K, N), dtype, 2000 + c["i"], scale=1.0 / np.sqrt(K))
     bias = synth.random_bits((N,), dtype, 3000 + c["i"]) if c["bias"] else None
-    out = empty((M, N), dtype, fill_bits=0x7E00)
+    flat, out = guarded(M, N, dtype)
     say("random case", c, sched)
     gba.set_schedule(sched)
     try:
@@ -87,6 +102,8 @@ def test_random_case(c):
     rep = compare.check(oracle.decode(got[rows], dtype), R, K=K, dtype=dtype,
                         act=oracle.ACTS[act], S=S)
     assert rep["ok"] and rep["strict_ok"], rep
+    assert not (got == 0x7E00).any(), "an element of C was not written"
+    check_guard(flat, M, N)
 
 
 N_CASES_FP8 = 40
@@ -116,7 +133,7 @@ def test_random_case_fp8(c):
     M, N, K, fmt, dtype, act = c["M"], c["N"], c["K"], c["fmt"], c["dtype"], c["act"]
     w = synth.Fp8Workload("r%d" % c["i"], M, N, K, fmt, dtype, act, c["bias"], 5000 + c["i"])
     A, W, bias, scale = synth.make_inputs_fp8(w)
-    out = empty((M, N), dtype, fill_bits=0x7E00)
+    flat, out = guarded(M, N, dtype)
     ws = None
     if c["ws"]:
         nb = gba.workspace_size(M, N, K, act, dtype, fp8=True)
@@ -132,3 +149,5 @@ def test_random_case_fp8(c):
     rep = compare.check(oracle.decode(got[rows], dtype), R, K=K, dtype=dtype,
                         act=oracle.ACTS[act], S=S, sum_rel=compare.fp8_sum_rel(K))
     assert rep["ok"] and rep["strict_ok"], rep
+    assert not (got == 0x7E00).any(), "an element of C was not written"
+    check_guard(flat, M, N)
