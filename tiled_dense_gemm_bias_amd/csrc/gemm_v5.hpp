@@ -388,7 +388,7 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // into the MFMA stream's shadow (a wave issues only a few instructions
     // between two MFMAs without delaying the second).
     constexpr int PQ = NPF + NBASE + 2;
-    static_assert(PQ + 6 < NMF, "payload slots inside the step");
+    static_assert(PQ + 8 < NMF, "payload slots inside the step");
     auto step = [&](int cur, auto reads_c, int pf_kk, auto move_c, int delta, auto dma_c,
                     uint32_t lds_stage, const SliceDma &d, auto &&payload) __attribute__((always_inline)) {
         constexpr bool READS = decltype(reads_c)::value;
@@ -482,28 +482,28 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             auto prep = [&](auto q_c) __attribute__((always_inline)) {
                 constexpr int q = decltype(q_c)::value;
                 if constexpr (q == PQ) {
-                    // The position's tile edges (uniform branch, taken once per
-                    // tile). The loads that used the old offsets were issued a
-                    // step earlier.
-                    if (__builtin_expect((!here) & (k2 == 0) & nxt_live, 0)) {
-                        if constexpr (!TB) set_bv(nxt_t.n0);
-                        if constexpr (TA) set_tv(nxt_t.m0);
-                    }
-                } else if constexpr (q == PQ + 2) {
-                    // Whether it is the partial last slice.
-                    if (__builtin_expect((k2 == tail_k) != (k1 == tail_k), 0)) set_av(k2 == tail_k);
-                } else if constexpr (q == PQ + 4) {
-                    // The first or partial last slice of a tile, or a dead
-                    // position: from scratch (a few times per tile); otherwise
-                    // one step on.
-                    if (__builtin_expect((k2 == 0) | (k2 == tail_k) | !(here | nxt_live), 0))
-                        pos = pos_full(here ? cur_t : nxt_t, here | nxt_live, k2);
-                    else
-                        pos_next(pos);
+                    // One step on along K: all a tile's slices but its last
+                    // three load the next slice of the same tile, full.
+                    pos_next(pos);
                     asm volatile("" : "+s"(pos.pa), "+s"(pos.pb), "+s"(pos.na), "+s"(pos.nb));
-                } else if constexpr (q == PQ + 6) {
+                } else if constexpr (q == PQ + 4) {
+                    // Near a tile's end (position kt+2 is the tile's partial last
+                    // slice, the next tile's first, or past the last tile): the
+                    // tile edges, the K-tail mask and the position from scratch,
+                    // in one rarely taken block.
+                    if (__builtin_expect(kt + 3 >= nk, 0)) {
+                        if ((!here) & (k2 == 0) & nxt_live) {
+                            if constexpr (!TB) set_bv(nxt_t.n0);
+                            if constexpr (TA) set_tv(nxt_t.m0);
+                        }
+                        if ((k2 == tail_k) != (k1 == tail_k)) set_av(k2 == tail_k);
+                        if ((k2 == 0) | (k2 == tail_k) | !(here | nxt_live))
+                            pos = pos_full(here ? cur_t : nxt_t, here | nxt_live, k2);
+                        bias_next = (bias != nullptr) & (!here) & (k2 == 0) & nxt_live;
+                    }
+                    asm volatile("" : "+s"(pos.pa), "+s"(pos.pb), "+s"(pos.na), "+s"(pos.nb));
+                } else if constexpr (q == PQ + 8) {
                     dn = make_dma(pos);
-                    bias_next = (bias != nullptr) & (!here) & (k2 == 0) & nxt_live;
                     // Formed here, in the MFMA shadow, not at their first use
                     // after the barrier.
                     asm volatile("" : "+s"(dn.ra), "+s"(dn.rb));
