@@ -395,7 +395,11 @@ gemm_v5_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         constexpr bool MOVE = decltype(move_c)::value, DMA = decltype(dma_c)::value;
         static_for<NMF>([&](auto q_c) __attribute__((always_inline)) {
             constexpr int q = decltype(q_c)::value;
-            constexpr int fn = q / FM, fm = q % FM;
+            // Column block outer, row blocks in alternating direction, so that
+            // consecutive MFMAs share an operand across the column-block change
+            // as well (0.3-0.8 % faster than restarting each column at row 0,
+            // same results: every accumulator still gets one MFMA per step).
+            constexpr int fn = q / FM, fm = (fn & 1) ? FM - 1 - q % FM : q % FM;
             u32x4 bop;
             if constexpr (TB)
                 bop = fw[cur][fn];
