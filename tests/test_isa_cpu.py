@@ -195,3 +195,29 @@ def test_persistent_main_loop_keeps_accumulators_in_place(kernels):
         assert not bad, (name, sorted(set(bad)))
         seen += 1
     assert seen >= 40
+
+
+def test_tile_kernel_main_loops_keep_accumulators_in_place(kernels):
+    """In kernel 3's first slice (2 steps of (BM/WM/16) x (BN/WN/16) 16x16x32
+    MFMAs per wave, the main loop) no accumulator is read, copied or rewritten
+    (v_accvgpr_*): split-K first passes and fused instances alike. A register
+    allocation that moves accumulators between register files there costs
+    every slice (the split-K pass once did 96 such moves per slice)."""
+    meta, _, seq = kernels
+    seen = 0
+    for name in meta:
+        if _kind(name) != "gemm_v3_kernel":
+            continue
+        a = _targs(name)
+        bm, bn, wm, wn, ms = a[0], a[1], a[3], a[4], a[8]
+        if ms != 16:
+            continue
+        per_slice = 2 * (bm // wm // 16) * (bn // wn // 16)
+        ops = seq[name]
+        mf = [i for i, op in enumerate(ops) if op.startswith("v_mfma")]
+        assert len(mf) >= per_slice, name
+        loop = ops[mf[0]:mf[per_slice - 1]]
+        bad = [op for op in loop if op.startswith(("v_accvgpr", "scratch_"))]
+        assert not bad, (name, sorted(set(bad)))
+        seen += 1
+    assert seen >= 40

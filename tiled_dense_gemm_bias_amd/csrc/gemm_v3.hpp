@@ -456,7 +456,13 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             for (int fm = 0; fm < FM; ++fm) {
                 const int r = prow + fm * BD;
                 if (m0 + r >= M) continue;
-                *reinterpret_cast<f32x4 *>(Pt + (size_t)r * N + cn) = acc[fn][fm];
+                // Through a vector-register copy, as the fused epilogue reads
+                // them: stored straight from the accumulators, the register
+                // allocator moved accumulators between register files in every
+                // slice of the main loop (96 moves per slice at 128x128).
+                f32x4 v = acc[fn][fm];
+                asm volatile("" : "+v"(v));
+                *reinterpret_cast<f32x4 *>(Pt + (size_t)r * N + cn) = v;
             }
         }
         return;
