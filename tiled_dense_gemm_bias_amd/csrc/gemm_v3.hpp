@@ -278,6 +278,50 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             buffer_load_lds16(d.rb, o, d.lb + (i - A_LD) * NTL * 16);
     };
 
+    // In the main loop of the [M,K]-A, one-pass instances a slice's corners and
+    // ranges are carried from the slice loaded before it (DmaPos): from one full
+    // slice to the next they move by a constant along K, so only the last slice,
+    // and slices past the last, are formed from scratch (with the K-tail
+    // offsets).
+    struct DmaPos {
+        const uint16_t *pa, *pb;
+        uint32_t na, nb;
+    };
+    auto pos_full = [&](int kt) __attribute__((always_inline)) {
+        const int k0 = (kt0 + kt) * BK;
+        const bool live = PARTIAL ? kt < nk : k0 < K;
+        DmaPos p;
+        if constexpr (TA) {
+            p.na = live ? (uint32_t)min(K - k0, BK) * (uint32_t)M * 2u : 0u;
+            p.pa = A + (size_t)(live ? k0 : 0) * M + m0;
+        } else {
+            p.na = live ? (uint32_t)rows_a * (uint32_t)K * 2u - (uint32_t)k0 * 2u : 0u;
+            p.pa = A + (size_t)m0 * K + (live ? k0 : 0);
+        }
+        if constexpr (TB) {
+            p.nb = live ? (uint32_t)rows_b * (uint32_t)K * 2u - (uint32_t)k0 * 2u : 0u;
+            p.pb = B + (size_t)n0 * K + (live ? k0 : 0);
+        } else {
+            p.nb = live ? (uint32_t)min(K - k0, BK) * (uint32_t)N * 2u : 0u;
+            p.pb = B + (size_t)(live ? k0 : 0) * N + n0;
+        }
+        return p;
+    };
+    auto pos_next = [&](DmaPos &p) __attribute__((always_inline)) {
+        if constexpr (TA) {
+            p.pa += (size_t)BK * M;
+        } else {
+            p.pa += BK;
+            p.na -= 2u * BK;
+        }
+        if constexpr (TB) {
+            p.pb += BK;
+            p.nb -= 2u * BK;
+        } else {
+            p.pb += (size_t)BK * N;
+        }
+    };
+
     // Fragment reads for MFMA step kk of a stage.
     const int lhalf = lane >> 5;
     const int tg = lane >> 4, tj = lane & 15;
@@ -390,6 +434,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             for (int i = 0; i < LD; ++i) dma_one(d, i);
         }
     }
+    DmaPos pos = pos_full(STAGES - 1);   // the slice loaded last (CARRY)
     wait_vmcnt<(STAGES - 1) * LD>();
     block_barrier();
 #pragma unroll
@@ -397,10 +442,16 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 
     // The step before the barrier forms the descriptors and offsets of slice
     // kt+STAGES in its shadow, from MFMA PQ on (after its fragment reads where
-    // the step has room): three descriptor pieces, then the NMASK offsets that
-    // carry the K mask (the k-th is load MI(k)).
+    // the step has room). With CARRY: three pieces, the position one slice on;
+    // near the end (slice kt+STAGES is the last or past it) the position from
+    // scratch and the K-tail offsets, in one rarely taken block; the
+    // descriptors. Otherwise three descriptor pieces from scratch, then the
+    // NMASK offsets that carry the K mask (the k-th is load MI(k)). (Carrying
+    // the position measured 2-6 % faster for the [M,K]-A one-pass instances
+    // and 2-3 % slower for the split-K pass and the [K,M]-A instances.)
+    constexpr bool CARRY = !TA && !PARTIAL;
     constexpr int NMASK = (TA ? 0 : A_LD) + (TB ? B_LD : 0);
-    constexpr int NITEM = 3 + NMASK;
+    constexpr int NITEM = CARRY ? 3 : 3 + NMASK;
     constexpr int PQ = NPF < NMF - NITEM ? NPF : (NMF - NITEM > 0 ? NMF - NITEM : 0);
     // Gap of payload item i (in a step shorter than the payload, several share one).
     auto item_q = [](int i) { return PQ + NITEM <= NMF ? PQ + i : i * NMF / NITEM; };
@@ -413,10 +464,35 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 #pragma unroll
             for (int i = 0; i < NITEM; ++i) {
                 if (item_q(i) != q) continue;
-                if (i < 3)
-                    dma_part(dnew, i, kt + STAGES);
-                else
-                    set_eo(dnew, MI(i - 3));
+                if constexpr (!CARRY) {
+                    if (i < 3)
+                        dma_part(dnew, i, kt + STAGES);
+                    else
+                        set_eo(dnew, MI(i - 3));
+                } else if (i == 0) {
+                    pos_next(pos);
+                    asm volatile("" : "+s"(pos.pa), "+s"(pos.pb), "+s"(pos.na), "+s"(pos.nb));
+                } else if (i == 1) {
+                    if (__builtin_expect(kt + STAGES + 1 >= nk, 0)) {
+                        const int kn = kt + STAGES;
+                        pos = pos_full(kn);
+                        const int k0n = (kt0 + kn) * BK;
+#pragma unroll
+                        for (int j = 0; j < LD; ++j)
+                            if (masked(j)) eo[j] = k0n + a_k[j] < K ? off[j] : kOobOffset;
+                    }
+                    asm volatile("" : "+s"(pos.pa), "+s"(pos.pb), "+s"(pos.na), "+s"(pos.nb));
+#pragma unroll
+                    for (int j = 0; j < LD; ++j)
+                        if (masked(j)) asm volatile("" : "+v"(eo[j]));
+                } else {
+                    dnew.la = __builtin_amdgcn_readfirstlane(
+                        smem_lds + (uint32_t)((kt % STAGES) * STAGE_BYTES + wid_s * 64 * 16));
+                    dnew.lb = dnew.la + A_BYTES;
+                    dnew.ra = make_rsrc(pos.pa, pos.na);
+                    dnew.rb = make_rsrc(pos.pb, pos.nb);
+                    asm volatile("" : "+s"(dnew.ra), "+s"(dnew.rb), "+s"(dnew.la), "+s"(dnew.lb));
+                }
             }
         };
 #pragma unroll
