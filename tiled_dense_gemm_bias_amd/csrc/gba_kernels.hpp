@@ -27,6 +27,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <utility>
 #include <stdint.h>
 
 namespace gba {
@@ -76,6 +77,16 @@ inline hipError_t current_cus(int *cus) {
     }
     *cus = c;
     return hipSuccess;
+}
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, unrolled at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_seq(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 // ---------------------------------------------------------------- scalars --

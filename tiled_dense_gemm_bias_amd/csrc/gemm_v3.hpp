@@ -456,9 +456,13 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // Gap of payload item i (in a step shorter than the payload, several share one).
     auto item_q = [](int i) { return PQ + NITEM <= NMF ? PQ + i : i * NMF / NITEM; };
     auto MI = [](int k) { return TA ? A_LD + k : k; };
-    for (int kt = 0; kt < nk; ++kt) {
-        const char *cur_base = smem + (kt % STAGES) * STAGE_BYTES;
-        const char *nxt_base = smem + ((kt + 1) % STAGES) * STAGE_BYTES;
+    // Slice kt in stage S = kt % STAGES, a compile-time constant in each of the
+    // STAGES copies of the slice below: the fragment reads then address their
+    // stage with constant offsets, not with per-slice address arithmetic.
+    auto slice = [&](int kt, auto s_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        const char *cur_base = smem + S * STAGE_BYTES;
+        const char *nxt_base = smem + ((S + 1) % STAGES) * STAGE_BYTES;
         SliceDma dnew;
         auto prep = [&](int q) __attribute__((always_inline)) {
 #pragma unroll
@@ -487,7 +491,7 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                         if (masked(j)) asm volatile("" : "+v"(eo[j]));
                 } else {
                     dnew.la = __builtin_amdgcn_readfirstlane(
-                        smem_lds + (uint32_t)((kt % STAGES) * STAGE_BYTES + wid_s * 64 * 16));
+                        smem_lds + (uint32_t)(S * STAGE_BYTES + wid_s * 64 * 16));
                     dnew.lb = dnew.la + A_BYTES;
                     dnew.ra = make_rsrc(pos.pa, pos.na);
                     dnew.rb = make_rsrc(pos.pb, pos.nb);
@@ -515,6 +519,12 @@ gemm_v3_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                     step(cur, nxt_base, 0, false, dnew, 0, 0, no_payload);
             }
         }
+    };
+    for (int kb = 0; kb < nk; kb += STAGES) {
+        static_for<STAGES>([&](auto s_c) __attribute__((always_inline)) {
+            constexpr int S = decltype(s_c)::value;
+            if (S == 0 || kb + S < nk) slice(kb + S, s_c);
+        });
     }
     // No direct-to-LDS write may outlive the workgroup's LDS.
     wait_vmcnt<0>();

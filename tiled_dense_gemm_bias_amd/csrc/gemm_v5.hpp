@@ -39,15 +39,6 @@
 
 namespace gba {
 
-// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, unrolled at compile time.
-template <class F, int... I>
-__device__ __forceinline__ void static_for_seq(F &&f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-    static_for_seq(f, std::make_integer_sequence<int, N>{});
-}
 
 // This lane's index in its wave, read afresh (volatile: not merged with earlier
 // reads, so no register has to hold it across the loops).
