@@ -56,7 +56,7 @@ def int_inputs(M, N, K, dtype, seed, transpose_b):
 
 
 # Deep K with few output tiles: the shapes the split is for (ragged M, N and K tails).
-SPLIT_SHAPES = [(256, 256, 4096), (300, 264, 8008), (129, 136, 2056), (520, 776, 6000),
+SPLIT_SHAPES = [(256, 256, 4096), (300, 264, 8008), (129, 136, 4104), (520, 776, 6000),
                 (64, 1024, 6144)]
 
 

@@ -538,18 +538,20 @@ int launch(const gba_schedule &s0, const void *A, const void *B, const void *bia
 // pass, when their tiles leave CUs idle and the split pays for itself. Units
 // (tiles x splits) stay within the CU count, each split keeps at least two K
 // slices, at most 16 splits. Cost model (measured on MI355X): a K slice takes
-// ~0.65 us per 128x128 tile and ~0.28 us per 64x64 tile (latency-bound); the
+// ~0.37 us per 128x128 tile and ~0.22 us per 64x64 tile (latency-bound); the
 // split adds the fp32 partials' round trip, 2 S M N 4 bytes at ~4 TB/s, and
-// ~5 us for the second kernel and its launch. Split only if that saves at least
-// 15 %. (At 1024^3 it does not: 19.6 us split against 14.3 us whole; at
-// 256x256x4096 it does.) *t_pred: the model's time for the returned factor.
+// ~6 us for the second kernel, its launch and the first pass's short units.
+// Split only if that saves at least 15 %. (At 1024^3 it does not; at
+// 256x256x4096 it does: 11.3 us split against 14.7 us whole; at 129x136x2056
+// it does not: 10.1 us split against 9.6 us whole.) *t_pred: the model's time
+// for the returned factor.
 int split_count(const gba_schedule &s0, int64_t M, int64_t N, int64_t K, int cus, int dtype,
                 int lay, double *t_pred = nullptr) {
     const gba_schedule s = effective(s0, K);
     const int i = find_entry(s);
     const int64_t nk = K > 0 ? (K + s.bk - 1) / s.bk : 0;
-    const double t_slice = (int64_t)s.bm * s.bn <= 64 * 64 ? 0.28e-6 : 0.65e-6;
-    const double bw = 4.0e12, t_fixed = 5.0e-6;
+    const double t_slice = (int64_t)s.bm * s.bn <= 64 * 64 ? 0.22e-6 : 0.37e-6;
+    const double bw = 4.0e12, t_fixed = 6.0e-6;
     const double whole = nk * t_slice;
     if (t_pred) *t_pred = whole;
     if (i < 0 || !partial_launcher(i, dtype, lay) || K <= 0) return 1;
@@ -577,7 +579,7 @@ int split_count(const gba_schedule &s0, int64_t M, int64_t N, int64_t K, int cus
 // with split_count's factor; but when the built-in choice is the 64x64 tile
 // (few tiles), the 128x128 tile split instead if the model predicts that
 // faster: its fewer tiles leave room for more splits (128x4096x14336: 64x64
-// whole 61 us, 64x64 in 2 splits 45 us, 128x128 in 8 splits 32 us).
+// whole 50 us, 64x64 in 2 splits 33 us, 128x128 in 8 splits 28 us).
 int split_plan(const DeviceInfo &d, int64_t M, int64_t N, int64_t K, int act, int dtype, int lay,
                gba_schedule *sch, const char **why) {
     *sch = choose(d, M, N, K, act, dtype, lay, why);
