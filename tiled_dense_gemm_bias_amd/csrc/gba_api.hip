@@ -196,18 +196,31 @@ long long lds_bytes(const gba_schedule &s) {
 }
 
 // Built-in choice when neither a forced schedule nor a cached one applies:
-// the largest tile that still gives every CU about one tile; at 256x256 the
-// persistent kernel (same tile and loop as kernel 3, measured 1-2% faster with
-// one tile per CU and 4-6% faster with several).
+// for shapes that fill the CUs, 256x256 tiles on the persistent kernel (same
+// tile and loop as kernel 3, measured 1-2% faster with one tile per CU and
+// 4-6% faster with several) or 256x128 / 128x256 tiles, by rounds of tiles;
+// below that the largest tile that still gives every CU about one tile.
 gba_schedule heuristic(int64_t M, int64_t N, int cus, int lay) {
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    auto rounds = [&](int64_t t) { return (double)((t + cus - 1) / cus); };
     const int64_t want = (int64_t)cus * 9 / 10;
+    const ScheduleEntry *half =
+        M >= N ? &gba::i_256x128x64_w2x2_s3_l4_p1_m16 : &gba::i_128x256x64_w2x2_s3_l4_p1_m16;
+    const int64_t t_full = tiles(256, 256), t_half = tiles(half->sched.bm, half->sched.bn);
     const ScheduleEntry *e;
-    if (tiles(256, 256) >= want)
-        e = &gba::p_256x256x64_w2x2;   // persistent: streams several tiles per CU
-    else if (tiles(256, 128) >= want)
-        e = M >= N ? &gba::i_256x128x64_w2x2_s3_l4_p1_m16 : &gba::i_128x256x64_w2x2_s3_l4_p1_m16;
-    else if (2 * tiles(128, 128) > cus || (lay & LAY_TA))   // 64x64 has no (K,M) A path
+    if (t_full >= want || t_half >= want) {
+        // Whichever finishes in less time by rounds of one tile per CU: a
+        // 256x256 round costs 1 (0.95 from the second round on, where the
+        // persistent kernel overlaps each epilogue with the next tile), a
+        // 256x128 round 0.58 (measured 0.53-0.62 of a 256x256 round). So 1.25
+        // or 1.5 rounds of 256x256 tiles (4096x5120, 6144x4096: 2 rounds) lose
+        // to 3 rounds of half tiles (8-18 % faster measured), 1.56 rounds
+        // (5120x5120) do not, nor does 0.75 of a round (3072x4096: 256x256
+        // 25 % faster than 2 rounds of half tiles).
+        const double r_full = rounds(t_full) * (rounds(t_full) >= 2 ? 0.95 : 1.0);
+        const double r_half = rounds(t_half) * 0.58;
+        e = r_full <= r_half ? &gba::p_256x256x64_w2x2 : half;
+    } else if (2 * tiles(128, 128) > cus || (lay & LAY_TA))   // 64x64 has no (K,M) A path
         e = &gba::i_128x128x64_w2x2_s4_l4_p1_m16;   // 4 stages: 10-20 % faster than 3 here
     else
         // 128x128 tiles would leave half the CUs or more idle: 4x the tiles
