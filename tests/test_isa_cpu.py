@@ -221,3 +221,26 @@ def test_tile_kernel_main_loops_keep_accumulators_in_place(kernels):
         assert not bad, (name, sorted(set(bad)))
         seen += 1
     assert seen >= 40
+
+
+def test_fp8_main_loops_keep_accumulators_in_place(kernels):
+    """The 8-bit persistent kernel's two slice bodies in the code (a tile's
+    first slice, whose MFMAs start from zero, and the steady slice: 64
+    16x16x128 MFMAs per wave each) neither copy nor rewrite an accumulator
+    (v_accvgpr_mov / v_accvgpr_write) nor touch scratch, for every format,
+    output dtype, activation and split-K first pass."""
+    meta, _, seq = kernels
+    seen = 0
+    for name in meta:
+        if _kind(name) != "gemm_f8_kernel":
+            continue
+        ops = seq[name]
+        mf = [i for i, op in enumerate(ops) if op.startswith("v_mfma")]
+        assert len(mf) >= 128, name
+        for lo, hi in ((0, 63), (64, 127)):
+            body = ops[mf[lo]:mf[hi]]
+            assert sum(op.startswith("v_mfma") for op in body) == hi - lo, name
+            bad = [op for op in body if op.startswith(("v_accvgpr_mov", "v_accvgpr_write", "scratch_"))]
+            assert not bad, (name, lo, sorted(set(bad)))
+        seen += 1
+    assert seen >= 26
