@@ -82,3 +82,51 @@ def test_noalloc_without_split_and_errors():
                                      64) == 2   # unknown flag bit
     assert lib.gemm_bias_act_noalloc(a.data_ptr(), b.data_ptr(), None, c.data_ptr(), M, N, 12, 1, 0,
                                      0) == 5   # K % 8
+
+
+def test_noalloc_in_a_graph_replays_like_eager():
+    """Recorded under HIP graph capture, the use it exists for: a split-K call
+    captured once and replayed four times with alternating inputs. Between
+    replays an eager allocation-free call of another shape rewrites the shared
+    scratch, with device synchronisation around it. Every replay and every
+    eager call must equal its eager reference bitwise."""
+    import torch
+    M, N, K, dt, act = 256, 384, 4096, "f16", "gelu"
+    A = [synth.random_bits((M, K), dt, s) for s in (41, 42)]
+    B = synth.random_bits((K, N), dt, 43, scale=1 / 64)
+    bias = synth.random_bits((N,), dt, 44)
+    a = [to_dev(x, dt) for x in A]
+    b, bb = to_dev(B, dt), to_dev(bias, dt)
+    M2, N2, K2 = 128, 256, 8192
+    assert gba.workspace_size(M, N, K, act, dt) > 0 and gba.workspace_size(M2, N2, K2, "relu", "bf16") > 0
+    a2 = to_dev(synth.random_bits((M2, K2), "bf16", 45), "bf16")
+    b2 = to_dev(synth.random_bits((K2, N2), "bf16", 46, scale=1 / 64), "bf16")
+    refs = []
+    for i in range(2):
+        r = empty((M, N), dt, fill_bits=0x7E00)
+        gba.gemm_bias_act_noalloc(a[i], b, bb, r, act)
+        refs.append(r)
+    ref2 = empty((M2, N2), "bf16", fill_bits=0x7E00)
+    gba.gemm_bias_act_noalloc(a2, b2, None, ref2, "relu")
+    torch.cuda.synchronize()
+    for r in refs + [ref2]:
+        assert not (to_bits(r) == 0x7E00).any()
+
+    src, out, c2 = a[0].clone(), empty((M, N), dt), empty((M2, N2), "bf16")
+    graph = torch.cuda.CUDAGraph()
+    say("noalloc graph capture", M, N, K)
+    with torch.cuda.graph(graph):
+        gba.gemm_bias_act_noalloc(src, b, bb, out, act)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        i = rep % 2
+        src.copy_(a[i])
+        out.fill_(0.0)
+        c2.fill_(0.0)
+        gba.gemm_bias_act_noalloc(a2, b2, None, c2, "relu")   # eager, same scratch
+        torch.cuda.synchronize()
+        say("noalloc graph replay", rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), refs[i].view(torch.int16)), rep
+        assert torch.equal(c2.view(torch.int16), ref2.view(torch.int16)), rep
