@@ -130,3 +130,15 @@ def test_noalloc_in_a_graph_replays_like_eager():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), refs[i].view(torch.int16)), rep
         assert torch.equal(c2.view(torch.int16), ref2.view(torch.int16)), rep
+
+
+def test_noalloc_first_call_under_capture():
+    """In a fresh process, the device's first allocation-free call (which takes
+    the scratch's address) made under graph capture: replays equal eager."""
+    import os
+    import subprocess
+    import sys
+    child = os.path.join(os.path.dirname(os.path.abspath(__file__)), "noalloc_capture_child.py")
+    say("noalloc first call under capture (child process)")
+    r = subprocess.run([sys.executable, child], capture_output=True, text=True, timeout=180)
+    assert r.returncode == 0 and "replay equals eager: True" in r.stdout, (r.stdout[-2000:], r.stderr[-2000:])
