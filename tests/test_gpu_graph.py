@@ -1,5 +1,5 @@
-"""The transpose_B, transpose_A, 8-bit and split-K entry points captured into
-HIP graphs.
+"""The transpose_B, transpose_A, 8-bit and split-K entry points, and the
+unfused gemm / bias_act pair, captured into HIP graphs.
 
 None of them allocates, copies, fills or synchronises, so a caller can capture
 them. Replays, with eager work and device synchronisation between them and the
@@ -127,6 +127,50 @@ def test_transpose_a_replays_like_eager():
             o.fill_(0.0)
         ws.fill_(255)
         say("graph replay transpose_A", r)
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, ref in zip(outs, refs[i]):
+            assert torch.equal(o.view(torch.int16), ref.view(torch.int16)), r
+
+
+def test_unfused_pair_and_plain_gemms_replay_like_eager():
+    """gemm (B [K,N] and W [N,K]) and bias_act, the unfused pair, captured in
+    one graph: the intermediate C of gemm feeds bias_act inside the graph."""
+    import torch
+    M, N, K = 392, 520, 264
+    A = [synth.random_bits((M, K), "bf16", s) for s in (51, 52)]
+    B = synth.random_bits((K, N), "bf16", 53)
+    W = synth.random_bits((N, K), "bf16", 54)
+    bias = synth.random_bits((N,), "bf16", 55)
+    a = [to_dev(x, "bf16") for x in A]
+    b, w, bb = to_dev(B, "bf16"), to_dev(W, "bf16"), to_dev(bias, "bf16")
+
+    def run_all(x, mid, y, z):
+        gba.gemm(x, b, mid)
+        gba.bias_act(mid, bb, y, "softplus")
+        gba.gemm(x, w, z, transpose_b=True)
+
+    def bufs():
+        return (empty((M, N), "bf16"), empty((M, N), "bf16"), empty((M, N), "bf16"))
+
+    refs = []
+    for i in range(2):
+        outs = bufs()
+        run_all(a[i], *outs)
+        refs.append(outs)
+    torch.cuda.synchronize()
+    src, outs = a[0].clone(), bufs()
+    graph = torch.cuda.CUDAGraph()
+    say("graph capture: gemm, bias_act, gemm [N,K]")
+    with torch.cuda.graph(graph):
+        run_all(src, *outs)
+    torch.cuda.synchronize()
+    for r in range(4):
+        i = r % 2
+        src.copy_(a[i])
+        for o in outs:
+            o.fill_(0.0)
+        say("graph replay unfused", r)
         graph.replay()
         torch.cuda.synchronize()
         for o, ref in zip(outs, refs[i]):
