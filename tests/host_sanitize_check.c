@@ -1,4 +1,4 @@
-/* Host-side driver for the AddressSanitizer / UndefinedBehaviorSanitizer build
+/* Host-side check program for the AddressSanitizer / UndefinedBehaviorSanitizer build
  * of the library's host code (tests/test_host_sanitizers_cpu.py builds and runs
  * it). It exercises every path that needs no GPU:
  *   - version, build id and status strings;
@@ -10,9 +10,9 @@
  *     corrupt, truncated and oversized files, an unwritable directory,
  *     GBA_DISABLE_CACHE, and writers in several threads.
  * No call here should reach a launch: pointers are NULL or fail a host-side
- * check. As a second guard the driver runs only where no GPU is visible (exit
+ * check. As a second guard the program runs only where no GPU is visible (exit
  * 77 otherwise), since a check that wrongly passed would launch on dummy
- * pointers. Prints "host sanitize driver ok" and exits 0 when every check holds. */
+ * pointers. Prints "host sanitize check ok" and exits 0 when every check holds. */
 #define _GNU_SOURCE
 #include <math.h>
 #include <pthread.h>
@@ -296,7 +296,7 @@ int main(int argc, char **argv) {
     }
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) == 0 && ndev > 0) {
-        printf("a GPU is visible: this driver runs only without one\n");
+        printf("a GPU is visible: this check runs only without one\n");
         return 77;
     }
     snprintf(g_base, sizeof g_base, "%s", argv[1]);
@@ -306,9 +306,9 @@ int main(int argc, char **argv) {
     corrupt_caches();
     threaded_writers();
     if (g_fail) {
-        fprintf(stderr, "host sanitize driver: FAILED\n");
+        fprintf(stderr, "host sanitize check: FAILED\n");
         return 1;
     }
-    printf("host sanitize driver ok\n");
+    printf("host sanitize check ok\n");
     return 0;
 }

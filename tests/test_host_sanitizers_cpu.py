@@ -4,7 +4,7 @@ gba_api.hip (the C ABI: argument checks, schedule choice, the on-disk schedule
 cache and its file locking) is compiled again with both sanitizers on its host
 side only (-Xarch_host; the device code is built as usual and never runs
 here), linked with the other objects of the current build and with
-tests/host_sanitize_driver.c, and run without a GPU. The driver covers every
+tests/host_sanitize_check.c, and run without a GPU. The program covers every
 GPU-less path: argument errors of each entry point, the schedule table, and the
 cache with missing, corrupt, truncated and oversized files, an unwritable
 directory, GBA_DISABLE_CACHE and writers in several threads. Any sanitizer
@@ -38,7 +38,7 @@ def _objects():
 
 
 @pytest.fixture(scope="module")
-def driver(tmp_path_factory):
+def program(tmp_path_factory):
     for tool in (HIPCC, CLANG, CLANGXX):
         if not os.path.exists(tool):
             pytest.skip("ROCm compilers not installed")
@@ -59,21 +59,21 @@ def driver(tmp_path_factory):
     # The host objects really are instrumented.
     syms = subprocess.run(["nm", api], capture_output=True, text=True, check=True).stdout
     assert "__asan_report" in syms and "__ubsan_handle" in syms
-    drv_o = os.path.join(d, "driver.o")
+    prog_o = os.path.join(d, "check.o")
     r = subprocess.run([CLANG, "-O1", "-I" + os.path.join(ROOT, "include")] + SAN +
-                       ["-c", os.path.join(ROOT, "tests", "host_sanitize_driver.c"), "-o", drv_o],
+                       ["-c", os.path.join(ROOT, "tests", "host_sanitize_check.c"), "-o", prog_o],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
-    exe = os.path.join(d, "host_sanitize_driver")
-    r = subprocess.run([CLANGXX, "-fsanitize=address", "-fsanitize=undefined", drv_o, api] + objs +
+    exe = os.path.join(d, "host_sanitize_check")
+    r = subprocess.run([CLANGXX, "-fsanitize=address", "-fsanitize=undefined", prog_o, api] + objs +
                        ["-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-lpthread",
                         "-lm", "-o", exe], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
     return exe, d
 
 
-def test_host_code_is_clean_under_asan_and_ubsan(driver):
-    exe, d = driver
+def test_host_code_is_clean_under_asan_and_ubsan(program):
+    exe, d = program
     scratch = os.path.join(d, "scratch")
     shutil.rmtree(scratch, ignore_errors=True)
     os.makedirs(scratch)
@@ -87,7 +87,7 @@ def test_host_code_is_clean_under_asan_and_ubsan(driver):
     report = r.stdout + r.stderr
     assert "AddressSanitizer" not in report and "LeakSanitizer" not in report, report[-6000:]
     assert "runtime error" not in report, report[-6000:]
-    assert r.returncode == 0 and "host sanitize driver ok" in r.stdout, report[-6000:]
+    assert r.returncode == 0 and "host sanitize check ok" in r.stdout, report[-6000:]
     # every writer thread's entries reached the shared cache file
     with open(os.path.join(scratch, "threads", "schedules.json")) as f:
         assert len(f.read().splitlines()) == 2 + 8 * 24
